@@ -1,0 +1,290 @@
+"""Benchmark of the MISA indexer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the MISA indexer over one prefill chunk resident in
+HBM: block pooling -> head routing -> routed-head token scoring -> top-k
+(the four kernels misa_indexer launches, issued through the C ABI one stage
+at a time so that HIP events on the launch stream time every kernel).  The
+default workload is the long-context final prefill chunk: M = 8192 queries
+against N = 131072 fp8 keys, H_I = 64 heads, h = 8, B = 128, top-2048.
+
+Printed: one JSON line.  value = scored (query, key, head) triples per second
+(G/s) of the whole step; ms_per_step = indexer milliseconds per chunk;
+roofline = the dominant kernel against its MI355X peak; stages = every
+kernel's time and roofline fraction; misa_dagger and dense = the same chunk
+through the MISA-dagger pipeline (k' = 8192) and through the dense all-head
+DSA indexer, timed in the same run; cpu_baseline = the fp64 oracle on the
+host cores over a bounded sample of the same chunk.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "indexer ms per chunk & G(query·key·head)/s at M=8192,N=131K; MFMA util %"
+UNIT = "G(query·key·head)/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="final_chunk_m8k_n128k_fp8")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the MISA-dagger and dense timings")
+    p.add_argument("--cpu-queries", type=int, default=192, help="queries in the oracle timing sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per unit: 256 flops per scored triple,
+# 4 bytes per causal-valid logit written and read once, 132/256 bytes per key
+# ---------------------------------------------------------------------------
+
+def work(cfg, q_pos0):
+    M, N, H, h, B = cfg.q_per_seq, cfg.n_keys, cfg.n_heads, cfg.h, cfg.block
+    t = q_pos0 + np.arange(M, dtype=np.int64)
+    pairs = int((t + 1).sum()) * cfg.n_seq                       # causal (query, key) pairs
+    n_full = (t + 1) // B
+    blocks = int((n_full + ((t + 1) % B != 0)).sum()) * cfg.n_seq  # (query, block) pairs incl. tail
+    key_bytes = N * (128 + 4 if cfg.kdtype == 1 else 256) * cfg.n_seq
+    return dict(
+        pairs=pairs,
+        triples=pairs * h,
+        score_flops=pairs * h * 256,
+        score_bytes=pairs * 4,
+        dense_flops=pairs * H * 256,
+        route_flops=blocks * H * 256,
+        route_bytes=cfg.n_seq * M * H * (256 + 4) + cfg.n_seq * (N // B) * 512 + cfg.n_seq * M * 512,
+        pool_bytes=key_bytes + cfg.n_seq * (N // B) * 512 + cfg.n_seq * M * 512,
+        topk_bytes=pairs * 4 + cfg.n_seq * M * cfg.topk * 8,
+    )
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_sparse_block_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "score": ("score.hip", "misa_common.h"),
+    "topk": ("topk.hip", "misa_common.h"),
+    "route": ("route.hip", "misa_common.h"),
+    "pool": ("pool.hip", "misa_common.h"),
+}
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload, {}).get(stage)
+    if not ent or ent.get("source_hash") != src_hash(*KERNEL_SOURCES[stage]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the indexer shards by query across GPUs "
+                                   "with no exchange (see DESIGN.md), but only the 1-GPU path is "
+                                   "built and measured; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    import long_context_sparse_block_amd as lcsb
+    from long_context_sparse_block_amd import inputs as gen
+
+    cfg = gen.CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    inp = gen.generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    lcsb.load()
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(inp.w).to(dev)
+    if inp.k_scale is None:
+        k = torch.from_numpy(inp.k.view(np.int16)).to(dev).view(torch.bfloat16)
+        ks = None
+    else:
+        k = torch.from_numpy(inp.k).to(dev)
+        ks = torch.from_numpy(inp.k_scale).to(dev)
+    sh = lcsb.make_shape(cfg.n_seq, cfg.q_per_seq, cfg.n_keys, inp.q_pos0, cfg.n_heads, cfg.block)
+    S, M, N, H, h, B, K = cfg.n_seq, cfg.q_per_seq, cfg.n_keys, cfg.n_heads, cfg.h, cfg.block, cfg.topk
+    ld = (N + 3) // 4 * 4
+    n_full = N // B
+    pooled = torch.empty((S, max(n_full, 1), 128), dtype=torch.float32, device=dev)
+    tail = torch.empty((S, M, 128), dtype=torch.float32, device=dev)
+    heads = torch.empty((S, M, h), dtype=torch.int32, device=dev)
+    logits = torch.empty((S, M, ld), dtype=torch.float32, device=dev)
+    idx = torch.empty((S, M, K), dtype=torch.int32, device=dev)
+    vals = torch.empty((S, M, K), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    W = work(cfg, inp.q_pos0)
+
+    def run_timed(stages, steps, warmup):
+        """stages: list of (name, fn).  Returns per-stage mean ms and step ms."""
+        for _ in range(warmup):
+            for _, fn in stages:
+                fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for s in range(steps):
+            evs[s][0].record(stream)
+            for j, (_, fn) in enumerate(stages):
+                fn()
+                evs[s][j + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - wall0) * 1e3 / steps
+        per = {}
+        for j, (name, _) in enumerate(stages):
+            per[name] = float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(steps)]))
+        step_ev = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
+        return per, step_ev, wall
+
+    misa_stages = [
+        ("pool", lambda: lcsb.misa_pool_keys(sh, k, ks, pooled=pooled, tail=tail)),
+        ("route", lambda: lcsb.misa_route_heads(sh, q, w, pooled[:, :n_full], tail, h, heads=heads)),
+        ("score", lambda: lcsb.misa_sparse_head_logits(sh, q, w, k, heads, k_scale=ks, logits=logits)),
+        ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals)),
+    ]
+    per, step_ms, wall_ms = run_timed(misa_stages, args.steps, args.warmup)
+    print(f"[bench] MISA step {step_ms:.3f} ms (wall {wall_ms:.3f}) {per}", file=sys.stderr, flush=True)
+
+    def roof(stage, ms):
+        if stage == "score":
+            a = W["score_flops"] / (ms * 1e-3) / 1e12
+            r = dict(bound="mfma", achieved=a, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+        elif stage == "route":
+            a = W["route_flops"] / (ms * 1e-3) / 1e12
+            r = dict(bound="mfma", achieved=a, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+        else:
+            nbytes = W["pool_bytes"] if stage == "pool" else W["topk_bytes"]
+            a = nbytes / (ms * 1e-3) / 1e9
+            r = dict(bound="hbm", achieved=a, peak=PEAK_HBM_GBS, unit="GB/s")
+        r["frac"] = r["achieved"] / r["peak"]
+        r["traffic"] = measured_traffic(stage, cfg.name) if stage in KERNEL_SOURCES else None
+        r["ms"] = ms
+        return r
+
+    stages_out = {name: roof(name, ms) for name, ms in per.items()}
+    dominant = max(per, key=per.get)
+    roofline = {kk: v for kk, v in stages_out[dominant].items() if kk != "ms"}
+    roofline["kernel"] = dominant
+    # the scoring kernel also streams the logits out: report that rate beside its MFMA rate
+    stages_out["score"]["logit_write_GBs"] = W["score_bytes"] / (per["score"] * 1e-3) / 1e9
+
+    extras = {}
+    if not args.no_extras:
+        kp = 8192
+        cand = torch.empty((S, M, kp), dtype=torch.int32, device=dev)
+        dlog = torch.empty((S, M, kp), dtype=torch.float32, device=dev)
+        dagger_stages = misa_stages[:3] + [
+            ("topk_kprime", lambda: lcsb.misa_topk(sh, logits, kp, idx=cand, want_vals=False)),
+            ("rerank", lambda: lcsb.dsa_dense_logits(sh, q, w, k, k_scale=ks, cand=cand, logits=dlog)),
+            ("topk_final", lambda: lcsb.misa_topk(sh, dlog, K, cand=cand, idx=idx, vals=vals)),
+        ]
+        dper, dstep, _ = run_timed(dagger_stages, max(3, args.steps // 4), 2)
+        extras["misa_dagger"] = dict(k_prime=kp, ms_per_step=dstep, stage_ms=dper,
+                                     rerank_TFLOPs=S * M * kp * H * 256 / (dper["rerank"] * 1e-3) / 1e12)
+        dense_stages = [
+            ("dense_score", lambda: lcsb.dsa_dense_logits(sh, q, w, k, k_scale=ks, logits=logits)),
+            ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals)),
+        ]
+        nper, nstep, _ = run_timed(dense_stages, max(3, args.steps // 4), 2)
+        extras["dense"] = dict(ms_per_step=nstep, stage_ms=nper,
+                               dense_score_TFLOPs=W["dense_flops"] / (nper["dense_score"] * 1e-3) / 1e12,
+                               dense_score_frac=W["dense_flops"] / (nper["dense_score"] * 1e-3) / 1e12
+                               / PEAK_BF16_TFLOPS,
+                               misa_speedup=nstep / step_ms)
+        print(f"[bench] dagger {dstep:.3f} ms {dper}; dense {nstep:.3f} ms {nper}", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_queries, W)
+
+    value = W["triples"] / (step_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian q/k/w with planted head-block affinity)",
+        "config": {"workload": cfg.name, "n_seq": S, "M": M, "N": N, "H_I": H, "h": h, "B": B, "topk": K,
+                   "k_dtype": "fp8_e4m3" if cfg.kdtype == 1 else "bf16", "head_dim": 128},
+        "roofline": roofline,
+        "stages": stages_out,
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line))
+
+
+def cpu_baseline(inp, n_queries, W):
+    """The fp64 oracle, as it stands, on a sample of the chunk's queries."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:   # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    cfg = inp.cfg
+    M = cfg.q_per_seq
+    rows = np.unique(np.linspace(0, M - 1, min(n_queries, M)).round().astype(int))
+    t0 = time.perf_counter()
+    ctx = oracle.SeqContext(inp, 0)
+    t_setup = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for i in rows:
+        ctx.misa(int(i), cfg.h, cfg.topk)
+    t_rows = time.perf_counter() - t1
+    per_chunk = (t_setup + t_rows * M / len(rows)) * cfg.n_seq
+    return dict(value=W["triples"] / per_chunk / 1e9, unit=UNIT, cores=int(threads), kind="oracle",
+                seconds_per_chunk_extrapolated=per_chunk, sample_seconds=t_setup + t_rows,
+                sample=f"{len(rows)} evenly spaced of {M} queries of sequence 0 (key widening + pooling of "
+                       f"the whole sequence, then route/score/top-k per sampled query), extrapolated "
+                       f"linearly to the chunk",
+                host_cpus=os.cpu_count(), affinity=len(os.sched_getaffinity(0)))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * misa.h -- C ABI of the MISA (Mixture of Indexer Sparse Attention) indexer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The indexer picks, for every query token, the top-k prefix tokens that
+ * DSA-style sparse attention will attend to.  MISA replaces the dense
+ * all-head DSA indexer with four stages (gist.science technical summary of
+ * "MISA: Mixture of Indexer Sparse Attention for Long-Context LLM Inference",
+ * "Metodologia: MISA" items 1-2; agents-report summary, method overview):
+ *
+ *   misa_pool_keys          block mean-pooling of the shared indexer keys
+ *   misa_route_heads        block-summary router: top-h indexer heads per query
+ *   misa_sparse_head_logits token scoring with the routed heads only
+ *   misa_topk               per-query top-k token selection
+ *
+ * plus the whole pipeline (misa_indexer, optionally the hierarchical
+ * MISA-dagger variant of "Variante Hierárquica (MISA†)") and the dense DSA
+ * indexer that MISA replaces (dsa_dense_logits; the baseline path named in
+ * the GitHub issue "Clarification on the Figure 3 baseline ...").
+ *
+ * Token score (the DSA indexer score, DeepSeek-V3.2 lightning indexer):
+ *     I[t, s] = sum_{j in heads(t)} w[t, j] * ReLU(q[t, j] . k[s] * sigma[s])
+ * for every prefix key s <= t, and -inf for s > t.  sigma[s] is the per-token
+ * scale of an fp8 key cache and 1 for bf16 keys.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory   All tensor pointers are DEVICE pointers owned by the caller.  The
+ *          library never allocates, frees or synchronises; scratch space comes
+ *          only from a caller-provided workspace.  Every tensor is densely
+ *          packed in the layout given (row-major, last index fastest) and
+ *          16-byte aligned.
+ * Streams  `stream` is a hipStream_t passed as void* (NULL = the default
+ *          stream).  Every call only enqueues work on it and returns.
+ * Errors   Arguments are checked on the host before anything is enqueued; a
+ *          bad argument returns a negative misa_status and enqueues nothing.
+ *          A failed kernel launch returns MISA_ERR_HIP.  No C++ exception
+ *          crosses this interface; there is no mutable global state, so calls
+ *          from several host threads are safe.
+ * Numerics Preconditions that are documented, not checked: inputs are finite;
+ *          fp8 scales are > 0.  Accumulation is fp32.
+ * Shapes   A call covers n_seq independent sequences.  Sequence b has n_keys
+ *          keys (positions 0..n_keys-1) and q_per_seq queries; query i of a
+ *          sequence sits at absolute position t = q_pos0 + i and sees the keys
+ *          0..t (causal).  Prefill chunk: n_seq = 1, q_pos0 = n_keys - M.
+ *          Decode batch: q_per_seq = 1, q_pos0 = n_keys - 1.
+ * Blocks   Block m covers key positions [m*B, (m+1)*B).  For query t the
+ *          prefix holds floor((t+1)/B) complete blocks and, when (t+1) % B != 0,
+ *          one partial block [floor((t+1)/B)*B, t] (its "tail").
+ */
+#ifndef MISA_H
+#define MISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MISA_OK = 0,
+  MISA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad alignment */
+  MISA_ERR_UNSUPPORTED = -2,   /* a valid request outside what is implemented */
+  MISA_ERR_WORKSPACE = -3,     /* workspace missing or too small */
+  MISA_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
+} misa_status;
+
+typedef enum {
+  MISA_K_BF16 = 0,             /* k: uint16 bf16 bits [n_seq][n_keys][128] */
+  MISA_K_FP8_E4M3 = 1          /* k: uint8 OCP e4m3fn codes [n_seq][n_keys][128],
+                                  k_scale: float [n_seq][n_keys], > 0 */
+} misa_kdtype;
+
+typedef struct {
+  int32_t n_seq;      /* independent sequences, >= 1 */
+  int32_t q_per_seq;  /* M: queries per sequence, >= 0 (0 = nothing to do) */
+  int64_t n_keys;     /* N: keys per sequence, >= 1 */
+  int64_t q_pos0;     /* position of query 0; 0 <= q_pos0 and q_pos0 + M <= N */
+  int32_t n_heads;    /* H: indexer heads (H_I on the pages), 1..64 */
+  int32_t head_dim;   /* d: must be 128 */
+  int32_t block;      /* B: pooling block size, >= 1 */
+} misa_shape;
+
+#define MISA_HEAD_DIM 128
+#define MISA_MAX_HEADS 64
+#define MISA_MAX_TOPK 8192
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* misa_status_str(misa_status s);
+
+/*
+ * Block mean-pooling of the shared indexer keys (gist.science summary,
+ * "Metodologia: MISA" item 1: mean-pooled indexer keys per block;
+ * agents-report: one summary key per block of the prefix).
+ *   pooled[b][m][:] = mean(key[b][m*B .. m*B+B-1][:])   for m < floor(N/B)
+ *   tail[b][i][:]   = mean(key[b][floor((t+1)/B)*B .. t][:]),  t = q_pos0+i,
+ *                     or all zeros when (t+1) % B == 0 (no partial block).
+ * key = bf16 value, or e4m3 value * k_scale.  fp32 sums in key order.
+ * k: see misa_kdtype.  k_scale: NULL for bf16, required for fp8.
+ * pooled: float [n_seq][floor(N/B)][128] (not touched when floor(N/B) = 0).
+ * tail:   float [n_seq][M][128].
+ */
+misa_status misa_pool_keys(const misa_shape* shape, const void* k, misa_kdtype kdtype,
+                           const float* k_scale, float* pooled, float* tail, void* stream);
+
+/*
+ * Head router (gist.science summary, "Metodologia: MISA" item 1: per-head
+ * affinities against the pooled keys, aggregated into a per-head importance,
+ * top-h heads kept; agents-report: MISA aggregates along the blocks to pick
+ * heads).  For query t of sequence b and head j:
+ *   S[j] = sum_{m < floor((t+1)/B)} ReLU(q[t,j] . pooled[m]) + ReLU(q[t,j] . tail[t])
+ *          (the tail term only when the partial block is non-empty)
+ *   r[j] = w[t,j] * S[j]
+ *   heads[b][i][:] = the h heads with the largest r (equal r -> lower head id),
+ *                    stored in ascending head order.
+ * q: uint16 bf16 bits [n_seq][M][H][128].  w: float [n_seq][M][H].
+ * pooled, tail: as written by misa_pool_keys.  1 <= h <= H.
+ * heads: int32 [n_seq][M][h].  scores: float [n_seq][M][H] receives r, or NULL.
+ */
+misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const float* w,
+                             const float* pooled, const float* tail, int32_t h,
+                             int32_t* heads, float* scores, void* stream);
+
+/*
+ * Token scoring with the routed heads only (gist.science summary,
+ * "Metodologia: MISA" item 2: only the h active heads score the whole prefix
+ * token by token).
+ *   logits[b][i][s] = sum_{j in heads[b][i]} w[t,j] * ReLU(q[t,j] . k[s] * sigma[s])
+ *                     for s <= t,   -inf for t < s < N.   Columns N..ld-1 untouched.
+ * heads: int32 [n_seq][M][h], ascending, distinct, each in [0, H).  1 <= h <= H.
+ * logits: float [n_seq][M][ld]; ld >= N and ld % 4 == 0.
+ */
+misa_status misa_sparse_head_logits(const misa_shape* shape, const uint16_t* q, const float* w,
+                                    const void* k, misa_kdtype kdtype, const float* k_scale,
+                                    const int32_t* heads, int32_t h, float* logits, int64_t ld,
+                                    void* stream);
+
+/*
+ * The dense DSA indexer: the token score with all H heads (the baseline MISA
+ * replaces; the abstract of arXiv 2605.07363 and the GitHub issue's dense
+ * all-head path).
+ * cand == NULL:  logits[b][i][s] over every key, exactly as
+ *                misa_sparse_head_logits with heads = 0..H-1 (and bitwise equal
+ *                to it); ld >= N, ld % 4 == 0.
+ * cand != NULL:  re-rank mode of MISA-dagger ("Variante Hierárquica (MISA†)":
+ *                the original all-head indexer re-scores only the candidates).
+ *                cand: int32 [n_seq][M][n_cand] token ids (any order; -1 = no
+ *                candidate); logits[b][i][c] = score of token cand[b][i][c]
+ *                (-inf where cand < 0); ld >= n_cand, ld % 4 == 0.  Every
+ *                candidate id must be in [0, t].  Each value is bitwise equal
+ *                to the cand == NULL value of the same (query, token).
+ */
+misa_status dsa_dense_logits(const misa_shape* shape, const uint16_t* q, const float* w,
+                             const void* k, misa_kdtype kdtype, const float* k_scale,
+                             const int32_t* cand, int32_t n_cand, float* logits, int64_t ld,
+                             void* stream);
+
+/*
+ * Per-query top-k token selection (the selection step after scoring; the
+ * issue's pipeline runs it as a separate top-k over the returned logits).
+ * Order: value descending; equal values (with -0.0 == +0.0) -> lower token id.
+ * cand == NULL:  row i of sequence b considers columns s in [0, min(n_cols, t+1));
+ *                the token id is the column.
+ * cand != NULL:  row considers columns c in [0, n_cols) with cand[b][i][c] >= 0;
+ *                the token id is cand[b][i][c] (ids distinct within a row).
+ * idx:  int32 [n_seq][M][k]; rows with fewer than k candidates are padded with -1.
+ * vals: float [n_seq][M][k] (the selected values, -inf padding), or NULL.
+ * 1 <= k <= MISA_MAX_TOPK.  logits: float [n_seq][M][ld], ld % 4 == 0, ld >= n_cols.
+ * ws / ws_bytes: workspace of at least misa_topk_workspace_bytes() bytes
+ *                (may be NULL when that is 0).
+ */
+misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld,
+                      const int32_t* cand, int32_t n_cols, int32_t k, int32_t* idx,
+                      float* vals, void* ws, size_t ws_bytes, void* stream);
+
+size_t misa_topk_workspace_bytes(const misa_shape* shape, int32_t n_cols, int32_t k);
+
+/*
+ * The whole indexer on the caller's stream: pool -> route -> routed scoring ->
+ * top-k (k_prime == 0, MISA), or pool -> route -> routed scoring -> top-k' ->
+ * all-head re-rank of the k' candidates -> top-k (k_prime >= topk, MISA-dagger;
+ * "Variante Hierárquica (MISA†)" of the gist.science summary).
+ * idx: int32 [n_seq][M][topk], vals: float [n_seq][M][topk] or NULL.
+ * 1 <= h <= H; 1 <= topk <= MISA_MAX_TOPK; k_prime == 0 or topk <= k_prime <= MISA_MAX_TOPK.
+ * ws / ws_bytes: at least misa_indexer_workspace_bytes() bytes (holds the
+ * pooled keys, tails, routed heads and the fp32 logits of the chunk).
+ */
+misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                         misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
+                         int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
+                         void* stream);
+
+size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk,
+                                    int32_t k_prime);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MISA_H */

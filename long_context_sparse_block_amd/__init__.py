@@ -1,0 +1,11 @@
+"""MISA (Mixture of Indexer Sparse Attention) indexer for AMD Instinct MI355X.
+
+The compute path is libmisa.so (hand-written HIP kernels for gfx950 behind a
+C ABI, include/misa.h); this package is its Python binding plus the seeded
+synthetic input generator.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED, MAX_TOPK, MisaError, MisaShape, dsa_dense_logits, load, make_shape, misa_indexer,
+    misa_indexer_workspace_bytes, misa_pool_keys, misa_route_heads, misa_sparse_head_logits, misa_topk,
+    status_str,
+)

@@ -1,0 +1,72 @@
+"""Build libmisa.so (HIP kernels + C ABI) for gfx950, in-tree.
+
+    python -m long_context_sparse_block_amd.build
+
+Every HIP source is compiled with hipcc for gfx950 only.  Packed-fp32 VALU
+instructions are switched off for device code (-packed-fp32-ops); the host
+pass prints a harmless warning that it does not know that feature.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmisa.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.isabs(cand) and os.path.exists(cand) or not os.path.isabs(cand)):
+            return cand
+    return "hipcc"
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build_library(verbose: bool = False, extra=()) -> str:
+    objs = []
+    obj_dir = os.path.join(PKG, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    common = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-I", INCLUDE, "-I", CSRC, *extra]
+    procs = []
+    for src in sources():
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        cmd = common + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, cmd, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        text = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append((src, text))
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        msg = "\n\n".join(f"== {s}\n{t}" for s, t in failed)
+        raise RuntimeError(f"hipcc failed:\n{msg}")
+    tmp = LIB + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose="-v" in sys.argv))

@@ -1,0 +1,226 @@
+// extern "C" entry points of libmisa: argument validation on the host, then
+// asynchronous launches on the caller's stream.  Nothing here allocates,
+// frees or synchronises; the indexer carves its scratch from the caller's
+// workspace.
+#include <stdint.h>
+#include <string.h>
+
+#include "misa.h"
+#include "misa_launch.h"
+
+namespace {
+
+using misa::launch_pool;
+using misa::launch_route;
+using misa::launch_score;
+using misa::launch_score_gather;
+using misa::launch_topk;
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+misa_status check_shape(const misa_shape* s) {
+  if (s == nullptr) return MISA_ERR_INVALID_ARG;
+  if (s->n_seq < 1 || s->q_per_seq < 0 || s->n_keys < 1 || s->q_pos0 < 0) return MISA_ERR_INVALID_ARG;
+  if (s->q_pos0 + s->q_per_seq > s->n_keys) return MISA_ERR_INVALID_ARG;
+  if (s->n_heads < 1 || s->n_heads > MISA_MAX_HEADS) return MISA_ERR_INVALID_ARG;
+  if (s->head_dim != MISA_HEAD_DIM) return MISA_ERR_UNSUPPORTED;
+  if (s->block < 1) return MISA_ERR_INVALID_ARG;
+  // grid dimensions and 32-bit row counters
+  if (s->n_keys > (int64_t)1 << 30) return MISA_ERR_UNSUPPORTED;
+  if (s->n_seq > 65535) return MISA_ERR_UNSUPPORTED;
+  return MISA_OK;
+}
+
+misa_status check_keys(const void* k, misa_kdtype kdtype, const float* k_scale) {
+  if (kdtype != MISA_K_BF16 && kdtype != MISA_K_FP8_E4M3) return MISA_ERR_INVALID_ARG;
+  if (k == nullptr || !aligned16(k)) return MISA_ERR_INVALID_ARG;
+  if (kdtype == MISA_K_FP8_E4M3 && k_scale == nullptr) return MISA_ERR_INVALID_ARG;
+  return MISA_OK;
+}
+
+inline misa_status from_hip(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
+
+#define MISA_TRY(expr)                 \
+  do {                                 \
+    misa_status _st = (expr);          \
+    if (_st != MISA_OK) return _st;    \
+  } while (0)
+
+struct IndexerLayout {
+  size_t pooled, tail, heads, logits, cand, dlog, topk_ws, total;
+  int64_t ld, ld_d;
+};
+
+IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime) {
+  IndexerLayout L{};
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  const int64_t n_full = s.n_keys / s.block;
+  L.ld = (s.n_keys + 3) / 4 * 4;
+  L.ld_d = (k_prime + 3) / 4 * 4;
+  size_t off = 0;
+  L.pooled = off;
+  off += align_up((size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(float));
+  L.tail = off;
+  off += align_up((size_t)rows * MISA_HEAD_DIM * sizeof(float));
+  L.heads = off;
+  off += align_up((size_t)rows * h * sizeof(int32_t));
+  L.logits = off;
+  off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
+  const int first_k = k_prime > 0 ? k_prime : topk;
+  if (k_prime > 0) {
+    L.cand = off;
+    off += align_up((size_t)rows * k_prime * sizeof(int32_t));
+    L.dlog = off;
+    off += align_up((size_t)rows * (size_t)L.ld_d * sizeof(float));
+  }
+  L.topk_ws = off;
+  size_t tw = misa::topk_workspace_bytes(s, (int)s.n_keys, first_k);
+  if (k_prime > 0) {
+    size_t tw2 = misa::topk_workspace_bytes(s, k_prime, topk);
+    if (tw2 > tw) tw = tw2;
+  }
+  off += align_up(tw);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* misa_status_str(misa_status s) {
+  switch (s) {
+    case MISA_OK: return "MISA_OK";
+    case MISA_ERR_INVALID_ARG: return "MISA_ERR_INVALID_ARG: invalid argument";
+    case MISA_ERR_UNSUPPORTED: return "MISA_ERR_UNSUPPORTED: request outside what is implemented";
+    case MISA_ERR_WORKSPACE: return "MISA_ERR_WORKSPACE: workspace missing or too small";
+    case MISA_ERR_HIP: return "MISA_ERR_HIP: HIP runtime error";
+  }
+  return "MISA: unknown status";
+}
+
+misa_status misa_pool_keys(const misa_shape* shape, const void* k, misa_kdtype kdtype,
+                           const float* k_scale, float* pooled, float* tail, void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  const int64_t n_full = shape->n_keys / shape->block;
+  if ((n_full > 0 && (pooled == nullptr || !aligned16(pooled))) || tail == nullptr || !aligned16(tail))
+    return MISA_ERR_INVALID_ARG;
+  if (shape->q_per_seq == 0 && n_full == 0) return MISA_OK;
+  return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, (hipStream_t)stream));
+}
+
+misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const float* w,
+                             const float* pooled, const float* tail, int32_t h, int32_t* heads,
+                             float* scores, void* stream) {
+  MISA_TRY(check_shape(shape));
+  if (q == nullptr || !aligned16(q) || w == nullptr || tail == nullptr || !aligned16(tail) ||
+      heads == nullptr)
+    return MISA_ERR_INVALID_ARG;
+  if (shape->n_keys / shape->block > 0 && (pooled == nullptr || !aligned16(pooled)))
+    return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return from_hip(launch_route(*shape, q, w, pooled, tail, h, heads, scores, (hipStream_t)stream));
+}
+
+misa_status misa_sparse_head_logits(const misa_shape* shape, const uint16_t* q, const float* w,
+                                    const void* k, misa_kdtype kdtype, const float* k_scale,
+                                    const int32_t* heads, int32_t h, float* logits, int64_t ld,
+                                    void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (q == nullptr || !aligned16(q) || w == nullptr || heads == nullptr || logits == nullptr ||
+      !aligned16(logits))
+    return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (ld < shape->n_keys || (ld & 3) != 0) return MISA_ERR_INVALID_ARG;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return from_hip(launch_score(*shape, q, w, k, kdtype, k_scale, heads, h, logits, ld, (hipStream_t)stream));
+}
+
+misa_status dsa_dense_logits(const misa_shape* shape, const uint16_t* q, const float* w,
+                             const void* k, misa_kdtype kdtype, const float* k_scale,
+                             const int32_t* cand, int32_t n_cand, float* logits, int64_t ld,
+                             void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (q == nullptr || !aligned16(q) || w == nullptr || logits == nullptr || !aligned16(logits))
+    return MISA_ERR_INVALID_ARG;
+  if ((ld & 3) != 0) return MISA_ERR_INVALID_ARG;
+  if (cand == nullptr) {
+    if (ld < shape->n_keys) return MISA_ERR_INVALID_ARG;
+    if (shape->q_per_seq == 0) return MISA_OK;
+    return from_hip(launch_score(*shape, q, w, k, kdtype, k_scale, nullptr, shape->n_heads, logits, ld,
+                                 (hipStream_t)stream));
+  }
+  if (n_cand < 1 || ld < n_cand) return MISA_ERR_INVALID_ARG;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return from_hip(launch_score_gather(*shape, q, w, k, kdtype, k_scale, cand, n_cand, logits, ld,
+                                      (hipStream_t)stream));
+}
+
+size_t misa_topk_workspace_bytes(const misa_shape* shape, int32_t n_cols, int32_t k) {
+  if (check_shape(shape) != MISA_OK) return 0;
+  return misa::topk_workspace_bytes(*shape, n_cols, k);
+}
+
+misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld, const int32_t* cand,
+                      int32_t n_cols, int32_t k, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
+                      void* stream) {
+  MISA_TRY(check_shape(shape));
+  if (logits == nullptr || !aligned16(logits) || idx == nullptr) return MISA_ERR_INVALID_ARG;
+  if (k < 1 || k > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
+  if (n_cols < 1 || ld < n_cols || (ld & 3) != 0) return MISA_ERR_INVALID_ARG;
+  if (cand != nullptr && !aligned16(cand)) return MISA_ERR_INVALID_ARG;
+  const size_t need = misa::topk_workspace_bytes(*shape, n_cols, k);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return from_hip(launch_topk(*shape, logits, ld, cand, n_cols, k, idx, vals, ws, ws_bytes,
+                              (hipStream_t)stream));
+}
+
+size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
+  return indexer_layout(*shape, h, topk, k_prime).total;
+}
+
+misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                         misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
+                         int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
+                         void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (q == nullptr || !aligned16(q) || w == nullptr || idx == nullptr) return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
+  if (k_prime != 0 && (k_prime < topk || k_prime > MISA_MAX_TOPK)) return MISA_ERR_INVALID_ARG;
+  const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  char* base = static_cast<char*>(ws);
+  float* pooled = reinterpret_cast<float*>(base + L.pooled);
+  float* tail = reinterpret_cast<float*>(base + L.tail);
+  int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
+  float* logits = reinterpret_cast<float*>(base + L.logits);
+  void* tws = base + L.topk_ws;
+  const size_t tws_bytes = L.total - L.topk_ws;
+  MISA_TRY(from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, st)));
+  MISA_TRY(from_hip(launch_route(*shape, q, w, pooled, tail, h, heads, nullptr, st)));
+  MISA_TRY(from_hip(launch_score(*shape, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, st)));
+  if (k_prime == 0)
+    return from_hip(launch_topk(*shape, logits, L.ld, nullptr, (int)shape->n_keys, topk, idx, vals, tws,
+                                tws_bytes, st));
+  int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
+  float* dlog = reinterpret_cast<float*>(base + L.dlog);
+  MISA_TRY(from_hip(launch_topk(*shape, logits, L.ld, nullptr, (int)shape->n_keys, k_prime, cand, nullptr,
+                                tws, tws_bytes, st)));
+  MISA_TRY(from_hip(launch_score_gather(*shape, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
+  return from_hip(launch_topk(*shape, dlog, L.ld_d, cand, k_prime, topk, idx, vals, tws, tws_bytes, st));
+}
+
+}  // extern "C"

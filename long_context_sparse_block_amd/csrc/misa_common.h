@@ -1,0 +1,88 @@
+// Device-side building blocks shared by the MISA kernels (gfx950 / CDNA4).
+//
+// Wavefronts are 64 lanes.  Matrix work uses v_mfma_f32_16x16x32_bf16, whose
+// operand layout (per lane l of the wave) is:
+//   A (16 rows x 32 k):  lane l supplies row l%16, k = 8*(l/16) .. 8*(l/16)+7
+//   B (32 k x 16 cols):  lane l supplies col l%16, k = 8*(l/16) .. 8*(l/16)+7
+//   D (16 x 16, fp32):   lane l holds rows 4*(l/16)+i (i = 0..3) of col l%16
+// so one MFMA consumes 16 bytes of A and 16 bytes of B per lane, and a full
+// 128-wide dot product is 4 MFMAs ("k-steps") accumulated in order 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace misa {
+
+constexpr int kWave = 64;
+constexpr int kD = 128;          // indexer head dim
+constexpr int kKSteps = kD / 32;  // MFMA k-steps per dot product
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// OCP e4m3fn -> bf16 is exact (3-bit mantissa inside bf16's 7 bits, exponent
+// range inside bf16's).  The hardware converter widens two codes to fp32; the
+// top half of an fp32 whose value is bf16-representable is that bf16.
+// Four codes (one dword) -> four bf16 (two dwords).
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t codes) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+  uint2 r;
+  r.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+  r.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
+  return r;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false);
+  return v.x;
+}
+
+// Canonical per-(query, key) reduction of one quad of four head terms:
+//   p = fma(w3, relu(x3), fma(w2, relu(x2), fma(w1, relu(x1), fma(w0, relu(x0), 0))))
+// Every kernel that must agree bitwise with another uses exactly this chain.
+__device__ __forceinline__ float quad_chain(const f32x4 x, float w0, float w1, float w2, float w3) {
+  float p = 0.0f;
+  p = __builtin_fmaf(w0, __builtin_fmaxf(x[0], 0.0f), p);
+  p = __builtin_fmaf(w1, __builtin_fmaxf(x[1], 0.0f), p);
+  p = __builtin_fmaf(w2, __builtin_fmaxf(x[2], 0.0f), p);
+  p = __builtin_fmaf(w3, __builtin_fmaxf(x[3], 0.0f), p);
+  return p;
+}
+
+// Order-preserving map float -> uint32 (larger float <=> larger key), with
+// -0.0 folded onto +0.0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+// Hardware dispatches workgroup i of a launch to XCD (i mod 8).  Remap the
+// linear id so that each XCD walks a contiguous range of logical tiles (tiles
+// that share key data then share that XCD's L2).
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
+  constexpr int64_t kXcds = 8;
+  int64_t per = total / kXcds;
+  if (i < per * kXcds) return (i % kXcds) * per + i / kXcds;
+  return i;
+}
+
+}  // namespace misa

@@ -1,0 +1,230 @@
+// Block-summary head router.
+//
+// Method (gist.science summary of MISA, "Metodologia: MISA" item 1;
+// agents-report summary, method overview and the HISA comparison): every
+// indexer head is scored against the mean-pooled block keys, the per-block
+// affinities are aggregated along the blocks into one importance per head,
+// and the top-h heads are kept for the query.  Reading taken here:
+//   S[t,j] = sum_{complete blocks m of t's prefix} ReLU(q[t,j] . pooled[m])
+//            + ReLU(q[t,j] . tail[t])      (partial block, when non-empty)
+//   r[t,j] = w[t,j] * S[t,j];  heads(t) = top-h of r, equal r -> lower j.
+//
+// Design.  The (query, head) x (block) products are a dense contraction, so
+// they run on bf16 MFMA: q is bf16 already, and each fp32 pooled key is split
+// exactly-enough into hi + lo bf16 parts (p - hi is exact in fp32; |p - hi -
+// lo| <= 2^-16 |p|), so q.p = q.hi + q.lo is accumulated by two MFMAs into
+// the same fp32 accumulator.  A wave owns 4 queries x 16 heads (four 16x16
+// row blocks: row r = query r/4, head 4*rb + r%4), keeps its q fragments in
+// registers and streams 64-block chunks of pooled keys staged once per
+// workgroup in LDS.  ReLU, the causal block mask and the block sum stay in
+// registers; the tail term is an fp32 dot per (query, head); the top-h
+// selection is a rank count over <= 64 values, one wave per query.
+#include "misa_common.h"
+#include "misa_launch.h"
+
+namespace misa {
+
+constexpr int kRouteChunk = 64;            // pooled rows staged per step
+constexpr int kRowStride = kD + 8;          // bf16 elements per LDS row (16 B pad)
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int NHC>  // 16-head chunks per query group (= ceil(H/16))
+__global__ void __launch_bounds__(256) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                               const float* __restrict__ pooled,
+                                               const float* __restrict__ tail,
+                                               int32_t* __restrict__ heads, float* __restrict__ scores,
+                                               int64_t q_pos0, int M, int H, int B, int h,
+                                               int64_t n_full_total) {
+  constexpr int QG = (NHC == 1) ? 4 : (NHC == 2 ? 2 : 1);  // query groups per workgroup
+  constexpr int NW = NHC * QG;                              // waves per workgroup
+  constexpr int QWG = 4 * QG;                               // queries per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[kRouteChunk * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lo[kRouteChunk * kRowStride];
+  __shared__ float s_r[QWG][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qg = wave / NHC;
+  const int hc = wave % NHC;
+  const int b = blockIdx.y;
+  const int q0_wg = blockIdx.x * QWG;
+  const int q0w = q0_wg + qg * 4;
+  const int g = lane >> 4;     // output row group -> query q0w + g
+  const int p16 = lane & 15;
+
+  // n_full of the last valid query of the workgroup bounds the chunk loop
+  const int q_last = min(q0_wg + QWG, M) - 1;
+  const int64_t nfull_wg = (q_pos0 + q_last + 1) / B;
+  const int qi_out = q0w + g;
+  const int64_t nfull_g = (qi_out < M) ? (q_pos0 + qi_out + 1) / B : 0;
+  const int q_last_w = min(q0w + 4, M) - 1;
+  const int64_t nfull_w = (q0w < M) ? (q_pos0 + q_last_w + 1) / B : 0;
+
+  // q fragments: row r = lane%16 -> query q0w + r/4, head hc*16 + 4*rb + r%4
+  bf16x8 afr[4][kKSteps];
+  {
+    const int qi = q0w + (p16 >> 2);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int j = hc * 16 + rb * 4 + (p16 & 3);
+      const bool ok = (qi < M) && (j < H);
+      const uint4* src = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + (ok ? qi : 0)) * H + (ok ? j : 0)) * kD);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        uint4 v = ok ? src[ks * 4 + g] : make_uint4(0, 0, 0, 0);
+        afr[rb][ks] = as_bf16x8(v);
+      }
+    }
+  }
+
+  float S[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[rb][i] = 0.f;
+
+  const float* pool_b = pooled + (int64_t)b * n_full_total * kD;
+  for (int64_t cbase = 0; cbase < nfull_wg; cbase += kRouteChunk) {
+    // stage pooled rows [cbase, cbase+64) as bf16 hi/lo
+    for (int e = tid; e < kRouteChunk * (kD / 4); e += NW * 64) {
+      const int row = e / (kD / 4);
+      const int c4 = e % (kD / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (cbase + row < nfull_wg) v = reinterpret_cast<const float4*>(pool_b + (cbase + row) * kD)[c4];
+      float f[4] = {v.x, v.y, v.z, v.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = f32_to_bf16_rne(f[i]);
+        lo[i] = f32_to_bf16_rne(f[i] - __uint_as_float(hi[i] << 16));
+      }
+      uint2 hv = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      uint2 lv = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+      *reinterpret_cast<uint2*>(&s_hi[row * kRowStride + c4 * 4]) = hv;
+      *reinterpret_cast<uint2*>(&s_lo[row * kRowStride + c4 * 4]) = lv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < kRouteChunk / 16; ++cb) {
+      const int64_t col0 = cbase + cb * 16;
+      if (col0 < nfull_w) {
+        bf16x8 bh[kKSteps], bl[kKSteps];
+        const int row = cb * 16 + p16;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_hi[row * kRowStride + ks * 32 + g * 8]));
+          bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_lo[row * kRowStride + ks * 32 + g * 8]));
+        }
+        const bool valid = (col0 + p16) < nfull_g;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) {
+            acc = mfma16(afr[rb][ks], bh[ks], acc);
+            acc = mfma16(afr[rb][ks], bl[ks], acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[rb][i] += valid ? __builtin_fmaxf(acc[i], 0.f) : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // sum over the 16 block columns held by the 16 lanes of a row group
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = S[rb][i];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      S[rb][i] = v;
+    }
+  // lane (g, p16) now handles head hc*16 + p16 of query q0w + g
+  float s_sel = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p16 == rb * 4 + i) s_sel = S[rb][i];
+  {
+    const int qi = q0w + g;
+    const int j = hc * 16 + p16;
+    if (qi < M && j < H) {
+      const int64_t t = q_pos0 + qi;
+      if (((t + 1) % B) != 0) {
+        const uint4* qr = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + qi) * H + j) * kD);
+        const float4* tr = reinterpret_cast<const float4*>(tail + ((int64_t)b * M + qi) * kD);
+        float dot = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < kD / 8; ++c) {
+          uint4 qv = qr[c];
+          float4 t0 = tr[2 * c], t1 = tr[2 * c + 1];
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.x & 0xFFFF), t0.x, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.x >> 16), t0.y, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.y & 0xFFFF), t0.z, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.y >> 16), t0.w, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.z & 0xFFFF), t1.x, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.z >> 16), t1.y, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.w & 0xFFFF), t1.z, dot);
+          dot = __builtin_fmaf(bf16_bits_to_f32(qv.w >> 16), t1.w, dot);
+        }
+        s_sel += __builtin_fmaxf(dot, 0.f);
+      }
+      s_r[qg * 4 + g][j] = w[((int64_t)b * M + qi) * H + j] * s_sel;
+    }
+  }
+  __syncthreads();
+
+  // top-h per query by rank counting (ties -> lower head id), stored ascending
+  for (int ql = wave; ql < QWG; ql += NW) {
+    const int qi = q0_wg + ql;
+    if (qi >= M) continue;
+    const int j = lane;
+    const float rj = (j < H) ? s_r[ql][j] : 0.f;
+    int cnt = 0;
+    for (int jj = 0; jj < H; ++jj) {
+      const float rv = s_r[ql][jj];
+      cnt += (rv > rj) || (rv == rj && jj < j);
+    }
+    const bool sel = (j < H) && (cnt < h);
+    const uint64_t mask = __ballot(sel);
+    const int pos = __popcll(mask & ((1ull << j) - 1ull));
+    const int64_t row = (int64_t)b * M + qi;
+    if (sel) heads[row * h + pos] = j;
+    if (scores != nullptr && j < H) scores[row * H + j] = rj;
+  }
+}
+
+hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
+                        const float* tail, int h, int32_t* heads, float* scores, hipStream_t st) {
+  const int H = s.n_heads;
+  const int nhc = (H + 15) / 16;
+  const int qg = (nhc == 1) ? 4 : (nhc == 2 ? 2 : 1);
+  const int qwg = 4 * qg;
+  const int64_t n_full_total = s.n_keys / s.block;
+  dim3 grid((unsigned)((s.q_per_seq + qwg - 1) / qwg), (unsigned)s.n_seq);
+  dim3 block((unsigned)(64 * nhc * qg));
+#define MISA_ROUTE_LAUNCH(NHC_)                                                                   \
+  hipLaunchKernelGGL(k_route<NHC_>, grid, block, 0, st, q, w, pooled, tail, heads, scores, s.q_pos0, \
+                     s.q_per_seq, H, s.block, h, n_full_total)
+  switch (nhc) {
+    case 1: MISA_ROUTE_LAUNCH(1); break;
+    case 2: MISA_ROUTE_LAUNCH(2); break;
+    case 3: MISA_ROUTE_LAUNCH(3); break;
+    default: MISA_ROUTE_LAUNCH(4); break;
+  }
+#undef MISA_ROUTE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace misa

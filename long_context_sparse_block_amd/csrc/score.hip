@@ -1,0 +1,429 @@
+// Token scoring: routed heads (MISA) and all heads (the dense DSA indexer).
+//
+//   I[t,s] = sum_{j in heads(t)} w[t,j] * ReLU(q[t,j] . k[s]) * sigma[s],  s <= t
+//   I[t,s] = -inf,                                                          t < s < N
+// (DSA indexer score; MISA scores every prefix token with the h routed heads
+// only: gist.science summary of MISA, "Metodologia: MISA" item 2.  The
+// fp8 scale sigma > 0 commutes with ReLU, so it is applied once after the
+// head sum.)
+//
+// Design (gfx950).  The (query, head) x key products are a dense contraction
+// on v_mfma_f32_16x16x32_bf16.  A 16-row MFMA block holds 4 queries x 4 heads
+// (row r = query r/4, head r%4 of a head quad), so the D layout hands each lane
+// all four heads of one (query, key): the ReLU / weight / head sum epilogue is
+// lane-local fp32 with no shuffles, and a lane ends with one finished logit per
+// 16-key column block.  q fragments are gathered by routed head straight from
+// HBM into registers once; K tiles of 64 (or 128) keys are staged in LDS once per
+// workgroup (fp8 codes widened to bf16 on the way in: exact), double buffered,
+// and shared by the workgroup's four waves.  Rows are padded by 16 bytes in LDS
+// so the per-lane 16-byte B reads hit distinct banks.  Workgroups are (query
+// tile x key range); the key-range split is mapped so that each XCD sweeps one
+// key range, keeping that slice of K resident in the XCD's L2.
+//
+// Summation order (fixed; every kernel that must agree bitwise uses it):
+//   quad partial  P = fma chain over the quad's 4 heads in ascending order, from 0
+//   16-head group T = (P0 + P1) + (P2 + P3)
+//   total         s = (((0 + T_0) + T_1) + ...) over 16-head groups ascending
+//   then s *= sigma (fp8).
+// k_score_c16 (h > 8, and all heads) follows it exactly; k_score_h8 (h <= 8)
+// uses s = P0 + P1 (its own order; compared to the oracle within tolerance).
+#include "misa_common.h"
+#include "misa_launch.h"
+
+namespace misa {
+
+constexpr int kKRow = kD + 8;   // bf16 elements per staged key row (272 B)
+
+// Head ids are a documented precondition (in [0, H)); clamping keeps a bad id
+// from turning into an out-of-bounds load.
+__device__ __forceinline__ int clamp_head(int j, int H) { return j < 0 ? 0 : (j >= H ? H - 1 : j); }
+
+// ---------------------------------------------------------------------------
+// K tile staging: global (bf16 or fp8) -> registers -> LDS (bf16)
+// ---------------------------------------------------------------------------
+template <int KDT, int KT, int NT>
+struct KStage {
+  // bf16: KT keys * 16 uint4 per key; fp8: KT keys * 8 uint4 per key
+  static constexpr int kVecPerKey = (KDT == MISA_K_BF16) ? 16 : 8;
+  static constexpr int kPerThread = KT * kVecPerKey / NT;
+  static_assert(KT * kVecPerKey % NT == 0, "tile not divisible");
+  uint4 r[kPerThread];
+  float sc;
+
+  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int64_t key0, int64_t N,
+                                       int tid) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int e = tid + u * NT;
+      const int key = e / kVecPerKey;
+      const int c = e % kVecPerKey;
+      const int64_t kk = key0 + key;
+      if (kk < N)
+        r[u] = reinterpret_cast<const uint4*>(kbase)[kk * kVecPerKey + c];
+      else
+        r[u] = make_uint4(0, 0, 0, 0);
+    }
+    if (KDT == MISA_K_FP8_E4M3) {
+      sc = 0.f;
+      if (tid < KT && key0 + tid < N) sc = sbase[key0 + tid];
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* s_k, float* s_sc, int tid) const {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int e = tid + u * NT;
+      const int key = e / kVecPerKey;
+      const int c = e % kVecPerKey;
+      if (KDT == MISA_K_BF16) {
+        *reinterpret_cast<uint4*>(&s_k[key * kKRow + c * 8]) = r[u];
+      } else {
+        uint2 a = e4m3x4_to_bf16x4(r[u].x), b2 = e4m3x4_to_bf16x4(r[u].y);
+        uint2 c2 = e4m3x4_to_bf16x4(r[u].z), d2 = e4m3x4_to_bf16x4(r[u].w);
+        *reinterpret_cast<uint4*>(&s_k[key * kKRow + c * 16]) = make_uint4(a.x, a.y, b2.x, b2.y);
+        *reinterpret_cast<uint4*>(&s_k[key * kKRow + c * 16 + 8]) = make_uint4(c2.x, c2.y, d2.x, d2.y);
+      }
+    }
+    if (KDT == MISA_K_FP8_E4M3 && tid < KT) s_sc[tid] = sc;
+  }
+};
+
+struct TileCoords {
+  int qt;            // query tile
+  int64_t k0, k1;    // key range [k0, k1)
+};
+
+__device__ __forceinline__ TileCoords tile_coords(int n_qtiles, int n_ksplits, int64_t KR, int64_t N) {
+  const int64_t total = (int64_t)n_qtiles * n_ksplits;
+  const int64_t T = xcd_remap(blockIdx.x, total);
+  TileCoords c;
+  c.qt = (int)(T % n_qtiles);
+  const int64_t ks = T / n_qtiles;
+  c.k0 = ks * KR;
+  c.k1 = c.k0 + KR < N ? c.k0 + KR : N;
+  return c;
+}
+
+// -inf for keys [from, to) of queries [qa, qb) (all of them lie after every query)
+__device__ __forceinline__ void fill_neg_inf(float* logits, int64_t ld, int b, int M, int qa, int qb,
+                                             int64_t from, int64_t to, int tid, int nt) {
+  if (from >= to) return;
+  const float ninf = -__builtin_inff();
+  const int64_t span = to - from;
+  for (int qi = qa; qi < qb; ++qi) {
+    float* row = logits + ((int64_t)b * M + qi) * ld;
+    // from is a multiple of 4 (tile aligned) and ld % 4 == 0
+    const int64_t n4 = span / 4;
+    for (int64_t e = tid; e < n4; e += nt)
+      __builtin_nontemporal_store(f32x4{ninf, ninf, ninf, ninf}, reinterpret_cast<f32x4*>(row + from) + e);
+    for (int64_t e = n4 * 4 + tid; e < span; e += nt) row[from + e] = ninf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// h <= 8: 8 queries per wave (2 groups x 2 head quads = 4 MFMA row blocks),
+// 32 queries per workgroup, 64-key tiles.
+// ---------------------------------------------------------------------------
+template <int KDT>
+__global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q,
+                                                  const float* __restrict__ w,
+                                                  const void* __restrict__ kptr,
+                                                  const float* __restrict__ kscale,
+                                                  const int32_t* __restrict__ heads, int h,
+                                                  float* __restrict__ logits, int64_t ld, int64_t N,
+                                                  int64_t q_pos0, int M, int H, int n_qtiles,
+                                                  int n_ksplits, int64_t KR) {
+  constexpr int NT = 256, KT = 64, QT = 32;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KT * kKRow];
+  __shared__ float s_sc[2][KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, p16 = lane & 15;
+  const int b = blockIdx.y;
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const int qa = tc.qt * QT;
+  const int qb = min(qa + QT, M);
+  const int64_t t_last = q_pos0 + qb - 1;
+  const int64_t kend = min(tc.k1, t_last + 1);   // keys past kend are masked for every query
+  const int n_tiles = kend > tc.k0 ? (int)((kend - tc.k0 + KT - 1) / KT) : 0;
+
+  const int q0w = qa + wave * 8;
+  // A fragments: row block rb = 2*G + qd; row r -> query q0w + 4G + r/4, slot 4*qd + r%4
+  bf16x8 afr[4][kKSteps];
+  float wv[2][8];
+  int64_t tq[2];
+  bool gvalid[2];
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    gvalid[G] = (q0w + 4 * G) < qb;
+    const int qo = q0w + 4 * G + g;          // query of this lane's output rows
+    tq[G] = (qo < qb) ? q_pos0 + qo : -1;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      float wvv = 0.f;
+      if (qo < qb && sl < h) {
+        const int j = clamp_head(heads[((int64_t)b * M + qo) * h + sl], H);
+        wvv = w[((int64_t)b * M + qo) * H + j];
+      }
+      wv[G][sl] = wvv;
+    }
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) {
+      const int qi = q0w + 4 * G + (p16 >> 2);
+      const int sl = 4 * qd + (p16 & 3);
+      const bool ok = (qi < qb) && (sl < h);
+      int j = 0;
+      if (ok) j = clamp_head(heads[((int64_t)b * M + qi) * h + sl], H);
+      const uint4* src = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + (ok ? qi : 0)) * H + j) * kD);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) afr[2 * G + qd][ks] = as_bf16x8(ok ? src[ks * 4 + g] : make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const void* kb_ptr = (KDT == MISA_K_BF16)
+                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * N * kD)
+                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * N * kD);
+  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * N : nullptr;
+
+  KStage<KDT, KT, NT> stg;
+  if (n_tiles > 0) {
+    stg.load(kb_ptr, sc_ptr, tc.k0, N, tid);
+    stg.store(s_k[0], s_sc[0], tid);
+  }
+  __syncthreads();
+  const float ninf = -__builtin_inff();
+  const int64_t t_wave_max = max(tq[0], tq[1]);   // per lane; wave max below
+  int64_t wmax = t_wave_max;
+  for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, (int64_t)__shfl_xor((long long)wmax, o));
+
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int buf = jt & 1;
+    const int64_t key0 = tc.k0 + (int64_t)jt * KT;
+    if (jt + 1 < n_tiles) stg.load(kb_ptr, sc_ptr, key0 + KT, N, tid);
+    if (q0w < qb) {
+#pragma unroll
+      for (int kb = 0; kb < KT / 16; ++kb) {
+        const int64_t kpos = key0 + kb * 16 + p16;   // this lane's key
+        if (key0 + kb * 16 > wmax) {
+          // whole column block is after every query of the wave
+#pragma unroll
+          for (int G = 0; G < 2; ++G)
+            if (tq[G] >= 0 && kpos < N) logits[((int64_t)b * M + (tq[G] - q_pos0)) * ld + kpos] = ninf;
+          continue;
+        }
+        bf16x8 bfr[kKSteps];
+        const uint16_t* rowp = &s_k[buf][(kb * 16 + p16) * kKRow + g * 8];
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) bfr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + ks * 32));
+        const float sc = (KDT == MISA_K_FP8_E4M3) ? s_sc[buf][kb * 16 + p16] : 1.f;
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+          if (!gvalid[G]) continue;
+          f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) {
+            a0 = mfma16(afr[2 * G][ks], bfr[ks], a0);
+            a1 = mfma16(afr[2 * G + 1][ks], bfr[ks], a1);
+          }
+          const float P0 = quad_chain(a0, wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
+          const float P1 = quad_chain(a1, wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
+          float s = P0 + P1;
+          if (KDT == MISA_K_FP8_E4M3) s *= sc;
+          if (kpos > tq[G]) s = ninf;
+          if (tq[G] >= 0 && kpos < N) logits[((int64_t)b * M + (tq[G] - q_pos0)) * ld + kpos] = s;
+        }
+      }
+    }
+    if (jt + 1 < n_tiles) stg.store(s_k[buf ^ 1], s_sc[buf ^ 1], tid);
+    __syncthreads();
+  }
+  // keys of this range after the last computed tile: -inf for every query
+  fill_neg_inf(logits, ld, b, M, qa, qb, tc.k0 + (int64_t)n_tiles * KT, tc.k1, tid, NT);
+}
+
+// ---------------------------------------------------------------------------
+// General head count (h > 8, or all H heads): 4 queries per wave, one 16-head
+// group per pass (4 MFMA row blocks = 4 head quads), q fragments re-read per
+// group, running per-(query,key) sums in registers.  16 queries per
+// workgroup, 128-key tiles.  HEADS = true gathers routed heads, false = all.
+// ---------------------------------------------------------------------------
+template <int KDT, bool HEADS>
+__global__ void __launch_bounds__(256) k_score_c16(const uint16_t* __restrict__ q,
+                                                   const float* __restrict__ w,
+                                                   const void* __restrict__ kptr,
+                                                   const float* __restrict__ kscale,
+                                                   const int32_t* __restrict__ heads, int h,
+                                                   float* __restrict__ logits, int64_t ld, int64_t N,
+                                                   int64_t q_pos0, int M, int H, int n_qtiles,
+                                                   int n_ksplits, int64_t KR) {
+  constexpr int NT = 256, KT = 128, QT = 16, NKB = KT / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KT * kKRow];
+  __shared__ float s_sc[2][KT];
+  __shared__ int s_head[QT][64];
+  __shared__ float s_w[QT][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, p16 = lane & 15;
+  const int b = blockIdx.y;
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const int qa = tc.qt * QT;
+  const int qb = min(qa + QT, M);
+  const int64_t t_last = q_pos0 + qb - 1;
+  const int64_t kend = min(tc.k1, t_last + 1);
+  const int n_tiles = kend > tc.k0 ? (int)((kend - tc.k0 + KT - 1) / KT) : 0;
+  const int n_grp = (h + 15) / 16;
+
+  // head ids and weights of the tile's queries (slot order), padded with w = 0
+  for (int e = tid; e < QT * 64; e += NT) {
+    const int ql = e / 64, sl = e % 64;
+    const int qi = qa + ql;
+    int j = 0;
+    float wj = 0.f;
+    if (qi < qb && sl < h) {
+      j = HEADS ? clamp_head(heads[((int64_t)b * M + qi) * h + sl], H) : sl;
+      wj = w[((int64_t)b * M + qi) * H + j];
+    }
+    s_head[ql][sl] = j;
+    s_w[ql][sl] = wj;
+  }
+
+  const int q0w = qa + wave * 4;
+  const int qo = q0w + g;
+  const int64_t tq = (qo < qb) ? q_pos0 + qo : -1;
+  int64_t wmax = tq;
+  for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, (int64_t)__shfl_xor((long long)wmax, o));
+
+  const void* kb_ptr = (KDT == MISA_K_BF16)
+                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * N * kD)
+                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * N * kD);
+  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * N : nullptr;
+
+  KStage<KDT, KT, NT> stg;
+  if (n_tiles > 0) {
+    stg.load(kb_ptr, sc_ptr, tc.k0, N, tid);
+    stg.store(s_k[0], s_sc[0], tid);
+  }
+  __syncthreads();
+  const float ninf = -__builtin_inff();
+
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int buf = jt & 1;
+    const int64_t key0 = tc.k0 + (int64_t)jt * KT;
+    if (jt + 1 < n_tiles) stg.load(kb_ptr, sc_ptr, key0 + KT, N, tid);
+    if (q0w < qb) {
+      float run[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) run[kb] = 0.f;
+      for (int grp = 0; grp < n_grp; ++grp) {
+        // A: row block qd, row r -> query q0w + r/4, slot grp*16 + 4*qd + r%4
+        bf16x8 afr[4][kKSteps];
+        {
+          const int ql = wave * 4 + (p16 >> 2);
+          const int qi = qa + ql;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int sl = grp * 16 + 4 * qd + (p16 & 3);
+            const bool ok = (qi < qb) && (sl < h);
+            const int j = s_head[ql][sl & 63];
+            const uint4* src = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + (ok ? qi : 0)) * H + (ok ? j : 0)) * kD);
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) afr[qd][ks] = as_bf16x8(ok ? src[ks * 4 + g] : make_uint4(0, 0, 0, 0));
+          }
+        }
+        float wq[16];
+        const int qlo = wave * 4 + g;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wq[e] = s_w[qlo][grp * 16 + e];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          if (key0 + kb * 16 > wmax) continue;
+          bf16x8 bfr[kKSteps];
+          const uint16_t* rowp = &s_k[buf][(kb * 16 + p16) * kKRow + g * 8];
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) bfr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + ks * 32));
+          float P[4];
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) acc = mfma16(afr[qd][ks], bfr[ks], acc);
+            P[qd] = quad_chain(acc, wq[4 * qd], wq[4 * qd + 1], wq[4 * qd + 2], wq[4 * qd + 3]);
+          }
+          const float T = (P[0] + P[1]) + (P[2] + P[3]);
+          run[kb] = run[kb] + T;
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int64_t kpos = key0 + kb * 16 + p16;
+        float s = run[kb];
+        if (KDT == MISA_K_FP8_E4M3) s *= s_sc[buf][kb * 16 + p16];
+        if (kpos > tq) s = ninf;
+        if (tq >= 0 && kpos < N) logits[((int64_t)b * M + qo) * ld + kpos] = s;
+      }
+    }
+    if (jt + 1 < n_tiles) stg.store(s_k[buf ^ 1], s_sc[buf ^ 1], tid);
+    __syncthreads();
+  }
+  fill_neg_inf(logits, ld, b, M, qa, qb, tc.k0 + (int64_t)n_tiles * KT, tc.k1, tid, NT);
+}
+
+// ---------------------------------------------------------------------------
+// Launch: pick the kernel, the key-range split and the grid.
+// ---------------------------------------------------------------------------
+static void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR) {
+  const int64_t n_ktiles = (N + KT - 1) / KT;
+  const int64_t target = 2048;   // workgroups: several per CU on 256 CUs
+  int64_t ns = (target + (int64_t)n_seq * n_qtiles - 1) / ((int64_t)n_seq * n_qtiles);
+  if (ns < 1) ns = 1;
+  if (ns > n_ktiles) ns = n_ktiles;
+  int64_t kr = ((n_ktiles + ns - 1) / ns) * KT;
+  ns = (N + kr - 1) / kr;
+  *n_ksplits = (int)ns;
+  *KR = kr;
+}
+
+hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
+                        int kdtype, const float* k_scale, const int32_t* heads, int h,
+                        float* logits, int64_t ld, hipStream_t st) {
+  const int M = s.q_per_seq, H = s.n_heads;
+  const int64_t N = s.n_keys;
+  if (heads != nullptr && h <= 8) {
+    const int n_qtiles = (M + 31) / 32;
+    int nks;
+    int64_t KR;
+    plan_split(N, s.n_seq, n_qtiles, 64, &nks, &KR);
+    dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+    if (kdtype == MISA_K_BF16)
+      hipLaunchKernelGGL(k_score_h8<MISA_K_BF16>, grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
+                         logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+    else
+      hipLaunchKernelGGL(k_score_h8<MISA_K_FP8_E4M3>, grid, dim3(256), 0, st, q, w, k, k_scale, heads,
+                         h, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+    return hipGetLastError();
+  }
+  const int hh = heads ? h : H;
+  const int n_qtiles = (M + 15) / 16;
+  int nks;
+  int64_t KR;
+  plan_split(N, s.n_seq, n_qtiles, 128, &nks, &KR);
+  dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  if (kdtype == MISA_K_BF16) {
+    if (heads)
+      hipLaunchKernelGGL((k_score_c16<MISA_K_BF16, true>), grid, dim3(256), 0, st, q, w, k, k_scale,
+                         heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+    else
+      hipLaunchKernelGGL((k_score_c16<MISA_K_BF16, false>), grid, dim3(256), 0, st, q, w, k, k_scale,
+                         heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+  } else {
+    if (heads)
+      hipLaunchKernelGGL((k_score_c16<MISA_K_FP8_E4M3, true>), grid, dim3(256), 0, st, q, w, k,
+                         k_scale, heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+    else
+      hipLaunchKernelGGL((k_score_c16<MISA_K_FP8_E4M3, false>), grid, dim3(256), 0, st, q, w, k,
+                         k_scale, heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace misa

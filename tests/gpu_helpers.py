@@ -1,0 +1,110 @@
+"""Helpers of the GPU parity tests: upload generator inputs, tolerance and
+selection-band checks (no indexer arithmetic here)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import long_context_sparse_block_amd as lcsb
+
+# Logits: bf16 inputs, fp32 accumulation -> within 1e-2 relative.  Near zero,
+# where the signed head sum cancels, the scale is the row's magnitude:
+#     |g - o| <= 1e-2 * max(|o|, 1e-3 * max_s |o[s]|)
+REL_TOL = 1e-2
+ROW_FLOOR = 1e-3
+# Selections: element margins beyond 1e-2 |v| + 1e-6 rowmax around the
+# boundary value v must be decided like the oracle decides them.
+BAND_REL = 1e-2
+BAND_ROW = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def device():
+    return torch.device("cuda:0")
+
+
+def upload(inp):
+    dev = device()
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(inp.w).to(dev)
+    if inp.k_scale is None:
+        k = torch.from_numpy(inp.k.view(np.int16)).to(dev).view(torch.bfloat16)
+        ks = None
+    else:
+        k = torch.from_numpy(inp.k).to(dev)
+        ks = torch.from_numpy(inp.k_scale).to(dev)
+    return dict(q=q, w=w, k=k, k_scale=ks)
+
+
+def shape_of(inp):
+    c = inp.cfg
+    return lcsb.make_shape(c.n_seq, c.q_per_seq, c.n_keys, inp.q_pos0, c.n_heads, c.block)
+
+
+def logits_close(g: np.ndarray, o: np.ndarray):
+    """g (fp32 from GPU) vs o (fp64 oracle), same shape; -inf must match exactly.
+    Returns (ok, worst relative error in the tolerance's own scale)."""
+    g = g.astype(np.float64)
+    ninf_o = np.isneginf(o)
+    if not np.array_equal(np.isneginf(g), ninf_o):
+        return False, float("inf")
+    fin = ~ninf_o
+    if not fin.any():
+        return True, 0.0
+    of, gf = np.where(fin, o, 0.0), np.where(fin, g, 0.0)
+    rowmax = np.abs(of).max(axis=-1, keepdims=True)
+    scale = np.maximum(np.abs(of), ROW_FLOOR * rowmax)
+    scale = np.where(scale > 0, scale, 1.0)
+    err = np.abs(gf - of) / scale
+    worst = float(err[fin].max())
+    return worst <= REL_TOL, worst
+
+
+def band_check(values: np.ndarray, ids: np.ndarray, picked: np.ndarray, count: int):
+    """Is `picked` (ids) a valid top-`count` of (values, ids) up to the band?
+    Returns (ok, n_inside_band_disagreements)."""
+    keep = ids >= 0
+    values, ids = values[keep], ids[keep]
+    count = min(count, len(ids))
+    picked = picked[picked >= 0]
+    if len(picked) != count or len(set(picked.tolist())) != count:
+        return False, -1
+    if count == 0:
+        return True, 0
+    order = np.argsort(-values, kind="stable")
+    v = values[order[count - 1]]
+    rowmax = np.abs(values[np.isfinite(values)]).max() if np.isfinite(values).any() else 0.0
+    delta = BAND_REL * abs(v) + BAND_ROW * rowmax
+    pos = {int(i): p for p, i in enumerate(ids)}
+    psel = np.zeros(len(ids), bool)
+    for i in picked:
+        if int(i) not in pos:
+            return False, -1
+        psel[pos[int(i)]] = True
+    must = values > v + delta
+    must_not = values < v - delta
+    if (must & ~psel).any() or (must_not & psel).any():
+        return False, -1
+    oracle_sel = np.zeros(len(ids), bool)
+    oracle_sel[order[:count]] = True
+    return True, int((oracle_sel != psel).sum() // 2)
+
+
+def recall(picked: np.ndarray, ref: np.ndarray) -> float:
+    r = ref[ref >= 0]
+    if len(r) == 0:
+        return 1.0
+    return len(set(picked[picked >= 0].tolist()) & set(r.tolist())) / len(r)
+
+
+def sample_rows(M: int, n: int):
+    if M <= n:
+        return list(range(M))
+    rows = np.unique(np.linspace(0, M - 1, n).round().astype(int))
+    return rows.tolist()

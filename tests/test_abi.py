@@ -1,0 +1,133 @@
+"""The C ABI library on the CPU: it loads, exports every function misa.h declares,
+and rejects bad arguments on the host before anything touches a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_sparse_block_amd as lcsb
+from long_context_sparse_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "misa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmisa.so is not built (python -m long_context_sparse_block_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def shape(**kw):
+    base = dict(n_seq=1, q_per_seq=4, n_keys=64, q_pos0=60, n_heads=8, block=16)
+    base.update(kw)
+    return lcsb.make_shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.misa_status_str(code)
+    assert b"unknown" in lib.misa_status_str(7)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_seq=0), -1), (dict(q_per_seq=-1), -1), (dict(n_keys=0), -1), (dict(q_pos0=-1), -1),
+    (dict(q_pos0=61), -1), (dict(n_heads=0), -1), (dict(n_heads=65), -1), (dict(block=0), -1),
+    (dict(head_dim=64), -2),
+])
+def test_pool_rejects_bad_shapes(lib, kw, code):
+    s = shape(**kw)
+    st = lib.misa_pool_keys(ctypes.byref(s), FAKE, 0, None, FAKE, FAKE, None)
+    assert st == code
+
+
+def test_null_shape_and_pointers(lib):
+    assert lib.misa_pool_keys(None, FAKE, 0, None, FAKE, FAKE, None) == -1
+    s = shape()
+    assert lib.misa_pool_keys(ctypes.byref(s), None, 0, None, FAKE, FAKE, None) == -1
+    assert lib.misa_pool_keys(ctypes.byref(s), FAKE, 1, None, FAKE, FAKE, None) == -1   # fp8 needs scale
+    assert lib.misa_pool_keys(ctypes.byref(s), FAKE, 5, None, FAKE, FAKE, None) == -1   # bad dtype
+    misaligned = ctypes.c_void_p(0x10004)
+    assert lib.misa_pool_keys(ctypes.byref(s), misaligned, 0, None, FAKE, FAKE, None) == -1
+
+
+def test_route_checks_h(lib):
+    s = shape()
+    for h in (0, 9):
+        assert lib.misa_route_heads(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, h, FAKE, None, None) == -1
+
+
+def test_logits_check_ld_and_h(lib):
+    s = shape()
+    f = lib.misa_sparse_head_logits
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 0, FAKE, 64, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 60, None) == -1   # ld < N
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 66, None) == -1   # ld % 4
+    g = lib.dsa_dense_logits
+    assert g(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, None, 0, FAKE, 62, None) == -1
+    assert g(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 0, FAKE, 64, None) == -1   # n_cand 0
+    assert g(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 80, FAKE, 64, None) == -1  # ld < n_cand
+
+
+def test_topk_checks(lib):
+    s = shape()
+    f = lib.misa_topk
+    assert f(ctypes.byref(s), FAKE, 64, None, 64, 0, FAKE, None, None, 0, None) == -1
+    assert f(ctypes.byref(s), FAKE, 64, None, 64, 8193, FAKE, None, None, 0, None) == -1
+    assert f(ctypes.byref(s), FAKE, 64, None, 65, 4, FAKE, None, None, 0, None) == -1     # ld < n_cols
+    assert f(ctypes.byref(s), FAKE, 64, None, 64, 4, None, None, None, 0, None) == -1     # idx null
+
+
+def test_indexer_checks_and_workspace(lib):
+    s = shape()
+    f = lib.misa_indexer
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 9, 4, 0, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 3, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, FAKE, None, None, 0, None) == -3
+    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 0)
+    assert need > 0
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, FAKE, None, FAKE, need - 1, None) == -3
+    # MISA-dagger needs room for candidates and their re-ranked scores
+    need_d = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 16)
+    assert need_d > need
+
+
+def test_empty_query_set_is_a_no_op(lib):
+    s = shape(q_per_seq=0, q_pos0=64)
+    assert lib.misa_sparse_head_logits(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 64,
+                                       None) == 0
+    assert lib.misa_topk(ctypes.byref(s), FAKE, 64, None, 64, 4, FAKE, None, None, 0, None) == 0
+
+
+def test_workspace_size_of_the_long_context_chunk(lib):
+    s = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
+    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 8, 2048, 0)
+    # dominated by the fp32 logits of the chunk: 8192 x 131072 x 4 bytes
+    assert 8192 * 131072 * 4 <= need < 8192 * 131072 * 4 * 1.01

@@ -1,0 +1,386 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Staged checks feed each kernel the inputs its oracle stage gets (the router
+the GPU's pooled keys, the scoring kernel the GPU's routed heads, the top-k
+the GPU's own logits), so every stage is compared on equal footing:
+  * pooled keys / tails and the fp8 decode: fp32 vs fp64, relative 1e-5;
+  * router scores r and logits: within 1e-2 relative (row-scaled near 0);
+  * routed heads and MISA token sets: bit-exact outside the tolerance band;
+  * top-k of given logits: bit-exact (the decision is taken on the same fp32
+    values on both sides);
+  * GPU identities, bitwise: routed scoring with every head == dense DSA;
+    MISA-dagger with k' >= L == dense top-k; repeated runs identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_block_amd as lcsb
+import oracle
+from gpu_helpers import (band_check, logits_close, recall, sample_rows, say, shape_of, upload)
+from long_context_sparse_block_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
+    lcsb.load()
+
+
+def f64(t):
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# stage runner
+# ---------------------------------------------------------------------------
+
+def run_stages(inp, t=None, h=None, rows_for_logits=None):
+    t = upload(inp) if t is None else t
+    sh = shape_of(inp)
+    h = inp.cfg.h if h is None else h
+    pooled, tail = lcsb.misa_pool_keys(sh, t["k"], t["k_scale"])
+    heads, r = lcsb.misa_route_heads(sh, t["q"], t["w"], pooled, tail, h, want_scores=True)
+    logits = lcsb.misa_sparse_head_logits(sh, t["q"], t["w"], t["k"], heads, k_scale=t["k_scale"])
+    torch.cuda.synchronize()
+    return dict(t=t, sh=sh, pooled=pooled, tail=tail, heads=heads, r=r, logits=logits)
+
+
+def check_pool(inp, st, rows=None):
+    M = inp.cfg.q_per_seq
+    rows = range(M) if rows is None else rows
+    for b in range(inp.cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b)
+        gp = f64(st["pooled"][b])
+        scale = max(np.abs(ctx.pooled).max(), 1e-30) if ctx.pooled.size else 1.0
+        if ctx.pooled.size:
+            np.testing.assert_allclose(gp, ctx.pooled, rtol=1e-5, atol=1e-6 * scale)
+        gt = st["tail"][b]
+        for i in rows:
+            tl = ctx.tail(i)
+            g = f64(gt[i])
+            if tl is None:
+                assert not g.any()
+            else:
+                np.testing.assert_allclose(g, tl, rtol=1e-5, atol=1e-6 * max(np.abs(tl).max(), 1e-30))
+
+
+def check_route(inp, st, rows=None, seqs=None):
+    M, H, h = inp.cfg.q_per_seq, inp.cfg.n_heads, st["heads"].shape[-1]
+    rows = list(range(M)) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    gh = st["heads"].cpu().numpy()
+    gr = st["r"].cpu().numpy().astype(np.float64)
+    worst, inside = 0.0, 0
+    for b in seqs:
+        ctx = oracle.SeqContext(inp, b)
+        for i in rows:
+            S, r, heads = ctx.route(i, h)
+            ok, wst = logits_close(gr[b, i][None], r[None])
+            assert ok, f"router scores seq {b} query {i}: worst {wst}"
+            worst = max(worst, wst)
+            assert np.all(np.diff(gh[b, i]) > 0), "heads not ascending/distinct"
+            ok, n_in = band_check(r, np.arange(H), gh[b, i], h)
+            assert ok, f"heads seq {b} query {i}: gpu {gh[b, i]} oracle {heads}"
+            inside += n_in
+    return worst, inside
+
+
+def check_logits(inp, st, rows=None, seqs=None):
+    M = inp.cfg.q_per_seq
+    rows = list(range(M)) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    gh = st["heads"].cpu().numpy()
+    worst = 0.0
+    N = inp.cfg.n_keys
+    for b in seqs:
+        ctx = oracle.SeqContext(inp, b)
+        idx = torch.tensor(rows, device=st["logits"].device)
+        g = st["logits"][b].index_select(0, idx)[:, :N].cpu().numpy()
+        for n, i in enumerate(rows):
+            o = ctx.score(i, gh[b, i])
+            ok, wst = logits_close(g[n][None], o[None])
+            assert ok, f"logits seq {b} query {i}: worst {wst}"
+            worst = max(worst, wst)
+    return worst
+
+
+def check_topk_exact(inp, logits, k, idx, vals, rows=None, seqs=None):
+    """top-k of the GPU's own logits: the oracle decides on the same fp32 values."""
+    M = inp.cfg.q_per_seq
+    rows = list(range(M)) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    for b in seqs:
+        ridx = torch.tensor(rows, device=logits.device)
+        g = logits[b].index_select(0, ridx).cpu().numpy().astype(np.float64)
+        gi = idx[b].index_select(0, ridx).cpu().numpy()
+        gv = vals[b].index_select(0, ridx).cpu().numpy() if vals is not None else None
+        for n, i in enumerate(rows):
+            t = inp.q_pos0 + i
+            oi, ov = oracle.topk_prefix(g[n], t, k)
+            assert np.array_equal(gi[n], oi), f"top-k seq {b} query {i}"
+            if gv is not None:
+                assert np.array_equal(gv[n].astype(np.float64), ov)
+
+
+# ---------------------------------------------------------------------------
+# fp8 decode and pooling
+# ---------------------------------------------------------------------------
+
+def test_fp8_decode_all_codes_through_pooling():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 finite codes
+    N = len(codes)
+    k = np.stack([np.roll(codes, -s)[:128] for s in range(N)]).astype(np.uint8)
+    scale = np.where(np.arange(N) % 2 == 0, 1.0, 0.25).astype(np.float32)   # powers of two: exact
+    sh = lcsb.make_shape(1, 1, N, N - 1, 1, 1)
+    dev = torch.device("cuda:0")
+    kt = torch.from_numpy(k[None]).to(dev)
+    st = torch.from_numpy(scale[None]).to(dev)
+    pooled, tail = lcsb.misa_pool_keys(sh, kt, st)
+    got = f64(pooled[0])
+    expect = oracle.e4m3fn_to_f64(k) * scale[:, None].astype(np.float64)
+    assert np.array_equal(got, expect)
+    nz = expect != 0          # a block sum starts at +0, so a lone -0.0 pools to +0.0
+    assert np.array_equal(np.signbit(got[nz]), np.signbit(expect[nz]))
+    assert not f64(tail).any()
+
+
+POOL_CASES = [
+    dict(m=37, n=1000, b=64), dict(m=64, n=512, b=1), dict(m=20, n=300, b=3),
+    dict(m=16, n=40, b=64), dict(m=33, n=777, b=128, kdtype=gen.KDTYPE_FP8),
+    dict(m=1, n=4096, b=64, n_seq=3), dict(m=10, n=600, b=7, q_pos0=100),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_pool_parity(case):
+    c = dict(case)
+    inp = gen.generate(gen.small_config(m=c.pop("m"), n=c.pop("n"), b=c.pop("b"), hh=16, h=4, k=16,
+                                        kdtype=c.pop("kdtype", gen.KDTYPE_BF16), n_seq=c.pop("n_seq", 1),
+                                        q_pos0=c.pop("q_pos0", None), seed=21))
+    say("pool case", case)
+    st = run_stages(inp)
+    check_pool(inp, st)
+
+
+# ---------------------------------------------------------------------------
+# staged parity on small workloads, including ragged and degenerate shapes
+# ---------------------------------------------------------------------------
+
+STAGE_CASES = [
+    dict(name="tiny", cfg=gen.CONFIGS["tiny_prefill_m256_n4k"]),
+    dict(name="ragged", cfg=gen.small_config(m=37, n=1003, hh=64, b=64, h=8, k=100, seed=5)),
+    dict(name="fp8", cfg=gen.small_config(m=70, n=2049, hh=64, b=128, h=8, k=300,
+                                          kdtype=gen.KDTYPE_FP8, seed=6)),
+    dict(name="h1_B1", cfg=gen.small_config(m=9, n=300, hh=16, b=1, h=1, k=40, seed=7)),
+    dict(name="h5_B3_H48", cfg=gen.small_config(m=45, n=650, hh=48, b=3, h=5, k=64, seed=8)),
+    dict(name="h12_H32", cfg=gen.small_config(m=40, n=900, hh=32, b=64, h=12, k=128, seed=9)),
+    dict(name="h24_fp8", cfg=gen.small_config(m=21, n=700, hh=64, b=32, h=24, k=77,
+                                              kdtype=gen.KDTYPE_FP8, seed=10)),
+    dict(name="Bbig", cfg=gen.small_config(m=30, n=200, hh=64, b=512, h=8, k=50, seed=11)),
+    dict(name="decode", cfg=gen.small_config(n_seq=5, m=1, n=3000, hh=32, b=64, h=8, k=256, seed=12)),
+    dict(name="mid_chunk", cfg=gen.small_config(m=50, n=1500, hh=64, b=64, h=8, k=120, q_pos0=600,
+                                                seed=13)),
+    dict(name="short_prefix", cfg=gen.small_config(m=40, n=40, hh=16, b=8, h=4, k=64, seed=14)),
+]
+
+
+@pytest.fixture(scope="module")
+def staged():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            case = next(c for c in STAGE_CASES if c["name"] == name)
+            inp = gen.generate(case["cfg"])
+            cache[name] = (inp, run_stages(inp))
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", [c["name"] for c in STAGE_CASES])
+def test_staged_parity(staged, name):
+    say("staged case", name)
+    inp, st = staged(name)
+    cfg = inp.cfg
+    check_pool(inp, st)
+    worst_r, inside = check_route(inp, st)
+    worst_l = check_logits(inp, st)
+    idx, vals = lcsb.misa_topk(st["sh"], st["logits"], cfg.topk)
+    check_topk_exact(inp, st["logits"], cfg.topk, idx, vals)
+    # masked region beyond each query is -inf, padding beyond N untouched by contract
+    say(f"  router worst {worst_r:.2e} (band disagreements {inside}); logits worst {worst_l:.2e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "fp8", "h5_B3_H48", "decode", "mid_chunk"])
+def test_dense_logits_parity_and_routed_all_heads_identity(staged, name):
+    say("dense case", name)
+    inp, st = staged(name)
+    cfg = inp.cfg
+    t = st["t"]
+    sh = st["sh"]
+    dense = lcsb.dsa_dense_logits(sh, t["q"], t["w"], t["k"], k_scale=t["k_scale"])
+    allh = torch.arange(cfg.n_heads, dtype=torch.int32, device=dense.device)
+    allh = allh.expand(cfg.n_seq, cfg.q_per_seq, cfg.n_heads).contiguous()
+    routed_all = lcsb.misa_sparse_head_logits(sh, t["q"], t["w"], t["k"], allh, k_scale=t["k_scale"])
+    torch.cuda.synchronize()
+    N = cfg.n_keys
+    assert torch.equal(dense[..., :N], routed_all[..., :N]), "h = H routed scoring != dense DSA"
+    rows = sample_rows(cfg.q_per_seq, 24)
+    for b in range(cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b)
+        g = dense[b, rows, :N].cpu().numpy()
+        for n, i in enumerate(rows):
+            ok, wst = logits_close(g[n][None], ctx.dense(i)[None])
+            assert ok, f"dense seq {b} query {i} worst {wst}"
+
+
+def test_topk_candidate_mode_ties_and_padding():
+    rng = np.random.default_rng(3)
+    M, n_cols, k = 7, 1003, 300
+    vals = (rng.integers(-6, 7, (1, M, n_cols)) / 2.0).astype(np.float32)
+    vals[rng.random(vals.shape) < 0.1] = -0.0
+    ids = np.stack([rng.permutation(5000)[:n_cols] for _ in range(M)])[None].astype(np.int32)
+    ids[rng.random(ids.shape) < 0.2] = -1
+    ids[0, 3, :] = -1                       # a row with no candidate at all
+    ids[0, 4, 50:] = -1                      # fewer candidates than k
+    sh = lcsb.make_shape(1, M, 5000, 0, 1, 1)
+    dev = torch.device("cuda:0")
+    ld = (n_cols + 3) // 4 * 4
+    lg = torch.full((1, M, ld), float("nan"), device=dev)
+    lg[..., :n_cols] = torch.from_numpy(vals).to(dev)
+    idx, v = lcsb.misa_topk(sh, lg, k, cand=torch.from_numpy(ids).to(dev))
+    gi, gv = idx.cpu().numpy(), v.cpu().numpy()
+    for i in range(M):
+        oi, ov = oracle.topk_row(vals[0, i].astype(np.float64), ids[0, i].astype(np.int64), k)
+        assert np.array_equal(gi[0, i], oi), f"row {i}"
+        assert np.array_equal(gv[0, i].astype(np.float64), ov)
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "two_values", "neg_zero_mix", "short_rows", "wide"])
+def test_topk_degenerate_rows(kind):
+    rng = np.random.default_rng(4)
+    M, N, k = 6, 20000, 2048
+    if kind == "all_equal":
+        vals = np.full((1, M, N), 0.5, np.float32)
+    elif kind == "two_values":
+        vals = np.where(rng.random((1, M, N)) < 0.5, 1.0, 2.0).astype(np.float32)
+    elif kind == "neg_zero_mix":
+        vals = np.where(rng.random((1, M, N)) < 0.5, -0.0, 0.0).astype(np.float32)
+        vals[0, :, ::97] = 1e-30
+    elif kind == "short_rows":
+        N = 3000
+        vals = rng.standard_normal((1, M, N)).astype(np.float32)
+    else:
+        k = 8192
+        vals = rng.standard_normal((1, M, N)).astype(np.float32)
+    q_pos0 = N - M if kind != "short_rows" else 1000
+    M_ = M
+    sh = lcsb.make_shape(1, M_, N, q_pos0, 1, 1)
+    dev = torch.device("cuda:0")
+    ld = (N + 3) // 4 * 4
+    lg = torch.zeros((1, M_, ld), device=dev)
+    lg[..., :N] = torch.from_numpy(vals).to(dev)
+    idx, v = lcsb.misa_topk(sh, lg, k)
+    check_topk_exact_arrays(vals, q_pos0, k, idx.cpu().numpy(), v.cpu().numpy())
+
+
+def check_topk_exact_arrays(vals, q_pos0, k, gi, gv):
+    for i in range(vals.shape[1]):
+        oi, ov = oracle.topk_prefix(vals[0, i].astype(np.float64), q_pos0 + i, k)
+        assert np.array_equal(gi[0, i], oi), f"row {i}"
+        assert np.array_equal(gv[0, i].astype(np.float64), ov)
+
+
+# ---------------------------------------------------------------------------
+# whole indexer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "fp8", "decode", "h12_H32"])
+def test_indexer_matches_stages_and_oracle(staged, name):
+    say("indexer case", name)
+    inp, st = staged(name)
+    cfg = inp.cfg
+    t = st["t"]
+    sh = st["sh"]
+    idx, vals = lcsb.misa_indexer(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, k_scale=t["k_scale"])
+    sidx, svals = lcsb.misa_topk(sh, st["logits"], cfg.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sidx) and torch.equal(vals, svals), "indexer != its stages"
+    gi = idx.cpu().numpy()
+    gh = st["heads"].cpu().numpy()
+    recs = []
+    for b in range(cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b)
+        for i in range(cfg.q_per_seq):
+            out = ctx.misa(i, cfg.h, cfg.topk)
+            recs.append(recall(gi[b, i], out["idx"]))
+            if np.array_equal(np.sort(out["heads"]), gh[b, i]):
+                T = inp.q_pos0 + i
+                ok, _ = band_check(out["I"][:T + 1], np.arange(T + 1), gi[b, i], cfg.topk)
+                assert ok, f"token set seq {b} query {i}"
+    say(f"  recall mean {np.mean(recs):.6f} min {np.min(recs):.4f}")
+    assert np.mean(recs) >= 0.999
+
+
+def test_indexer_is_deterministic(staged):
+    inp, st = staged("fp8")
+    cfg = inp.cfg
+    t = st["t"]
+    outs = [lcsb.misa_indexer(st["sh"], t["q"], t["w"], t["k"], cfg.h, cfg.topk, k_prime=2 * cfg.topk,
+                              k_scale=t["k_scale"]) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
+
+
+@pytest.mark.parametrize("kdtype", [gen.KDTYPE_BF16, gen.KDTYPE_FP8])
+def test_dagger_with_all_candidates_is_dense_topk(kdtype):
+    # k' >= L: every prefix token is a candidate, the re-rank is the dense indexer
+    cfg = gen.small_config(m=48, n=2000, hh=64, b=64, h=8, k=256, kp=2048, kdtype=kdtype, seed=31)
+    inp = gen.generate(cfg)
+    t = upload(inp)
+    sh = shape_of(inp)
+    idx, vals = lcsb.misa_indexer(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, k_prime=cfg.k_prime,
+                                  k_scale=t["k_scale"])
+    dense = lcsb.dsa_dense_logits(sh, t["q"], t["w"], t["k"], k_scale=t["k_scale"])
+    didx, dvals = lcsb.misa_topk(sh, dense, cfg.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, didx) and torch.equal(vals, dvals)
+    ctx = oracle.SeqContext(inp, 0)
+    gi = idx.cpu().numpy()
+    for i in sample_rows(cfg.q_per_seq, 12):
+        T = inp.q_pos0 + i
+        ok, _ = band_check(ctx.dense(i)[:T + 1], np.arange(T + 1), gi[0, i], cfg.topk)
+        assert ok, f"query {i}"
+
+
+def test_dagger_rerank_parity():
+    cfg = gen.small_config(m=40, n=3000, hh=64, b=64, h=8, k=128, kp=512, seed=32)
+    inp = gen.generate(cfg)
+    st = run_stages(inp)
+    t, sh = st["t"], st["sh"]
+    cand, _ = lcsb.misa_topk(sh, st["logits"], cfg.k_prime)
+    D = lcsb.dsa_dense_logits(sh, t["q"], t["w"], t["k"], cand=cand)
+    fidx, fvals = lcsb.misa_topk(sh, D, cfg.topk, cand=cand)
+    idx, vals = lcsb.misa_indexer(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, k_prime=cfg.k_prime)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, fidx) and torch.equal(vals, fvals)
+    dense = lcsb.dsa_dense_logits(sh, t["q"], t["w"], t["k"])
+    torch.cuda.synchronize()
+    ctx = oracle.SeqContext(inp, 0)
+    gc, gD = cand.cpu().numpy()[0], D.cpu().numpy()[0]
+    gdense = dense.cpu().numpy()[0]
+    gfi = fidx.cpu().numpy()[0]
+    for i in range(cfg.q_per_seq):
+        # re-ranked score of a candidate is bitwise the dense logit of that token
+        ok_c = gc[i] >= 0
+        assert np.array_equal(gD[i, :cfg.k_prime][ok_c], gdense[i, gc[i][ok_c]])
+        o = oracle.score_candidates(ctx.q[i], ctx.w[i], ctx.keys, gc[i].astype(np.int64))
+        ok, wst = logits_close(gD[i, :cfg.k_prime][None], o[None])
+        assert ok, f"rerank query {i} worst {wst}"
+        oi, _ = oracle.topk_row(gD[i, :cfg.k_prime].astype(np.float64), gc[i].astype(np.int64), cfg.topk)
+        assert np.array_equal(gfi[i], oi)
