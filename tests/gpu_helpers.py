@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 import long_context_sparse_block_amd as lcsb
+import oracle
 
 # Logits: bf16 inputs, fp32 accumulation -> within 1e-2 relative.  Near zero,
 # where the signed head sum cancels, the scale is the row's magnitude:
@@ -108,3 +109,109 @@ def sample_rows(M: int, n: int):
         return list(range(M))
     rows = np.unique(np.linspace(0, M - 1, n).round().astype(int))
     return rows.tolist()
+
+
+def f64(t):
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+_CTX = {}
+
+
+def ctx_of(inp, b):
+    """Oracle context of sequence b (widened keys + pooled keys), cached per input set."""
+    key = (id(inp), b)
+    if key not in _CTX:
+        if len(_CTX) > 8:
+            _CTX.clear()
+        _CTX[key] = (inp, oracle.SeqContext(inp, b))
+    return _CTX[key][1]
+
+
+def run_stages(inp, t=None, h=None, rows_for_logits=None):
+    t = upload(inp) if t is None else t
+    sh = shape_of(inp)
+    h = inp.cfg.h if h is None else h
+    pooled, tail = lcsb.misa_pool_keys(sh, t["k"], t["k_scale"])
+    heads, r = lcsb.misa_route_heads(sh, t["q"], t["w"], pooled, tail, h, want_scores=True)
+    logits = lcsb.misa_sparse_head_logits(sh, t["q"], t["w"], t["k"], heads, k_scale=t["k_scale"])
+    torch.cuda.synchronize()
+    return dict(t=t, sh=sh, pooled=pooled, tail=tail, heads=heads, r=r, logits=logits)
+
+
+def check_pool(inp, st, rows=None, seqs=None):
+    M = inp.cfg.q_per_seq
+    rows = range(M) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    for b in seqs:
+        ctx = ctx_of(inp, b)
+        gp = f64(st["pooled"][b])
+        scale = max(np.abs(ctx.pooled).max(), 1e-30) if ctx.pooled.size else 1.0
+        if ctx.pooled.size:
+            np.testing.assert_allclose(gp, ctx.pooled, rtol=1e-5, atol=1e-6 * scale)
+        gt = st["tail"][b]
+        for i in rows:
+            tl = ctx.tail(i)
+            g = f64(gt[i])
+            if tl is None:
+                assert not g.any()
+            else:
+                np.testing.assert_allclose(g, tl, rtol=1e-5, atol=1e-6 * max(np.abs(tl).max(), 1e-30))
+
+
+def check_route(inp, st, rows=None, seqs=None):
+    M, H, h = inp.cfg.q_per_seq, inp.cfg.n_heads, st["heads"].shape[-1]
+    rows = list(range(M)) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    gh = st["heads"].cpu().numpy()
+    gr = st["r"].cpu().numpy().astype(np.float64)
+    worst, inside = 0.0, 0
+    for b in seqs:
+        ctx = ctx_of(inp, b)
+        for i in rows:
+            S, r, heads = ctx.route(i, h)
+            ok, wst = logits_close(gr[b, i][None], r[None])
+            assert ok, f"router scores seq {b} query {i}: worst {wst}"
+            worst = max(worst, wst)
+            assert np.all(np.diff(gh[b, i]) > 0), "heads not ascending/distinct"
+            ok, n_in = band_check(r, np.arange(H), gh[b, i], h)
+            assert ok, f"heads seq {b} query {i}: gpu {gh[b, i]} oracle {heads}"
+            inside += n_in
+    return worst, inside
+
+
+def check_logits(inp, st, rows=None, seqs=None):
+    M = inp.cfg.q_per_seq
+    rows = list(range(M)) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    gh = st["heads"].cpu().numpy()
+    worst = 0.0
+    N = inp.cfg.n_keys
+    for b in seqs:
+        ctx = ctx_of(inp, b)
+        idx = torch.tensor(rows, device=st["logits"].device)
+        g = st["logits"][b].index_select(0, idx)[:, :N].cpu().numpy()
+        for n, i in enumerate(rows):
+            o = ctx.score(i, gh[b, i])
+            ok, wst = logits_close(g[n][None], o[None])
+            assert ok, f"logits seq {b} query {i}: worst {wst}"
+            worst = max(worst, wst)
+    return worst
+
+
+def check_topk_exact(inp, logits, k, idx, vals, rows=None, seqs=None):
+    """top-k of the GPU's own logits: the oracle decides on the same fp32 values."""
+    M = inp.cfg.q_per_seq
+    rows = list(range(M)) if rows is None else rows
+    seqs = range(inp.cfg.n_seq) if seqs is None else seqs
+    for b in seqs:
+        ridx = torch.tensor(rows, device=logits.device)
+        g = logits[b].index_select(0, ridx).cpu().numpy().astype(np.float64)
+        gi = idx[b].index_select(0, ridx).cpu().numpy()
+        gv = vals[b].index_select(0, ridx).cpu().numpy() if vals is not None else None
+        for n, i in enumerate(rows):
+            t = inp.q_pos0 + i
+            oi, ov = oracle.topk_prefix(g[n], t, k)
+            assert np.array_equal(gi[n], oi), f"top-k seq {b} query {i}"
+            if gv is not None:
+                assert np.array_equal(gv[n].astype(np.float64), ov)
