@@ -205,7 +205,7 @@ def main():
         cand = torch.empty((S, M, kp), dtype=torch.int32, device=dev)
         dlog = torch.empty((S, M, kp), dtype=torch.float32, device=dev)
         dagger_stages = misa_stages[:3] + [
-            ("topk_kprime", lambda: lcsb.misa_topk(sh, logits, kp, idx=cand, want_vals=False)),
+            ("topk_kprime", lambda: lcsb.misa_topk(sh, logits, kp, idx=cand, want_vals=False, sorted=False)),
             ("rerank", lambda: lcsb.dsa_dense_logits(sh, q, w, k, k_scale=ks, cand=cand, logits=dlog)),
             ("topk_final", lambda: lcsb.misa_topk(sh, dlog, K, cand=cand, idx=idx, vals=vals)),
         ]

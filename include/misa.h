@@ -164,15 +164,18 @@ misa_status dsa_dense_logits(const misa_shape* shape, const uint16_t* q, const f
  *                the token id is the column.
  * cand != NULL:  row considers columns c in [0, n_cols) with cand[b][i][c] >= 0;
  *                the token id is cand[b][i][c] (ids distinct within a row).
- * idx:  int32 [n_seq][M][k]; rows with fewer than k candidates are padded with -1.
+ * sorted != 0: idx lists the selection in that order.  sorted == 0: the same set in an
+ *                unspecified order (enough for a candidate list), cheaper.
+ * idx:  int32 [n_seq][M][k]; rows with fewer than k candidates are padded with -1 (the
+ *       padding always comes last).
  * vals: float [n_seq][M][k] (the selected values, -inf padding), or NULL.
  * 1 <= k <= MISA_MAX_TOPK.  logits: float [n_seq][M][ld], ld % 4 == 0, ld >= n_cols.
  * ws / ws_bytes: workspace of at least misa_topk_workspace_bytes() bytes
  *                (may be NULL when that is 0).
  */
 misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld,
-                      const int32_t* cand, int32_t n_cols, int32_t k, int32_t* idx,
-                      float* vals, void* ws, size_t ws_bytes, void* stream);
+                      const int32_t* cand, int32_t n_cols, int32_t k, int32_t sorted,
+                      int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream);
 
 size_t misa_topk_workspace_bytes(const misa_shape* shape, int32_t n_cols, int32_t k);
 

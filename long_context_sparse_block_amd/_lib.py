@@ -65,7 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_route_heads": [S, P, P, P, P, i32, P, P, P],
         "misa_sparse_head_logits": [S, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "dsa_dense_logits": [S, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
-        "misa_topk": [S, P, i64, P, i32, i32, P, P, P, sz, P],
+        "misa_topk": [S, P, i64, P, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
     }
     for name, args in sigs.items():
@@ -207,8 +207,9 @@ def dsa_dense_logits(shape: MisaShape, q, w, k, k_scale=None, cand=None, logits=
 
 
 def misa_topk(shape: MisaShape, logits, k: int, n_cols=None, cand=None, idx=None, vals=None,
-              want_vals=True, ws=None, stream=None):
-    """Top-k ids [n_seq, M, k] (int32, -1 padded) and values (fp32, -inf padded)."""
+              want_vals=True, sorted=True, ws=None, stream=None):
+    """Top-k ids [n_seq, M, k] (int32, -1 padded) and values (fp32, -inf padded);
+    sorted=False returns the same set in an unspecified order."""
     M = shape.q_per_seq
     _need(logits, torch.float32, (shape.n_seq, M, logits.shape[-1]), "logits")
     if cand is not None:
@@ -225,7 +226,7 @@ def misa_topk(shape: MisaShape, logits, k: int, n_cols=None, cand=None, idx=None
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
     st = lib.misa_topk(ctypes.byref(shape), _ptr(logits), int(logits.shape[-1]), _ptr(cand), int(n_cols),
-                       int(k), _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel() if ws is not None else 0),
+                       int(k), int(bool(sorted)), _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel() if ws is not None else 0),
                        _stream(stream))
     _check(st, "misa_topk")
     return idx, vals

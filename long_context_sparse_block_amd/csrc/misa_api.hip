@@ -169,8 +169,8 @@ size_t misa_topk_workspace_bytes(const misa_shape* shape, int32_t n_cols, int32_
 }
 
 misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld, const int32_t* cand,
-                      int32_t n_cols, int32_t k, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      int32_t n_cols, int32_t k, int32_t sorted, int32_t* idx, float* vals, void* ws,
+                      size_t ws_bytes, void* stream) {
   MISA_TRY(check_shape(shape));
   if (logits == nullptr || !aligned16(logits) || idx == nullptr) return MISA_ERR_INVALID_ARG;
   if (k < 1 || k > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
@@ -180,7 +180,7 @@ misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld, 
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   return from_hip(launch_topk(*shape, logits, ld, cand, n_cols, k, idx, vals, ws, ws_bytes,
-                              (hipStream_t)stream));
+                              (hipStream_t)stream, sorted != 0));
 }
 
 size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
@@ -217,8 +217,9 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
                                 tws_bytes, st));
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
   float* dlog = reinterpret_cast<float*>(base + L.dlog);
+  // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
   MISA_TRY(from_hip(launch_topk(*shape, logits, L.ld, nullptr, (int)shape->n_keys, k_prime, cand, nullptr,
-                                tws, tws_bytes, st)));
+                                tws, tws_bytes, st, /*sorted=*/false)));
   MISA_TRY(from_hip(launch_score_gather(*shape, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
   return from_hip(launch_topk(*shape, dlog, L.ld_d, cand, k_prime, topk, idx, vals, tws, tws_bytes, st));
 }

@@ -25,9 +25,10 @@ hipError_t launch_score_gather(const misa_shape& s, const uint16_t* q, const flo
                                int kdtype, const float* k_scale, const int32_t* cand, int n_cand,
                                float* logits, int64_t ld, hipStream_t st);
 
+// sorted = false writes the selected set in no particular order (candidate lists).
 hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, const int32_t* cand,
                        int n_cols, int k, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
-                       hipStream_t st);
+                       hipStream_t st, bool sorted = true);
 
 size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k);
 

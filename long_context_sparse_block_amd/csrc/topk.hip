@@ -5,30 +5,69 @@
 // "Metodologia: MISA" item 2).  Order: score descending, equal scores (with
 // -0.0 == +0.0) -> lower token id.
 //
-// Design: exact MSB-first radix select, one workgroup (8 waves) per row.
-// Every element becomes a unique 64-bit composite
+// Every element has a unique 64-bit composite
 //     (order-preserving uint32 of the score) << 32 | ~token_id
-// so "larger composite first" is exactly the required order and ties are
-// impossible.  Each pass streams the row (float4 loads) and builds an LDS
-// histogram of the next 12-bit digit among elements still matching the
-// selected prefix; a block scan from the top bin finds the bin holding the
-// k-th element.  As soon as the elements above that bin plus the bin itself
-// fit the LDS buffer, one more pass collects them, a bitonic sort in LDS
-// orders them, and the first k are written.  Usually one histogram pass
-// suffices, so a row is read twice (the second read mostly from cache).
+// so "larger composite first" is exactly the required order and no two
+// elements tie.  The candidate buffer holds raw (token id, score bits) pairs;
+// composites are formed only when candidates are ranked.
+//
+// Design: one workgroup per row, one read of the row from HBM.
+//  1. Threshold from a sample: every 32nd 128-byte line of the row (1/32 of it)
+//     is loaded and the score key of the k_s-th largest sampled element becomes
+//     the threshold, with k_s = 1.5 k (sample size / row length) + 16, so about
+//     1.5 k row elements are expected to pass.  (Rows that fit the buffer take
+//     every element.)
+//  2. Optimistic stream: the row is read in float4s with no workgroup barrier
+//     (the next four loads per thread in flight while four are filtered); a float compare against the threshold
+//     flags the candidates and a wave appends all of its candidates to the LDS
+//     buffer with one atomic (positions from three ballots).
+//  3. Only if that overflowed the buffer (then more than CAP >= k elements pass
+//     the threshold, so it is a proven bound) or let fewer than k through (then
+//     the threshold is dropped), the row is streamed again in lock-step:
+//     whenever the buffer could overflow on the next step it is compacted: an
+//     MSB-first radix select over the buffered composites finds a threshold
+//     with at least k buffered elements at or above it, and the rest is
+//     dropped.  At least k elements always sit at or above the threshold, so
+//     nothing below it can belong to the top k.
+//  4. The radix select cuts the buffer to exactly k candidates.  They are
+//     ranked by a counting sort on the top 11 bits of their composite span
+//     followed by a rank count inside each (small) bucket, and each is written
+//     straight to its output position.  Buckets too large for that fall back
+//     to a bitonic sort held in registers.  Candidate lists that only need the
+//     set skip the ranking.
+// Radix digits start at the highest bit in which the buffered composites
+// differ, so the histogram bins spread over the values actually present.
+// The result is exact for every input; the sample only decides how much
+// buffering and compaction work is done.
 #include "misa_common.h"
 #include "misa_launch.h"
 
 namespace misa {
 
-constexpr int kTopkThreads = 512;
-constexpr int kHistBins = 4096;
+constexpr int kDigit = 11;                 // radix digit width
+constexpr int kHistBins = 1 << kDigit;
+constexpr uint32_t kMaxRankBucket = 64;    // larger buckets -> bitonic fallback
 
-__device__ __forceinline__ uint64_t composite(float v, int32_t id) {
-  return ((uint64_t)order_key(v) << 32) | (uint64_t)(~(uint32_t)id);
+__device__ __forceinline__ uint64_t pack_raw(float v, int32_t id) {
+  return ((uint64_t)(uint32_t)id << 32) | (uint64_t)__float_as_uint(v);
+}
+__device__ __forceinline__ uint64_t raw_to_comp(uint64_t r) {
+  return ((uint64_t)order_key(__uint_as_float((uint32_t)r)) << 32) | (uint64_t)(~(uint32_t)(r >> 32));
+}
+__device__ __forceinline__ int32_t comp_id(uint64_t c) { return (int32_t)(~(uint32_t)c); }
+__device__ __forceinline__ float comp_val(uint64_t c) { return key_to_float((uint32_t)(c >> 32)); }
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// inclusive scan over the workgroup; returns the exclusive prefix of `x`
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, m), hi = __shfl_xor((uint32_t)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Workgroup-wide exclusive scan of x; *total receives the sum.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s_wave, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t v = x;
@@ -41,7 +80,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int wv = 0; wv < kTopkThreads / 64; ++wv) {
+  for (int wv = 0; wv < NT / 64; ++wv) {
     const uint32_t t = s_wave[wv];
     if (wv < wave) before += t;
     all += t;
@@ -51,19 +90,279 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
   return before + v - x;
 }
 
-template <int CAP>
-__global__ void __launch_bounds__(kTopkThreads) k_topk(const float* __restrict__ logits, int64_t ld,
-                                                       const int32_t* __restrict__ cand, int n_cols,
-                                                       int k, int64_t q_pos0, int M,
-                                                       int32_t* __restrict__ idx_out,
-                                                       float* __restrict__ val_out) {
-  __shared__ uint32_t s_hist[kHistBins];
+// Workgroup min and max of the composites of buf[0, n).
+template <int NT>
+__device__ void block_minmax(const uint64_t* buf, uint32_t n, uint64_t* s_red, uint64_t* mn, uint64_t* mx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t lo = ~0ull, hi = 0;
+  for (uint32_t e = threadIdx.x; e < n; e += NT) {
+    const uint64_t c = raw_to_comp(buf[e]);
+    lo = c < lo ? c : lo;
+    hi = c > hi ? c : hi;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t a = shfl_xor_u64(lo, o), b = shfl_xor_u64(hi, o);
+    lo = a < lo ? a : lo;
+    hi = b > hi ? b : hi;
+  }
+  if (lane == 0) {
+    s_red[2 * wave] = lo;
+    s_red[2 * wave + 1] = hi;
+  }
+  __syncthreads();
+  lo = ~0ull;
+  hi = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    lo = s_red[2 * w] < lo ? s_red[2 * w] : lo;
+    hi = s_red[2 * w + 1] > hi ? s_red[2 * w + 1] : hi;
+  }
+  __syncthreads();
+  *mn = lo;
+  *mx = hi;
+}
+
+__device__ __forceinline__ int bit_width64(uint64_t x) { return x ? 64 - __clzll((long long)x) : 0; }
+
+// Radix select over the composites of the n raw entries of buf: returns a
+// threshold T with need <= #{c >= T} <= limit (the upper bound can only fail
+// for duplicate entries); with limit == need it selects exactly the need
+// largest.  Requires 1 <= need <= n.  Every thread of the workgroup must call it.
+template <int NT>
+__device__ uint64_t select_threshold(const uint64_t* buf, uint32_t n, uint32_t need, uint32_t limit,
+                                     uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint64_t* s_red) {
+  const int tid = threadIdx.x;
+  constexpr int BPT = kHistBins / NT;  // bins per thread
+  uint64_t cmin, cmax;
+  block_minmax<NT>(buf, n, s_red, &cmin, &cmax);
+  const int nb = bit_width64(cmax - cmin);
+  if (nb == 0) return cmin;
+  // digits over x = c - cmin, from the highest bit in which the composites differ
+  int shift = nb > kDigit ? nb - kDigit : 0;
+  int width = nb - shift;
+  uint64_t prefix = 0, pmask = 0;
+  uint32_t above = 0;
+  for (;;) {
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int e = tid; e < kHistBins; e += NT) s_hist[e] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < n; e += NT) {
+      const uint64_t x = raw_to_comp(buf[e]) - cmin;
+      if ((x & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(x >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // rank order r = 0 is the highest bin; thread owns r in [BPT*tid, BPT*tid+BPT)
+    uint32_t hv[BPT], ls = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      hv[u] = s_hist[kHistBins - 1 - (BPT * tid + u)];
+      ls += hv[u];
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan<NT>(ls, s_wave, &total);
+    const uint32_t need_here = need - above;   // >= 1, <= total
+    if (excl < need_here && need_here <= excl + ls) {
+      uint32_t c = excl;
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        if (c + hv[u] >= need_here) {
+          s_sel[0] = kHistBins - 1 - (BPT * tid + u);
+          s_sel[1] = c;
+          s_sel[2] = hv[u];
+          break;
+        }
+        c += hv[u];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = s_sel[0], cab = s_sel[1], cnt = s_sel[2];
+    __syncthreads();
+    above += cab;
+    prefix |= (uint64_t)bin << shift;
+    pmask |= (uint64_t)dmask << shift;
+    if (above + cnt <= limit || shift == 0) return cmin + prefix;
+    if (shift >= kDigit) {
+      shift -= kDigit;
+      width = kDigit;
+    } else {
+      width = shift;
+      shift = 0;
+    }
+  }
+}
+
+// Keep the raw entries whose composite is >= T; returns the new count.  In
+// place, in chunks of 4*NT entries: kept entries only move to lower positions,
+// and each chunk is fully read (scan barrier) before any of it is written.
+template <int NT>
+__device__ uint32_t compact(uint64_t* buf, uint32_t n, uint64_t T, uint32_t* s_wave) {
+  const int tid = threadIdx.x;
+  uint32_t base = 0;
+  for (uint32_t c0 = 0; c0 < n; c0 += 4 * NT) {
+    uint64_t v[4];
+    bool keep[4];
+    uint32_t nk = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t e = c0 + tid + u * NT;
+      v[u] = (e < n) ? buf[e] : 0;
+      keep[u] = (e < n) && raw_to_comp(v[u]) >= T;
+      nk += keep[u];
+    }
+    uint32_t total;
+    uint32_t pos = base + block_exclusive_scan<NT>(nk, s_wave, &total);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (keep[u]) buf[pos++] = v[u];
+    base += total;
+    __syncthreads();
+  }
+  return base;
+}
+
+// Bitonic sort of the composites of the first cnt raw entries of buf held in
+// registers (E consecutive network positions per thread; strides below E are
+// in-thread, below 64E lane shuffles, wider ones go through LDS), then the
+// top k are written.  Positions past cnt hold 0, below every composite.
+template <int NT, int E>
+__device__ void bitonic_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out,
+                              float* val_out) {
+  const int tid = threadIdx.x;
+  uint64_t v[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const uint32_t p = tid * E + j;
+    v[j] = (p < cnt) ? raw_to_comp(buf[p]) : 0;
+  }
+  __syncthreads();
+  constexpr uint32_t L = (uint32_t)NT * E;
+  for (uint32_t size = 2; size <= L; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t o[E];
+      if (stride >= 64u * E) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) buf[tid * E + j] = v[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < E; ++j) o[j] = buf[(tid * E + j) ^ stride];
+        __syncthreads();
+      } else if (stride >= (uint32_t)E) {
+        const int lx = (int)(stride / E);
+#pragma unroll
+        for (int j = 0; j < E; ++j) o[j] = shfl_xor_u64(v[j], lx);
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) o[j] = v[j ^ stride];
+      }
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const uint32_t p = tid * E + j;
+        const bool take_max = ((p & size) == 0) == ((p & stride) == 0);
+        const uint64_t hi = v[j] > o[j] ? v[j] : o[j];
+        const uint64_t lo = v[j] > o[j] ? o[j] : v[j];
+        v[j] = take_max ? hi : lo;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const uint32_t p = tid * E + j;
+    if (p < (uint32_t)k && p < cnt) {
+      idx_out[row * k + p] = comp_id(v[j]);
+      if (val_out) val_out[row * k + p] = comp_val(v[j]);
+    }
+  }
+}
+
+// Order the first cnt (<= CAP/2) raw entries of buf by composite and write the
+// top k of them, then the padding.  Counting sort into 2048 buckets of the
+// composite span (stored in buf[CAP/2 ...]), then each candidate's rank inside
+// its bucket by direct comparison.
+template <int CAP, int NT>
+__device__ void rank_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out, float* val_out,
+                           uint32_t* s_hist, uint32_t* s_wave, uint64_t* s_red) {
+  const int tid = threadIdx.x;
+  constexpr int BPT = kHistBins / NT;
+  uint64_t* sorted = buf + CAP / 2;
+  if (cnt > 0) {
+    uint64_t cmin, cmax;
+    block_minmax<NT>(buf, cnt, s_red, &cmin, &cmax);
+    const int nb = bit_width64(cmax - cmin);
+    const int shift = nb > kDigit ? nb - kDigit : 0;
+    for (int e = tid; e < kHistBins; e += NT) s_hist[e] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < cnt; e += NT)
+      atomicAdd(&s_hist[(uint32_t)((raw_to_comp(buf[e]) - cmin) >> shift)], 1u);
+    __syncthreads();
+    // bucket starts, highest bucket first: thread owns buckets 2047-BPT*tid-u
+    uint32_t hv[BPT], ls = 0, big = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      hv[u] = s_hist[kHistBins - 1 - (BPT * tid + u)];
+      ls += hv[u];
+      big = hv[u] > big ? hv[u] : big;
+    }
+    uint32_t total;
+    uint32_t start = block_exclusive_scan<NT>(ls, s_wave, &total);
+    const uint32_t n_big = __syncthreads_or(big > kMaxRankBucket);
+    if (n_big) {
+      constexpr int EMAX = CAP / (2 * NT);
+      if (cnt <= (uint32_t)NT) bitonic_write<NT, 1>(buf, cnt, k, row, idx_out, val_out);
+      else if (cnt <= 2u * NT) bitonic_write<NT, 2>(buf, cnt, k, row, idx_out, val_out);
+      else if (cnt <= 4u * NT || EMAX <= 4) bitonic_write<NT, (EMAX < 4 ? EMAX : 4)>(buf, cnt, k, row, idx_out, val_out);
+      else bitonic_write<NT, EMAX>(buf, cnt, k, row, idx_out, val_out);
+    } else {
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        s_hist[kHistBins - 1 - (BPT * tid + u)] = start;   // cursor = bucket start
+        start += hv[u];
+      }
+      __syncthreads();
+      for (uint32_t e = tid; e < cnt; e += NT) {
+        const uint64_t c = raw_to_comp(buf[e]);
+        const uint32_t d = (uint32_t)((c - cmin) >> shift);
+        sorted[atomicAdd(&s_hist[d], 1u)] = c;
+      }
+      __syncthreads();
+      // s_hist[d] is now the end of bucket d; bucket d spans [end(d+1), end(d))
+      for (uint32_t e = tid; e < cnt; e += NT) {
+        const uint64_t c = sorted[e];
+        const uint32_t d = (uint32_t)((c - cmin) >> shift);
+        const uint32_t b0 = (d + 1 < (uint32_t)kHistBins) ? s_hist[d + 1] : 0;
+        const uint32_t b1 = s_hist[d];
+        uint32_t r = b0;
+        for (uint32_t q = b0; q < b1; ++q) r += sorted[q] > c;
+        if (r < (uint32_t)k) {
+          idx_out[row * k + r] = comp_id(c);
+          if (val_out) val_out[row * k + r] = comp_val(c);
+        }
+      }
+    }
+  }
+  for (uint32_t p = cnt + tid; p < (uint32_t)k; p += NT) {
+    idx_out[row * k + p] = -1;
+    if (val_out) val_out[row * k + p] = -__builtin_inff();
+  }
+}
+
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits, int64_t ld,
+                                                const int32_t* __restrict__ cand, int n_cols, int k,
+                                                int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
+                                                float* __restrict__ val_out, int sorted) {
+  constexpr int VPT = 2;                  // float4s per thread per lock-step (robust) step
+  constexpr int STEP = 4 * VPT * NT;      // elements per lock-step step
+  static_assert(CAP / 2 >= STEP, "a lock-step step must fit the free half of the buffer");
   __shared__ uint64_t s_buf[CAP];
-  __shared__ uint32_t s_wave[kTopkThreads / 64];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_wave[NT / 64];
+  __shared__ uint64_t s_red[2 * (NT / 64)];
+  __shared__ uint32_t s_sel[3];
   __shared__ uint32_t s_count;
-  __shared__ uint32_t s_sel_bin, s_sel_above;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t row = (int64_t)b * M + i;
   const int64_t t = q_pos0 + i;
@@ -72,140 +371,190 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(const float* __restrict__
   const int32_t* crow = cand ? cand + row * (int64_t)n_cols : nullptr;
   // float4 / int4 loads need 16-byte aligned rows: ld % 4 == 0 always, and the
   // candidate rows when n_cols % 4 == 0; otherwise every element is read singly
-  const int n4 = (crow == nullptr || (n_cols & 3) == 0) ? (n >> 2) : 0;
+  const bool vec = (crow == nullptr || (n_cols & 3) == 0);
 
-  // visit every candidate element: f(composite)
-  auto visit = [&](auto&& f) {
-    for (int e = tid; e < n4; e += kTopkThreads) {
-      const float4 v = reinterpret_cast<const float4*>(lrow)[e];
-      int4 id;
-      if (crow) id = reinterpret_cast<const int4*>(crow)[e];
-      else id = make_int4(4 * e, 4 * e + 1, 4 * e + 2, 4 * e + 3);
-      if (id.x >= 0) f(composite(v.x, id.x));
-      if (id.y >= 0) f(composite(v.y, id.y));
-      if (id.z >= 0) f(composite(v.z, id.z));
-      if (id.w >= 0) f(composite(v.w, id.w));
-    }
-    for (int c = 4 * n4 + tid; c < n; c += kTopkThreads) {
-      const int id = crow ? crow[c] : c;
-      if (id >= 0) f(composite(lrow[c], id));
+  // the 4 elements starting at column e0 (id -1 = no candidate)
+  auto fetch4 = [&](int e0, float4& v, int4& id) {
+    if (vec && e0 + 3 < n) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lrow) + (e0 >> 2));
+      v = make_float4(x[0], x[1], x[2], x[3]);
+      if (crow) id = reinterpret_cast<const int4*>(crow)[e0 >> 2];
+      else id = make_int4(e0, e0 + 1, e0 + 2, e0 + 3);
+    } else {
+      float vv[4];
+      int ii[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u;
+        vv[u] = (e < n) ? lrow[e] : 0.f;
+        ii[u] = (e < n) ? (crow ? crow[e] : e) : -1;
+      }
+      v = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      id = make_int4(ii[0], ii[1], ii[2], ii[3]);
     }
   };
+  // append the flagged elements of the wave's float4s with one LDS atomic;
+  // entries past CAP are counted but dropped
+  auto append4 = [&](const float4& v, const int4& id, bool f0, bool f1, bool f2, bool f3) {
+    const uint32_t c = (uint32_t)f0 + f1 + f2 + f3;
+    const uint64_t m0 = __ballot(c & 1u), m1 = __ballot(c & 2u), m2 = __ballot(c & 4u);
+    if ((m0 | m1 | m2) == 0) return;
+    uint32_t pos = lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2);
+    uint32_t base = 0;
+    if (lane == __ffsll((unsigned long long)__ballot(1)) - 1)   // first active lane
+      base = atomicAdd(&s_count, (uint32_t)(__popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2)));
+    pos += __builtin_amdgcn_readfirstlane(base);
+    if (f0) { if (pos < (uint32_t)CAP) s_buf[pos] = pack_raw(v.x, id.x); ++pos; }
+    if (f1) { if (pos < (uint32_t)CAP) s_buf[pos] = pack_raw(v.y, id.y); ++pos; }
+    if (f2) { if (pos < (uint32_t)CAP) s_buf[pos] = pack_raw(v.z, id.z); ++pos; }
+    if (f3) { if (pos < (uint32_t)CAP) s_buf[pos] = pack_raw(v.w, id.w); }
+  };
+  auto append_ge = [&](const float4& v, const int4& id, uint64_t T) {   // exact composite test
+    append4(v, id, id.x >= 0 && raw_to_comp(pack_raw(v.x, id.x)) >= T,
+            id.y >= 0 && raw_to_comp(pack_raw(v.y, id.y)) >= T,
+            id.z >= 0 && raw_to_comp(pack_raw(v.z, id.z)) >= T,
+            id.w >= 0 && raw_to_comp(pack_raw(v.w, id.w)) >= T);
+  };
 
-  uint64_t prefix = 0, pmask = 0;
-  uint32_t above = 0, need = 0;
-  bool take_all = false;
-  int shift = 52;
-  for (int pass = 0;; ++pass) {
-    const uint32_t dmask = (shift >= 4) ? 0xFFFu : 0xFu;
-    for (int e = tid; e < kHistBins; e += kTopkThreads) s_hist[e] = 0;
-    __syncthreads();
-    visit([&](uint64_t c) {
-      if ((c & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(c >> shift) & dmask], 1u);
-    });
-    __syncthreads();
-    // rank order r = 0 is the highest bin; thread owns r in [8*tid, 8*tid+8)
-    uint32_t h8[8], ls = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      h8[u] = s_hist[kHistBins - 1 - (8 * tid + u)];
-      ls += h8[u];
-    }
-    uint32_t total;
-    const uint32_t excl = block_exclusive_scan(ls, s_wave, &total);
-    if (pass == 0) {
-      const uint32_t n_valid = total;
-      need = min((uint32_t)k, n_valid);
-      if (n_valid <= (uint32_t)CAP) {
-        take_all = true;
-        break;
-      }
-    }
-    if (excl < need && need <= excl + ls) {
-      uint32_t c = excl;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (c + h8[u] >= need) {
-          s_sel_bin = kHistBins - 1 - (8 * tid + u);
-          s_sel_above = c;
-          break;
-        }
-        c += h8[u];
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = s_sel_bin, cab = s_sel_above;
-    const uint32_t bin_count = s_hist[bin];
-    above += cab;
-    need -= cab;
-    prefix |= (uint64_t)bin << shift;
-    pmask |= (uint64_t)dmask << shift;
-    __syncthreads();
-    if (above + bin_count <= (uint32_t)CAP || shift == 0) break;
-    shift = (shift >= 16) ? shift - 12 : (shift == 4 ? 0 : 4);
-  }
-
-  // collect the elements above the threshold bin and the bin itself
   if (tid == 0) s_count = 0;
   __syncthreads();
-  visit([&](uint64_t c) {
-    const uint64_t top = c & pmask;
-    if (take_all || top >= prefix) {
-      const uint32_t pos = atomicAdd(&s_count, 1u);
-      if (pos < (uint32_t)CAP) s_buf[pos] = c;   // can only overflow on duplicate candidate ids
+
+  // 1. threshold key from a sample of every 32nd 128-byte line; rows that fit
+  //    the buffer keep T0 = 0 (every element passes)
+  uint64_t T0 = 0;
+  const int n_samp = (n / 32) / 32;   // sampled lines
+  if (n > CAP && n_samp > 0) {
+    for (int e0 = 0; e0 < n_samp * 8; e0 += NT) {   // 8 float4 per line; every lane takes part
+      const int e = e0 + tid;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      int4 id = make_int4(-1, -1, -1, -1);
+      if (e < n_samp * 8) fetch4((e / 8) * 32 * 32 + (e % 8) * 4, v, id);
+      append4(v, id, id.x >= 0, id.y >= 0, id.z >= 0, id.w >= 0);
     }
-  });
-  __syncthreads();
-  const uint32_t cnt = min(s_count, (uint32_t)CAP);
-  // sort only the smallest power of two holding cnt entries
-  uint32_t len = 2;
-  while (len < cnt) len <<= 1;
-  for (uint32_t e = cnt + tid; e < len; e += kTopkThreads) s_buf[e] = 0;
-  __syncthreads();
-  for (uint32_t size = 2; size <= len; size <<= 1) {
-    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-      for (uint32_t e = tid; e < len / 2; e += kTopkThreads) {
-        const uint32_t a = (e / stride) * 2 * stride + (e % stride);
-        const uint32_t c = a + stride;
-        const uint64_t x = s_buf[a], y = s_buf[c];
-        const bool desc = (a & size) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          s_buf[a] = y;
-          s_buf[c] = x;
-        }
+    __syncthreads();
+    const uint32_t ns = min(s_count, (uint32_t)CAP);
+    const uint64_t ks = (uint64_t)3 * k * ns / (2 * (uint64_t)n) + 16;
+    if (ks < ns) {
+      // keep only the score-key part: passing then depends on the score alone
+      T0 = select_threshold<NT>(s_buf, ns, (uint32_t)ks, (uint32_t)ks, s_hist, s_wave, s_sel, s_red) &
+           0xFFFFFFFF00000000ull;
+    }
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+  }
+
+  // 2. optimistic stream: v >= tf  <=>  composite >= T0 (T0 has a zero id part)
+  {
+    float tf = -__builtin_inff();
+    if (T0 != 0) {
+      tf = key_to_float((uint32_t)(T0 >> 32));
+      if (tf != tf) tf = -__builtin_inff();   // a key prefix below every finite value
+    }
+    constexpr int U = 4;
+    constexpr int SPAN = 4 * U * NT;
+    float4 nv[U];
+    int4 nid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) fetch4(4 * (tid + u * NT), nv[u], nid[u]);
+    for (int base = 0; base < n; base += SPAN) {
+      float4 v[U];
+      int4 id[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v[u] = nv[u];
+        id[u] = nid[u];
       }
+      if (base + SPAN < n) {   // next loads in flight while this batch is filtered
+#pragma unroll
+        for (int u = 0; u < U; ++u) fetch4(base + SPAN + 4 * (tid + u * NT), nv[u], nid[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        append4(v[u], id[u], id[u].x >= 0 && v[u].x >= tf, id[u].y >= 0 && v[u].y >= tf,
+                id[u].z >= 0 && v[u].z >= tf, id[u].w >= 0 && v[u].w >= tf);
+    }
+  }
+  __syncthreads();
+  const uint32_t got = s_count;
+  __syncthreads();
+
+  // 3. lock-step stream with compaction when the optimistic pass overflowed
+  //    (T0 is then a proven bound) or let fewer than k through while filtering
+  if (got > (uint32_t)CAP || (got < (uint32_t)k && T0 != 0)) {
+    uint64_t T = (got > (uint32_t)CAP) ? T0 : 0;
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    const int n_steps = (n + STEP - 1) / STEP;
+    float4 nv[VPT];
+    int4 nid[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) fetch4(4 * (tid + u * NT), nv[u], nid[u]);
+    for (int s = 0; s < n_steps; ++s) {
+      float4 v[VPT];
+      int4 id[VPT];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        v[u] = nv[u];
+        id[u] = nid[u];
+      }
+      if (s + 1 < n_steps) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) fetch4((s + 1) * STEP + 4 * (tid + u * NT), nv[u], nid[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) append_ge(v[u], id[u], T);
       __syncthreads();
+      const uint32_t cnt = min(s_count, (uint32_t)CAP);
+      if (cnt > (uint32_t)(CAP - STEP) && s + 1 < n_steps) {
+        // make room: a threshold with at least k buffered elements above it
+        T = select_threshold<NT>(s_buf, cnt, min((uint32_t)k, cnt), (uint32_t)((k + CAP / 2) / 2), s_hist,
+                                 s_wave, s_sel, s_red);
+        const uint32_t nc = compact<NT>(s_buf, cnt, T, s_wave);
+        if (tid == 0) s_count = nc;
+        __syncthreads();
+      }
     }
   }
-  const uint32_t n_out = min((uint32_t)k, cnt);
-  for (int e = tid; e < k; e += kTopkThreads) {
-    int32_t id = -1;
-    float v = -__builtin_inff();
-    if ((uint32_t)e < n_out) {
-      const uint64_t c = s_buf[e];
-      id = (int32_t)(~(uint32_t)c);
-      v = key_to_float((uint32_t)(c >> 32));
-    }
-    idx_out[row * k + e] = id;
-    if (val_out) val_out[row * k + e] = v;
+
+  // 4. exactly the top min(k, count)
+  uint32_t cnt = min(s_count, (uint32_t)CAP);
+  __syncthreads();
+  const uint32_t kk = min((uint32_t)k, cnt);
+  if (cnt > kk) {
+    const uint64_t Tk = select_threshold<NT>(s_buf, cnt, kk, kk, s_hist, s_wave, s_sel, s_red);
+    cnt = compact<NT>(s_buf, cnt, Tk, s_wave);
   }
+  cnt = min(cnt, (uint32_t)(CAP / 2));   // more only with duplicate candidate ids
+  if (!sorted) {   // the set only (any order): candidate lists
+    for (int e = tid; e < k; e += NT) {
+      int32_t id = -1;
+      float v = -__builtin_inff();
+      if ((uint32_t)e < cnt) {
+        const uint64_t c = raw_to_comp(s_buf[e]);
+        id = comp_id(c);
+        v = comp_val(c);
+      }
+      idx_out[row * k + e] = id;
+      if (val_out) val_out[row * k + e] = v;
+    }
+    return;
+  }
+  rank_write<CAP, NT>(s_buf, cnt, k, row, idx_out, val_out, s_hist, s_wave, s_red);
 }
 
 size_t topk_workspace_bytes(const misa_shape&, int, int) { return 0; }
 
 hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, const int32_t* cand,
-                       int n_cols, int k, int32_t* idx, float* vals, void*, size_t, hipStream_t st) {
+                       int n_cols, int k, int32_t* idx, float* vals, void*, size_t, hipStream_t st,
+                       bool sorted) {
   dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
-  dim3 block(kTopkThreads);
-  if (k <= 512)
-    hipLaunchKernelGGL(k_topk<1024>, grid, block, 0, st, logits, ld, cand, n_cols, k, s.q_pos0,
-                       s.q_per_seq, idx, vals);
-  else if (k <= 2048)
-    hipLaunchKernelGGL(k_topk<4096>, grid, block, 0, st, logits, ld, cand, n_cols, k, s.q_pos0,
-                       s.q_per_seq, idx, vals);
+  // CAP/2 >= max(k, one lock-step step of 4096 elements)
+  if (k <= 4096)
+    hipLaunchKernelGGL((k_topk<8192, 512>), grid, dim3(512), 0, st, logits, ld, cand, n_cols, k, s.q_pos0,
+                       s.q_per_seq, idx, vals, (int)sorted);
   else
-    hipLaunchKernelGGL(k_topk<16384>, grid, block, 0, st, logits, ld, cand, n_cols, k, s.q_pos0,
-                       s.q_per_seq, idx, vals);
+    hipLaunchKernelGGL((k_topk<16384, 512>), grid, dim3(512), 0, st, logits, ld, cand, n_cols, k,
+                       s.q_pos0, s.q_per_seq, idx, vals, (int)sorted);
   return hipGetLastError();
 }
 

@@ -99,10 +99,10 @@ def test_logits_check_ld_and_h(lib):
 def test_topk_checks(lib):
     s = shape()
     f = lib.misa_topk
-    assert f(ctypes.byref(s), FAKE, 64, None, 64, 0, FAKE, None, None, 0, None) == -1
-    assert f(ctypes.byref(s), FAKE, 64, None, 64, 8193, FAKE, None, None, 0, None) == -1
-    assert f(ctypes.byref(s), FAKE, 64, None, 65, 4, FAKE, None, None, 0, None) == -1     # ld < n_cols
-    assert f(ctypes.byref(s), FAKE, 64, None, 64, 4, None, None, None, 0, None) == -1     # idx null
+    assert f(ctypes.byref(s), FAKE, 64, None, 64, 0, 1, FAKE, None, None, 0, None) == -1
+    assert f(ctypes.byref(s), FAKE, 64, None, 64, 8193, 1, FAKE, None, None, 0, None) == -1
+    assert f(ctypes.byref(s), FAKE, 64, None, 65, 4, 1, FAKE, None, None, 0, None) == -1     # ld < n_cols
+    assert f(ctypes.byref(s), FAKE, 64, None, 64, 4, 1, None, None, None, 0, None) == -1     # idx null
 
 
 def test_indexer_checks_and_workspace(lib):
@@ -123,7 +123,7 @@ def test_empty_query_set_is_a_no_op(lib):
     s = shape(q_per_seq=0, q_pos0=64)
     assert lib.misa_sparse_head_logits(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 64,
                                        None) == 0
-    assert lib.misa_topk(ctypes.byref(s), FAKE, 64, None, 64, 4, FAKE, None, None, 0, None) == 0
+    assert lib.misa_topk(ctypes.byref(s), FAKE, 64, None, 64, 4, 1, FAKE, None, None, 0, None) == 0
 
 
 def test_workspace_size_of_the_long_context_chunk(lib):

@@ -289,3 +289,44 @@ def test_dagger_rerank_parity():
         assert ok, f"rerank query {i} worst {wst}"
         oi, _ = oracle.topk_row(gD[i, :cfg.k_prime].astype(np.float64), gc[i].astype(np.int64), cfg.topk)
         assert np.array_equal(gfi[i], oi)
+
+
+@pytest.mark.parametrize("kind", ["sample_too_high", "sample_too_low", "ascending"])
+def test_topk_rows_that_defeat_the_sampled_threshold(kind):
+    # the top-k samples every 32nd 128-byte line to pick its first threshold;
+    # these rows make that guess wrong in both directions, forcing the exact
+    # fallback stream (rescan without threshold, or lock-step with compaction)
+    M, N, k = 3, 131072, 2048
+    line = np.arange(N) // 32
+    sampled = (line % 32) == 0
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((1, M, N)).astype(np.float32)
+    if kind == "sample_too_high":
+        vals = base.copy()
+        vals[0, :, sampled & (np.arange(N) % 32 == 7)] = 100.0     # 128 huge values, all sampled
+    elif kind == "sample_too_low":
+        vals = np.where(sampled, base - 10.0, base + 10.0).astype(np.float32)
+    else:
+        vals = np.broadcast_to(np.arange(N, dtype=np.float32), (1, M, N)).copy()
+    sh = lcsb.make_shape(1, M, N, N - M, 1, 1)
+    lg = torch.from_numpy(vals).to(torch.device("cuda:0"))
+    idx, v = lcsb.misa_topk(sh, lg, k)
+    check_topk_exact_arrays(vals, N - M, k, idx.cpu().numpy(), v.cpu().numpy())
+
+
+@pytest.mark.parametrize("k", [300, 2048, 8192])
+def test_topk_unsorted_returns_the_same_set(k):
+    rng = np.random.default_rng(6)
+    M, N = 4, 20000
+    vals = rng.standard_normal((1, M, N)).astype(np.float32)
+    vals[0, 1, :] = np.round(vals[0, 1, :])            # ties
+    sh = lcsb.make_shape(1, M, N, N - M, 1, 1)
+    lg = torch.from_numpy(vals).to(torch.device("cuda:0"))
+    si, sv = lcsb.misa_topk(sh, lg, k)
+    ui, uv = lcsb.misa_topk(sh, lg, k, sorted=False)
+    si, ui, uv = si.cpu().numpy(), ui.cpu().numpy(), uv.cpu().numpy()
+    for i in range(M):
+        n_ok = (si[0, i] >= 0).sum()
+        assert np.all(ui[0, i, n_ok:] == -1)
+        assert sorted(ui[0, i, :n_ok].tolist()) == sorted(si[0, i, :n_ok].tolist())
+        assert np.array_equal(uv[0, i, :n_ok], vals[0, i, ui[0, i, :n_ok]])
