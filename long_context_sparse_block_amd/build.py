@@ -38,6 +38,8 @@ def build_library(verbose: bool = False, extra=()) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     common = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              # MFMA results straight into VGPRs (no accumulator-register round trip)
+              "-mllvm", "-amdgpu-mfma-vgpr-form=1",
               "-I", INCLUDE, "-I", CSRC, *extra]
     procs = []
     for src in sources():

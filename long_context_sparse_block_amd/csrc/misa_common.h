@@ -50,15 +50,21 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return v.x;
 }
 
+// ReLU as an integer max on the bit pattern: non-negative floats are
+// non-negative integers and negative floats negative ones, so max(bits, 0)
+// keeps x >= 0 and gives +0.0 otherwise.  One VALU op, and unlike fmaxf no
+// NaN canonicalisation (inputs are finite).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Canonical per-(query, key) reduction of one quad of four head terms:
 //   p = fma(w3, relu(x3), fma(w2, relu(x2), fma(w1, relu(x1), fma(w0, relu(x0), 0))))
 // Every kernel that must agree bitwise with another uses exactly this chain.
 __device__ __forceinline__ float quad_chain(const f32x4 x, float w0, float w1, float w2, float w3) {
   float p = 0.0f;
-  p = __builtin_fmaf(w0, __builtin_fmaxf(x[0], 0.0f), p);
-  p = __builtin_fmaf(w1, __builtin_fmaxf(x[1], 0.0f), p);
-  p = __builtin_fmaf(w2, __builtin_fmaxf(x[2], 0.0f), p);
-  p = __builtin_fmaf(w3, __builtin_fmaxf(x[3], 0.0f), p);
+  p = __builtin_fmaf(w0, relu(x[0]), p);
+  p = __builtin_fmaf(w1, relu(x[1]), p);
+  p = __builtin_fmaf(w2, relu(x[2]), p);
+  p = __builtin_fmaf(w3, relu(x[3]), p);
   return p;
 }
 

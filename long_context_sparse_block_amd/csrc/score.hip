@@ -50,23 +50,19 @@ struct KStage {
   uint4 r[kPerThread];
   float sc;
 
-  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int64_t key0, int64_t N,
-                                       int tid) {
+  // Unconditional loads (rows past N read row N-1 instead; those keys are never
+  // stored): no exec-masked loads, so waiting for this prefetch never becomes a
+  // full vmcnt(0) in the compute that overlaps it.
+  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int tid) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
       const int e = tid + u * NT;
       const int key = e / kVecPerKey;
       const int c = e % kVecPerKey;
-      const int64_t kk = key0 + key;
-      if (kk < N)
-        r[u] = reinterpret_cast<const uint4*>(kbase)[kk * kVecPerKey + c];
-      else
-        r[u] = make_uint4(0, 0, 0, 0);
+      const int kk = min(key0 + key, N - 1);
+      r[u] = reinterpret_cast<const uint4*>(kbase)[(int64_t)kk * kVecPerKey + c];
     }
-    if (KDT == MISA_K_FP8_E4M3) {
-      sc = 0.f;
-      if (tid < KT && key0 + tid < N) sc = sbase[key0 + tid];
-    }
+    if (KDT == MISA_K_FP8_E4M3) sc = sbase[min(key0 + (tid % KT), N - 1)];
   }
 
   __device__ __forceinline__ void store(uint16_t* s_k, float* s_sc, int tid) const {
@@ -121,8 +117,27 @@ __device__ __forceinline__ void fill_neg_inf(float* logits, int64_t ld, int b, i
 }
 
 // ---------------------------------------------------------------------------
+// Raw buffer resource over [base, base + bytes): buffer stores outside it are
+// dropped by the hardware range check (gfx9-family descriptor word 3).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  // the b32 store takes the raw 32-bit pattern (an int), not a value to convert
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, (int)byte_off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // h <= 8: 8 queries per wave (2 groups x 2 head quads = 4 MFMA row blocks),
-// 32 queries per workgroup, 64-key tiles.
+// 32 queries per workgroup, 64-key tiles.  Per 16-key column block a wave
+// issues its 16 MFMAs first and then the two epilogues, so the matrix pipe
+// and the vector ALU overlap; the causal mask is applied only on blocks that
+// touch the diagonal.  Every block ends in exactly two buffer stores per lane
+// (rows past M and keys past N fall outside the store resource and are
+// dropped), and the next tile's prefetch is unconditional, so the compiler
+// can count outstanding memory operations exactly and never waits for the
+// logit stores.  Key positions are 32-bit (N <= 2^30).
 // ---------------------------------------------------------------------------
 template <int KDT>
 __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q,
@@ -130,53 +145,76 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
                                                   const void* __restrict__ kptr,
                                                   const float* __restrict__ kscale,
                                                   const int32_t* __restrict__ heads, int h,
-                                                  float* __restrict__ logits, int64_t ld, int64_t N,
-                                                  int64_t q_pos0, int M, int H, int n_qtiles,
+                                                  float* __restrict__ logits, int64_t ld, int64_t N64,
+                                                  int64_t q_pos0_64, int M, int H, int n_qtiles,
                                                   int n_ksplits, int64_t KR) {
   constexpr int NT = 256, KT = 64, QT = 32;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KT * kKRow];
   __shared__ float s_sc[2][KT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = (int)N64, q_pos0 = (int)q_pos0_64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
   const int g = lane >> 4, p16 = lane & 15;
   const int b = blockIdx.y;
-  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N64);
+  const int k0 = (int)tc.k0, k1 = (int)tc.k1;
   const int qa = tc.qt * QT;
   const int qb = min(qa + QT, M);
-  const int64_t t_last = q_pos0 + qb - 1;
-  const int64_t kend = min(tc.k1, t_last + 1);   // keys past kend are masked for every query
-  const int n_tiles = kend > tc.k0 ? (int)((kend - tc.k0 + KT - 1) / KT) : 0;
+  const int t_last = q_pos0 + qb - 1;
+  const int kend = min(k1, t_last + 1);   // keys past kend are masked for every query
+  const int n_tiles = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
 
   const int q0w = qa + wave * 8;
+  const int t_lo = q_pos0 + q0w;                    // first query of the wave
+  const int t_hi = q_pos0 + min(q0w + 8, qb) - 1;   // last query of the wave (< t_lo if none)
   // A fragments: row block rb = 2*G + qd; row r -> query q0w + 4G + r/4, slot 4*qd + r%4
+  // (all prologue loads are unconditional, clamped in range, so they issue in
+  //  two dependent batches: head ids, then weights and q rows)
   bf16x8 afr[4][kKSteps];
   float wv[2][8];
-  int64_t tq[2];
-  bool gvalid[2];
+  int tq[2];
+  __amdgpu_buffer_rsrc_t orsrc[2];
+  const uint32_t row_bytes = (uint32_t)ld * 4u;
+  const uint32_t lane_row_off = (uint32_t)g * row_bytes;
+  const int64_t qrow0 = (int64_t)b * M;
+  int hw[2][8], ha[2][2];
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
-    gvalid[G] = (q0w + 4 * G) < qb;
-    const int qo = q0w + 4 * G + g;          // query of this lane's output rows
+    const int qg0 = q0w + 4 * G;                      // first query of group G
+    const int nrows = max(0, min(4, qb - qg0));       // its queries inside the tile
+    orsrc[G] = out_rsrc(logits + (qrow0 + min(qg0, M - 1)) * ld, (uint32_t)nrows * row_bytes);
+    const int qo = qg0 + g;                           // query of this lane's output rows
     tq[G] = (qo < qb) ? q_pos0 + qo : -1;
+    const int qoc = min(qo, M - 1);
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) hw[G][sl] = heads[(qrow0 + qoc) * h + min(sl, h - 1)];
+    const int qic = min(qg0 + (p16 >> 2), M - 1);
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) ha[G][qd] = heads[(qrow0 + qic) * h + min(4 * qd + (p16 & 3), h - 1)];
+  }
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    const int qg0 = q0w + 4 * G;
+    const int qo = qg0 + g;
+    const int qoc = min(qo, M - 1);
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      float wvv = 0.f;
-      if (qo < qb && sl < h) {
-        const int j = clamp_head(heads[((int64_t)b * M + qo) * h + sl], H);
-        wvv = w[((int64_t)b * M + qo) * H + j];
-      }
-      wv[G][sl] = wvv;
+      const float wj = w[(qrow0 + qoc) * H + clamp_head(hw[G][sl], H)];
+      wv[G][sl] = wj * ((qo < qb && sl < h) ? 1.f : 0.f);   // (a select would sink the load into a branch)
     }
+    const int qi = qg0 + (p16 >> 2);
+    const int qic = min(qi, M - 1);
 #pragma unroll
     for (int qd = 0; qd < 2; ++qd) {
-      const int qi = q0w + 4 * G + (p16 >> 2);
-      const int sl = 4 * qd + (p16 & 3);
-      const bool ok = (qi < qb) && (sl < h);
-      int j = 0;
-      if (ok) j = clamp_head(heads[((int64_t)b * M + qi) * h + sl], H);
-      const uint4* src = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + (ok ? qi : 0)) * H + j) * kD);
+      const bool ok = (qi < qb) && (4 * qd + (p16 & 3) < h);
+      const uint4* src = reinterpret_cast<const uint4*>(q + ((qrow0 + qic) * H + clamp_head(ha[G][qd], H)) * kD);
+      const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) afr[2 * G + qd][ks] = as_bf16x8(ok ? src[ks * 4 + g] : make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const uint4 v = src[ks * 4 + g];
+        afr[2 * G + qd][ks] = as_bf16x8(make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep));
+      }
     }
   }
 
@@ -186,59 +224,66 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * N : nullptr;
 
   KStage<KDT, KT, NT> stg;
-  if (n_tiles > 0) {
-    stg.load(kb_ptr, sc_ptr, tc.k0, N, tid);
-    stg.store(s_k[0], s_sc[0], tid);
-  }
+  stg.load(kb_ptr, sc_ptr, k0, N, tid);
+  stg.store(s_k[0], s_sc[0], tid);
+  // every load issued so far (q fragments, weights) has landed: without this the
+  // compiler cannot prove it inside the loop and waits for all memory traffic
+  // (the next tile's prefetch included) before each block's first MFMA
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const float ninf = -__builtin_inff();
-  const int64_t t_wave_max = max(tq[0], tq[1]);   // per lane; wave max below
-  int64_t wmax = t_wave_max;
-  for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, (int64_t)__shfl_xor((long long)wmax, o));
+  constexpr uint32_t kDrop = 0x80000000u;   // a byte offset past every store resource
 
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int buf = jt & 1;
-    const int64_t key0 = tc.k0 + (int64_t)jt * KT;
-    if (jt + 1 < n_tiles) stg.load(kb_ptr, sc_ptr, key0 + KT, N, tid);
-    if (q0w < qb) {
+    const int key0 = k0 + jt * KT;
+    stg.load(kb_ptr, sc_ptr, key0 + KT, N, tid);   // next tile (clamped past the end)
 #pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb) {
-        const int64_t kpos = key0 + kb * 16 + p16;   // this lane's key
-        if (key0 + kb * 16 > wmax) {
-          // whole column block is after every query of the wave
-#pragma unroll
-          for (int G = 0; G < 2; ++G)
-            if (tq[G] >= 0 && kpos < N) logits[((int64_t)b * M + (tq[G] - q_pos0)) * ld + kpos] = ninf;
-          continue;
-        }
+    for (int kb = 0; kb < KT / 16; ++kb) {
+      const int kbase = key0 + kb * 16;
+      const int kpos = kbase + p16;   // this lane's key
+      const uint32_t off = (kpos < N) ? lane_row_off + (uint32_t)kpos * 4u : kDrop;
+      float out[2];
+      if (kbase > t_hi) {
+        // the whole column block lies after every query of the wave
+        out[0] = ninf;
+        out[1] = ninf;
+      } else {
         bf16x8 bfr[kKSteps];
         const uint16_t* rowp = &s_k[buf][(kb * 16 + p16) * kKRow + g * 8];
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) bfr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + ks * 32));
         const float sc = (KDT == MISA_K_FP8_E4M3) ? s_sc[buf][kb * 16 + p16] : 1.f;
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int G = 0; G < 2; ++G)
+#pragma unroll
+          for (int qd = 0; qd < 2; ++qd) acc[G][qd] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+          for (int G = 0; G < 2; ++G)
+#pragma unroll
+            for (int qd = 0; qd < 2; ++qd) acc[G][qd] = mfma16(afr[2 * G + qd][ks], bfr[ks], acc[G][qd]);
+        const bool diag = kbase + 15 > t_lo;   // some key of this block lies after some query
 #pragma unroll
         for (int G = 0; G < 2; ++G) {
-          if (!gvalid[G]) continue;
-          f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) {
-            a0 = mfma16(afr[2 * G][ks], bfr[ks], a0);
-            a1 = mfma16(afr[2 * G + 1][ks], bfr[ks], a1);
-          }
-          const float P0 = quad_chain(a0, wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
-          const float P1 = quad_chain(a1, wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
+          const float P0 = quad_chain(acc[G][0], wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
+          const float P1 = quad_chain(acc[G][1], wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
           float s = P0 + P1;
           if (KDT == MISA_K_FP8_E4M3) s *= sc;
-          if (kpos > tq[G]) s = ninf;
-          if (tq[G] >= 0 && kpos < N) logits[((int64_t)b * M + (tq[G] - q_pos0)) * ld + kpos] = s;
+          if (diag && kpos > tq[G]) s = ninf;
+          out[G] = s;
         }
       }
+      store_f32(orsrc[0], off, out[0]);
+      store_f32(orsrc[1], off, out[1]);
     }
-    if (jt + 1 < n_tiles) stg.store(s_k[buf ^ 1], s_sc[buf ^ 1], tid);
+    stg.store(s_k[buf ^ 1], s_sc[buf ^ 1], tid);
     __syncthreads();
   }
   // keys of this range after the last computed tile: -inf for every query
-  fill_neg_inf(logits, ld, b, M, qa, qb, tc.k0 + (int64_t)n_tiles * KT, tc.k1, tid, NT);
+  fill_neg_inf(logits, ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
 }
 
 // ---------------------------------------------------------------------------
@@ -300,16 +345,17 @@ __global__ void __launch_bounds__(256) k_score_c16(const uint16_t* __restrict__ 
 
   KStage<KDT, KT, NT> stg;
   if (n_tiles > 0) {
-    stg.load(kb_ptr, sc_ptr, tc.k0, N, tid);
+    stg.load(kb_ptr, sc_ptr, (int)tc.k0, (int)N, tid);
     stg.store(s_k[0], s_sc[0], tid);
   }
+  __builtin_amdgcn_s_waitcnt(0);   // as in k_score_h8
   __syncthreads();
   const float ninf = -__builtin_inff();
 
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int buf = jt & 1;
     const int64_t key0 = tc.k0 + (int64_t)jt * KT;
-    if (jt + 1 < n_tiles) stg.load(kb_ptr, sc_ptr, key0 + KT, N, tid);
+    if (jt + 1 < n_tiles) stg.load(kb_ptr, sc_ptr, (int)key0 + KT, (int)N, tid);
     if (q0w < qb) {
       float run[NKB];
 #pragma unroll
