@@ -38,6 +38,12 @@ the design notes of this repository):
   * a query sees its own key (s <= t);
   * rows shorter than k are padded with id -1 (value -inf);
   * fp8 keys are OCP e4m3fn codes times a per-token fp32 scale.
+
+Parity unpinned: the router's definition (how the partial block enters and
+how the per-block affinities and the head weight combine into one head
+importance) is a reading; the pages fix no formula or worked example for it.
+Its arithmetic is pinned (brute force, the B = 1 closed form, relabelling and
+scaling invariants), its agreement with the pages is not.
 """
 from __future__ import annotations
 
