@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--workload", default="final_chunk_m8k_n128k_fp8")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the MISA-dagger and dense timings")
-    p.add_argument("--cpu-queries", type=int, default=192, help="queries in the oracle timing sample")
+    p.add_argument("--cpu-queries", type=int, default=1536, help="queries in the oracle timing sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()

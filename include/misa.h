@@ -75,7 +75,7 @@ typedef enum {
 typedef struct {
   int32_t n_seq;      /* independent sequences, >= 1 */
   int32_t q_per_seq;  /* M: queries per sequence, >= 0 (0 = nothing to do) */
-  int64_t n_keys;     /* N: keys per sequence, >= 1 */
+  int64_t n_keys;     /* N: keys per sequence, 1..2^26 (larger: MISA_ERR_UNSUPPORTED) */
   int64_t q_pos0;     /* position of query 0; 0 <= q_pos0 and q_pos0 + M <= N */
   int32_t n_heads;    /* H: indexer heads (H_I on the pages), 1..64 */
   int32_t head_dim;   /* d: must be 128 */
@@ -129,7 +129,8 @@ misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const f
  *   logits[b][i][s] = sum_{j in heads[b][i]} w[t,j] * ReLU(q[t,j] . k[s] * sigma[s])
  *                     for s <= t,   -inf for t < s < N.   Columns N..ld-1 untouched.
  * heads: int32 [n_seq][M][h], ascending, distinct, each in [0, H).  1 <= h <= H.
- * logits: float [n_seq][M][ld]; ld >= N and ld % 4 == 0.
+ * logits: float [n_seq][M][ld]; ld >= N, ld % 4 == 0 and ld <= 2^27 (larger:
+ *         MISA_ERR_UNSUPPORTED; row offsets of a 4-row group stay 32-bit).
  */
 misa_status misa_sparse_head_logits(const misa_shape* shape, const uint16_t* q, const float* w,
                                     const void* k, misa_kdtype kdtype, const float* k_scale,
@@ -142,7 +143,7 @@ misa_status misa_sparse_head_logits(const misa_shape* shape, const uint16_t* q, 
  * all-head path).
  * cand == NULL:  logits[b][i][s] over every key, exactly as
  *                misa_sparse_head_logits with heads = 0..H-1 (and bitwise equal
- *                to it); ld >= N, ld % 4 == 0.
+ *                to it); ld >= N, ld % 4 == 0, ld <= 2^27.
  * cand != NULL:  re-rank mode of MISA-dagger ("Variante Hierárquica (MISA†)":
  *                the original all-head indexer re-scores only the candidates).
  *                cand: int32 [n_seq][M][n_cand] token ids (any order; -1 = no

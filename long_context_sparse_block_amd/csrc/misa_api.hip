@@ -18,6 +18,9 @@ using misa::launch_topk;
 
 constexpr size_t kAlign = 256;
 
+constexpr int64_t kMaxKeys = (int64_t)1 << 26;
+constexpr int64_t kMaxLogitLd = (int64_t)1 << 27;   // 4 rows of ld floats < 2^31 bytes
+
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -28,8 +31,8 @@ misa_status check_shape(const misa_shape* s) {
   if (s->n_heads < 1 || s->n_heads > MISA_MAX_HEADS) return MISA_ERR_INVALID_ARG;
   if (s->head_dim != MISA_HEAD_DIM) return MISA_ERR_UNSUPPORTED;
   if (s->block < 1) return MISA_ERR_INVALID_ARG;
-  // grid dimensions and 32-bit row counters
-  if (s->n_keys > (int64_t)1 << 30) return MISA_ERR_UNSUPPORTED;
+  // grid dimensions, 32-bit row counters and 32-bit buffer offsets
+  if (s->n_keys > kMaxKeys) return MISA_ERR_UNSUPPORTED;
   if (s->n_seq > 65535) return MISA_ERR_UNSUPPORTED;
   return MISA_OK;
 }
@@ -138,6 +141,7 @@ misa_status misa_sparse_head_logits(const misa_shape* shape, const uint16_t* q, 
     return MISA_ERR_INVALID_ARG;
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (ld < shape->n_keys || (ld & 3) != 0) return MISA_ERR_INVALID_ARG;
+  if (ld > kMaxLogitLd) return MISA_ERR_UNSUPPORTED;
   if (shape->q_per_seq == 0) return MISA_OK;
   return from_hip(launch_score(*shape, q, w, k, kdtype, k_scale, heads, h, logits, ld, (hipStream_t)stream));
 }
@@ -153,6 +157,7 @@ misa_status dsa_dense_logits(const misa_shape* shape, const uint16_t* q, const f
   if ((ld & 3) != 0) return MISA_ERR_INVALID_ARG;
   if (cand == nullptr) {
     if (ld < shape->n_keys) return MISA_ERR_INVALID_ARG;
+    if (ld > kMaxLogitLd) return MISA_ERR_UNSUPPORTED;
     if (shape->q_per_seq == 0) return MISA_OK;
     return from_hip(launch_score(*shape, q, w, k, kdtype, k_scale, nullptr, shape->n_heads, logits, ld,
                                  (hipStream_t)stream));

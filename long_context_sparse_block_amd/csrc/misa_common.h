@@ -33,16 +33,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 }
 
 // OCP e4m3fn -> bf16 is exact (3-bit mantissa inside bf16's 7 bits, exponent
-// range inside bf16's).  The hardware converter widens two codes to fp32; the
-// top half of an fp32 whose value is bf16-representable is that bf16.
-// Four codes (one dword) -> four bf16 (two dwords).
+// range inside bf16's; e4m3 subnormals are bf16 normals).  gfx950 converts two
+// codes to a packed bf16 pair in one instruction; a scale of 1.0 leaves the
+// value unchanged.  Four codes (one dword) -> four bf16 (two dwords).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t codes) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
-  uint2 r;
-  r.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-  r.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
-  return r;
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);   // codes 0, 1
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);    // codes 2, 3
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
@@ -79,6 +77,21 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ float key_to_float(uint32_t key) {
   uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
   return __uint_as_float(u);
+}
+
+// Raw buffer descriptor over [base, base + bytes).  Its fields are read from
+// the first lane, so the compiler knows the descriptor is wave-uniform and
+// emits plain buffer instructions (no per-lane descriptor loop); callers pass
+// values that are uniform anyway.  With stride 0 the hardware range check
+// (gfx9-family descriptor word 3) drops stores and zero-fills loads whose byte
+// offset is at or past `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  void* pu = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, n, 0x00020000);
 }
 
 // Hardware dispatches workgroup i of a launch to XCD (i mod 8).  Remap the

@@ -45,24 +45,29 @@ template <int KDT, int KT, int NT>
 struct KStage {
   // bf16: KT keys * 16 uint4 per key; fp8: KT keys * 8 uint4 per key
   static constexpr int kVecPerKey = (KDT == MISA_K_BF16) ? 16 : 8;
+  static constexpr int kRowBytes = kVecPerKey * 16;
   static constexpr int kPerThread = KT * kVecPerKey / NT;
   static_assert(KT * kVecPerKey % NT == 0, "tile not divisible");
   uint4 r[kPerThread];
   float sc;
 
-  // Unconditional loads (rows past N read row N-1 instead; those keys are never
-  // stored): no exec-masked loads, so waiting for this prefetch never becomes a
-  // full vmcnt(0) in the compute that overlaps it.
+  // Keys [key0, key0 + KT) through buffer descriptors based at the tile and
+  // bounded by N: rows past N read as zeros (their logits are never stored).
+  // The loads are unconditional and need no clamping, so waiting for this
+  // prefetch never becomes a full memory wait inside the compute it overlaps.
   __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int tid) {
+    const int rem = max(0, min(KT, N - key0));
+    const __amdgpu_buffer_rsrc_t kr =
+        uniform_rsrc(static_cast<const char*>(kbase) + (int64_t)key0 * kRowBytes, (uint32_t)(rem * kRowBytes));
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
-      const int e = tid + u * NT;
-      const int key = e / kVecPerKey;
-      const int c = e % kVecPerKey;
-      const int kk = min(key0 + key, N - 1);
-      r[u] = reinterpret_cast<const uint4*>(kbase)[(int64_t)kk * kVecPerKey + c];
+      const int e = tid + u * NT;   // 16-byte chunk e of the (contiguous) tile
+      r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, e * 16, 0, 0));
     }
-    if (KDT == MISA_K_FP8_E4M3) sc = sbase[min(key0 + (tid % KT), N - 1)];
+    if (KDT == MISA_K_FP8_E4M3) {
+      const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + key0, (uint32_t)(rem * 4));
+      sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, (tid % KT) * 4, 0, 0));
+    }
   }
 
   __device__ __forceinline__ void store(uint16_t* s_k, float* s_sc, int tid) const {
@@ -116,13 +121,7 @@ __device__ __forceinline__ void fill_neg_inf(float* logits, int64_t ld, int b, i
   }
 }
 
-// ---------------------------------------------------------------------------
-// Raw buffer resource over [base, base + bytes): buffer stores outside it are
-// dropped by the hardware range check (gfx9-family descriptor word 3).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-}
+// One logit through a uniform_rsrc descriptor (offsets past its size are dropped).
 __device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
   // the b32 store takes the raw 32-bit pattern (an int), not a value to convert
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, (int)byte_off, 0, 0);
@@ -183,7 +182,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   for (int G = 0; G < 2; ++G) {
     const int qg0 = q0w + 4 * G;                      // first query of group G
     const int nrows = max(0, min(4, qb - qg0));       // its queries inside the tile
-    orsrc[G] = out_rsrc(logits + (qrow0 + min(qg0, M - 1)) * ld, (uint32_t)nrows * row_bytes);
+    orsrc[G] = uniform_rsrc(logits + (qrow0 + min(qg0, M - 1)) * ld, (uint32_t)nrows * row_bytes);
     const int qo = qg0 + g;                           // query of this lane's output rows
     tq[G] = (qo < qb) ? q_pos0 + qo : -1;
     const int qoc = min(qo, M - 1);

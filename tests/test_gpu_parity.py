@@ -53,6 +53,43 @@ def test_fp8_decode_all_codes_through_pooling():
     assert not f64(tail).any()
 
 
+def test_fp8_decode_all_codes_through_scoring():
+    """Every finite e4m3 code through the scoring kernels' fp8 -> bf16 widening.
+    Query i reads dimension i // 2 with sign +-1 through a one-hot head, so each
+    logit is exactly ReLU(+-decode(code)) * sigma: the routed kernel (h = 1),
+    the dense kernel (H = 2, the second head weighted 0) and the candidate
+    re-rank kernel must all reproduce the oracle's decoder value for value."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 finite codes
+    n_code = len(codes)
+    M = 256                                  # 128 dims x 2 signs
+    N = n_code + M                           # queries at t >= n_code see every code row
+    k = np.zeros((N, 128), np.uint8)
+    k[:n_code] = np.stack([np.roll(codes, -s)[:128] for s in range(n_code)])
+    scale = np.where(np.arange(N) % 2 == 0, 1.0, 0.25).astype(np.float32)
+    q = np.zeros((M, 2, 128), np.float32)
+    for i in range(M):
+        q[i, 0, i // 2] = 1.0 if i % 2 == 0 else -1.0
+    w = np.zeros((M, 2), np.float32)
+    w[:, 0] = 1.0
+    dev = torch.device("cuda:0")
+    sh = lcsb.make_shape(1, M, N, n_code, 2, 64)
+    qt = torch.from_numpy(q[None]).to(dev).to(torch.bfloat16)
+    wt = torch.from_numpy(w[None]).to(dev)
+    kt = torch.from_numpy(k[None]).to(dev)
+    st = torch.from_numpy(scale[None]).to(dev)
+    heads = torch.zeros((1, M, 1), dtype=torch.int32, device=dev)
+    dec = oracle.e4m3fn_to_f64(k[:n_code]) * scale[:n_code, None].astype(np.float64)   # [code row, dim]
+    sign = np.where(np.arange(M) % 2 == 0, 1.0, -1.0)
+    expect = np.maximum(sign[:, None] * dec[:, np.arange(M) // 2].T, 0.0)            # [query, code row]
+    routed = f64(lcsb.misa_sparse_head_logits(sh, qt, wt, kt, heads, k_scale=st)[0])
+    dense = f64(lcsb.dsa_dense_logits(sh, qt, wt, kt, k_scale=st)[0])
+    cand = torch.arange(n_code, dtype=torch.int32, device=dev).repeat(M, 1)[None].contiguous()
+    gather = f64(lcsb.dsa_dense_logits(sh, qt, wt, kt, k_scale=st, cand=cand)[0])
+    for name, got in (("routed", routed[:, :n_code]), ("dense", dense[:, :n_code]), ("gather", gather[:, :n_code])):
+        bad = np.argwhere(got != expect)
+        assert len(bad) == 0, f"{name}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+
+
 POOL_CASES = [
     dict(m=37, n=1000, b=64), dict(m=64, n=512, b=1), dict(m=20, n=300, b=3),
     dict(m=16, n=40, b=64), dict(m=33, n=777, b=128, kdtype=gen.KDTYPE_FP8),
