@@ -127,7 +127,8 @@ misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const f
  * "Metodologia: MISA" item 2: only the h active heads score the whole prefix
  * token by token).
  *   logits[b][i][s] = sum_{j in heads[b][i]} w[t,j] * ReLU(q[t,j] . k[s] * sigma[s])
- *                     for s <= t,   -inf for t < s < N.   Columns N..ld-1 untouched.
+ *                     for s <= t,   -inf for t < s < N.   Columns N..roundup4(N)-1
+ *                     may also be set to -inf; columns roundup4(N)..ld-1 are untouched.
  * heads: int32 [n_seq][M][h], ascending, distinct, each in [0, H).  1 <= h <= H.
  * logits: float [n_seq][M][ld]; ld >= N, ld % 4 == 0 and ld <= 2^27 (larger:
  *         MISA_ERR_UNSUPPORTED; row offsets of a 4-row group stay 32-bit).

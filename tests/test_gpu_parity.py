@@ -90,6 +90,33 @@ def test_fp8_decode_all_codes_through_scoring():
         assert len(bad) == 0, f"{name}: {len(bad)} mismatches, first {bad[:3].tolist()}"
 
 
+@pytest.mark.parametrize("kdtype", [gen.KDTYPE_BF16, gen.KDTYPE_FP8])
+@pytest.mark.parametrize("n", [517, 640])
+def test_logit_columns_past_n(kdtype, n):
+    """Routed and dense logits leave columns roundup4(N)..ld-1 untouched; the
+    columns N..roundup4(N)-1 hold either their old value or -inf."""
+    say("columns past N", kdtype, n)
+    cfg = gen.small_config(m=40, n=n, b=16, k=32, kdtype=kdtype, seed=31)
+    inp = gen.generate(cfg)
+    d = upload(inp)
+    sh = shape_of(inp)
+    dev = torch.device("cuda:0")
+    ld = (n + 3) // 4 * 4 + 12
+    heads = torch.tensor(np.tile(np.arange(cfg.h, dtype=np.int32), (1, cfg.q_per_seq, 1)), device=dev)
+    r4 = (n + 3) // 4 * 4
+    for name in ("routed", "dense"):
+        lg = torch.full((1, cfg.q_per_seq, ld), float("nan"), device=dev)
+        if name == "routed":
+            lcsb.misa_sparse_head_logits(sh, d["q"], d["w"], d["k"], heads, k_scale=d["k_scale"], logits=lg)
+        else:
+            lcsb.dsa_dense_logits(sh, d["q"], d["w"], d["k"], k_scale=d["k_scale"], logits=lg)
+        x = lg.cpu().numpy()
+        assert not np.isnan(x[..., :n]).any(), name
+        assert np.isnan(x[..., r4:]).all(), f"{name}: columns past roundup4(N) were written"
+        pad = x[..., n:r4]
+        assert (np.isnan(pad) | np.isneginf(pad)).all(), name
+
+
 POOL_CASES = [
     dict(m=37, n=1000, b=64), dict(m=64, n=512, b=1), dict(m=20, n=300, b=3),
     dict(m=16, n=40, b=64), dict(m=33, n=777, b=128, kdtype=gen.KDTYPE_FP8),
