@@ -144,6 +144,10 @@ def main():
     vals = torch.empty((S, M, K), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     W = work(cfg, inp.q_pos0)
+    kp = 8192
+    tk_ws_bytes = max(lcsb.misa_topk_workspace_bytes(sh, N, K), lcsb.misa_topk_workspace_bytes(sh, N, kp),
+                      lcsb.misa_topk_workspace_bytes(sh, kp, K), 1)
+    tk_ws = torch.empty(tk_ws_bytes, dtype=torch.uint8, device=dev)   # top-k scratch, allocated once
 
     def run_timed(stages, steps, warmup):
         """stages: list of (name, fn).  Returns per-stage mean ms and step ms."""
@@ -171,7 +175,7 @@ def main():
         ("pool", lambda: lcsb.misa_pool_keys(sh, k, ks, pooled=pooled, tail=tail)),
         ("route", lambda: lcsb.misa_route_heads(sh, q, w, pooled[:, :n_full], tail, h, heads=heads)),
         ("score", lambda: lcsb.misa_sparse_head_logits(sh, q, w, k, heads, k_scale=ks, logits=logits)),
-        ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals)),
+        ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals, ws=tk_ws)),
     ]
     per, step_ms, wall_ms = run_timed(misa_stages, args.steps, args.warmup)
     print(f"[bench] MISA step {step_ms:.3f} ms (wall {wall_ms:.3f}) {per}", file=sys.stderr, flush=True)
@@ -201,20 +205,19 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        kp = 8192
         cand = torch.empty((S, M, kp), dtype=torch.int32, device=dev)
         dlog = torch.empty((S, M, kp), dtype=torch.float32, device=dev)
         dagger_stages = misa_stages[:3] + [
-            ("topk_kprime", lambda: lcsb.misa_topk(sh, logits, kp, idx=cand, want_vals=False, sorted=False)),
+            ("topk_kprime", lambda: lcsb.misa_topk(sh, logits, kp, idx=cand, want_vals=False, sorted=False, ws=tk_ws)),
             ("rerank", lambda: lcsb.dsa_dense_logits(sh, q, w, k, k_scale=ks, cand=cand, logits=dlog)),
-            ("topk_final", lambda: lcsb.misa_topk(sh, dlog, K, cand=cand, idx=idx, vals=vals)),
+            ("topk_final", lambda: lcsb.misa_topk(sh, dlog, K, cand=cand, idx=idx, vals=vals, ws=tk_ws)),
         ]
         dper, dstep, _ = run_timed(dagger_stages, max(3, args.steps // 4), 2)
         extras["misa_dagger"] = dict(k_prime=kp, ms_per_step=dstep, stage_ms=dper,
                                      rerank_TFLOPs=S * M * kp * H * 256 / (dper["rerank"] * 1e-3) / 1e12)
         dense_stages = [
             ("dense_score", lambda: lcsb.dsa_dense_logits(sh, q, w, k, k_scale=ks, logits=logits)),
-            ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals)),
+            ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals, ws=tk_ws)),
         ]
         nper, nstep, _ = run_timed(dense_stages, max(3, args.steps // 4), 2)
         extras["dense"] = dict(ms_per_step=nstep, stage_ms=nper,

@@ -232,6 +232,10 @@ def misa_topk(shape: MisaShape, logits, k: int, n_cols=None, cand=None, idx=None
     return idx, vals
 
 
+def misa_topk_workspace_bytes(shape: MisaShape, n_cols: int, k: int) -> int:
+    return int(load().misa_topk_workspace_bytes(ctypes.byref(shape), int(n_cols), int(k)))
+
+
 def misa_indexer_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:
     return int(load().misa_indexer_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime)))
 

@@ -92,7 +92,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
 
 // Workgroup min and max of the composites of buf[0, n).
 template <int NT>
-__device__ void block_minmax(const uint64_t* buf, uint32_t n, uint64_t* s_red, uint64_t* mn, uint64_t* mx) {
+__device__ __forceinline__ void block_minmax(const uint64_t* buf, uint32_t n, uint64_t* s_red, uint64_t* mn, uint64_t* mx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t lo = ~0ull, hi = 0;
   for (uint32_t e = threadIdx.x; e < n; e += NT) {
@@ -130,7 +130,7 @@ __device__ __forceinline__ int bit_width64(uint64_t x) { return x ? 64 - __clzll
 // for duplicate entries); with limit == need it selects exactly the need
 // largest.  Requires 1 <= need <= n.  Every thread of the workgroup must call it.
 template <int NT>
-__device__ uint64_t select_threshold(const uint64_t* buf, uint32_t n, uint32_t need, uint32_t limit,
+__device__ __forceinline__ uint64_t select_threshold(const uint64_t* buf, uint32_t n, uint32_t need, uint32_t limit,
                                      uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint64_t* s_red) {
   const int tid = threadIdx.x;
   constexpr int BPT = kHistBins / NT;  // bins per thread
@@ -196,7 +196,7 @@ __device__ uint64_t select_threshold(const uint64_t* buf, uint32_t n, uint32_t n
 // place, in chunks of 4*NT entries: kept entries only move to lower positions,
 // and each chunk is fully read (scan barrier) before any of it is written.
 template <int NT>
-__device__ uint32_t compact(uint64_t* buf, uint32_t n, uint64_t T, uint32_t* s_wave) {
+__device__ __forceinline__ uint32_t compact(uint64_t* buf, uint32_t n, uint64_t T, uint32_t* s_wave) {
   const int tid = threadIdx.x;
   uint32_t base = 0;
   for (uint32_t c0 = 0; c0 < n; c0 += 4 * NT) {
@@ -226,7 +226,7 @@ __device__ uint32_t compact(uint64_t* buf, uint32_t n, uint64_t T, uint32_t* s_w
 // in-thread, below 64E lane shuffles, wider ones go through LDS), then the
 // top k are written.  Positions past cnt hold 0, below every composite.
 template <int NT, int E>
-__device__ void bitonic_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out,
+__device__ __forceinline__ void bitonic_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out,
                               float* val_out) {
   const int tid = threadIdx.x;
   uint64_t v[E];
@@ -280,7 +280,7 @@ __device__ void bitonic_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, i
 // composite span (stored in buf[CAP/2 ...]), then each candidate's rank inside
 // its bucket by direct comparison.
 template <int CAP, int NT>
-__device__ void rank_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out, float* val_out,
+__device__ __forceinline__ void rank_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out, float* val_out,
                            uint32_t* s_hist, uint32_t* s_wave, uint64_t* s_red) {
   const int tid = threadIdx.x;
   constexpr int BPT = kHistBins / NT;
@@ -346,20 +346,31 @@ __device__ void rank_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int3
   }
 }
 
+// LDS of one top-k workgroup
 template <int CAP, int NT>
-__global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits, int64_t ld,
-                                                const int32_t* __restrict__ cand, int n_cols, int k,
-                                                int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
-                                                float* __restrict__ val_out, int sorted) {
+struct TopkShared {
+  uint64_t buf[CAP];
+  uint32_t hist[kHistBins];
+  uint32_t wave[NT / 64];
+  uint64_t red[2 * (NT / 64)];
+  uint32_t sel[3];
+  uint32_t count;
+};
+
+template <int CAP, int NT>
+__device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, const float* __restrict__ logits, int64_t ld,
+                                         const int32_t* __restrict__ cand, int n_cols, int k, int64_t q_pos0,
+                                         int M, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                                         int sorted) {
   constexpr int VPT = 2;                  // float4s per thread per lock-step (robust) step
   constexpr int STEP = 4 * VPT * NT;      // elements per lock-step step
   static_assert(CAP / 2 >= STEP, "a lock-step step must fit the free half of the buffer");
-  __shared__ uint64_t s_buf[CAP];
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ uint32_t s_wave[NT / 64];
-  __shared__ uint64_t s_red[2 * (NT / 64)];
-  __shared__ uint32_t s_sel[3];
-  __shared__ uint32_t s_count;
+  uint64_t* s_buf = sh.buf;
+  uint32_t* s_hist = sh.hist;
+  uint32_t* s_wave = sh.wave;
+  uint64_t* s_red = sh.red;
+  uint32_t* s_sel = sh.sel;
+  uint32_t& s_count = sh.count;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -542,12 +553,266 @@ __global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits
   rank_write<CAP, NT>(s_buf, cnt, k, row, idx_out, val_out, s_hist, s_wave, s_red);
 }
 
-size_t topk_workspace_bytes(const misa_shape&, int, int) { return 0; }
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits, int64_t ld,
+                                                const int32_t* __restrict__ cand, int n_cols, int k,
+                                                int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
+                                                float* __restrict__ val_out, int sorted) {
+  __shared__ TopkShared<CAP, NT> sh;
+  topk_row<CAP, NT>(sh, logits, ld, cand, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
+}
+
+// ---------------------------------------------------------------------------
+// Long rows: the threshold, the stream and the selection run as three kernels
+// so that the stream fills the whole chip with row chunks while the select and
+// rank work, which reads no logits, runs afterwards on short candidate lists.
+// ---------------------------------------------------------------------------
+constexpr int kSplitMinCols = 16384;   // rows at least this long take the split path
+constexpr int kChunk = 16384;          // elements per filter workgroup
+constexpr int kChunkCap = 2048;        // candidates a filter workgroup can hold
+
+// candidates kept per row (the LDS buffer of the select kernel)
+inline int list_cap(int k) { return k <= 4096 ? 8192 : 16384; }
+
+struct SplitWs {
+  float* thr;
+  uint32_t* count;
+  uint32_t* flag;
+  uint64_t* list;
+  int capg;
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static size_t split_ws_bytes(int64_t rows, int k) {
+  return 3 * align256((size_t)rows * 4) + align256((size_t)rows * list_cap(k) * sizeof(uint64_t));
+}
+
+static SplitWs split_ws(void* ws, int64_t rows, int k) {
+  char* p = static_cast<char*>(ws);
+  SplitWs w;
+  w.capg = list_cap(k);
+  w.thr = reinterpret_cast<float*>(p);
+  p += align256((size_t)rows * 4);
+  w.count = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 4);
+  w.flag = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 4);
+  w.list = reinterpret_cast<uint64_t*>(p);
+  return w;
+}
+
+// Per-row threshold from a sample, one wave per row: at most 128 lines of 32
+// elements at a regular line stride (>= 32 lines).  The threshold is the score
+// of the k_s-th largest sampled element, k_s chosen so that about `target` row
+// elements are expected at or above it; it is found exactly by deciding the
+// bits of its order key from the top, counting sampled keys with ballots.
+// Rows no longer than `target` keep every element.  Also resets the row's
+// list count and overflow flag.
+constexpr int kThreshWaves = 4;
+__global__ void __launch_bounds__(64 * kThreshWaves) k_topk_thresh(const float* __restrict__ logits, int64_t ld,
+                                                                   int n_cols, int target, int64_t q_pos0, int M,
+                                                                   int64_t rows, float* __restrict__ thr,
+                                                                   uint32_t* __restrict__ count,
+                                                                   uint32_t* __restrict__ flag) {
+  constexpr int J = 64;   // sampled values per lane (128 lines x 32 = 4096 per row)
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kThreshWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int i = (int)(row % M);
+  const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
+  const float* lrow = logits + row * ld;
+  float tf = -__builtin_inff();
+  const int n_lines = n / 32;
+  const int stride = max(32, (n_lines + 127) / 128);
+  const int ns = (n_lines / stride) * 32;
+  const uint64_t ks = (ns > 0) ? (uint64_t)target * (uint64_t)ns / (uint64_t)n + 2 : 0;
+  if (n > target && ns > 0 && ks < (uint64_t)ns) {
+    uint32_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;                      // sample element e: line e / 32, offset e % 32
+      const int ec = min(e, ns - 1);
+      const float v = lrow[(ec / 32) * stride * 32 + (ec % 32)];
+      key[j] = (e < ns) ? order_key(v) : 0u;            // 0: below every candidate key tested
+    }
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) cnt += (uint32_t)__popcll(__ballot(key[j] >= c));
+      if (cnt >= (uint32_t)ks) T = c;
+    }
+    tf = key_to_float(T);
+    if (tf != tf) tf = -__builtin_inff();
+  }
+  if (lane == 0) {
+    thr[row] = tf;
+    count[row] = 0;
+    flag[row] = 0;
+  }
+}
+
+// Stream one chunk of a row and append every element >= the row's threshold
+// to the row's candidate list (LDS first, then one global atomic per chunk).
+// A chunk with more candidates than it can hold, or a list that would pass its
+// capacity, flags the row for the exact fallback.
+template <int NT>
+__global__ void __launch_bounds__(NT) k_topk_filter(const float* __restrict__ logits, int64_t ld, int n_cols,
+                                                    int n_chunks, int64_t q_pos0, int M,
+                                                    const float* __restrict__ thr, uint32_t* __restrict__ count,
+                                                    uint32_t* __restrict__ flag, uint64_t* __restrict__ list,
+                                                    int capg) {
+  __shared__ uint64_t s_c[kChunkCap];
+  __shared__ uint32_t s_count, s_base;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int i = blockIdx.x / n_chunks, ch = blockIdx.x % n_chunks, b = blockIdx.y;
+  const int64_t row = (int64_t)b * M + i;
+  const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
+  const int c0 = ch * kChunk;
+  if (c0 >= n) return;
+  const int c1 = min(n, c0 + kChunk);
+  const float* lrow = logits + row * ld;
+  const float tf = thr[row];
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+
+  auto append4 = [&](const f32x4 v, int e0, bool f0, bool f1, bool f2, bool f3) {
+    const uint32_t c = (uint32_t)f0 + f1 + f2 + f3;
+    const uint64_t m0 = __ballot(c & 1u), m1 = __ballot(c & 2u), m2 = __ballot(c & 4u);
+    if ((m0 | m1 | m2) == 0) return;
+    uint32_t pos = lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2);
+    uint32_t base = 0;
+    if (lane == __ffsll((unsigned long long)__ballot(1)) - 1)
+      base = atomicAdd(&s_count, (uint32_t)(__popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2)));
+    pos += __builtin_amdgcn_readfirstlane(base);
+    if (f0) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[0], e0); ++pos; }
+    if (f1) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[1], e0 + 1); ++pos; }
+    if (f2) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[2], e0 + 2); ++pos; }
+    if (f3) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[3], e0 + 3); }
+  };
+
+  // float4s of the chunk (rows are 16-byte aligned: ld % 4 == 0, c0 % 4 == 0)
+  constexpr int U = 8;
+  const int n4 = (c1 - c0 + 3) / 4;
+  for (int base4 = 0; base4 < n4; base4 += U * NT) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e4 = base4 + tid + u * NT;
+      const int e4c = min(e4, n4 - 1);
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lrow + c0) + e4c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e4 = base4 + tid + u * NT;
+      const int e0 = c0 + 4 * e4;
+      const bool in = e4 < n4;
+      append4(v[u], e0, in && e0 < c1 && v[u][0] >= tf, in && e0 + 1 < c1 && v[u][1] >= tf,
+              in && e0 + 2 < c1 && v[u][2] >= tf, in && e0 + 3 < c1 && v[u][3] >= tf);
+    }
+  }
+  __syncthreads();
+  const uint32_t c = s_count;
+  if (c == 0) return;
+  if (c > (uint32_t)kChunkCap) {
+    if (tid == 0) flag[row] = 1;
+    return;
+  }
+  if (tid == 0) s_base = atomicAdd(&count[row], c);
+  __syncthreads();
+  const uint32_t base = s_base;
+  if (base + c > (uint32_t)capg) {
+    if (tid == 0) flag[row] = 1;
+    return;
+  }
+  uint64_t* dst = list + row * (int64_t)capg + base;
+  for (uint32_t e = tid; e < c; e += NT) dst[e] = s_c[e];
+}
+
+// Exact top-k of a row's candidate list (every element at or above the row's
+// threshold).  A row whose list overflowed or came up short of k is done by
+// the whole-row path instead, in the same workgroup, so the result is exact
+// for every input.
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk_list(const float* __restrict__ logits, int64_t ld, int n_cols,
+                                                     int k, int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
+                                                     float* __restrict__ val_out, int sorted,
+                                                     const uint64_t* __restrict__ list,
+                                                     const uint32_t* __restrict__ count,
+                                                     const uint32_t* __restrict__ flag, int capg) {
+  __shared__ TopkShared<CAP, NT> sh;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int64_t row = (int64_t)b * M + i;
+  const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
+  const uint32_t c = count[row];
+  if (flag[row] != 0 || c < (uint32_t)min(k, n) || c > (uint32_t)min(capg, CAP)) {
+    topk_row<CAP, NT>(sh, logits, ld, nullptr, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
+    return;
+  }
+  const uint64_t* src = list + row * (int64_t)capg;
+  for (uint32_t e = tid; e < c; e += NT) sh.buf[e] = src[e];
+  __syncthreads();
+  uint32_t cnt = c;
+  if (sorted && cnt <= (uint32_t)(CAP / 2)) {   // rank every candidate; ranks >= k are not written
+    rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
+    return;
+  }
+  const uint32_t kk = min((uint32_t)k, cnt);
+  if (cnt > kk) {
+    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red);
+    cnt = compact<NT>(sh.buf, cnt, Tk, sh.wave);
+  }
+  cnt = min(cnt, (uint32_t)(CAP / 2));
+  if (!sorted) {
+    for (int e = tid; e < k; e += NT) {
+      int32_t id = -1;
+      float v = -__builtin_inff();
+      if ((uint32_t)e < cnt) {
+        const uint64_t cc = raw_to_comp(sh.buf[e]);
+        id = comp_id(cc);
+        v = comp_val(cc);
+      }
+      idx_out[row * k + e] = id;
+      if (val_out) val_out[row * k + e] = v;
+    }
+    return;
+  }
+  rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
+}
+
+size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k) {
+  if (n_cols < kSplitMinCols) return 0;
+  return split_ws_bytes((int64_t)s.n_seq * s.q_per_seq, k);
+}
 
 hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, const int32_t* cand,
-                       int n_cols, int k, int32_t* idx, float* vals, void*, size_t, hipStream_t st,
+                       int n_cols, int k, int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t st,
                        bool sorted) {
   dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  const bool split = cand == nullptr && n_cols >= kSplitMinCols && ws != nullptr &&
+                     ws_bytes >= split_ws_bytes(rows, k);
+  if (split) {
+    const SplitWs w = split_ws(ws, rows, k);
+    const int target = min(3 * k / 2, (k + w.capg) / 2);
+    hipLaunchKernelGGL(k_topk_thresh, dim3((unsigned)((rows + kThreshWaves - 1) / kThreshWaves)),
+                       dim3(64 * kThreshWaves), 0, st, logits, ld, n_cols, target, s.q_pos0, s.q_per_seq, rows,
+                       w.thr, w.count, w.flag);
+    const int n_chunks = (n_cols + kChunk - 1) / kChunk;
+    dim3 fgrid((unsigned)((int64_t)s.q_per_seq * n_chunks), (unsigned)s.n_seq);
+    hipLaunchKernelGGL(k_topk_filter<256>, fgrid, dim3(256), 0, st, logits, ld, n_cols, n_chunks, s.q_pos0,
+                       s.q_per_seq, w.thr, w.count, w.flag, w.list, w.capg);
+    if (k <= 4096)
+      hipLaunchKernelGGL((k_topk_list<8192, 512>), grid, dim3(512), 0, st, logits, ld, n_cols, k, s.q_pos0,
+                         s.q_per_seq, idx, vals, (int)sorted, w.list, w.count, w.flag, w.capg);
+    else
+      hipLaunchKernelGGL((k_topk_list<16384, 512>), grid, dim3(512), 0, st, logits, ld, n_cols, k, s.q_pos0,
+                         s.q_per_seq, idx, vals, (int)sorted, w.list, w.count, w.flag, w.capg);
+    return hipGetLastError();
+  }
   // CAP/2 >= max(k, one lock-step step of 4096 elements)
   if (k <= 4096)
     hipLaunchKernelGGL((k_topk<8192, 512>), grid, dim3(512), 0, st, logits, ld, cand, n_cols, k, s.q_pos0,

@@ -378,6 +378,28 @@ def test_topk_rows_that_defeat_the_sampled_threshold(kind):
     check_topk_exact_arrays(vals, N - M, k, idx.cpu().numpy(), v.cpu().numpy())
 
 
+@pytest.mark.parametrize("n,k", [(40001, 2048), (50003, 8192), (16384, 2048)])
+def test_topk_long_rows_split_path(n, k):
+    """Rows long enough for the threshold / filter / select kernels: ragged
+    lengths, causal prefixes across chunk boundaries, repeated values."""
+    say("split top-k", n, k)
+    M = 40
+    rng = np.random.default_rng(n + k)
+    vals = rng.standard_normal((1, M, n)).astype(np.float32)
+    vals[0, :, ::7] = np.round(vals[0, :, ::7], 1)          # many exact ties
+    q_pos0 = n - M
+    sh = lcsb.make_shape(1, M, n, q_pos0, 1, 1)
+    dev = torch.device("cuda:0")
+    ld = (n + 3) // 4 * 4
+    lg = torch.full((1, M, ld), float("nan"), device=dev)
+    lg[..., :n] = torch.from_numpy(vals).to(dev)
+    idx, v = lcsb.misa_topk(sh, lg, k)
+    check_topk_exact_arrays(vals, q_pos0, k, idx.cpu().numpy(), v.cpu().numpy())
+    idx2, _ = lcsb.misa_topk(sh, lg, k, sorted=False)
+    for i in range(M):
+        assert set(idx2[0, i].cpu().numpy().tolist()) == set(idx[0, i].cpu().numpy().tolist())
+
+
 @pytest.mark.parametrize("k", [300, 2048, 8192])
 def test_topk_unsorted_returns_the_same_set(k):
     rng = np.random.default_rng(6)
