@@ -568,8 +568,8 @@ __global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits
 // rank work, which reads no logits, runs afterwards on short candidate lists.
 // ---------------------------------------------------------------------------
 constexpr int kSplitMinCols = 16384;   // rows at least this long take the split path
-constexpr int kChunk = 16384;          // elements per filter workgroup
-constexpr int kChunkCap = 2048;        // candidates a filter workgroup can hold
+constexpr int kChunkMax = 65536;       // elements per filter workgroup, at most (256 KB of logits)
+constexpr int kChunkCap = 4096;        // candidates a filter workgroup (4 waves) can hold
 
 // candidates kept per row (the LDS buffer of the select kernel)
 inline int list_cap(int k) { return k <= 4096 ? 8192 : 16384; }
@@ -602,20 +602,21 @@ static SplitWs split_ws(void* ws, int64_t rows, int k) {
   return w;
 }
 
-// Per-row threshold from a sample, one wave per row: at most 128 lines of 32
-// elements at a regular line stride (>= 32 lines).  The threshold is the score
-// of the k_s-th largest sampled element, k_s chosen so that about `target` row
-// elements are expected at or above it; it is found exactly by deciding the
-// bits of its order key from the top, counting sampled keys with ballots.
-// Rows no longer than `target` keep every element.  Also resets the row's
-// list count and overflow flag.
+// Per-row threshold from a sample, one wave per row: 16 runs of 256
+// consecutive elements (1 KB each) spread evenly over the row.  The threshold
+// is the lower edge of the 16-bit order-key bucket holding the k_s-th largest
+// sampled element, k_s chosen so that about `target` row elements are
+// expected at or above it.  Rows no longer than `target` keep every element.
+// Also resets the row's list count and overflow flag.
 constexpr int kThreshWaves = 4;
+constexpr int kSampleRuns = 16;
+constexpr int kSampleRun = 256;
 __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_thresh(const float* __restrict__ logits, int64_t ld,
                                                                    int n_cols, int target, int64_t q_pos0, int M,
                                                                    int64_t rows, float* __restrict__ thr,
                                                                    uint32_t* __restrict__ count,
                                                                    uint32_t* __restrict__ flag) {
-  constexpr int J = 64;   // sampled values per lane (128 lines x 32 = 4096 per row)
+  constexpr int ns = kSampleRuns * kSampleRun;   // 4096
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kThreshWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -623,26 +624,25 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_thresh(const float* 
   const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
   const float* lrow = logits + row * ld;
   float tf = -__builtin_inff();
-  const int n_lines = n / 32;
-  const int stride = max(32, (n_lines + 127) / 128);
-  const int ns = (n_lines / stride) * 32;
-  const uint64_t ks = (ns > 0) ? (uint64_t)target * (uint64_t)ns / (uint64_t)n + 2 : 0;
-  if (n > target && ns > 0 && ks < (uint64_t)ns) {
-    uint32_t key[J];
+  const uint64_t ks = (uint64_t)target * ns / (uint64_t)max(n, 1) + 2;
+  if (n > target && n >= 2 * ns && ks < (uint64_t)ns) {
+    uint32_t key[4 * kSampleRuns];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = lane + 64 * j;                      // sample element e: line e / 32, offset e % 32
-      const int ec = min(e, ns - 1);
-      const float v = lrow[(ec / 32) * stride * 32 + (ec % 32)];
-      key[j] = (e < ns) ? order_key(v) : 0u;            // 0: below every candidate key tested
+    for (int r = 0; r < kSampleRuns; ++r) {
+      // run r starts at a multiple of 4 (16-byte aligned: ld % 4 == 0)
+      const int start = (int)(((int64_t)(n - kSampleRun) * r / (kSampleRuns - 1)) & ~(int64_t)3);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(lrow + start + 4 * lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * r + j] = order_key(v[j]);
     }
+    // bits decided from the top: per-lane counts, one wave sum per bit
     uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 31; bit >= 16; --bit) {
       const uint32_t c = T | (1u << bit);
-      uint32_t cnt = 0;
+      uint32_t cl = 0;
 #pragma unroll
-      for (int j = 0; j < J; ++j) cnt += (uint32_t)__popcll(__ballot(key[j] >= c));
-      if (cnt >= (uint32_t)ks) T = c;
+      for (int j = 0; j < 4 * kSampleRuns; ++j) cl += (key[j] >= c) ? 1u : 0u;
+      if (__reduce_add_sync(~0ull, cl) >= (uint32_t)ks) T = c;
     }
     tf = key_to_float(T);
     if (tf != tf) tf = -__builtin_inff();
@@ -655,80 +655,89 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_thresh(const float* 
 }
 
 // Stream one chunk of a row and append every element >= the row's threshold
-// to the row's candidate list (LDS first, then one global atomic per chunk).
-// A chunk with more candidates than it can hold, or a list that would pass its
-// capacity, flags the row for the exact fallback.
+// to the row's candidate list.  Each wave filters its own share of the chunk
+// into its own LDS region, its running count in a scalar register (positions
+// from ballots of the lanes' per-batch counts, no atomics), and then appends
+// the region to the row's list with one global atomic.  A wave region that
+// fills up, or a list that would pass its capacity, flags the row for the
+// exact whole-row path.
+constexpr int kWaveCap = 1024;   // candidates a wave can hold
 template <int NT>
 __global__ void __launch_bounds__(NT) k_topk_filter(const float* __restrict__ logits, int64_t ld, int n_cols,
-                                                    int n_chunks, int64_t q_pos0, int M,
+                                                    int chunk, int n_chunks, int64_t q_pos0, int M,
                                                     const float* __restrict__ thr, uint32_t* __restrict__ count,
                                                     uint32_t* __restrict__ flag, uint64_t* __restrict__ list,
                                                     int capg) {
-  __shared__ uint64_t s_c[kChunkCap];
-  __shared__ uint32_t s_count, s_base;
+  constexpr int NW = NT / 64;
+  constexpr int U = 4;                      // float4s per lane per batch
+  __shared__ uint64_t s_c[NW][kWaveCap];
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = blockIdx.x / n_chunks, ch = blockIdx.x % n_chunks, b = blockIdx.y;
   const int64_t row = (int64_t)b * M + i;
   const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
-  const int c0 = ch * kChunk;
+  const int c0 = ch * chunk;
   if (c0 >= n) return;
-  const int c1 = min(n, c0 + kChunk);
+  const int c1 = min(n, c0 + chunk);
   const float* lrow = logits + row * ld;
   const float tf = thr[row];
-  if (tid == 0) s_count = 0;
-  __syncthreads();
+  uint64_t* reg = s_c[wv];
 
-  auto append4 = [&](const f32x4 v, int e0, bool f0, bool f1, bool f2, bool f3) {
-    const uint32_t c = (uint32_t)f0 + f1 + f2 + f3;
-    const uint64_t m0 = __ballot(c & 1u), m1 = __ballot(c & 2u), m2 = __ballot(c & 4u);
-    if ((m0 | m1 | m2) == 0) return;
-    uint32_t pos = lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2);
-    uint32_t base = 0;
-    if (lane == __ffsll((unsigned long long)__ballot(1)) - 1)
-      base = atomicAdd(&s_count, (uint32_t)(__popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2)));
-    pos += __builtin_amdgcn_readfirstlane(base);
-    if (f0) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[0], e0); ++pos; }
-    if (f1) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[1], e0 + 1); ++pos; }
-    if (f2) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[2], e0 + 2); ++pos; }
-    if (f3) { if (pos < (uint32_t)kChunkCap) s_c[pos] = pack_raw(v[3], e0 + 3); }
-  };
-
-  // float4s of the chunk (rows are 16-byte aligned: ld % 4 == 0, c0 % 4 == 0)
-  constexpr int U = 8;
+  // float4s of the chunk (rows are 16-byte aligned: ld % 4 == 0, c0 % 4 == 0),
+  // interleaved across the waves, non-temporal (each is read once), the next
+  // batch always in flight (index clamped to the chunk: no branch)
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(lrow + c0);
   const int n4 = (c1 - c0 + 3) / 4;
+  uint32_t run = 0;                         // candidates found by this wave (uniform)
+  f32x4 nv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) nv[u] = __builtin_nontemporal_load(p4 + min(tid + u * NT, n4 - 1));
   for (int base4 = 0; base4 < n4; base4 += U * NT) {
     f32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e4 = base4 + tid + u * NT;
-      const int e4c = min(e4, n4 - 1);
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lrow + c0) + e4c);
-    }
+    for (int u = 0; u < U; ++u) v[u] = nv[u];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      nv[u] = __builtin_nontemporal_load(p4 + min(base4 + U * NT + tid + u * NT, n4 - 1));
+    uint32_t fl = 0;   // bit 4u+j: element j of float4 u passes
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e4 = base4 + tid + u * NT;
-      const int e0 = c0 + 4 * e4;
-      const bool in = e4 < n4;
-      append4(v[u], e0, in && e0 < c1 && v[u][0] >= tf, in && e0 + 1 < c1 && v[u][1] >= tf,
-              in && e0 + 2 < c1 && v[u][2] >= tf, in && e0 + 3 < c1 && v[u][3] >= tf);
+      const int e0 = c0 + 4 * (base4 + tid + u * NT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fl |= (uint32_t)(e0 + j < c1 && v[u][j] >= tf) << (4 * u + j);
+    }
+    const uint32_t cnt = __popc(fl);           // 0..16
+    const uint64_t m0 = __ballot(cnt & 1u), m1 = __ballot(cnt & 2u), m2 = __ballot(cnt & 4u),
+                   m3 = __ballot(cnt & 8u), m4 = __ballot(cnt & 16u);
+    if ((m0 | m1 | m2 | m3 | m4) == 0) continue;
+    uint32_t pos = run + lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2) + 8 * lanes_below(m3) +
+                   16 * lanes_below(m4);
+    run += __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2) + 8 * __popcll(m3) + 16 * __popcll(m4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e0 = c0 + 4 * (base4 + tid + u * NT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (fl & (1u << (4 * u + j))) {
+          if (pos < (uint32_t)kWaveCap) reg[pos] = pack_raw(v[u][j], e0 + j);
+          ++pos;
+        }
     }
   }
-  __syncthreads();
-  const uint32_t c = s_count;
-  if (c == 0) return;
-  if (c > (uint32_t)kChunkCap) {
-    if (tid == 0) flag[row] = 1;
+  if (run == 0) return;
+  if (run > (uint32_t)kWaveCap) {
+    if (lane == 0) flag[row] = 1;
     return;
   }
-  if (tid == 0) s_base = atomicAdd(&count[row], c);
-  __syncthreads();
-  const uint32_t base = s_base;
-  if (base + c > (uint32_t)capg) {
-    if (tid == 0) flag[row] = 1;
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(&count[row], run);
+  base = __builtin_amdgcn_readfirstlane(base);
+  if (base + run > (uint32_t)capg) {
+    if (lane == 0) flag[row] = 1;
     return;
   }
   uint64_t* dst = list + row * (int64_t)capg + base;
-  for (uint32_t e = tid; e < c; e += NT) dst[e] = s_c[e];
+  for (uint32_t e = lane; e < run; e += 64) dst[e] = reg[e];
 }
 
 // Exact top-k of a row's candidate list (every element at or above the row's
@@ -801,10 +810,13 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
     hipLaunchKernelGGL(k_topk_thresh, dim3((unsigned)((rows + kThreshWaves - 1) / kThreshWaves)),
                        dim3(64 * kThreshWaves), 0, st, logits, ld, n_cols, target, s.q_pos0, s.q_per_seq, rows,
                        w.thr, w.count, w.flag);
-    const int n_chunks = (n_cols + kChunk - 1) / kChunk;
+    // chunk length: about target / 2 candidates expected per chunk buffer half
+    int64_t chunk = (int64_t)(kChunkCap / 2) * n_cols / target;
+    chunk = chunk >= kChunkMax ? kChunkMax : (chunk < 4096 ? 4096 : chunk / 4096 * 4096);
+    const int n_chunks = (int)((n_cols + chunk - 1) / chunk);
     dim3 fgrid((unsigned)((int64_t)s.q_per_seq * n_chunks), (unsigned)s.n_seq);
-    hipLaunchKernelGGL(k_topk_filter<256>, fgrid, dim3(256), 0, st, logits, ld, n_cols, n_chunks, s.q_pos0,
-                       s.q_per_seq, w.thr, w.count, w.flag, w.list, w.capg);
+    hipLaunchKernelGGL(k_topk_filter<256>, fgrid, dim3(256), 0, st, logits, ld, n_cols, (int)chunk, n_chunks,
+                       s.q_pos0, s.q_per_seq, w.thr, w.count, w.flag, w.list, w.capg);
     if (k <= 4096)
       hipLaunchKernelGGL((k_topk_list<8192, 512>), grid, dim3(512), 0, st, logits, ld, n_cols, k, s.q_pos0,
                          s.q_per_seq, idx, vals, (int)sorted, w.list, w.count, w.flag, w.capg);
