@@ -602,51 +602,55 @@ static SplitWs split_ws(void* ws, int64_t rows, int k) {
   return w;
 }
 
-// Per-row threshold from a sample, one wave per row: 16 runs of 256
-// consecutive elements (1 KB each) spread evenly over the row.  The threshold
-// is the lower edge of the 16-bit order-key bucket holding the k_s-th largest
-// sampled element, k_s chosen so that about `target` row elements are
-// expected at or above it.  Rows no longer than `target` keep every element.
-// Also resets the row's list count and overflow flag.
+// Per-row threshold from a sample: 1024 float4s (4096 elements) at a regular
+// stride over the row.  Sampling in 16-byte pieces keeps a cluster of large
+// scores (a block of related keys) from taking more than its share of the
+// sample.  The threshold is the lower edge of the 20-bit order-key bucket
+// holding the k_s-th largest sampled element, k_s chosen so that about
+// `target` row elements are expected at or above it; rows no longer than
+// `target` keep every element (-inf).  Computed by one wave.
+__device__ __forceinline__ float row_threshold(const float* __restrict__ lrow, int n, int target) {
+  constexpr int L = 16;          // float4 loads per lane
+  constexpr int ns = 64 * L * 4;  // 4096 sampled elements
+  const int lane = threadIdx.x & 63;
+  const uint64_t ks = (uint64_t)target * ns / (uint64_t)max(n, 1) + 2;
+  if (!(n > target && n >= 2 * ns && ks < (uint64_t)ns)) return -__builtin_inff();
+  const uint32_t n4 = (uint32_t)n / 4;                // whole float4s (16-byte aligned rows)
+  const uint32_t stride = n4 / (uint32_t)(ns / 4);    // >= 2 (n >= 2 ns)
+  uint32_t key[4 * L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    const f32x4 v = *(reinterpret_cast<const f32x4*>(lrow) + (uint32_t)(j * 64 + lane) * stride);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * j + e] = order_key(v[e]);
+  }
+  // bits decided from the top: per-lane counts, one wave sum per bit
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 12; --bit) {
+    const uint32_t c = T | (1u << bit);
+    uint32_t cl = 0;
+#pragma unroll
+    for (int j = 0; j < 4 * L; ++j) cl += (key[j] >= c) ? 1u : 0u;
+    if (__reduce_add_sync(~0ull, cl) >= (uint32_t)ks) T = c;
+  }
+  const float tf = key_to_float(T);
+  return (tf != tf) ? -__builtin_inff() : tf;
+}
+
+// One wave per row: the row's threshold (row_threshold), and the row's list
+// count and overflow flag reset.
 constexpr int kThreshWaves = 4;
-constexpr int kSampleRuns = 16;
-constexpr int kSampleRun = 256;
 __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_thresh(const float* __restrict__ logits, int64_t ld,
                                                                    int n_cols, int target, int64_t q_pos0, int M,
                                                                    int64_t rows, float* __restrict__ thr,
                                                                    uint32_t* __restrict__ count,
                                                                    uint32_t* __restrict__ flag) {
-  constexpr int ns = kSampleRuns * kSampleRun;   // 4096
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kThreshWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int i = (int)(row % M);
   const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
-  const float* lrow = logits + row * ld;
-  float tf = -__builtin_inff();
-  const uint64_t ks = (uint64_t)target * ns / (uint64_t)max(n, 1) + 2;
-  if (n > target && n >= 2 * ns && ks < (uint64_t)ns) {
-    uint32_t key[4 * kSampleRuns];
-#pragma unroll
-    for (int r = 0; r < kSampleRuns; ++r) {
-      // run r starts at a multiple of 4 (16-byte aligned: ld % 4 == 0)
-      const int start = (int)(((int64_t)(n - kSampleRun) * r / (kSampleRuns - 1)) & ~(int64_t)3);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(lrow + start + 4 * lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) key[4 * r + j] = order_key(v[j]);
-    }
-    // bits decided from the top: per-lane counts, one wave sum per bit
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 16; --bit) {
-      const uint32_t c = T | (1u << bit);
-      uint32_t cl = 0;
-#pragma unroll
-      for (int j = 0; j < 4 * kSampleRuns; ++j) cl += (key[j] >= c) ? 1u : 0u;
-      if (__reduce_add_sync(~0ull, cl) >= (uint32_t)ks) T = c;
-    }
-    tf = key_to_float(T);
-    if (tf != tf) tf = -__builtin_inff();
-  }
+  const float tf = row_threshold(logits + row * ld, n, target);
   if (lane == 0) {
     thr[row] = tf;
     count[row] = 0;
