@@ -11,21 +11,28 @@
 //
 // Design.  The (query, head) x (block) products are a dense contraction, so
 // they run on bf16 MFMA: q is bf16 already, and each fp32 pooled key is split
-// exactly-enough into hi + lo bf16 parts (p - hi is exact in fp32; |p - hi -
-// lo| <= 2^-16 |p|), so q.p = q.hi + q.lo is accumulated by two MFMAs into
-// the same fp32 accumulator.  A wave owns 4 queries x 16 heads (four 16x16
-// row blocks: row r = query r/4, head 4*rb + r%4), keeps its q fragments in
-// registers and streams 64-block chunks of pooled keys staged once per
-// workgroup in LDS.  ReLU, the causal block mask and the block sum stay in
-// registers; the tail term is an fp32 dot per (query, head); the top-h
-// selection is a rank count over <= 64 values, one wave per query.
+// into hi + lo bf16 parts when it is staged (p - hi is exact in fp32;
+// |p - hi - lo| <= 2^-16 |p|), so q.p = q.hi + q.lo is accumulated by two
+// MFMAs into the same fp32 accumulator (bf16 pooled keys alone are not
+// accurate enough where a block's dot product cancels).  A wave owns
+// 4 queries x 16 heads (four 16x16 row blocks: row r = query r/4, head
+// 4*rb + r%4), keeps its q fragments in registers and streams 64-block chunks
+// of pooled keys staged once per workgroup in LDS (XOR-swizzled 256-byte rows,
+// as in the scoring kernel, so the fragment reads are free of bank conflicts);
+// a workgroup serves 4 (H = 64) to 16 (H <= 16) queries.  ReLU, the causal
+// block mask and the block sum stay in registers; the tail term is an fp32 dot
+// per (query, head); the top-h selection is a rank count over <= 64 values,
+// one wave per query.
 #include "misa_common.h"
 #include "misa_launch.h"
 
 namespace misa {
 
 constexpr int kRouteChunk = 64;            // pooled rows staged per step
-constexpr int kRowStride = kD + 8;          // bf16 elements per LDS row (16 B pad)
+constexpr int kRowBytes = kD * 2;           // bf16 LDS row (256 bytes), 16-byte chunks XOR-swizzled
+
+// byte offset of 16-byte chunk c of staged row j
+__device__ __forceinline__ uint32_t rt_off(int j, int c) { return (uint32_t)j * kRowBytes + (uint32_t)((c ^ (j & 15)) << 4); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -33,7 +40,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 
 template <int NHC>  // 16-head chunks per query group (= ceil(H/16))
-__global__ void __launch_bounds__(256) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
+__global__ void __launch_bounds__(512) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
                                                const float* __restrict__ pooled,
                                                const float* __restrict__ tail,
                                                int32_t* __restrict__ heads, float* __restrict__ scores,
@@ -42,8 +49,8 @@ __global__ void __launch_bounds__(256) k_route(const uint16_t* __restrict__ q, c
   constexpr int QG = (NHC == 1) ? 4 : (NHC == 2 ? 2 : 1);  // query groups per workgroup
   constexpr int NW = NHC * QG;                              // waves per workgroup
   constexpr int QWG = 4 * QG;                               // queries per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t s_hi[kRouteChunk * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_lo[kRouteChunk * kRowStride];
+  __shared__ __attribute__((aligned(16))) unsigned char s_hi[kRouteChunk * kRowBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_lo[kRouteChunk * kRowBytes];
   __shared__ float s_r[QWG][64];
 
   const int tid = threadIdx.x;
@@ -96,17 +103,16 @@ __global__ void __launch_bounds__(256) k_route(const uint16_t* __restrict__ q, c
       const int c4 = e % (kD / 4);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (cbase + row < nfull_wg) v = reinterpret_cast<const float4*>(pool_b + (cbase + row) * kD)[c4];
-      float f[4] = {v.x, v.y, v.z, v.w};
+      const float f[4] = {v.x, v.y, v.z, v.w};
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         hi[i] = f32_to_bf16_rne(f[i]);
-        lo[i] = f32_to_bf16_rne(f[i] - __uint_as_float(hi[i] << 16));
+        lo[i] = f32_to_bf16_rne(f[i] - __uint_as_float(hi[i] << 16));   // f - hi is exact in fp32
       }
-      uint2 hv = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-      uint2 lv = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-      *reinterpret_cast<uint2*>(&s_hi[row * kRowStride + c4 * 4]) = hv;
-      *reinterpret_cast<uint2*>(&s_lo[row * kRowStride + c4 * 4]) = lv;
+      const uint32_t o = rt_off(row, c4 >> 1) + (c4 & 1) * 8;
+      *reinterpret_cast<uint2*>(&s_hi[o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *reinterpret_cast<uint2*>(&s_lo[o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
     __syncthreads();
 #pragma unroll
@@ -117,8 +123,8 @@ __global__ void __launch_bounds__(256) k_route(const uint16_t* __restrict__ q, c
         const int row = cb * 16 + p16;
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
-          bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_hi[row * kRowStride + ks * 32 + g * 8]));
-          bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_lo[row * kRowStride + ks * 32 + g * 8]));
+          bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_hi[rt_off(row, ks * 4 + g)]));
+          bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_lo[rt_off(row, ks * 4 + g)]));
         }
         const bool valid = (col0 + p16) < nfull_g;
 #pragma unroll
