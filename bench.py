@@ -3,19 +3,22 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one pass of the MISA indexer over one prefill chunk resident in
-HBM: block pooling -> head routing -> routed-head token scoring -> top-k
-(the four kernels misa_indexer launches, issued through the C ABI one stage
-at a time so that HIP events on the launch stream time every kernel).  The
-default workload is the long-context final prefill chunk: M = 8192 queries
-against N = 131072 fp8 keys, H_I = 64 heads, h = 8, B = 128, top-2048.
+HBM: block pooling -> head routing -> routed-head token scoring fused with
+the top-k selection (misa_sparse_head_topk: the logits are not written), each
+issued through the C ABI on the launch stream with HIP events between them.
+The default workload is the long-context final prefill chunk: M = 8192
+queries against N = 131072 fp8 keys, H_I = 64 heads, h = 8, B = 128,
+top-2048.
 
 Printed: one JSON line.  value = scored (query, key, head) triples per second
 (G/s) of the whole step; ms_per_step = indexer milliseconds per chunk;
-roofline = the dominant kernel against its MI355X peak; stages = every
-kernel's time and roofline fraction; misa_dagger and dense = the same chunk
-through the MISA-dagger pipeline (k' = 8192) and through the dense all-head
-DSA indexer, timed in the same run; cpu_baseline = the fp64 oracle on the
-host cores over a bounded sample of the same chunk.
+roofline = the dominant stage (the fused scoring + selection) against the
+bf16 MFMA peak, with its scoring work; stages = every stage's time and
+roofline fraction, plus the same chunk through the separate logits kernel
+and top-k kernel (staged_score, staged_topk); misa_dagger and dense = the
+chunk through the MISA-dagger pipeline (k' = 8192) and through the dense
+all-head DSA indexer, timed in the same run; cpu_baseline = the fp64 oracle
+on the host cores over a bounded sample of the same chunk.
 """
 from __future__ import annotations
 
@@ -85,8 +88,9 @@ def src_hash(*names):
 
 
 KERNEL_SOURCES = {
-    "score": ("score.hip", "misa_common.h"),
-    "topk": ("topk.hip", "misa_common.h"),
+    "select": ("score.hip", "topk.hip", "misa_common.h"),
+    "staged_score": ("score.hip", "misa_common.h"),
+    "staged_topk": ("topk.hip", "misa_common.h"),
     "route": ("route.hip", "misa_common.h"),
     "pool": ("pool.hip", "misa_common.h"),
 }
@@ -148,6 +152,8 @@ def main():
     tk_ws_bytes = max(lcsb.misa_topk_workspace_bytes(sh, N, K), lcsb.misa_topk_workspace_bytes(sh, N, kp),
                       lcsb.misa_topk_workspace_bytes(sh, kp, K), 1)
     tk_ws = torch.empty(tk_ws_bytes, dtype=torch.uint8, device=dev)   # top-k scratch, allocated once
+    sel_ws = torch.empty(max(lcsb.misa_sparse_head_topk_workspace_bytes(sh, h, K),
+                             lcsb.misa_sparse_head_topk_workspace_bytes(sh, h, kp)), dtype=torch.uint8, device=dev)
 
     def run_timed(stages, steps, warmup):
         """stages: list of (name, fn).  Returns per-stage mean ms and step ms."""
@@ -174,14 +180,28 @@ def main():
     misa_stages = [
         ("pool", lambda: lcsb.misa_pool_keys(sh, k, ks, pooled=pooled, tail=tail)),
         ("route", lambda: lcsb.misa_route_heads(sh, q, w, pooled[:, :n_full], tail, h, heads=heads)),
-        ("score", lambda: lcsb.misa_sparse_head_logits(sh, q, w, k, heads, k_scale=ks, logits=logits)),
-        ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals, ws=tk_ws)),
+        ("select", lambda: lcsb.misa_sparse_head_topk(sh, q, w, k, heads, K, k_scale=ks, idx=idx, vals=vals,
+                                                      ws=sel_ws)),
     ]
     per, step_ms, wall_ms = run_timed(misa_stages, args.steps, args.warmup)
     print(f"[bench] MISA step {step_ms:.3f} ms (wall {wall_ms:.3f}) {per}", file=sys.stderr, flush=True)
+    # the same scoring and selection as two kernels with materialised logits
+    staged = [
+        ("staged_score", lambda: lcsb.misa_sparse_head_logits(sh, q, w, k, heads, k_scale=ks, logits=logits)),
+        ("staged_topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals, ws=tk_ws)),
+    ]
+    sper, sstep, _ = run_timed(staged, max(3, args.steps // 2), 2)
+    print(f"[bench] staged score + top-k {sstep:.3f} ms {sper}", file=sys.stderr, flush=True)
+    # the whole indexer as one C call (the same kernels as the step)
+    ix_ws = torch.empty(lcsb.misa_indexer_workspace_bytes(sh, h, K), dtype=torch.uint8, device=dev)
+    _, ix_ms, _ = run_timed([("indexer", lambda: lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks, idx=idx,
+                                                                   vals=vals, ws=ix_ws))],
+                            max(3, args.steps // 2), 2)
+    del ix_ws
+    print(f"[bench] misa_indexer call {ix_ms:.3f} ms", file=sys.stderr, flush=True)
 
     def roof(stage, ms):
-        if stage == "score":
+        if stage in ("select", "staged_score"):
             a = W["score_flops"] / (ms * 1e-3) / 1e12
             r = dict(bound="mfma", achieved=a, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
         elif stage == "route":
@@ -196,19 +216,20 @@ def main():
         r["ms"] = ms
         return r
 
-    stages_out = {name: roof(name, ms) for name, ms in per.items()}
+    stages_out = {name: roof(name, ms) for name, ms in list(per.items()) + list(sper.items())}
     dominant = max(per, key=per.get)
     roofline = {kk: v for kk, v in stages_out[dominant].items() if kk != "ms"}
     roofline["kernel"] = dominant
-    # the scoring kernel also streams the logits out: report that rate beside its MFMA rate
-    stages_out["score"]["logit_write_GBs"] = W["score_bytes"] / (per["score"] * 1e-3) / 1e9
+    # the logits kernel also streams the logits out: report that rate beside its MFMA rate
+    stages_out["staged_score"]["logit_write_GBs"] = W["score_bytes"] / (sper["staged_score"] * 1e-3) / 1e9
 
     extras = {}
     if not args.no_extras:
         cand = torch.empty((S, M, kp), dtype=torch.int32, device=dev)
         dlog = torch.empty((S, M, kp), dtype=torch.float32, device=dev)
-        dagger_stages = misa_stages[:3] + [
-            ("topk_kprime", lambda: lcsb.misa_topk(sh, logits, kp, idx=cand, want_vals=False, sorted=False, ws=tk_ws)),
+        dagger_stages = misa_stages[:2] + [
+            ("select_kprime", lambda: lcsb.misa_sparse_head_topk(sh, q, w, k, heads, kp, k_scale=ks, sorted=False,
+                                                                 idx=cand, want_vals=False, ws=sel_ws)),
             ("rerank", lambda: lcsb.dsa_dense_logits(sh, q, w, k, k_scale=ks, cand=cand, logits=dlog)),
             ("topk_final", lambda: lcsb.misa_topk(sh, dlog, K, cand=cand, idx=idx, vals=vals, ws=tk_ws)),
         ]
@@ -256,6 +277,7 @@ def main():
                    "k_dtype": "fp8_e4m3" if cfg.kdtype == 1 else "bf16", "head_dim": 128},
         "roofline": roofline,
         "stages": stages_out,
+        "indexer_call_ms": ix_ms,
         "cpu_baseline": cpu,
     }
     line.update(extras)

@@ -182,6 +182,31 @@ misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld,
 size_t misa_topk_workspace_bytes(const misa_shape* shape, int32_t n_cols, int32_t k);
 
 /*
+ * Routed-head scoring and top-k token selection in one call, without
+ * materialising the logits where that can be avoided (the fused scoring ->
+ * top-k the GitHub issue asks for as a "fused MISA kernel").  The result is
+ * exactly misa_topk(misa_sparse_head_logits(...), topk, sorted): same ids,
+ * same values, same order (sorted != 0) or the same set (sorted == 0).
+ * When every query's prefix has at least 32768 keys and h <= 8, the scores of
+ * a key sample (every kstride-th key, kstride >= 32) give each row a
+ * threshold; the routed scoring keeps only the scores at or above it, as
+ * candidates, and the exact top-k is taken over them.  A row whose
+ * candidates fall short of topk (or overflow their buffers) is re-scored into
+ * full logits in the workspace and selected from them, so the result does
+ * not depend on the sample.  Otherwise the logits are materialised in the
+ * workspace and misa_topk runs on them.
+ * heads: int32 [n_seq][M][h], as misa_sparse_head_logits.  idx / vals: as
+ * misa_topk.  1 <= topk <= MISA_MAX_TOPK.
+ * ws / ws_bytes: at least misa_sparse_head_topk_workspace_bytes() bytes.
+ */
+misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, const float* w,
+                                  const void* k, misa_kdtype kdtype, const float* k_scale,
+                                  const int32_t* heads, int32_t h, int32_t topk, int32_t sorted,
+                                  int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream);
+
+size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk);
+
+/*
  * The whole indexer on the caller's stream: pool -> route -> routed scoring ->
  * top-k (k_prime == 0, MISA), or pool -> route -> routed scoring -> top-k' ->
  * all-head re-rank of the k' candidates -> top-k (k_prime >= topk, MISA-dagger;

@@ -27,8 +27,8 @@ MAX_HEADS = 64
 MAX_TOPK = 8192
 
 EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_sparse_head_logits",
-            "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_indexer",
-            "misa_indexer_workspace_bytes")
+            "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_sparse_head_topk",
+            "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes")
 
 
 class MisaShape(ctypes.Structure):
@@ -66,6 +66,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_sparse_head_logits": [S, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "dsa_dense_logits": [S, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "misa_topk": [S, P, i64, P, i32, i32, i32, P, P, P, sz, P],
+        "misa_sparse_head_topk": [S, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
     }
     for name, args in sigs.items():
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.misa_topk_workspace_bytes.argtypes = [S, i32, i32]
     lib.misa_topk_workspace_bytes.restype = sz
+    lib.misa_sparse_head_topk_workspace_bytes.argtypes = [S, i32, i32]
+    lib.misa_sparse_head_topk_workspace_bytes.restype = sz
     lib.misa_indexer_workspace_bytes.argtypes = [S, i32, i32, i32]
     lib.misa_indexer_workspace_bytes.restype = sz
     _lib = lib
@@ -234,6 +237,34 @@ def misa_topk(shape: MisaShape, logits, k: int, n_cols=None, cand=None, idx=None
 
 def misa_topk_workspace_bytes(shape: MisaShape, n_cols: int, k: int) -> int:
     return int(load().misa_topk_workspace_bytes(ctypes.byref(shape), int(n_cols), int(k)))
+
+
+def misa_sparse_head_topk_workspace_bytes(shape: MisaShape, h: int, topk: int) -> int:
+    return int(load().misa_sparse_head_topk_workspace_bytes(ctypes.byref(shape), int(h), int(topk)))
+
+
+def misa_sparse_head_topk(shape: MisaShape, q, w, k, heads, topk: int, k_scale=None, sorted=True, idx=None,
+                          vals=None, want_vals=True, ws=None, stream=None):
+    """Routed scoring + top-k in one call (no logits where they can be avoided);
+    the same result as misa_topk(misa_sparse_head_logits(...), topk)."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    h = heads.shape[-1]
+    _need(heads, torch.int32, (shape.n_seq, M, h), "heads")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(misa_sparse_head_topk_workspace_bytes(shape, h, topk), 1), dtype=torch.uint8,
+                         device=q.device)
+    st = load().misa_sparse_head_topk(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale),
+                                      _ptr(heads), int(h), int(topk), int(bool(sorted)), _ptr(idx), _ptr(vals),
+                                      _ptr(ws), int(ws.numel()), _stream(stream))
+    _check(st, "misa_sparse_head_topk")
+    return idx, vals
 
 
 def misa_indexer_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:

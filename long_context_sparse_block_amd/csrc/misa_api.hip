@@ -52,16 +52,75 @@ inline misa_status from_hip(hipError_t e) { return e == hipSuccess ? MISA_OK : M
     if (_st != MISA_OK) return _st;    \
   } while (0)
 
+// Workspace of the routed scoring + top-k selection (misa_sparse_head_topk,
+// and the first selection of misa_indexer), placed from offset `off`.
+struct SelectLayout {
+  size_t logits, sample, thr, flag, rcount, regions, topk_ws, end;
+  int64_t ld;
+  misa::FusedPlan fused;
+};
+
+SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off) {
+  SelectLayout L{};
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  L.ld = (s.n_keys + 3) / 4 * 4;
+  L.logits = off;   // full logits: the unfused path, or the rows the fused path re-scores
+  off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
+  L.fused = misa::plan_fused(s, h, k);
+  if (L.fused.ok) {
+    const misa::FusedPlan& p = L.fused;
+    L.sample = off;
+    off += align_up((size_t)rows * (size_t)p.ld_sample * sizeof(float));
+    L.thr = off;
+    off += align_up((size_t)rows * sizeof(float));
+    L.flag = off;
+    off += align_up((size_t)rows * sizeof(uint32_t));
+    L.rcount = off;
+    off += align_up((size_t)rows * p.n_splits * sizeof(uint32_t));
+    L.regions = off;
+    off += align_up((size_t)rows * p.n_splits * (size_t)p.cap_region * sizeof(uint64_t));
+  } else {
+    L.topk_ws = off;
+    off += align_up(misa::topk_workspace_bytes(s, (int)s.n_keys, k));
+  }
+  L.end = off;
+  return L;
+}
+
+// Routed scoring + exact top-k (see misa_sparse_head_topk).
+misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, const uint16_t* q, const float* w,
+                       const void* k, int kdtype, const float* k_scale, const int32_t* heads, int h, int topk,
+                       bool sorted, int32_t* idx, float* vals, hipStream_t st) {
+  float* logits = reinterpret_cast<float*>(base + L.logits);
+  if (!L.fused.ok) {
+    MISA_TRY(from_hip(launch_score(s, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, st)));
+    return from_hip(launch_topk(s, logits, L.ld, nullptr, (int)s.n_keys, topk, idx, vals, base + L.topk_ws,
+                                L.end - L.topk_ws, st, sorted));
+  }
+  const misa::FusedPlan& p = L.fused;
+  float* sample = reinterpret_cast<float*>(base + L.sample);
+  float* thr = reinterpret_cast<float*>(base + L.thr);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(base + L.flag);
+  uint32_t* rcount = reinterpret_cast<uint32_t*>(base + L.rcount);
+  uint64_t* regions = reinterpret_cast<uint64_t*>(base + L.regions);
+  MISA_TRY(from_hip(misa::launch_score_sampled(s, q, w, k, kdtype, k_scale, heads, h, p, sample, st)));
+  MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
+  MISA_TRY(from_hip(misa::launch_score_cands(s, q, w, k, kdtype, k_scale, heads, h, p, thr, regions, rcount, st)));
+  MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, regions, rcount, flag, idx, vals, sorted, st)));
+  MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, k, kdtype, k_scale, heads, h, flag, logits, L.ld, st)));
+  return from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st));
+}
+
 struct IndexerLayout {
-  size_t pooled, tail, heads, logits, cand, dlog, topk_ws, total;
-  int64_t ld, ld_d;
+  size_t pooled, tail, heads, cand, dlog, total;
+  int64_t ld_d;
+  SelectLayout sel;
 };
 
 IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime) {
   IndexerLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   const int64_t n_full = s.n_keys / s.block;
-  L.ld = (s.n_keys + 3) / 4 * 4;
   L.ld_d = (k_prime + 3) / 4 * 4;
   size_t off = 0;
   L.pooled = off;
@@ -70,22 +129,16 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime) 
   off += align_up((size_t)rows * MISA_HEAD_DIM * sizeof(float));
   L.heads = off;
   off += align_up((size_t)rows * h * sizeof(int32_t));
-  L.logits = off;
-  off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
-  const int first_k = k_prime > 0 ? k_prime : topk;
   if (k_prime > 0) {
     L.cand = off;
     off += align_up((size_t)rows * k_prime * sizeof(int32_t));
     L.dlog = off;
     off += align_up((size_t)rows * (size_t)L.ld_d * sizeof(float));
   }
-  L.topk_ws = off;
-  size_t tw = misa::topk_workspace_bytes(s, (int)s.n_keys, first_k);
-  if (k_prime > 0) {
-    size_t tw2 = misa::topk_workspace_bytes(s, k_prime, topk);
-    if (tw2 > tw) tw = tw2;
-  }
-  off += align_up(tw);
+  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off);
+  off = L.sel.end;
+  // the final top-k of MISA-dagger runs over k' candidate columns
+  if (k_prime > 0) off += align_up(misa::topk_workspace_bytes(s, k_prime, topk));
   L.total = off;
   return L;
 }
@@ -211,22 +264,39 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
   float* pooled = reinterpret_cast<float*>(base + L.pooled);
   float* tail = reinterpret_cast<float*>(base + L.tail);
   int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
-  float* logits = reinterpret_cast<float*>(base + L.logits);
-  void* tws = base + L.topk_ws;
-  const size_t tws_bytes = L.total - L.topk_ws;
   MISA_TRY(from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, st)));
   MISA_TRY(from_hip(launch_route(*shape, q, w, pooled, tail, h, heads, nullptr, st)));
-  MISA_TRY(from_hip(launch_score(*shape, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, st)));
   if (k_prime == 0)
-    return from_hip(launch_topk(*shape, logits, L.ld, nullptr, (int)shape->n_keys, topk, idx, vals, tws,
-                                tws_bytes, st));
+    return run_select(*shape, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st);
+  // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
   float* dlog = reinterpret_cast<float*>(base + L.dlog);
-  // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
-  MISA_TRY(from_hip(launch_topk(*shape, logits, L.ld, nullptr, (int)shape->n_keys, k_prime, cand, nullptr,
-                                tws, tws_bytes, st, /*sorted=*/false)));
+  MISA_TRY(run_select(*shape, L.sel, base, q, w, k, kdtype, k_scale, heads, h, k_prime, false, cand, nullptr, st));
   MISA_TRY(from_hip(launch_score_gather(*shape, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
-  return from_hip(launch_topk(*shape, dlog, L.ld_d, cand, k_prime, topk, idx, vals, tws, tws_bytes, st));
+  return from_hip(launch_topk(*shape, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
+                              L.total - L.sel.end, st));
+}
+
+misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                  misa_kdtype kdtype, const float* k_scale, const int32_t* heads, int32_t h,
+                                  int32_t topk, int32_t sorted, int32_t* idx, float* vals, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (q == nullptr || !aligned16(q) || w == nullptr || heads == nullptr || idx == nullptr)
+    return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
+  const SelectLayout L = select_layout(*shape, h, topk, 0);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < L.end) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return run_select(*shape, L, static_cast<char*>(ws), q, w, k, kdtype, k_scale, heads, h, topk, sorted != 0, idx,
+                    vals, (hipStream_t)stream);
+}
+
+size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1) return 0;
+  return select_layout(*shape, h, topk, 0).end;
 }
 
 }  // extern "C"

@@ -66,6 +66,11 @@ __device__ __forceinline__ float quad_chain(const f32x4 x, float w0, float w1, f
   return p;
 }
 
+// Number of set bits of m below the calling lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Order-preserving map float -> uint32 (larger float <=> larger key), with
 // -0.0 folded onto +0.0.
 __device__ __forceinline__ uint32_t order_key(float f) {

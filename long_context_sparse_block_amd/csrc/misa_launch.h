@@ -32,4 +32,48 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
 
 size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k);
 
+// ---------------------------------------------------------------------------
+// Fused scoring -> top-k (the indexer's path for h <= 8 and long prefixes):
+//  1. scores of a key sample (every kstride-th key) -> sample logits;
+//  2. per-row threshold from the sample row (k_s-th largest sampled score);
+//  3. routed-head scoring that keeps only scores >= the row threshold, as
+//     candidates in per-(row, key range) regions, writing no logits;
+//  4. exact top-k of each row's candidates; a row whose regions overflowed or
+//     hold fewer than k candidates is flagged, re-scored into full logits and
+//     selected from them, so the result is exact for every input.
+// ---------------------------------------------------------------------------
+struct FusedPlan {
+  bool ok;             // the fused path applies
+  int kstride;         // key sampling stride of step 1
+  int64_t n_sample;    // sampled keys per row (<= 4096)
+  int64_t ld_sample;   // row stride of the sample logits
+  int cap_list;        // candidates the select kernel can hold per row
+  int target;          // candidates aimed for per row
+  int n_splits;        // key ranges of the scoring grid
+  int64_t key_range;   // keys per range
+  int cap_region;      // candidates one (row, key range) region holds
+};
+FusedPlan plan_fused(const misa_shape& s, int h, int k);
+
+hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
+                                const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
+                                float* sample_logits, hipStream_t st);
+hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
+                              const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
+                              const float* thr, uint64_t* regions, uint32_t* rcount, hipStream_t st);
+// full logits rows of the workgroups that hold a row with row_flag != 0
+hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
+                                int kdtype, const float* k_scale, const int32_t* heads, int h,
+                                const uint32_t* row_flag, float* logits, int64_t ld, hipStream_t st);
+// thr[row] from the sample logits; row_flag[row] = 0
+hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, const float* sample_logits,
+                                     float* thr, uint32_t* row_flag, hipStream_t st);
+// top-k of the candidate regions; rows it cannot settle get row_flag = 1
+hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const uint64_t* regions,
+                               const uint32_t* rcount, uint32_t* row_flag, int32_t* idx, float* vals, bool sorted,
+                               hipStream_t st);
+// whole-row top-k of the flagged rows from full logits
+hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* logits, int64_t ld,
+                               const uint32_t* row_flag, int32_t* idx, float* vals, bool sorted, hipStream_t st);
+
 }  // namespace misa

@@ -27,6 +27,7 @@
 //   then s *= sigma (fp8).
 // k_score_c16 (h > 8, and all heads) follows it exactly; k_score_h8 (h <= 8)
 // uses s = P0 + P1 (its own order; compared to the oracle within tolerance).
+#include <algorithm>
 #include <type_traits>
 
 #include "misa_common.h"
@@ -157,23 +158,26 @@ struct KStageSw {
   uint4 r[kPerThread];
   float sc;
 
-  // Keys [key0, key0 + 64) through descriptors based at the tile and bounded
-  // by N (rows past N read as zeros; their logits are never kept).  Thread
+  // Tile keys [key0, key0 + 64) of the key sequence 0, ks, 2 ks, ... (ks = 1:
+  // every key) through descriptors based at the tile and bounded by the N
+  // keys (rows past N read as zeros; their logits are never kept).  Thread
   // chunk e fills LDS row e / kVecPerKey, i.e. tile key sw_tile_key(row).
-  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int tid) {
-    const int rem = max(0, min(kSwKT, N - key0));
+  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int ks, int tid) {
+    const int64_t first = (int64_t)key0 * ks;   // position of the tile's first key
+    const int rem = (int)max((int64_t)0, min((int64_t)kSwKT * ks, (int64_t)N - first));   // keys in range
     const __amdgpu_buffer_rsrc_t kr =
-        uniform_rsrc(static_cast<const char*>(kbase) + (int64_t)key0 * kRowBytes, (uint32_t)(rem * kRowBytes));
+        uniform_rsrc(static_cast<const char*>(kbase) + first * kRowBytes, (uint32_t)rem * kRowBytes);
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
       const int e = tid + u * NT;
       const int j = e / kVecPerKey, c = e % kVecPerKey;
-      r[u] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, sw_tile_key(j) * kRowBytes + c * 16, 0, 0));
+      r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           kr, (uint32_t)(sw_tile_key(j) * ks) * kRowBytes + c * 16, 0, 0));
     }
     if (KDT == MISA_K_FP8_E4M3) {
-      const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + key0, (uint32_t)(rem * 4));
-      sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, sw_tile_key(tid % kSwKT) * 4, 0, 0));
+      const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + first, (uint32_t)rem * 4u);
+      sc = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(sw_tile_key(tid % kSwKT) * ks) * 4u, 0, 0));
     }
   }
 
@@ -202,47 +206,83 @@ __device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t b
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
 }
 
+// Where a k_score_h8 pass puts its results.
+//  MODE kLogits: logits[row][u] for key u of the scored key sequence (u ks).
+//  MODE kCands: no logits; every (query, key) score >= thr[row] of a key the
+//    query sees is appended as (key << 32 | score bits) to the region of that
+//    row and of the workgroup's key range: region (row * n_splits + split),
+//    `cap` entries; rcount[row * n_splits + split] receives the number found
+//    (more than cap: the region overflowed and holds only the first cap).
+//  row_flag != nullptr: only workgroups holding a row with row_flag[row] != 0
+//    run (re-scoring of the rows a candidate pass could not settle).
+struct ScoreOut {
+  float* logits;
+  int64_t ld;
+  const float* thr;
+  uint64_t* regions;
+  uint32_t* rcount;
+  int cap;
+  const uint32_t* row_flag;
+};
+constexpr int kLogits = 0;
+constexpr int kCands = 1;
+
 // ---------------------------------------------------------------------------
 // h <= 8: 8 queries per wave (2 groups x 2 head quads = 4 MFMA row blocks),
 // 32 queries per workgroup, 64-key tiles in the swizzled layout above.  The B
 // fragments of the next column block are read from LDS while the current
 // block's 16 MFMAs and epilogue run.  After a tile each lane holds 4
-// consecutive logits of 2 queries and writes each group with one 16-byte
-// buffer store (rows past M and key groups past N fall outside the store
-// descriptor and are dropped; a group straddling N also writes -inf into
-// columns N .. roundup4(N)-1, which lie inside the row).  All loads are
-// unconditional, so the compiler never waits on the logit stores.  The tile
-// loop is unrolled by two so both LDS buffers are addressed by immediates.
+// consecutive scores of 2 queries.
+//   kLogits: each group is written with one 16-byte buffer store (rows past M
+//   and key groups past N fall outside the store descriptor and are dropped; a
+//   group straddling N also writes -inf into columns N .. roundup4(N)-1,
+//   which lie inside the row).
+//   kCands: the scores at or above the row threshold are appended to the
+//   row's region (positions from ballots within the 16 lanes that hold one
+//   query); the appends of a tile are issued at the start of the next tile,
+//   before its key prefetch, so waiting for that prefetch never waits for a
+//   store issued after it.
+// All loads are unconditional, so the compiler never waits on the stores.
+// The tile loop is unrolled by two so both LDS buffers are addressed by
+// immediates.  Keys are scored along the sequence 0, ks, 2 ks, ... (ks = 1:
+// every key; a stride samples the keys): key index u < ceil(N / ks) is the key
+// at position u ks, and query t sees indices u <= t / ks.  N is 32-bit here.
 // ---------------------------------------------------------------------------
-template <int KDT>
+template <int KDT, int MODE>
 __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q,
                                                   const float* __restrict__ w,
                                                   const void* __restrict__ kptr,
                                                   const float* __restrict__ kscale,
-                                                  const int32_t* __restrict__ heads, int h,
-                                                  float* __restrict__ logits, int64_t ld, int64_t N64,
-                                                  int64_t q_pos0_64, int M, int H, int n_qtiles,
-                                                  int n_ksplits, int64_t KR) {
+                                                  const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
+                                                  int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
+                                                  int n_qtiles, int n_ksplits, int64_t KR) {
   constexpr int NT = 256, KT = kSwKT, QT = 32;
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2 * kSwTileBytes];
   __shared__ float s_sc[2][KT];
 
-  const int N = (int)N64, q_pos0 = (int)q_pos0_64;
+  const int Nk = (int)N64, q_pos0 = (int)q_pos0_64;   // keys; position of query 0
+  const int N = (Nk + kstride - 1) / kstride;          // scored key indices
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
   const int g = lane >> 4, p16 = lane & 15;
   const int b = blockIdx.y;
-  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N64);
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
   const int k0 = (int)tc.k0, k1 = (int)tc.k1;
   const int qa = tc.qt * QT;
   const int qb = min(qa + QT, M);
-  const int t_last = q_pos0 + qb - 1;
-  const int kend = min(k1, t_last + 1);   // keys past kend are masked for every query
+  const int64_t qrow0 = (int64_t)b * M;
+  if (out_spec.row_flag != nullptr) {
+    bool any = false;
+    for (int i = qa; i < qb; ++i) any |= out_spec.row_flag[qrow0 + i] != 0;
+    if (!any) return;   // uniform over the workgroup
+  }
+  const int t_last = (q_pos0 + qb - 1) / kstride;
+  const int kend = min(k1, t_last + 1);   // key indices past kend are masked for every query
   const int n_tiles = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
 
   const int q0w = qa + wave * 8;
-  const int t_lo = q_pos0 + q0w;                    // first query of the wave
-  const int t_hi = q_pos0 + min(q0w + 8, qb) - 1;   // last query of the wave (< t_lo if none)
+  const int t_lo = (q_pos0 + q0w) / kstride;                                   // first query of the wave
+  const int t_hi = (q0w < qb) ? (q_pos0 + min(q0w + 8, qb) - 1) / kstride : -1;   // last one (-1: none)
   // A fragments: row block rb = 2*G + qd; row r -> query q0w + 4G + r/4, slot 4*qd + r%4
   // (all prologue loads are unconditional, clamped in range, so they issue in
   //  two dependent batches: head ids, then weights and q rows)
@@ -250,18 +290,26 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   float wv[2][8];
   int tq[2];
   __amdgpu_buffer_rsrc_t orsrc[2];
-  const uint32_t row_bytes = (uint32_t)ld * 4u;
+  float thr[2];
+  uint64_t* reg[2];
+  const uint32_t row_bytes = (uint32_t)out_spec.ld * 4u;
   const uint32_t lane_row_off = (uint32_t)g * row_bytes;
-  const int64_t qrow0 = (int64_t)b * M;
+  const int split = (int)(k0 / KR);
   int hw[2][8], ha[2][2];
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
     const int qg0 = q0w + 4 * G;                      // first query of group G
     const int nrows = max(0, min(4, qb - qg0));       // its queries inside the tile
-    orsrc[G] = uniform_rsrc(logits + (qrow0 + min(qg0, M - 1)) * ld, (uint32_t)nrows * row_bytes);
     const int qo = qg0 + g;                           // query of this lane's output rows
-    tq[G] = (qo < qb) ? q_pos0 + qo : -1;
+    tq[G] = (qo < qb) ? (q_pos0 + qo) / kstride : -1;
     const int qoc = min(qo, M - 1);
+    if (MODE == kLogits) {
+      orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld,
+                              (uint32_t)nrows * row_bytes);
+    } else {
+      thr[G] = out_spec.thr[qrow0 + qoc];
+      reg[G] = out_spec.regions + ((qrow0 + qoc) * n_ksplits + split) * (int64_t)out_spec.cap;
+    }
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) hw[G][sl] = heads[(qrow0 + qoc) * h + min(sl, h - 1)];
     const int qic = min(qg0 + (p16 >> 2), M - 1);
@@ -294,9 +342,9 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   }
 
   const void* kb_ptr = (KDT == MISA_K_BF16)
-                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * N * kD)
-                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * N * kD);
-  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * N : nullptr;
+                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * Nk * kD)
+                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * Nk * kD);
+  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * Nk : nullptr;
 
   // lane's B-fragment byte offsets inside a tile (column block 0), one per k-step
   uint32_t rd[kKSteps];
@@ -304,7 +352,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   for (int ks = 0; ks < kKSteps; ++ks) rd[ks] = sw_off(p16, 4 * ks + g);
 
   KStageSw<KDT, NT> stg;
-  stg.load(kb_ptr, sc_ptr, k0, N, tid);
+  stg.load(kb_ptr, sc_ptr, k0, Nk, kstride, tid);
   stg.store(s_k, s_sc[0], tid);
   // every load issued so far (q fragments, weights) has landed: without this the
   // compiler cannot prove it inside the loop and waits for all memory traffic
@@ -314,12 +362,41 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   const float ninf = -__builtin_inff();
   constexpr uint32_t kDrop = 0x80000000u;   // a byte offset past every store resource
 
-  // one tile from LDS buffer BUF; returns after its stores are issued
+  // kCands: the previous tile's scores, appended at the start of the next tile
+  f32x4 pend[2] = {f32x4{ninf, ninf, ninf, ninf}, f32x4{ninf, ninf, ninf, ninf}};
+  int pend_kg = 0x3FFFFFFF;   // no pending tile: past every query
+  uint32_t run[2] = {0u, 0u};   // candidates of the lane's query group so far
+  const uint64_t gmask = 0xFFFFull << (16 * g);
+  auto append = [&]() {
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      bool f[4];
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = (pend_kg + e <= tq[G]) && (pend[G][e] >= thr[G]);
+        c += f[e];
+      }
+      const uint64_t m0 = __ballot(c & 1u), m1 = __ballot(c & 2u), m2 = __ballot(c & 4u);
+      if ((m0 | m1 | m2) == 0) continue;   // uniform
+      uint32_t pos = run[G] + lanes_below(m0 & gmask) + 2 * lanes_below(m1 & gmask) +
+                     4 * lanes_below(m2 & gmask);
+      run[G] += __popcll(m0 & gmask) + 2 * __popcll(m1 & gmask) + 4 * __popcll(m2 & gmask);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (f[e]) {
+          if (pos < (uint32_t)out_spec.cap)
+            reg[G][pos] = ((uint64_t)(uint32_t)(pend_kg + e) << 32) | (uint64_t)__float_as_uint(pend[G][e]);
+          ++pos;
+        }
+    }
+  };
+
+  // one tile from LDS buffer BUF
   auto tile = [&](auto buf_tag, int key0) {
     constexpr int BUF = decltype(buf_tag)::value;
     const unsigned char* sk = s_k + BUF * kSwTileBytes;
-    const int kg = key0 + 4 * p16;   // this lane's first key
-    const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
+    const int kg = key0 + 4 * p16;   // this lane's first key index
     f32x4 out[2];
     if (key0 > t_hi) {
       // the whole tile lies after every query of the wave
@@ -364,27 +441,45 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
         }
       }
     }
-    store_f32x4(orsrc[0], off, out[0]);
-    store_f32x4(orsrc[1], off, out[1]);
+    if (MODE == kLogits) {
+      const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
+      store_f32x4(orsrc[0], off, out[0]);
+      store_f32x4(orsrc[1], off, out[1]);
+    } else {
+      pend[0] = out[0];
+      pend[1] = out[1];
+      pend_kg = kg;
+    }
   };
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   for (int jt = 0; jt < n_tiles; jt += 2) {
     const int key0 = k0 + jt * KT;
-    stg.load(kb_ptr, sc_ptr, key0 + KT, N, tid);   // tile jt+1 (zeros past N)
+    if (MODE == kCands) append();
+    stg.load(kb_ptr, sc_ptr, key0 + KT, Nk, kstride, tid);   // tile jt+1 (zeros past N)
     tile(B0{}, key0);
     stg.store(s_k + kSwTileBytes, s_sc[1], tid);
     __syncthreads();
     if (jt + 1 < n_tiles) {
-      stg.load(kb_ptr, sc_ptr, key0 + 2 * KT, N, tid);   // tile jt+2
+      if (MODE == kCands) append();
+      stg.load(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, kstride, tid);   // tile jt+2
       tile(B1{}, key0 + KT);
       stg.store(s_k, s_sc[0], tid);
       __syncthreads();
     }
   }
-  // keys of this range after the last computed tile: -inf for every query
-  fill_neg_inf(logits, ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
+  if (MODE == kLogits) {
+    // keys of this range after the last computed tile: -inf for every query
+    fill_neg_inf(out_spec.logits, out_spec.ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
+  } else {
+    if (n_tiles > 0) append();
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const int qo = q0w + 4 * G + g;
+      if (qo < qb && p16 == 0) out_spec.rcount[(qrow0 + qo) * n_ksplits + split] = run[G];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -530,24 +625,33 @@ static void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplit
   *KR = kr;
 }
 
+template <int MODE>
+static hipError_t launch_h8(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
+                            const float* k_scale, const int32_t* heads, int h, const ScoreOut& o, int kstride,
+                            int nks, int64_t KR, hipStream_t st) {
+  const int M = s.q_per_seq;
+  const int n_qtiles = (M + 31) / 32;
+  dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  if (kdtype == MISA_K_BF16)
+    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h, o,
+                       s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+  else
+    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
+                       o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                         int kdtype, const float* k_scale, const int32_t* heads, int h,
                         float* logits, int64_t ld, hipStream_t st) {
   const int M = s.q_per_seq, H = s.n_heads;
   const int64_t N = s.n_keys;
   if (heads != nullptr && h <= 8) {
-    const int n_qtiles = (M + 31) / 32;
     int nks;
     int64_t KR;
-    plan_split(N, s.n_seq, n_qtiles, 64, &nks, &KR);
-    dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
-    if (kdtype == MISA_K_BF16)
-      hipLaunchKernelGGL(k_score_h8<MISA_K_BF16>, grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
-                         logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
-    else
-      hipLaunchKernelGGL(k_score_h8<MISA_K_FP8_E4M3>, grid, dim3(256), 0, st, q, w, k, k_scale, heads,
-                         h, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
-    return hipGetLastError();
+    plan_split(N, s.n_seq, (M + 31) / 32, 64, &nks, &KR);
+    const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, 0, nullptr};
+    return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
   }
   const int hh = heads ? h : H;
   const int n_qtiles = (M + 15) / 16;
@@ -571,6 +675,63 @@ hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, 
                          k_scale, heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused scoring -> top-k (the indexer's path for h <= 8 and long prefixes)
+// ---------------------------------------------------------------------------
+FusedPlan plan_fused(const misa_shape& s, int h, int k) {
+  FusedPlan p{};
+  const int64_t N = s.n_keys;
+  const int64_t n_min = s.q_pos0 + 1;   // shortest prefix of the chunk
+  p.ok = h <= 8 && k <= 8192 && n_min >= 32768 && s.q_per_seq > 0;
+  if (!p.ok) return p;
+  p.kstride = (int)std::max<int64_t>(32, (N + 4095) / 4096);   // <= 4096 sampled keys per row
+  p.n_sample = (N + p.kstride - 1) / p.kstride;
+  p.ld_sample = (p.n_sample + 3) / 4 * 4;
+  p.cap_list = k <= 4096 ? 8192 : 16384;               // the list select kernel's buffer
+  p.target = std::min(3 * k / 2, (k + p.cap_list) / 2);
+  int nks;
+  int64_t KR;
+  plan_split(N, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
+  p.n_splits = nks;
+  p.key_range = KR;
+  if (nks > 64) {   // the region select holds at most 64 key ranges per row
+    p.ok = false;
+    return p;
+  }
+  // expected candidates per (row, key range), doubled, plus room for a few
+  // clusters of large scores
+  const int64_t expect = (int64_t)p.target * KR / n_min + 1;
+  p.cap_region = (int)((2 * expect + 1024 + 255) / 256 * 256);
+  return p;
+}
+
+hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
+                                const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
+                                float* sample_logits, hipStream_t st) {
+  int nks;
+  int64_t KR;
+  plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
+  const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, 0, nullptr};
+  return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
+}
+
+hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
+                              const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
+                              const float* thr, uint64_t* regions, uint32_t* rcount, hipStream_t st) {
+  const ScoreOut o{nullptr, 0, thr, regions, rcount, p.cap_region, nullptr};
+  return launch_h8<kCands>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, p.n_splits, p.key_range, st);
+}
+
+hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
+                                int kdtype, const float* k_scale, const int32_t* heads, int h,
+                                const uint32_t* row_flag, float* logits, int64_t ld, hipStream_t st) {
+  int nks;
+  int64_t KR;
+  plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
+  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, 0, row_flag};
+  return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
 }
 
 }  // namespace misa

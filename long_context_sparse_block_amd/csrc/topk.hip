@@ -39,6 +39,8 @@
 // differ, so the histogram bins spread over the values actually present.
 // The result is exact for every input; the sample only decides how much
 // buffering and compaction work is done.
+#include <algorithm>
+
 #include "misa_common.h"
 #include "misa_launch.h"
 
@@ -57,9 +59,6 @@ __device__ __forceinline__ uint64_t raw_to_comp(uint64_t r) {
 __device__ __forceinline__ int32_t comp_id(uint64_t c) { return (int32_t)(~(uint32_t)c); }
 __device__ __forceinline__ float comp_val(uint64_t c) { return key_to_float((uint32_t)(c >> 32)); }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)x, m), hi = __shfl_xor((uint32_t)(x >> 32), m);
@@ -358,10 +357,10 @@ struct TopkShared {
 };
 
 template <int CAP, int NT>
-__device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, const float* __restrict__ logits, int64_t ld,
-                                         const int32_t* __restrict__ cand, int n_cols, int k, int64_t q_pos0,
-                                         int M, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
-                                         int sorted) {
+__device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, int i, int b, const float* __restrict__ logits,
+                                         int64_t ld, const int32_t* __restrict__ cand, int n_cols, int k,
+                                         int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
+                                         float* __restrict__ val_out, int sorted) {
   constexpr int VPT = 2;                  // float4s per thread per lock-step (robust) step
   constexpr int STEP = 4 * VPT * NT;      // elements per lock-step step
   static_assert(CAP / 2 >= STEP, "a lock-step step must fit the free half of the buffer");
@@ -374,7 +373,6 @@ __device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, const float* _
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int i = blockIdx.x, b = blockIdx.y;
   const int64_t row = (int64_t)b * M + i;
   const int64_t t = q_pos0 + i;
   const int n = cand ? n_cols : (int)min((int64_t)n_cols, t + 1);
@@ -559,7 +557,7 @@ __global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits
                                                 int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
                                                 float* __restrict__ val_out, int sorted) {
   __shared__ TopkShared<CAP, NT> sh;
-  topk_row<CAP, NT>(sh, logits, ld, cand, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
+  topk_row<CAP, NT>(sh, blockIdx.x, blockIdx.y, logits, ld, cand, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
 }
 
 // ---------------------------------------------------------------------------
@@ -744,31 +742,12 @@ __global__ void __launch_bounds__(NT) k_topk_filter(const float* __restrict__ lo
   for (uint32_t e = lane; e < run; e += 64) dst[e] = reg[e];
 }
 
-// Exact top-k of a row's candidate list (every element at or above the row's
-// threshold).  A row whose list overflowed or came up short of k is done by
-// the whole-row path instead, in the same workgroup, so the result is exact
-// for every input.
+// Exact top-k (sorted, or the set in no order) of the cnt candidates held in
+// sh.buf, written to the row's outputs.
 template <int CAP, int NT>
-__global__ void __launch_bounds__(NT, 2) k_topk_list(const float* __restrict__ logits, int64_t ld, int n_cols,
-                                                     int k, int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
-                                                     float* __restrict__ val_out, int sorted,
-                                                     const uint64_t* __restrict__ list,
-                                                     const uint32_t* __restrict__ count,
-                                                     const uint32_t* __restrict__ flag, int capg) {
-  __shared__ TopkShared<CAP, NT> sh;
+__device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
+                                            int32_t* __restrict__ idx_out, float* __restrict__ val_out, int sorted) {
   const int tid = threadIdx.x;
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int64_t row = (int64_t)b * M + i;
-  const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
-  const uint32_t c = count[row];
-  if (flag[row] != 0 || c < (uint32_t)min(k, n) || c > (uint32_t)min(capg, CAP)) {
-    topk_row<CAP, NT>(sh, logits, ld, nullptr, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
-    return;
-  }
-  const uint64_t* src = list + row * (int64_t)capg;
-  for (uint32_t e = tid; e < c; e += NT) sh.buf[e] = src[e];
-  __syncthreads();
-  uint32_t cnt = c;
   if (sorted && cnt <= (uint32_t)(CAP / 2)) {   // rank every candidate; ranks >= k are not written
     rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
     return;
@@ -794,6 +773,33 @@ __global__ void __launch_bounds__(NT, 2) k_topk_list(const float* __restrict__ l
     return;
   }
   rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
+}
+
+// Exact top-k of a row's candidate list (every element at or above the row's
+// threshold).  A row whose list overflowed or came up short of k is done by
+// the whole-row path instead, in the same workgroup, so the result is exact
+// for every input.
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk_list(const float* __restrict__ logits, int64_t ld, int n_cols,
+                                                     int k, int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
+                                                     float* __restrict__ val_out, int sorted,
+                                                     const uint64_t* __restrict__ list,
+                                                     const uint32_t* __restrict__ count,
+                                                     const uint32_t* __restrict__ flag, int capg) {
+  __shared__ TopkShared<CAP, NT> sh;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int64_t row = (int64_t)b * M + i;
+  const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
+  const uint32_t c = count[row];
+  if (flag[row] != 0 || c < (uint32_t)min(k, n) || c > (uint32_t)min(capg, CAP)) {
+    topk_row<CAP, NT>(sh, i, b, logits, ld, nullptr, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
+    return;
+  }
+  const uint64_t* src = list + row * (int64_t)capg;
+  for (uint32_t e = tid; e < c; e += NT) sh.buf[e] = src[e];
+  __syncthreads();
+  finish_list<CAP, NT>(sh, c, k, row, idx_out, val_out, sorted);
 }
 
 size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k) {
@@ -836,6 +842,151 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
   else
     hipLaunchKernelGGL((k_topk<16384, 512>), grid, dim3(512), 0, st, logits, ld, cand, n_cols, k,
                        s.q_pos0, s.q_per_seq, idx, vals, (int)sorted);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused scoring -> top-k: the top-k side (see plan_fused)
+// ---------------------------------------------------------------------------
+
+// One wave per row: the threshold from the row's sampled scores (key indices
+// u <= t / kstride of the sample logits), the lower edge of the 20-bit
+// order-key bucket of the k_s-th largest sample, k_s chosen so that about
+// `target` of the row's t + 1 scores are expected at or above it.  Every
+// sampled key is one key, so a cluster of large scores takes only its share
+// of the sample.  Also clears the row's flag.
+__global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const float* __restrict__ sample,
+                                                                          int64_t ld_s, int n_sample, int kstride,
+                                                                          int target, int64_t q_pos0, int M,
+                                                                          int64_t rows, float* __restrict__ thr,
+                                                                          uint32_t* __restrict__ flag) {
+  constexpr int L = 16;   // float4 loads per lane: 4096 sampled scores at most
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kThreshWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t t = q_pos0 + row % M;
+  const int ns = (int)min((int64_t)n_sample, t / kstride + 1);   // sampled keys the query sees
+  const uint64_t ks = (uint64_t)target * (uint64_t)ns / (uint64_t)(t + 1) + 2;
+  float tf = -__builtin_inff();
+  if (ks < (uint64_t)ns) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(sample + row * ld_s);   // ld_s % 4 == 0
+    const int n4 = (ns + 3) / 4;
+    uint32_t key[4 * L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int f = j * 64 + lane;
+      const f32x4 v = src[min(f, n4 - 1)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * j + e] = (4 * f + e < ns) ? order_key(v[e]) : 0u;
+    }
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 12; --bit) {
+      const uint32_t c = T | (1u << bit);
+      uint32_t cl = 0;
+#pragma unroll
+      for (int j = 0; j < 4 * L; ++j) cl += (key[j] >= c) ? 1u : 0u;
+      if (__reduce_add_sync(~0ull, cl) >= (uint32_t)ks) T = c;
+    }
+    tf = key_to_float(T);
+    if (tf != tf) tf = -__builtin_inff();
+  }
+  if (lane == 0) {
+    thr[row] = tf;
+    flag[row] = 0;
+  }
+}
+
+// Exact top-k of a row's candidates, gathered from its key-range regions.  A
+// row with an overflowed region, more candidates than the buffer holds, or
+// fewer than k is flagged (and left for the re-scoring path).
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, int64_t q_pos0, int M, int n_splits,
+                                                        int cap_region, int cap_list,
+                                                        const uint64_t* __restrict__ regions,
+                                                        const uint32_t* __restrict__ rcount,
+                                                        uint32_t* __restrict__ flag, int32_t* __restrict__ idx_out,
+                                                        float* __restrict__ val_out, int sorted) {
+  __shared__ TopkShared<CAP, NT> sh;
+  __shared__ uint32_t s_off[65];
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int64_t row = (int64_t)b * M + i;
+  const int n = (int)min(n_keys, q_pos0 + i + 1);
+  if (tid == 0) {
+    uint32_t tot = 0;
+    bool bad = false;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const uint32_t c = rcount[row * n_splits + sp];
+      bad |= c > (uint32_t)cap_region;
+      s_off[sp] = tot;
+      tot += min(c, (uint32_t)cap_region);
+    }
+    s_off[n_splits] = (bad || tot > (uint32_t)min(cap_list, CAP) || tot < (uint32_t)min(k, n)) ? 0xFFFFFFFFu : tot;
+  }
+  __syncthreads();
+  const uint32_t tot = s_off[n_splits];
+  if (tot == 0xFFFFFFFFu) {
+    if (tid == 0) flag[row] = 1;
+    return;
+  }
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const uint32_t o = s_off[sp], c = ((sp + 1 < n_splits) ? s_off[sp + 1] : tot) - o;
+    const uint64_t* src = regions + (row * n_splits + sp) * (int64_t)cap_region;
+    for (uint32_t e = tid; e < c; e += NT) sh.buf[o + e] = src[e];
+  }
+  __syncthreads();
+  finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted);
+}
+
+// Whole-row top-k of the flagged rows from full logits; a fixed grid walks
+// the rows, so the (rare) flagged rows cost one cheap flag check each.
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk_flagged(const float* __restrict__ logits, int64_t ld,
+                                                        int64_t n_keys, int k, int64_t q_pos0, int M, int64_t rows,
+                                                        const uint32_t* __restrict__ flag,
+                                                        int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                                                        int sorted) {
+  __shared__ TopkShared<CAP, NT> sh;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    if (flag[r] == 0) continue;   // uniform over the workgroup
+    topk_row<CAP, NT>(sh, (int)(r % M), (int)(r / M), logits, ld, nullptr, (int)n_keys, k, q_pos0, M, idx_out,
+                      val_out, sorted);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, const float* sample_logits,
+                                     float* thr, uint32_t* row_flag, hipStream_t st) {
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  hipLaunchKernelGGL(k_topk_sample_thresh, dim3((unsigned)((rows + kThreshWaves - 1) / kThreshWaves)),
+                     dim3(64 * kThreshWaves), 0, st, sample_logits, p.ld_sample, (int)p.n_sample, p.kstride,
+                     p.target, s.q_pos0, s.q_per_seq, rows, thr, row_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const uint64_t* regions,
+                               const uint32_t* rcount, uint32_t* row_flag, int32_t* idx, float* vals, bool sorted,
+                               hipStream_t st) {
+  dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
+  if (k <= 4096)
+    hipLaunchKernelGGL((k_topk_regions<8192, 512>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0, s.q_per_seq,
+                       p.n_splits, p.cap_region, p.cap_list, regions, rcount, row_flag, idx, vals, (int)sorted);
+  else
+    hipLaunchKernelGGL((k_topk_regions<16384, 512>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0, s.q_per_seq,
+                       p.n_splits, p.cap_region, p.cap_list, regions, rcount, row_flag, idx, vals, (int)sorted);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* logits, int64_t ld,
+                               const uint32_t* row_flag, int32_t* idx, float* vals, bool sorted, hipStream_t st) {
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  const unsigned g = (unsigned)std::min<int64_t>(rows, 512);
+  if (k <= 4096)
+    hipLaunchKernelGGL((k_topk_flagged<8192, 512>), dim3(g), dim3(512), 0, st, logits, ld, s.n_keys, k, s.q_pos0,
+                       s.q_per_seq, rows, row_flag, idx, vals, (int)sorted);
+  else
+    hipLaunchKernelGGL((k_topk_flagged<16384, 512>), dim3(g), dim3(512), 0, st, logits, ld, s.n_keys, k,
+                       s.q_pos0, s.q_per_seq, rows, row_flag, idx, vals, (int)sorted);
   return hipGetLastError();
 }
 

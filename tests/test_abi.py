@@ -119,6 +119,25 @@ def test_indexer_checks_and_workspace(lib):
     assert need_d > need
 
 
+def test_sparse_head_topk_checks_and_workspace(lib):
+    s = shape()
+    f = lib.misa_sparse_head_topk
+    # h out of range, topk out of range, missing heads, missing workspace
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 9, 4, 1, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, 0, 1, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, None, 2, 4, 1, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, None, 0, None) == -3
+    need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 2, 4)
+    assert need > 0
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, FAKE, need - 1, None) == -3
+    # the long-context chunk takes the fused path: sampled scores and candidate
+    # regions instead of the whole-row top-k's lists, beside the full logits
+    # kept for rows the candidates cannot settle
+    big = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
+    fused = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(big), 8, 2048)
+    assert fused == 8192 * 131072 * 4 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4 + 8192 * 8 * 2048 * 8
+
+
 def test_empty_query_set_is_a_no_op(lib):
     s = shape(q_per_seq=0, q_pos0=64)
     assert lib.misa_sparse_head_logits(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 64,
@@ -129,7 +148,9 @@ def test_empty_query_set_is_a_no_op(lib):
 def test_workspace_size_of_the_long_context_chunk(lib):
     s = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
     need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 8, 2048, 0)
-    # the fp32 logits of the chunk (8192 x 131072 x 4 bytes) plus the top-k
-    # candidate lists of the long-row path (8192 rows x 8192 entries x 8 bytes)
-    main = 8192 * 131072 * 4 + 8192 * 8192 * 8
+    # the fp32 logits of the chunk (8192 x 131072 x 4 bytes; the fused path
+    # writes them only for rows its candidates cannot settle), the sampled
+    # scores (8192 x 4096 x 4) and the candidate regions (8192 rows x 8 key
+    # ranges x 2048 entries x 8 bytes)
+    main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 2048 * 8
     assert main <= need < main * 1.01

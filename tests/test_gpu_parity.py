@@ -306,6 +306,100 @@ def test_indexer_is_deterministic(staged):
         assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
 
 
+# ---------------------------------------------------------------------------
+# fused scoring -> top-k (the indexer's path when every prefix is >= 32768 keys)
+# ---------------------------------------------------------------------------
+
+def _staged_selection(inp, st, k_prime):
+    """The indexer's result rebuilt from the separate stage calls."""
+    cfg, t, sh = inp.cfg, st["t"], st["sh"]
+    if not k_prime:
+        return lcsb.misa_topk(sh, st["logits"], cfg.topk)
+    cand, _ = lcsb.misa_topk(sh, st["logits"], k_prime, want_vals=False, sorted=False)
+    D = lcsb.dsa_dense_logits(sh, t["q"], t["w"], t["k"], k_scale=t["k_scale"], cand=cand)
+    return lcsb.misa_topk(sh, D, cfg.topk, cand=cand)
+
+
+def _check_sparse_head_topk(inp, st):
+    """misa_sparse_head_topk == misa_topk(misa_sparse_head_logits): the sorted
+    result exactly, the unsorted one as a set per row."""
+    cfg, t, sh = inp.cfg, st["t"], st["sh"]
+    fi, fv = lcsb.misa_sparse_head_topk(sh, t["q"], t["w"], t["k"], st["heads"], cfg.topk, k_scale=t["k_scale"])
+    ti, tv = lcsb.misa_topk(sh, st["logits"], cfg.topk)
+    ui, _ = lcsb.misa_sparse_head_topk(sh, t["q"], t["w"], t["k"], st["heads"], cfg.topk, k_scale=t["k_scale"],
+                                       sorted=False, want_vals=False)
+    torch.cuda.synchronize()
+    assert torch.equal(fi, ti) and torch.equal(fv, tv), "fused selection != logits + top-k"
+    a, b = torch.sort(ui, dim=-1)[0], torch.sort(ti, dim=-1)[0]
+    assert torch.equal(a, b), "unsorted fused selection is not the same set"
+
+
+@pytest.mark.parametrize("name", ["tiny", "fp8", "decode"])
+def test_sparse_head_topk_short_prefixes_equals_logits_topk(staged, name):
+    """Prefixes too short for the fused path: logits in the workspace, then top-k."""
+    inp, st = staged(name)
+    _check_sparse_head_topk(inp, st)
+
+
+FUSED_CASES = [
+    dict(name="fused_bf16", n_seq=1, m=96, n=40000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_BF16),
+    dict(name="fused_fp8_h5", n_seq=1, m=40, n=36001, hh=48, b=128, h=5, k=1000, kdtype=gen.KDTYPE_FP8),
+    dict(name="fused_dagger", n_seq=1, m=64, n=40000, hh=32, b=64, h=8, k=1024, kp=4096,
+         kdtype=gen.KDTYPE_BF16),
+    dict(name="fused_decode", n_seq=6, m=1, n=50000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_BF16),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: c["name"])
+def test_fused_indexer_equals_stages_and_oracle(case):
+    c = dict(case)
+    name, kp = c.pop("name"), c.pop("kp", 0)
+    say("fused indexer", name)
+    cfg = gen.small_config(name=name, n_seq=c["n_seq"], m=c["m"], n=c["n"], hh=c["hh"], b=c["b"], h=c["h"],
+                           k=c["k"], kdtype=c["kdtype"], seed=41)
+    inp = gen.generate(cfg)
+    st = run_stages(inp)
+    idx, vals = lcsb.misa_indexer(st["sh"], st["t"]["q"], st["t"]["w"], st["t"]["k"], cfg.h, cfg.topk,
+                                  k_prime=kp, k_scale=st["t"]["k_scale"])
+    sidx, svals = _staged_selection(inp, st, kp)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sidx) and torch.equal(vals, svals), "fused indexer != its stages"
+    _check_sparse_head_topk(inp, st)
+    gi = idx.cpu().numpy()
+    recs = []
+    for b in range(cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b)
+        for i in sample_rows(cfg.q_per_seq, 6):
+            out = ctx.misa_dagger(i, cfg.h, kp, cfg.topk) if kp else ctx.misa(i, cfg.h, cfg.topk)
+            recs.append(recall(gi[b, i], out["idx"]))
+    assert np.mean(recs) >= 0.999, np.mean(recs)
+
+
+def test_fused_indexer_rows_the_sample_misjudges():
+    """Every sampled key position (multiples of the sampling stride, 32 here)
+    gets a huge score, so the sampled threshold admits far fewer than k
+    candidates in every row: each row must be re-scored and selected from full
+    logits, and the result must still equal the staged pipeline."""
+    say("fused indexer: threshold defeated")
+    cfg = gen.small_config(name="fused_adv", m=48, n=40000, hh=16, b=64, h=8, k=2048, seed=43, plant=False)
+    inp = gen.generate(cfg)
+    q = oracle.bf16_bits_to_f64(inp.q).astype(np.float32)
+    kf = oracle.bf16_bits_to_f64(inp.k).astype(np.float32)
+    u = np.ones(128, np.float32) / np.sqrt(128.0)
+    q += 4.0 * u
+    kf[:, ::32, :] += 40.0 * u
+    inp.q[...] = gen.to_bf16_bits(q)
+    inp.k[...] = gen.to_bf16_bits(kf)
+    inp.w[...] = np.abs(inp.w)
+    st = run_stages(inp)
+    idx, vals = lcsb.misa_indexer(st["sh"], st["t"]["q"], st["t"]["w"], st["t"]["k"], cfg.h, cfg.topk)
+    sidx, svals = _staged_selection(inp, st, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sidx) and torch.equal(vals, svals)
+    check_topk_exact(inp, st["logits"], cfg.topk, idx, vals)
+    _check_sparse_head_topk(inp, st)
+
+
 @pytest.mark.parametrize("kdtype", [gen.KDTYPE_BF16, gen.KDTYPE_FP8])
 def test_dagger_with_all_candidates_is_dense_topk(kdtype):
     # k' >= L: every prefix token is a candidate, the re-rank is the dense indexer
