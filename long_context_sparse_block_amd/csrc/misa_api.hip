@@ -55,7 +55,7 @@ inline misa_status from_hip(hipError_t e) { return e == hipSuccess ? MISA_OK : M
 // Workspace of the routed scoring + top-k selection (misa_sparse_head_topk,
 // and the first selection of misa_indexer), placed from offset `off`.
 struct SelectLayout {
-  size_t logits, sample, thr, flag, rcount, regions, topk_ws, end;
+  size_t logits, sample, thr, flag, rcount, gvals, gkeys, topk_ws, end;
   int64_t ld;
   misa::FusedPlan fused;
 };
@@ -77,8 +77,11 @@ SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off) {
     off += align_up((size_t)rows * sizeof(uint32_t));
     L.rcount = off;
     off += align_up((size_t)rows * p.n_splits * sizeof(uint32_t));
-    L.regions = off;
-    off += align_up((size_t)rows * p.n_splits * (size_t)p.cap_region * sizeof(uint64_t));
+    const size_t groups = (size_t)rows * p.n_splits * (size_t)p.cap_region;
+    L.gvals = off;
+    off += align_up(groups * 4 * sizeof(float));
+    L.gkeys = off;
+    off += align_up(groups * sizeof(int32_t));
   } else {
     L.topk_ws = off;
     off += align_up(misa::topk_workspace_bytes(s, (int)s.n_keys, k));
@@ -102,11 +105,13 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   float* thr = reinterpret_cast<float*>(base + L.thr);
   uint32_t* flag = reinterpret_cast<uint32_t*>(base + L.flag);
   uint32_t* rcount = reinterpret_cast<uint32_t*>(base + L.rcount);
-  uint64_t* regions = reinterpret_cast<uint64_t*>(base + L.regions);
+  float* gvals = reinterpret_cast<float*>(base + L.gvals);
+  int32_t* gkeys = reinterpret_cast<int32_t*>(base + L.gkeys);
   MISA_TRY(from_hip(misa::launch_score_sampled(s, q, w, k, kdtype, k_scale, heads, h, p, sample, st)));
   MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
-  MISA_TRY(from_hip(misa::launch_score_cands(s, q, w, k, kdtype, k_scale, heads, h, p, thr, regions, rcount, st)));
-  MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, regions, rcount, flag, idx, vals, sorted, st)));
+  MISA_TRY(from_hip(
+      misa::launch_score_cands(s, q, w, k, kdtype, k_scale, heads, h, p, thr, gvals, gkeys, rcount, st)));
+  MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
   MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, k, kdtype, k_scale, heads, h, flag, logits, L.ld, st)));
   return from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st));
 }

@@ -51,16 +51,18 @@ struct FusedPlan {
   int target;          // candidates aimed for per row
   int n_splits;        // key ranges of the scoring grid
   int64_t key_range;   // keys per range
-  int cap_region;      // candidates one (row, key range) region holds
+  int cap_region;      // candidate groups of 4 keys one (row, key range) region holds
 };
 FusedPlan plan_fused(const misa_shape& s, int h, int k);
 
 hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                                 const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
                                 float* sample_logits, hipStream_t st);
+// candidate regions: groups of 4 consecutive scores (gvals, float4 each) and
+// their first key (gkeys), cap_region groups per (row, key range)
 hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                               const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
-                              const float* thr, uint64_t* regions, uint32_t* rcount, hipStream_t st);
+                              const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st);
 // full logits rows of the workgroups that hold a row with row_flag != 0
 hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                                 int kdtype, const float* k_scale, const int32_t* heads, int h,
@@ -69,9 +71,9 @@ hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const fl
 hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, const float* sample_logits,
                                      float* thr, uint32_t* row_flag, hipStream_t st);
 // top-k of the candidate regions; rows it cannot settle get row_flag = 1
-hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const uint64_t* regions,
-                               const uint32_t* rcount, uint32_t* row_flag, int32_t* idx, float* vals, bool sorted,
-                               hipStream_t st);
+hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const float* thr,
+                               const float* gvals, const int32_t* gkeys, const uint32_t* rcount, uint32_t* row_flag,
+                               int32_t* idx, float* vals, bool sorted, hipStream_t st);
 // whole-row top-k of the flagged rows from full logits
 hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* logits, int64_t ld,
                                const uint32_t* row_flag, int32_t* idx, float* vals, bool sorted, hipStream_t st);

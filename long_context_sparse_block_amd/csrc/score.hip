@@ -208,18 +208,21 @@ __device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t b
 
 // Where a k_score_h8 pass puts its results.
 //  MODE kLogits: logits[row][u] for key u of the scored key sequence (u ks).
-//  MODE kCands: no logits; every (query, key) score >= thr[row] of a key the
-//    query sees is appended as (key << 32 | score bits) to the region of that
-//    row and of the workgroup's key range: region (row * n_splits + split),
-//    `cap` entries; rcount[row * n_splits + split] receives the number found
-//    (more than cap: the region overflowed and holds only the first cap).
+//  MODE kCands: no logits; every group of 4 consecutive keys (4c .. 4c+3)
+//    holding a score >= thr[row] (a finite threshold, so masked -inf scores
+//    never qualify) is appended to the region of that row and of the
+//    workgroup's key range, region (row * n_splits + split) of `cap` groups:
+//    its 4 scores to gvals, its first key to gkeys.  rcount[row * n_splits +
+//    split] receives the number of groups found (more than cap: the region
+//    overflowed and holds only the first cap).
 //  row_flag != nullptr: only workgroups holding a row with row_flag[row] != 0
 //    run (re-scoring of the rows a candidate pass could not settle).
 struct ScoreOut {
   float* logits;
   int64_t ld;
   const float* thr;
-  uint64_t* regions;
+  f32x4* gvals;
+  int32_t* gkeys;
   uint32_t* rcount;
   int cap;
   const uint32_t* row_flag;
@@ -237,8 +240,9 @@ constexpr int kCands = 1;
 //   and key groups past N fall outside the store descriptor and are dropped; a
 //   group straddling N also writes -inf into columns N .. roundup4(N)-1,
 //   which lie inside the row).
-//   kCands: the scores at or above the row threshold are appended to the
-//   row's region (positions from ballots within the 16 lanes that hold one
+//   kCands: a lane's group of 4 scores with one at or above the row
+//   threshold is appended whole (a float4 and its first key) to the row's
+//   region (positions from a ballot within the 16 lanes that hold one
 //   query); the appends of a tile are issued at the start of the next tile,
 //   before its key prefetch, so waiting for that prefetch never waits for a
 //   store issued after it.
@@ -257,6 +261,9 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
                                                   int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
                                                   int n_qtiles, int n_ksplits, int64_t KR) {
   constexpr int NT = 256, KT = kSwKT, QT = 32;
+  // B fragments read one column block ahead where the registers allow it
+  // (16 more VGPRs; the other variants would drop to 2 waves per SIMD)
+  constexpr bool kPrefetchB = MODE == kLogits && KDT == MISA_K_FP8_E4M3;
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2 * kSwTileBytes];
   __shared__ float s_sc[2][KT];
 
@@ -291,7 +298,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   int tq[2];
   __amdgpu_buffer_rsrc_t orsrc[2];
   float thr[2];
-  uint64_t* reg[2];
+  uint32_t reg[2];   // kCands: group offset of the lane's region
   const uint32_t row_bytes = (uint32_t)out_spec.ld * 4u;
   const uint32_t lane_row_off = (uint32_t)g * row_bytes;
   const int split = (int)(k0 / KR);
@@ -307,8 +314,8 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
       orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld,
                               (uint32_t)nrows * row_bytes);
     } else {
-      thr[G] = out_spec.thr[qrow0 + qoc];
-      reg[G] = out_spec.regions + ((qrow0 + qoc) * n_ksplits + split) * (int64_t)out_spec.cap;
+      thr[G] = __builtin_fmaxf(out_spec.thr[qrow0 + qoc], -__FLT_MAX__);   // finite: -inf never qualifies
+      reg[G] = (uint32_t)(((qrow0 + qoc) * n_ksplits + split) * (int64_t)out_spec.cap);
     }
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) hw[G][sl] = heads[(qrow0 + qoc) * h + min(sl, h - 1)];
@@ -364,31 +371,21 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
 
   // kCands: the previous tile's scores, appended at the start of the next tile
   f32x4 pend[2] = {f32x4{ninf, ninf, ninf, ninf}, f32x4{ninf, ninf, ninf, ninf}};
-  int pend_kg = 0x3FFFFFFF;   // no pending tile: past every query
-  uint32_t run[2] = {0u, 0u};   // candidates of the lane's query group so far
+  int pend_kg = 0;   // with pend at -inf nothing is appended before the first tile
+  uint32_t run[2] = {0u, 0u};   // groups appended for the lane's query so far
   const uint64_t gmask = 0xFFFFull << (16 * g);
   auto append = [&]() {
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
-      bool f[4];
-      uint32_t c = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] = (pend_kg + e <= tq[G]) && (pend[G][e] >= thr[G]);
-        c += f[e];
+      const float vmax = __builtin_fmaxf(__builtin_fmaxf(pend[G][0], pend[G][1]), __builtin_fmaxf(pend[G][2], pend[G][3]));
+      const bool pass = vmax >= thr[G];
+      const uint64_t m = __ballot(pass) & gmask;
+      const uint32_t pos = run[G] + lanes_below(m);
+      run[G] += (uint32_t)__popcll(m);
+      if (pass && pos < (uint32_t)out_spec.cap) {
+        out_spec.gvals[reg[G] + pos] = pend[G];
+        out_spec.gkeys[reg[G] + pos] = pend_kg;
       }
-      const uint64_t m0 = __ballot(c & 1u), m1 = __ballot(c & 2u), m2 = __ballot(c & 4u);
-      if ((m0 | m1 | m2) == 0) continue;   // uniform
-      uint32_t pos = run[G] + lanes_below(m0 & gmask) + 2 * lanes_below(m1 & gmask) +
-                     4 * lanes_below(m2 & gmask);
-      run[G] += __popcll(m0 & gmask) + 2 * __popcll(m1 & gmask) + 4 * __popcll(m2 & gmask);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (f[e]) {
-          if (pos < (uint32_t)out_spec.cap)
-            reg[G][pos] = ((uint64_t)(uint32_t)(pend_kg + e) << 32) | (uint64_t)__float_as_uint(pend[G][e]);
-          ++pos;
-        }
     }
   };
 
@@ -405,11 +402,17 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
     } else {
       const bool diag = key0 + KT - 1 > t_lo;   // some key of the tile lies after some query
       bf16x8 bcur[kKSteps], bnxt[kKSteps];
+      if (kPrefetchB) {
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + rd[ks]));
+        for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + rd[ks]));
+      }
 #pragma unroll
       for (int kb = 0; kb < KT / 16; ++kb) {
-        if (kb + 1 < KT / 16) {
+        if (!kPrefetchB) {
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks)
+            bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kb * 16 * kSwRowBytes + rd[ks]));
+        } else if (kb + 1 < KT / 16) {
 #pragma unroll
           for (int ks = 0; ks < kKSteps; ++ks)
             bnxt[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (kb + 1) * 16 * kSwRowBytes + rd[ks]));
@@ -435,7 +438,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
           if (diag && kg + kb > tq[G]) s = ninf;
           out[G][kb] = s;
         }
-        if (kb + 1 < KT / 16) {
+        if (kPrefetchB && kb + 1 < KT / 16) {
 #pragma unroll
           for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = bnxt[ks];
         }
@@ -650,7 +653,7 @@ hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, 
     int nks;
     int64_t KR;
     plan_split(N, s.n_seq, (M + 31) / 32, 64, &nks, &KR);
-    const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, 0, nullptr};
+    const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
     return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
   }
   const int hh = heads ? h : H;
@@ -696,14 +699,12 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   plan_split(N, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
   p.n_splits = nks;
   p.key_range = KR;
-  if (nks > 64) {   // the region select holds at most 64 key ranges per row
-    p.ok = false;
-    return p;
-  }
-  // expected candidates per (row, key range), doubled, plus room for a few
-  // clusters of large scores
+  // expected candidate groups of 4 keys per (row, key range) (at most the
+  // expected candidates), doubled, plus room for a few clusters of large scores
   const int64_t expect = (int64_t)p.target * KR / n_min + 1;
-  p.cap_region = (int)((2 * expect + 1024 + 255) / 256 * 256);
+  p.cap_region = (int)((2 * expect + 512 + 255) / 256 * 256);
+  // region entries are addressed with 32-bit offsets
+  if ((int64_t)s.n_seq * s.q_per_seq * p.n_splits * p.cap_region >= ((int64_t)1 << 32)) p.ok = false;
   return p;
 }
 
@@ -713,14 +714,14 @@ hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const fl
   int nks;
   int64_t KR;
   plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
-  const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, 0, nullptr};
+  const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
   return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
 }
 
 hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                               const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
-                              const float* thr, uint64_t* regions, uint32_t* rcount, hipStream_t st) {
-  const ScoreOut o{nullptr, 0, thr, regions, rcount, p.cap_region, nullptr};
+                              const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st) {
+  const ScoreOut o{nullptr, 0, thr, reinterpret_cast<f32x4*>(gvals), gkeys, rcount, p.cap_region, nullptr};
   return launch_h8<kCands>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, p.n_splits, p.key_range, st);
 }
 
@@ -730,7 +731,7 @@ hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const fl
   int nks;
   int64_t KR;
   plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
-  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, 0, row_flag};
+  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
   return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
 }
 

@@ -896,45 +896,74 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const 
   }
 }
 
-// Exact top-k of a row's candidates, gathered from its key-range regions.  A
-// row with an overflowed region, more candidates than the buffer holds, or
-// fewer than k is flagged (and left for the re-scoring path).
+// Exact top-k of a row's candidates, gathered from its key-range regions:
+// groups of 4 consecutive scores, of which the ones at or above the row's
+// threshold (clamped finite, as the scoring pass used it) are kept.  A row
+// with an overflowed region, more candidates than the buffer holds, or fewer
+// than k is flagged (and left for the re-scoring path).
 template <int CAP, int NT>
 __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, int64_t q_pos0, int M, int n_splits,
-                                                        int cap_region, int cap_list,
-                                                        const uint64_t* __restrict__ regions,
+                                                        int cap_region, int cap_list, const float* __restrict__ thr,
+                                                        const f32x4* __restrict__ gvals,
+                                                        const int32_t* __restrict__ gkeys,
                                                         const uint32_t* __restrict__ rcount,
                                                         uint32_t* __restrict__ flag, int32_t* __restrict__ idx_out,
                                                         float* __restrict__ val_out, int sorted) {
   __shared__ TopkShared<CAP, NT> sh;
-  __shared__ uint32_t s_off[65];
-  const int tid = threadIdx.x;
+  __shared__ uint32_t s_bad;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t row = (int64_t)b * M + i;
   const int n = (int)min(n_keys, q_pos0 + i + 1);
+  const float tf = __builtin_fmaxf(thr[row], -__FLT_MAX__);
   if (tid == 0) {
-    uint32_t tot = 0;
-    bool bad = false;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const uint32_t c = rcount[row * n_splits + sp];
-      bad |= c > (uint32_t)cap_region;
-      s_off[sp] = tot;
-      tot += min(c, (uint32_t)cap_region);
-    }
-    s_off[n_splits] = (bad || tot > (uint32_t)min(cap_list, CAP) || tot < (uint32_t)min(k, n)) ? 0xFFFFFFFFu : tot;
+    sh.count = 0;
+    s_bad = 0;
   }
   __syncthreads();
-  const uint32_t tot = s_off[n_splits];
-  if (tot == 0xFFFFFFFFu) {
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const uint32_t c = rcount[row * n_splits + sp];
+    if (c > (uint32_t)cap_region) {   // uniform: every thread reads the same count
+      if (tid == 0) s_bad = 1;
+      break;
+    }
+    const int64_t base = (row * n_splits + sp) * (int64_t)cap_region;
+    for (uint32_t e0 = 0; e0 < c; e0 += NT) {
+      const uint32_t e = e0 + tid;
+      f32x4 v = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      int32_t key = 0;
+      if (e < c) {
+        v = gvals[base + e];
+        key = gkeys[base + e];
+      }
+      bool f[4];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[j] = v[j] >= tf;
+        cnt += f[j];
+      }
+      const uint64_t m0 = __ballot(cnt & 1u), m1 = __ballot(cnt & 2u), m2 = __ballot(cnt & 4u);
+      if ((m0 | m1 | m2) == 0) continue;
+      uint32_t pos = lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2);
+      uint32_t wbase = 0;
+      if (lane == __ffsll((unsigned long long)__ballot(1)) - 1)
+        wbase = atomicAdd(&sh.count, (uint32_t)(__popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2)));
+      pos += __builtin_amdgcn_readfirstlane(wbase);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (f[j]) {
+          if (pos < (uint32_t)CAP) sh.buf[pos] = pack_raw(v[j], key + j);
+          ++pos;
+        }
+    }
+  }
+  __syncthreads();
+  const uint32_t tot = sh.count;
+  if (s_bad != 0 || tot > (uint32_t)min(cap_list, CAP) || tot < (uint32_t)min(k, n)) {
     if (tid == 0) flag[row] = 1;
     return;
   }
-  for (int sp = 0; sp < n_splits; ++sp) {
-    const uint32_t o = s_off[sp], c = ((sp + 1 < n_splits) ? s_off[sp + 1] : tot) - o;
-    const uint64_t* src = regions + (row * n_splits + sp) * (int64_t)cap_region;
-    for (uint32_t e = tid; e < c; e += NT) sh.buf[o + e] = src[e];
-  }
-  __syncthreads();
   finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted);
 }
 
@@ -964,16 +993,19 @@ hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, co
   return hipGetLastError();
 }
 
-hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const uint64_t* regions,
-                               const uint32_t* rcount, uint32_t* row_flag, int32_t* idx, float* vals, bool sorted,
-                               hipStream_t st) {
+hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const float* thr,
+                               const float* gvals, const int32_t* gkeys, const uint32_t* rcount, uint32_t* row_flag,
+                               int32_t* idx, float* vals, bool sorted, hipStream_t st) {
   dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
+  const f32x4* gv = reinterpret_cast<const f32x4*>(gvals);
   if (k <= 4096)
     hipLaunchKernelGGL((k_topk_regions<8192, 512>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0, s.q_per_seq,
-                       p.n_splits, p.cap_region, p.cap_list, regions, rcount, row_flag, idx, vals, (int)sorted);
+                       p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, vals,
+                       (int)sorted);
   else
     hipLaunchKernelGGL((k_topk_regions<16384, 512>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0, s.q_per_seq,
-                       p.n_splits, p.cap_region, p.cap_list, regions, rcount, row_flag, idx, vals, (int)sorted);
+                       p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, vals,
+                       (int)sorted);
   return hipGetLastError();
 }
 

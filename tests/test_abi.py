@@ -135,7 +135,10 @@ def test_sparse_head_topk_checks_and_workspace(lib):
     # kept for rows the candidates cannot settle
     big = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
     fused = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(big), 8, 2048)
-    assert fused == 8192 * 131072 * 4 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4 + 8192 * 8 * 2048 * 8
+    # target 3072 candidates per row, 8 key ranges of 16384 keys over a shortest
+    # prefix of 122881: 410 expected groups per range, doubled, + 512, rounded
+    # up to 256 = 1536 groups of 4 scores (16 bytes) and their first key (4)
+    assert fused == 8192 * 131072 * 4 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4 + 8192 * 8 * 1536 * 20
 
 
 def test_empty_query_set_is_a_no_op(lib):
@@ -151,6 +154,6 @@ def test_workspace_size_of_the_long_context_chunk(lib):
     # the fp32 logits of the chunk (8192 x 131072 x 4 bytes; the fused path
     # writes them only for rows its candidates cannot settle), the sampled
     # scores (8192 x 4096 x 4) and the candidate regions (8192 rows x 8 key
-    # ranges x 2048 entries x 8 bytes)
-    main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 2048 * 8
+    # ranges x 1536 groups of 4 scores and a key, 20 bytes)
+    main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 1536 * 20
     assert main <= need < main * 1.01
