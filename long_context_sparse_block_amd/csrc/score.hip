@@ -205,6 +205,9 @@ __device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t b
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
 }
+__device__ __forceinline__ void store_i32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, int v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)byte_off, 0, 0);
+}
 
 // Where a k_score_h8 pass puts its results.
 //  MODE kLogits: logits[row][u] for key u of the scored key sequence (u ks).
@@ -243,9 +246,8 @@ constexpr int kCands = 1;
 //   kCands: a lane's group of 4 scores with one at or above the row
 //   threshold is appended whole (a float4 and its first key) to the row's
 //   region (positions from a ballot within the 16 lanes that hold one
-//   query); the appends of a tile are issued at the start of the next tile,
-//   before its key prefetch, so waiting for that prefetch never waits for a
-//   store issued after it.
+//   query), through buffer stores that every lane issues (the others' are
+//   dropped by the descriptor bounds).
 // All loads are unconditional, so the compiler never waits on the stores.
 // The tile loop is unrolled by two so both LDS buffers are addressed by
 // immediates.  Keys are scored along the sequence 0, ks, 2 ks, ... (ks = 1:
@@ -296,12 +298,20 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   bf16x8 afr[4][kKSteps];
   float wv[2][8];
   int tq[2];
-  __amdgpu_buffer_rsrc_t orsrc[2];
+  __amdgpu_buffer_rsrc_t orsrc[2];   // kLogits: the two groups' rows; kCands: gvals, gkeys of the workgroup
   float thr[2];
-  uint32_t reg[2];   // kCands: group offset of the lane's region
+  uint32_t reg[2];   // kCands: group offset of the lane's region from the workgroup's first
   const uint32_t row_bytes = (uint32_t)out_spec.ld * 4u;
   const uint32_t lane_row_off = (uint32_t)g * row_bytes;
   const int split = (int)(k0 / KR);
+  if (MODE == kCands) {
+    // regions of rows qa..qb-1 in this key range: row r's starts (r - qa) *
+    // n_ksplits * cap groups after row qa's (fits 31 bits: checked on the host)
+    const int64_t g0 = ((qrow0 + qa) * n_ksplits + split) * (int64_t)out_spec.cap;
+    const uint32_t span = (uint32_t)(((int64_t)(qb - 1 - qa) * n_ksplits + 1) * out_spec.cap);
+    orsrc[0] = uniform_rsrc(out_spec.gvals + g0, span * 16u);
+    orsrc[1] = uniform_rsrc(out_spec.gkeys + g0, span * 4u);
+  }
   int hw[2][8], ha[2][2];
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
@@ -314,8 +324,10 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
       orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld,
                               (uint32_t)nrows * row_bytes);
     } else {
-      thr[G] = __builtin_fmaxf(out_spec.thr[qrow0 + qoc], -__FLT_MAX__);   // finite: -inf never qualifies
-      reg[G] = (uint32_t)(((qrow0 + qoc) * n_ksplits + split) * (int64_t)out_spec.cap);
+      // finite, so masked -inf scores never qualify; +inf for lanes past the
+      // last query, whose scores belong to no row
+      thr[G] = (qo < qb) ? __builtin_fmaxf(out_spec.thr[qrow0 + qoc], -__FLT_MAX__) : __builtin_inff();
+      reg[G] = (uint32_t)(qoc - qa) * (uint32_t)n_ksplits * (uint32_t)out_spec.cap;
     }
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) hw[G][sl] = heads[(qrow0 + qoc) * h + min(sl, h - 1)];
@@ -369,25 +381,8 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   const float ninf = -__builtin_inff();
   constexpr uint32_t kDrop = 0x80000000u;   // a byte offset past every store resource
 
-  // kCands: the previous tile's scores, appended at the start of the next tile
-  f32x4 pend[2] = {f32x4{ninf, ninf, ninf, ninf}, f32x4{ninf, ninf, ninf, ninf}};
-  int pend_kg = 0;   // with pend at -inf nothing is appended before the first tile
-  uint32_t run[2] = {0u, 0u};   // groups appended for the lane's query so far
+  uint32_t run[2] = {0u, 0u};   // kCands: groups found for the lane's query so far
   const uint64_t gmask = 0xFFFFull << (16 * g);
-  auto append = [&]() {
-#pragma unroll
-    for (int G = 0; G < 2; ++G) {
-      const float vmax = __builtin_fmaxf(__builtin_fmaxf(pend[G][0], pend[G][1]), __builtin_fmaxf(pend[G][2], pend[G][3]));
-      const bool pass = vmax >= thr[G];
-      const uint64_t m = __ballot(pass) & gmask;
-      const uint32_t pos = run[G] + lanes_below(m);
-      run[G] += (uint32_t)__popcll(m);
-      if (pass && pos < (uint32_t)out_spec.cap) {
-        out_spec.gvals[reg[G] + pos] = pend[G];
-        out_spec.gkeys[reg[G] + pos] = pend_kg;
-      }
-    }
-  };
 
   // one tile from LDS buffer BUF
   auto tile = [&](auto buf_tag, int key0) {
@@ -400,58 +395,79 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
       out[0] = f32x4{ninf, ninf, ninf, ninf};
       out[1] = out[0];
     } else {
-      const bool diag = key0 + KT - 1 > t_lo;   // some key of the tile lies after some query
-      bf16x8 bcur[kKSteps], bnxt[kKSteps];
-      if (kPrefetchB) {
+      // DIAG: some key of the tile may lie after some query of the wave.  In
+      // kCands only those tiles pay for the causal mask (the logits variants
+      // have no registers to spare for a second copy of the tile)
+      const bool diag = key0 + KT - 1 > t_lo;
+      auto scores = [&](auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        bf16x8 bcur[kKSteps], bnxt[kKSteps];
+        if (kPrefetchB) {
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + rd[ks]));
-      }
-#pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb) {
-        if (!kPrefetchB) {
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks)
-            bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kb * 16 * kSwRowBytes + rd[ks]));
-        } else if (kb + 1 < KT / 16) {
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks)
-            bnxt[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (kb + 1) * 16 * kSwRowBytes + rd[ks]));
+          for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + rd[ks]));
         }
-        const float sc = (KDT == MISA_K_FP8_E4M3) ? s_sc[BUF][kb * 16 + p16] : 1.f;
-        f32x4 acc[2][2];
 #pragma unroll
-        for (int G = 0; G < 2; ++G)
+        for (int kb = 0; kb < KT / 16; ++kb) {
+          if (!kPrefetchB) {
 #pragma unroll
-          for (int qd = 0; qd < 2; ++qd) acc[G][qd] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < kKSteps; ++ks)
+              bcur[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kb * 16 * kSwRowBytes + rd[ks]));
+          } else if (kb + 1 < KT / 16) {
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks)
+            for (int ks = 0; ks < kKSteps; ++ks)
+              bnxt[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (kb + 1) * 16 * kSwRowBytes + rd[ks]));
+          }
+          const float sc = (KDT == MISA_K_FP8_E4M3) ? s_sc[BUF][kb * 16 + p16] : 1.f;
+          f32x4 acc[2][2];
 #pragma unroll
           for (int G = 0; G < 2; ++G)
 #pragma unroll
-            for (int qd = 0; qd < 2; ++qd) acc[G][qd] = mfma16(afr[2 * G + qd][ks], bcur[ks], acc[G][qd]);
+            for (int qd = 0; qd < 2; ++qd) acc[G][qd] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int G = 0; G < 2; ++G) {
-          const float P0 = quad_chain(acc[G][0], wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
-          const float P1 = quad_chain(acc[G][1], wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
-          float s = P0 + P1;
-          if (KDT == MISA_K_FP8_E4M3) s *= sc;
-          if (diag && kg + kb > tq[G]) s = ninf;
-          out[G][kb] = s;
-        }
-        if (kPrefetchB && kb + 1 < KT / 16) {
+          for (int ks = 0; ks < kKSteps; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = bnxt[ks];
+            for (int G = 0; G < 2; ++G)
+#pragma unroll
+              for (int qd = 0; qd < 2; ++qd) acc[G][qd] = mfma16(afr[2 * G + qd][ks], bcur[ks], acc[G][qd]);
+#pragma unroll
+          for (int G = 0; G < 2; ++G) {
+            const float P0 = quad_chain(acc[G][0], wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
+            const float P1 = quad_chain(acc[G][1], wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
+            float s = P0 + P1;
+            if (KDT == MISA_K_FP8_E4M3) s *= sc;
+            if (DIAG && diag && kg + kb > tq[G]) s = ninf;
+            out[G][kb] = s;
+          }
+          if (kPrefetchB && kb + 1 < KT / 16) {
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) bcur[ks] = bnxt[ks];
+          }
         }
-      }
+      };
+      if (MODE == kLogits || diag)
+        scores(std::true_type{});
+      else
+        scores(std::false_type{});
     }
     if (MODE == kLogits) {
       const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
       store_f32x4(orsrc[0], off, out[0]);
       store_f32x4(orsrc[1], off, out[1]);
     } else {
-      pend[0] = out[0];
-      pend[1] = out[1];
-      pend_kg = kg;
+      // every lane issues its stores (dropped unless the group qualifies and
+      // the region has room), so the wait for the next tile's prefetch,
+      // issued before them, is a fixed count
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        const float vmax = __builtin_fmaxf(__builtin_fmaxf(out[G][0], out[G][1]), __builtin_fmaxf(out[G][2], out[G][3]));
+        const bool pass = vmax >= thr[G];
+        const uint64_t m = __ballot(pass) & gmask;
+        const uint32_t pos = run[G] + lanes_below(m);
+        run[G] += (uint32_t)__popcll(m);
+        const bool put = pass && pos < (uint32_t)out_spec.cap;
+        store_f32x4(orsrc[0], put ? (reg[G] + pos) * 16u : kDrop, out[G]);
+        store_i32(orsrc[1], put ? (reg[G] + pos) * 4u : kDrop, kg);
+      }
     }
   };
 
@@ -459,14 +475,12 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   using B1 = std::integral_constant<int, 1>;
   for (int jt = 0; jt < n_tiles; jt += 2) {
     const int key0 = k0 + jt * KT;
-    if (MODE == kCands) append();
     stg.load(kb_ptr, sc_ptr, key0 + KT, Nk, kstride, tid);   // tile jt+1 (zeros past N)
     tile(B0{}, key0);
     stg.store(s_k + kSwTileBytes, s_sc[1], tid);
     __syncthreads();
     if (jt + 1 < n_tiles) {
-      if (MODE == kCands) append();
-      stg.load(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, kstride, tid);   // tile jt+2
+        stg.load(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, kstride, tid);   // tile jt+2
       tile(B1{}, key0 + KT);
       stg.store(s_k, s_sc[0], tid);
       __syncthreads();
@@ -476,7 +490,6 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
     // keys of this range after the last computed tile: -inf for every query
     fill_neg_inf(out_spec.logits, out_spec.ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
   } else {
-    if (n_tiles > 0) append();
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       const int qo = q0w + 4 * G + g;
@@ -703,8 +716,8 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   // expected candidates), doubled, plus room for a few clusters of large scores
   const int64_t expect = (int64_t)p.target * KR / n_min + 1;
   p.cap_region = (int)((2 * expect + 512 + 255) / 256 * 256);
-  // region entries are addressed with 32-bit offsets
-  if ((int64_t)s.n_seq * s.q_per_seq * p.n_splits * p.cap_region >= ((int64_t)1 << 32)) p.ok = false;
+  // a workgroup's 32 rows of regions are addressed with byte offsets below 2^31
+  if ((int64_t)32 * p.n_splits * p.cap_region * 16 >= ((int64_t)1 << 31)) p.ok = false;
   return p;
 }
 

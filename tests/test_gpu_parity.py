@@ -400,6 +400,27 @@ def test_fused_indexer_rows_the_sample_misjudges():
     _check_sparse_head_topk(inp, st)
 
 
+def test_fused_indexer_nonpositive_scores_ragged_query_tile():
+    """All head weights negative: every score is <= 0 and a good share of each
+    row is exactly 0 (no routed head with a positive dot product), so the row
+    thresholds are <= 0 and the top-k is decided by index among equal zeros.
+    M = 37 leaves a query tile with padding lanes, whose zero scores would
+    pass such a threshold; they belong to no row and must not reach any
+    row's candidates."""
+    say("fused indexer: scores <= 0, ragged query tile")
+    cfg = gen.small_config(name="fused_neg", m=37, n=40000, hh=16, b=64, h=4, k=256, seed=44, plant=False)
+    inp = gen.generate(cfg)
+    inp.w[...] = -np.abs(inp.w)
+    st = run_stages(inp)
+    idx, vals = lcsb.misa_indexer(st["sh"], st["t"]["q"], st["t"]["w"], st["t"]["k"], cfg.h, cfg.topk)
+    sidx, svals = _staged_selection(inp, st, 0)
+    torch.cuda.synchronize()
+    assert float(svals.max()) <= 0.0 and int((svals == 0).sum()) > 0
+    assert torch.equal(idx, sidx) and torch.equal(vals, svals)
+    check_topk_exact(inp, st["logits"], cfg.topk, idx, vals)
+    _check_sparse_head_topk(inp, st)
+
+
 @pytest.mark.parametrize("kdtype", [gen.KDTYPE_BF16, gen.KDTYPE_FP8])
 def test_dagger_with_all_candidates_is_dense_topk(kdtype):
     # k' >= L: every prefix token is a candidate, the re-rank is the dense indexer
