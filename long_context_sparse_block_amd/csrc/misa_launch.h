@@ -42,6 +42,9 @@ size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k);
 //     hold fewer than k candidates is flagged, re-scored into full logits and
 //     selected from them, so the result is exact for every input.
 // ---------------------------------------------------------------------------
+// key ranges of one row the region select can take (its LDS prefix table)
+constexpr int kMaxRegionSplits = 1024;
+
 struct FusedPlan {
   bool ok;             // the fused path applies
   int kstride;         // key sampling stride of step 1

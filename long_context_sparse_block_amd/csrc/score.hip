@@ -712,6 +712,10 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   plan_split(N, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
   p.n_splits = nks;
   p.key_range = KR;
+  if (nks > kMaxRegionSplits) {
+    p.ok = false;
+    return p;
+  }
   // expected candidate groups of 4 keys per (row, key range) (at most the
   // expected candidates), doubled, plus room for a few clusters of large scores
   const int64_t expect = (int64_t)p.target * KR / n_min + 1;

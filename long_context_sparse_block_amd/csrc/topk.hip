@@ -910,37 +910,70 @@ __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, i
                                                         uint32_t* __restrict__ flag, int32_t* __restrict__ idx_out,
                                                         float* __restrict__ val_out, int sorted) {
   __shared__ TopkShared<CAP, NT> sh;
+  __shared__ uint32_t s_start[kMaxRegionSplits + 1];   // first flat group of each region
   __shared__ uint32_t s_bad;
   const int tid = threadIdx.x, lane = tid & 63;
   const int i = blockIdx.x, b = blockIdx.y;
   const int64_t row = (int64_t)b * M + i;
   const int n = (int)min(n_keys, q_pos0 + i + 1);
   const float tf = __builtin_fmaxf(thr[row], -__FLT_MAX__);
-  if (tid == 0) {
-    sh.count = 0;
-    s_bad = 0;
+  if (tid < 64) {   // the regions' counts and their prefix, one wave
+    uint32_t run = 0, bad = 0;
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+      const int sp = s0 + lane;
+      const uint32_t c = (sp < n_splits) ? rcount[row * n_splits + sp] : 0u;
+      bad |= c > (uint32_t)cap_region;
+      uint32_t x = c;   // inclusive scan over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      if (sp < n_splits) s_start[sp] = run + x - c;
+      run += __shfl(x, 63);
+    }
+    if (lane == 0) {
+      s_start[n_splits] = run;
+      sh.count = 0;
+    }
+    bad = __ballot(bad != 0) != 0;
+    if (lane == 0) s_bad = bad;
   }
   __syncthreads();
-  for (int sp = 0; sp < n_splits; ++sp) {
-    const uint32_t c = rcount[row * n_splits + sp];
-    if (c > (uint32_t)cap_region) {   // uniform: every thread reads the same count
-      if (tid == 0) s_bad = 1;
-      break;
-    }
-    const int64_t base = (row * n_splits + sp) * (int64_t)cap_region;
-    for (uint32_t e0 = 0; e0 < c; e0 += NT) {
-      const uint32_t e = e0 + tid;
-      f32x4 v = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-      int32_t key = 0;
-      if (e < c) {
-        v = gvals[base + e];
-        key = gkeys[base + e];
+  if (s_bad != 0) {
+    if (tid == 0) flag[row] = 1;
+    return;
+  }
+  // every group of every region, flat: U groups per thread loaded together
+  constexpr int U = 4;
+  const uint32_t total = s_start[n_splits];
+  for (uint32_t e0 = 0; e0 < total; e0 += U * NT) {
+    f32x4 v[U];
+    int32_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t e = e0 + u * NT + tid;
+      v[u] = f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      key[u] = 0;
+      if (e < total) {
+        int lo = 0, hi = n_splits;   // region: the last one starting at or before e
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_start[mid] <= e) lo = mid;
+          else hi = mid;
+        }
+        const int64_t g = (row * n_splits + lo) * (int64_t)cap_region + (e - s_start[lo]);
+        v[u] = gvals[g];
+        key[u] = gkeys[g];
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       bool f[4];
       uint32_t cnt = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f[j] = v[j] >= tf;
+        f[j] = v[u][j] >= tf;
         cnt += f[j];
       }
       const uint64_t m0 = __ballot(cnt & 1u), m1 = __ballot(cnt & 2u), m2 = __ballot(cnt & 4u);
@@ -953,14 +986,14 @@ __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, i
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (f[j]) {
-          if (pos < (uint32_t)CAP) sh.buf[pos] = pack_raw(v[j], key + j);
+          if (pos < (uint32_t)CAP) sh.buf[pos] = pack_raw(v[u][j], key[u] + j);
           ++pos;
         }
     }
   }
   __syncthreads();
   const uint32_t tot = sh.count;
-  if (s_bad != 0 || tot > (uint32_t)min(cap_list, CAP) || tot < (uint32_t)min(k, n)) {
+  if (tot > (uint32_t)min(cap_list, CAP) || tot < (uint32_t)min(k, n)) {
     if (tid == 0) flag[row] = 1;
     return;
   }
