@@ -5,83 +5,103 @@
 // summarised by the mean of its indexer keys (gist.science summary of MISA,
 // "Metodologia: MISA" item 1; agents-report summary, method overview).
 //
-// One workgroup (one wave) per (sequence, block m).  Lane l owns dims 2l, 2l+1
-// and walks the block's keys in order, so a wave reads one 256-byte (bf16) or
-// 128-byte (fp8) key row per step: fully coalesced, one pass over K.  The
-// running fp32 sum is also the prefix sum that the tails of queries inside
-// this block need, so tails cost no extra traffic.  HBM-bound.
+// One workgroup of kPoolWaves waves per (sequence, block m); wave w sums the
+// w-th slice of the block's keys.  Lane l owns dims 2l, 2l+1, so a wave reads
+// one 256-byte (bf16) or 128-byte (fp8) key row per load, 8 rows in flight.
+// The block mean is the slices' sums added in order.  Blocks that hold
+// queries walk their slice a second time (an L2 hit) with the running sum
+// started at the sum of the slices before it: that running sum is the prefix
+// sum the tails of those queries need.  HBM-bound: one pass over K.
 #include "misa_common.h"
 #include "misa_launch.h"
 
 namespace misa {
 
+constexpr int kPoolWaves = 4;
+
 template <int KDT>
-__global__ void __launch_bounds__(kWave) k_pool(const void* __restrict__ kptr,
-                                                const float* __restrict__ kscale,
-                                                float* __restrict__ pooled, float* __restrict__ tail,
-                                                int64_t N, int64_t q_pos0, int M, int B,
-                                                int64_t n_blk_total, int64_t n_full) {
+__device__ __forceinline__ f32x2 pool_load(const void* kptr, const float* kscale, int64_t row, int lane) {
+  if (KDT == MISA_K_BF16) {
+    const uint32_t two = reinterpret_cast<const uint32_t*>(kptr)[row * (kD / 2) + lane];
+    return f32x2{bf16_bits_to_f32(two & 0xFFFFu), bf16_bits_to_f32(two >> 16)};
+  } else {
+    const uint32_t two = reinterpret_cast<const uint16_t*>(kptr)[row * (kD / 2) + lane];
+    const float sc = kscale[row];
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
+    return f32x2{f.x * sc, f.y * sc};
+  }
+}
+
+template <int KDT>
+__global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restrict__ kptr,
+                                                             const float* __restrict__ kscale,
+                                                             float* __restrict__ pooled, float* __restrict__ tail,
+                                                             int64_t N, int64_t q_pos0, int M, int B,
+                                                             int64_t n_blk_total, int64_t n_full) {
+  __shared__ f32x2 s_part[kPoolWaves][kWave];
   const int64_t m = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t s0 = m * B;
   const int64_t s1 = (s0 + B < N) ? s0 + B : N;
   // only blocks that are complete or hold a query need any work
   const int64_t q_lo = q_pos0, q_hi = q_pos0 + M;  // queries occupy [q_lo, q_hi)
   const bool full = (s0 + B <= N);
   const bool has_query = (s1 > q_lo) && (s0 < q_hi);
-  if (!full && !has_query) return;
+  if (!full && !has_query) return;   // uniform over the workgroup
+  const int64_t per = (s1 - s0 + kPoolWaves - 1) / kPoolWaves;
+  const int64_t w0 = min(s0 + w * per, s1), w1 = min(w0 + per, s1);   // this wave's slice
 
-  float a0 = 0.f, a1 = 0.f;
   constexpr int U = 8;
-  for (int64_t s = s0; s < s1; s += U) {
-    float v0[U], v1[U];
+  float a0 = 0.f, a1 = 0.f;
+  for (int64_t s = w0; s < w1; s += U) {
+    f32x2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (s + u < w1) ? pool_load<KDT>(kptr, kscale, (int64_t)b * N + s + u, lane) : f32x2{0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int64_t ss = s + u;
-      v0[u] = 0.f;
-      v1[u] = 0.f;
-      if (ss < s1) {
-        int64_t row = (int64_t)b * N + ss;
-        if (KDT == MISA_K_BF16) {
-          uint32_t two = reinterpret_cast<const uint32_t*>(kptr)[row * (kD / 2) + lane];
-          v0[u] = bf16_bits_to_f32(two & 0xFFFFu);
-          v1[u] = bf16_bits_to_f32(two >> 16);
-        } else {
-          uint32_t two = reinterpret_cast<const uint16_t*>(kptr)[row * (kD / 2) + lane];
-          float sc = kscale[row];
-          f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
-          v0[u] = f.x * sc;
-          v1[u] = f.y * sc;
-        }
-      }
+      a0 += v[u].x;
+      a1 += v[u].y;
     }
+  }
+  s_part[w][lane] = f32x2{a0, a1};
+  __syncthreads();
+  if (full && m < n_full && w == 0) {
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < kPoolWaves; ++v) {
+      t0 += s_part[v][lane].x;
+      t1 += s_part[v][lane].y;
+    }
+    reinterpret_cast<float2*>(pooled)[((int64_t)b * n_full + m) * (kD / 2) + lane] =
+        make_float2(t0 / (float)B, t1 / (float)B);
+  }
+  if (!has_query) return;
+  // tails: running prefix from the sum of the slices before this one
+  a0 = 0.f;
+  a1 = 0.f;
+  for (int v = 0; v < w; ++v) {
+    a0 += s_part[v][lane].x;
+    a1 += s_part[v][lane].y;
+  }
+  for (int64_t s = w0; s < w1; s += U) {
+    f32x2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (s + u < w1) ? pool_load<KDT>(kptr, kscale, (int64_t)b * N + s + u, lane) : f32x2{0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int64_t ss = s + u;
-      if (ss < s1) {
-        a0 += v0[u];
-        a1 += v1[u];
-        // query t = ss has a partial block iff (t+1) % B != 0; its tail is
-        // keys [m*B, t] of this block
-        if (ss >= q_lo && ss < q_hi && ((ss + 1) % B) != 0) {
-          float len = (float)(ss - s0 + 1);
-          float2 o = make_float2(a0 / len, a1 / len);
-          reinterpret_cast<float2*>(tail)[((int64_t)b * M + (ss - q_lo)) * (kD / 2) + lane] = o;
-        }
+      const int64_t ss = s + u;
+      a0 += v[u].x;
+      a1 += v[u].y;
+      if (ss < w1 && ss >= q_lo && ss < q_hi) {
+        // query t = ss: its tail is keys [m*B, t] of this block, empty (zeros)
+        // when its prefix ends on the block's end
+        const bool empty = ((ss + 1) % B) == 0;
+        const float len = (float)(ss - s0 + 1);
+        const float2 o = empty ? make_float2(0.f, 0.f) : make_float2(a0 / len, a1 / len);
+        reinterpret_cast<float2*>(tail)[((int64_t)b * M + (ss - q_lo)) * (kD / 2) + lane] = o;
       }
     }
-  }
-  if (full && m < n_full) {
-    float2 o = make_float2(a0 / (float)B, a1 / (float)B);
-    reinterpret_cast<float2*>(pooled)[((int64_t)b * n_full + m) * (kD / 2) + lane] = o;
-  }
-  // queries whose prefix ends exactly on this block's end have no tail: zeros
-  if (full) {
-    int64_t t = s0 + B - 1;
-    if (t >= q_lo && t < q_hi)
-      reinterpret_cast<float2*>(tail)[((int64_t)b * M + (t - q_lo)) * (kD / 2) + lane] =
-          make_float2(0.f, 0.f);
   }
 }
 
@@ -93,10 +113,10 @@ hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const flo
   const int64_t n_full = N / B;
   dim3 grid((unsigned)n_blk_total, (unsigned)s.n_seq);
   if (kdtype == MISA_K_BF16)
-    hipLaunchKernelGGL(k_pool<MISA_K_BF16>, grid, dim3(kWave), 0, st, k, k_scale, pooled, tail, N,
+    hipLaunchKernelGGL(k_pool<MISA_K_BF16>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail, N,
                        s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
   else
-    hipLaunchKernelGGL(k_pool<MISA_K_FP8_E4M3>, grid, dim3(kWave), 0, st, k, k_scale, pooled, tail,
+    hipLaunchKernelGGL(k_pool<MISA_K_FP8_E4M3>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
                        N, s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
   return hipGetLastError();
 }
