@@ -17,7 +17,7 @@
 
 namespace misa {
 
-constexpr int kPoolWaves = 4;
+constexpr int kPoolWaves = 8;
 
 template <int KDT>
 __device__ __forceinline__ f32x2 pool_load(const void* kptr, const float* kscale, int64_t row, int lane) {

@@ -34,13 +34,14 @@ constexpr int kRowBytes = kD * 2;           // bf16 LDS row (256 bytes), 16-byte
 // byte offset of 16-byte chunk c of staged row j
 __device__ __forceinline__ uint32_t rt_off(int j, int c) { return (uint32_t)j * kRowBytes + (uint32_t)((c ^ (j & 15)) << 4); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// two fp32 -> packed bf16 (element 0 in the low half), round to nearest even
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2_t));
 }
 
 template <int NHC>  // 16-head chunks per query group (= ceil(H/16))
-__global__ void __launch_bounds__(512) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
                                                const float* __restrict__ pooled,
                                                const float* __restrict__ tail,
                                                int32_t* __restrict__ heads, float* __restrict__ scores,
@@ -71,6 +72,7 @@ __global__ void __launch_bounds__(512) k_route(const uint16_t* __restrict__ q, c
   const int64_t nfull_g = (qi_out < M) ? (q_pos0 + qi_out + 1) / B : 0;
   const int q_last_w = min(q0w + 4, M) - 1;
   const int64_t nfull_w = (q0w < M) ? (q_pos0 + q_last_w + 1) / B : 0;
+  const int64_t nfull_lo = (q0w < M) ? (q_pos0 + q0w + 1) / B : 0;   // fewest complete blocks in the wave
 
   // q fragments: row r = lane%16 -> query q0w + r/4, head hc*16 + 4*rb + r%4
   bf16x8 afr[4][kKSteps];
@@ -98,21 +100,33 @@ __global__ void __launch_bounds__(512) k_route(const uint16_t* __restrict__ q, c
   const float* pool_b = pooled + (int64_t)b * n_full_total * kD;
   for (int64_t cbase = 0; cbase < nfull_wg; cbase += kRouteChunk) {
     // stage pooled rows [cbase, cbase+64) as bf16 hi/lo
-    for (int e = tid; e < kRouteChunk * (kD / 4); e += NW * 64) {
-      const int row = e / (kD / 4);
-      const int c4 = e % (kD / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (cbase + row < nfull_wg) v = reinterpret_cast<const float4*>(pool_b + (cbase + row) * kD)[c4];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-      uint32_t hi[4], lo[4];
+    constexpr int kTotal = kRouteChunk * (kD / 4);                 // float4 of a chunk
+    constexpr int kPer = (kTotal + NW * 64 - 1) / (NW * 64);       // per thread (3 waves: ragged)
+    constexpr int kBatch = NW == 4 ? 4 : 2;   // loads in flight per batch (3 waves: ragged, fewer registers)
+#pragma unroll 1   // (unrolled, the compiler keeps both batches live and spills)
+    for (int u0 = 0; u0 < kPer; u0 += kBatch) {
+      float4 v[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi[i] = f32_to_bf16_rne(f[i]);
-        lo[i] = f32_to_bf16_rne(f[i] - __uint_as_float(hi[i] << 16));   // f - hi is exact in fp32
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = tid + (u0 + u) * NW * 64;
+        const int row = e / (kD / 4);
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u0 + u < kPer && e < kTotal && cbase + row < nfull_wg) v[u] = reinterpret_cast<const float4*>(pool_b + (cbase + row) * kD)[e % (kD / 4)];
       }
-      const uint32_t o = rt_off(row, c4 >> 1) + (c4 & 1) * 8;
-      *reinterpret_cast<uint2*>(&s_hi[o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-      *reinterpret_cast<uint2*>(&s_lo[o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = tid + (u0 + u) * NW * 64;
+        const int row = e / (kD / 4);
+        const int c4 = e % (kD / 4);
+        if (u0 + u >= kPer || e >= kTotal) break;
+        const uint32_t h01 = pk_bf16(v[u].x, v[u].y), h23 = pk_bf16(v[u].z, v[u].w);
+        // f - hi is exact in fp32
+        const uint32_t l01 = pk_bf16(v[u].x - __uint_as_float(h01 << 16), v[u].y - __uint_as_float(h01 & 0xFFFF0000u));
+        const uint32_t l23 = pk_bf16(v[u].z - __uint_as_float(h23 << 16), v[u].w - __uint_as_float(h23 & 0xFFFF0000u));
+        const uint32_t o = rt_off(row, c4 >> 1) + (c4 & 1) * 8;
+        *reinterpret_cast<uint2*>(&s_hi[o]) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(&s_lo[o]) = make_uint2(l01, l23);
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -126,18 +140,27 @@ __global__ void __launch_bounds__(512) k_route(const uint16_t* __restrict__ q, c
           bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_hi[rt_off(row, ks * 4 + g)]));
           bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_lo[rt_off(row, ks * 4 + g)]));
         }
-        const bool valid = (col0 + p16) < nfull_g;
+        // only column blocks reaching past the wave's first query's complete
+        // blocks need the per-lane mask
+        auto accumulate = [&](auto mask_tag) {
+          constexpr bool MASK = decltype(mask_tag)::value;
+          const bool valid = !MASK || (col0 + p16) < nfull_g;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int rb = 0; rb < 4; ++rb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) {
-            acc = mfma16(afr[rb][ks], bh[ks], acc);
-            acc = mfma16(afr[rb][ks], bl[ks], acc);
+            for (int ks = 0; ks < kKSteps; ++ks) {
+              acc = mfma16(afr[rb][ks], bh[ks], acc);
+              acc = mfma16(afr[rb][ks], bl[ks], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[rb][i] += (MASK && !valid) ? 0.f : __builtin_fmaxf(acc[i], 0.f);
           }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[rb][i] += valid ? __builtin_fmaxf(acc[i], 0.f) : 0.f;
-        }
+        };
+        if (col0 + 16 <= nfull_lo)
+          accumulate(std::false_type{});
+        else
+          accumulate(std::true_type{});
       }
     }
     __syncthreads();
