@@ -55,7 +55,7 @@ inline misa_status from_hip(hipError_t e) { return e == hipSuccess ? MISA_OK : M
 // Workspace of the routed scoring + top-k selection (misa_sparse_head_topk,
 // and the first selection of misa_indexer), placed from offset `off`.
 struct SelectLayout {
-  size_t logits, sample, thr, flag, rcount, gvals, gkeys, topk_ws, end;
+  size_t logits, kwide, sample, thr, flag, rcount, gvals, gkeys, topk_ws, end;
   int64_t ld;
   misa::FusedPlan fused;
 };
@@ -69,6 +69,8 @@ SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off) {
   L.fused = misa::plan_fused(s, h, k);
   if (L.fused.ok) {
     const misa::FusedPlan& p = L.fused;
+    L.kwide = off;   // bf16 copy of fp8 keys (reserved for either key type)
+    off += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128 (shape check)
     L.sample = off;
     off += align_up((size_t)rows * (size_t)p.ld_sample * sizeof(float));
     L.thr = off;
@@ -107,12 +109,19 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   uint32_t* rcount = reinterpret_cast<uint32_t*>(base + L.rcount);
   float* gvals = reinterpret_cast<float*>(base + L.gvals);
   int32_t* gkeys = reinterpret_cast<int32_t*>(base + L.gkeys);
-  MISA_TRY(from_hip(misa::launch_score_sampled(s, q, w, k, kdtype, k_scale, heads, h, p, sample, st)));
+  // the scoring launches stage bf16 keys by direct loads into LDS
+  const void* kb = k;
+  if (kdtype == MISA_K_FP8_E4M3) {
+    uint16_t* kwide = reinterpret_cast<uint16_t*>(base + L.kwide);
+    MISA_TRY(from_hip(misa::launch_widen_fp8(s, k, kwide, st)));
+    kb = kwide;
+  }
+  MISA_TRY(from_hip(misa::launch_score_sampled(s, q, w, kb, kdtype, k_scale, heads, h, p, sample, st)));
   MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
   MISA_TRY(from_hip(
-      misa::launch_score_cands(s, q, w, k, kdtype, k_scale, heads, h, p, thr, gvals, gkeys, rcount, st)));
+      misa::launch_score_cands(s, q, w, kb, kdtype, k_scale, heads, h, p, thr, gvals, gkeys, rcount, st)));
   MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
-  MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, k, kdtype, k_scale, heads, h, flag, logits, L.ld, st)));
+  MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, kb, kdtype, k_scale, heads, h, flag, logits, L.ld, st)));
   return from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st));
 }
 

@@ -58,6 +58,10 @@ struct FusedPlan {
 };
 FusedPlan plan_fused(const misa_shape& s, int h, int k);
 
+// The fused path's scoring launches take bf16 keys in `k` whatever kdtype is
+// (fp8 keys widened by launch_widen_fp8; kdtype then says that k_scale
+// applies) and stage them by direct global -> LDS loads.
+hipError_t launch_widen_fp8(const misa_shape& s, const void* k, uint16_t* out, hipStream_t st);
 hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                                 const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
                                 float* sample_logits, hipStream_t st);

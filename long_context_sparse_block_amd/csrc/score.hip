@@ -199,6 +199,42 @@ struct KStageSw {
   }
 };
 
+// Tile staging straight from global memory into LDS (buffer loads with the
+// LDS flag: no registers, no VALU), for bf16 keys in global memory (the
+// input's, or fp8 keys widened once by k_widen_fp8).  A wave-wide load writes
+// 16 bytes per lane to consecutive LDS slots from the address in M0, so wave
+// v's load u fills LDS rows r0 .. r0+3, r0 = 4 (u NT/64 + v): lane l fills
+// slot l % 16 of row r0 + l / 16, which holds chunk (l % 16) ^ (row % 16) of
+// tile key sw_tile_key(row) -- the layout KStageSw writes.  With fp8 scales,
+// every wave loads the tile's 64 scales (256 bytes) into the same LDS floats
+// (identical data).  Rows past N read as zeros.
+template <int KDT, int NT>
+__device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sbase, int key0, int N, int ks,
+                                         int lane, int wave, unsigned char* s_dst, float* s_sc_dst) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int64_t first = (int64_t)key0 * ks;
+  const int rem = (int)max((int64_t)0, min((int64_t)kSwKT * ks, (int64_t)N - first));
+  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + first * kD, (uint32_t)rem * kSwRowBytes);
+  constexpr int kLoads = kSwKT / 4 / (NT / 64);
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int r0 = (u * (NT / 64) + wave) * 4;
+    const int j = r0 + (lane >> 4);
+    const int c = (lane & 15) ^ (j & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)(s_dst + r0 * kSwRowBytes), 16,
+                                             (uint32_t)(sw_tile_key(j) * ks) * kSwRowBytes + c * 16, 0, 0, 0);
+  }
+  if (KDT == MISA_K_FP8_E4M3) {
+    const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + first, (uint32_t)rem * 4u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr)s_sc_dst, 4, (uint32_t)(sw_tile_key(lane) * ks) * 4u, 0,
+                                             0, 0);
+  }
+}
+
+// s_waitcnt immediate: wait until at most n vector-memory operations of the
+// wave are outstanding (the export and LDS/scalar counters are not waited on)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
 // Four consecutive logits through a uniform_rsrc descriptor (offsets past its
 // size are dropped).  The store takes raw 32-bit patterns.
 __device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
@@ -254,7 +290,7 @@ constexpr int kCands = 1;
 // every key; a stride samples the keys): key index u < ceil(N / ks) is the key
 // at position u ks, and query t sees indices u <= t / ks.  N is 32-bit here.
 // ---------------------------------------------------------------------------
-template <int KDT, int MODE>
+template <int KDT, int MODE, bool DMA>
 __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q,
                                                   const float* __restrict__ w,
                                                   const void* __restrict__ kptr,
@@ -266,8 +302,17 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   // B fragments read one column block ahead where the registers allow it
   // (16 more VGPRs; the other variants would drop to 2 waves per SIMD)
   constexpr bool kPrefetchB = MODE == kLogits && KDT == MISA_K_FP8_E4M3;
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[2 * kSwTileBytes];
-  __shared__ float s_sc[2][KT];
+  // with direct loads the two tile buffers are separate arrays, so the
+  // compiler can see that loads into one never alias reads of the other (one
+  // array otherwise: the register-staged variants allocate better with it)
+  __shared__ __attribute__((aligned(16))) unsigned char s_kk[DMA ? 1 : 2 * kSwTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_kd0[DMA ? kSwTileBytes : 1], s_kd1[DMA ? kSwTileBytes : 1];
+  __shared__ float s_scc[DMA ? 1 : 2 * KT];
+  __shared__ float s_scd0[DMA ? KT : 1], s_scd1[DMA ? KT : 1];
+  unsigned char* const s_k0 = DMA ? s_kd0 : s_kk;
+  unsigned char* const s_k1 = DMA ? s_kd1 : s_kk + kSwTileBytes;
+  float* const s_sc0 = DMA ? s_scd0 : s_scc;
+  float* const s_sc1 = DMA ? s_scd1 : s_scc + KT;
 
   const int Nk = (int)N64, q_pos0 = (int)q_pos0_64;   // keys; position of query 0
   const int N = (Nk + kstride - 1) / kstride;          // scored key indices
@@ -360,7 +405,9 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
     }
   }
 
-  const void* kb_ptr = (KDT == MISA_K_BF16)
+  // DMA: kptr holds bf16 keys whatever KDT is (KDT then only says whether the
+  // fp8 scales apply)
+  const void* kb_ptr = (KDT == MISA_K_BF16 || DMA)
                            ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * Nk * kD)
                            : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * Nk * kD);
   const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * Nk : nullptr;
@@ -370,9 +417,24 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) rd[ks] = sw_off(p16, 4 * ks + g);
 
+  // staging of tile `key` into LDS buffer `buf`: issued before the current
+  // tile's compute, completed (stage_done) after it, before the barrier
   KStageSw<KDT, NT> stg;
-  stg.load(kb_ptr, sc_ptr, k0, Nk, kstride, tid);
-  stg.store(s_k, s_sc[0], tid);
+  auto stage_issue = [&](int key, int buf) {
+    if (DMA)
+      dma_tile<KDT, NT>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
+                        buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0);
+    else
+      stg.load(kb_ptr, sc_ptr, key, Nk, kstride, tid);
+  };
+  auto stage_done = [&](int buf) {
+    if (DMA)   // the stores issued after the loads (2 per tile, or 4 with candidates) may stay in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(MODE == kLogits ? 2 : 4));
+    else
+      stg.store(buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0, tid);
+  };
+  stage_issue(k0, 0);
+  if (!DMA) stage_done(0);
   // every load issued so far (q fragments, weights) has landed: without this the
   // compiler cannot prove it inside the loop and waits for all memory traffic
   // (the next tile's prefetch included) before each block's first MFMA
@@ -387,7 +449,8 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   // one tile from LDS buffer BUF
   auto tile = [&](auto buf_tag, int key0) {
     constexpr int BUF = decltype(buf_tag)::value;
-    const unsigned char* sk = s_k + BUF * kSwTileBytes;
+    const unsigned char* sk = BUF ? s_k1 : s_k0;
+    const float* ssc = BUF ? s_sc1 : s_sc0;
     const int kg = key0 + 4 * p16;   // this lane's first key index
     f32x4 out[2];
     if (key0 > t_hi) {
@@ -417,7 +480,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
             for (int ks = 0; ks < kKSteps; ++ks)
               bnxt[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (kb + 1) * 16 * kSwRowBytes + rd[ks]));
           }
-          const float sc = (KDT == MISA_K_FP8_E4M3) ? s_sc[BUF][kb * 16 + p16] : 1.f;
+          const float sc = (KDT == MISA_K_FP8_E4M3) ? ssc[kb * 16 + p16] : 1.f;
           f32x4 acc[2][2];
 #pragma unroll
           for (int G = 0; G < 2; ++G)
@@ -475,14 +538,14 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   using B1 = std::integral_constant<int, 1>;
   for (int jt = 0; jt < n_tiles; jt += 2) {
     const int key0 = k0 + jt * KT;
-    stg.load(kb_ptr, sc_ptr, key0 + KT, Nk, kstride, tid);   // tile jt+1 (zeros past N)
+    stage_issue(key0 + KT, 1);   // tile jt+1 (zeros past N)
     tile(B0{}, key0);
-    stg.store(s_k + kSwTileBytes, s_sc[1], tid);
+    stage_done(1);
     __syncthreads();
     if (jt + 1 < n_tiles) {
-        stg.load(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, kstride, tid);   // tile jt+2
+      stage_issue(key0 + 2 * KT, 0);   // tile jt+2
       tile(B1{}, key0 + KT);
-      stg.store(s_k, s_sc[0], tid);
+      stage_done(0);
       __syncthreads();
     }
   }
@@ -641,7 +704,9 @@ static void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplit
   *KR = kr;
 }
 
-template <int MODE>
+// DMA: k holds bf16 keys (for kdtype fp8: the widened copy; k_scale still
+// applies), staged by direct loads into LDS
+template <int MODE, bool DMA = false>
 static hipError_t launch_h8(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                             const float* k_scale, const int32_t* heads, int h, const ScoreOut& o, int kstride,
                             int nks, int64_t KR, hipStream_t st) {
@@ -649,11 +714,11 @@ static hipError_t launch_h8(const misa_shape& s, const uint16_t* q, const float*
   const int n_qtiles = (M + 31) / 32;
   dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
   if (kdtype == MISA_K_BF16)
-    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h, o,
-                       s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
-  else
-    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
+    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE, DMA>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
                        o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+  else
+    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE, DMA>), grid, dim3(256), 0, st, q, w, k, k_scale, heads,
+                       h, o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
   return hipGetLastError();
 }
 
@@ -732,14 +797,14 @@ hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const fl
   int64_t KR;
   plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
   const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
-  return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
+  return launch_h8<kLogits, true>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
 }
 
 hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                               const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
                               const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st) {
   const ScoreOut o{nullptr, 0, thr, reinterpret_cast<f32x4*>(gvals), gkeys, rcount, p.cap_region, nullptr};
-  return launch_h8<kCands>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, p.n_splits, p.key_range, st);
+  return launch_h8<kCands, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, p.n_splits, p.key_range, st);
 }
 
 hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
@@ -749,7 +814,29 @@ hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const fl
   int64_t KR;
   plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
   const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
-  return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
+  return launch_h8<kLogits, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
+}
+
+// fp8 keys widened to bf16 (exactly: every e4m3 value is a bf16 value) for the
+// direct-load staging; 16 codes per thread, the same decoder as the
+// register staging, so both stagings put identical bits in LDS
+__global__ void __launch_bounds__(256) k_widen_fp8(const uint4* __restrict__ codes, uint4* __restrict__ out,
+                                                   int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const uint4 v = codes[i];
+  const uint2 a = e4m3x4_to_bf16x4(v.x), b2 = e4m3x4_to_bf16x4(v.y);
+  const uint2 c2 = e4m3x4_to_bf16x4(v.z), d2 = e4m3x4_to_bf16x4(v.w);
+  out[2 * i] = make_uint4(a.x, a.y, b2.x, b2.y);
+  out[2 * i + 1] = make_uint4(c2.x, c2.y, d2.x, d2.y);
+}
+
+hipError_t launch_widen_fp8(const misa_shape& s, const void* k, uint16_t* out, hipStream_t st) {
+  const int64_t n16 = (int64_t)s.n_seq * s.n_keys * kD / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_widen_fp8, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(k), reinterpret_cast<uint4*>(out), n16);
+  return hipGetLastError();
 }
 
 }  // namespace misa

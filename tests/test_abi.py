@@ -138,7 +138,9 @@ def test_sparse_head_topk_checks_and_workspace(lib):
     # target 3072 candidates per row, 8 key ranges of 16384 keys over a shortest
     # prefix of 122881: 410 expected groups per range, doubled, + 512, rounded
     # up to 256 = 1536 groups of 4 scores (16 bytes) and their first key (4)
-    assert fused == 8192 * 131072 * 4 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4 + 8192 * 8 * 1536 * 20
+    # plus the bf16 copy of the keys the scoring stages by direct loads (131072 x 256)
+    assert fused == (8192 * 131072 * 4 + 131072 * 256 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4
+                     + 8192 * 8 * 1536 * 20)
 
 
 def test_empty_query_set_is_a_no_op(lib):
@@ -153,7 +155,7 @@ def test_workspace_size_of_the_long_context_chunk(lib):
     need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 8, 2048, 0)
     # the fp32 logits of the chunk (8192 x 131072 x 4 bytes; the fused path
     # writes them only for rows its candidates cannot settle), the sampled
-    # scores (8192 x 4096 x 4) and the candidate regions (8192 rows x 8 key
-    # ranges x 1536 groups of 4 scores and a key, 20 bytes)
-    main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 1536 * 20
+    # scores (8192 x 4096 x 4), the candidate regions (8192 rows x 8 key
+    # ranges x 1536 groups of 4 scores and a key, 20 bytes) and the bf16 keys
+    main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 1536 * 20 + 131072 * 256
     assert main <= need < main * 1.01
