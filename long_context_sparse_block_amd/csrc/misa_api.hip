@@ -126,7 +126,7 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
 }
 
 struct IndexerLayout {
-  size_t pooled, tail, heads, cand, dlog, total;
+  size_t pooled, split, tail, heads, cand, dlog, total;
   int64_t ld_d;
   SelectLayout sel;
 };
@@ -139,6 +139,8 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime) 
   size_t off = 0;
   L.pooled = off;
   off += align_up((size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(float));
+  L.split = off;   // bf16 hi and lo rows of the pooled keys, for the router
+  off += align_up(2 * (size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(uint16_t));
   L.tail = off;
   off += align_up((size_t)rows * MISA_HEAD_DIM * sizeof(float));
   L.heads = off;
@@ -180,7 +182,7 @@ misa_status misa_pool_keys(const misa_shape* shape, const void* k, misa_kdtype k
   if ((n_full > 0 && (pooled == nullptr || !aligned16(pooled))) || tail == nullptr || !aligned16(tail))
     return MISA_ERR_INVALID_ARG;
   if (shape->q_per_seq == 0 && n_full == 0) return MISA_OK;
-  return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, (hipStream_t)stream));
+  return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, nullptr, (hipStream_t)stream));
 }
 
 misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const float* w,
@@ -194,7 +196,7 @@ misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const f
     return MISA_ERR_INVALID_ARG;
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (shape->q_per_seq == 0) return MISA_OK;
-  return from_hip(launch_route(*shape, q, w, pooled, tail, h, heads, scores, (hipStream_t)stream));
+  return from_hip(launch_route(*shape, q, w, pooled, nullptr, tail, h, heads, scores, (hipStream_t)stream));
 }
 
 misa_status misa_sparse_head_logits(const misa_shape* shape, const uint16_t* q, const float* w,
@@ -278,8 +280,9 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
   float* pooled = reinterpret_cast<float*>(base + L.pooled);
   float* tail = reinterpret_cast<float*>(base + L.tail);
   int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
-  MISA_TRY(from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, st)));
-  MISA_TRY(from_hip(launch_route(*shape, q, w, pooled, tail, h, heads, nullptr, st)));
+  uint16_t* split = reinterpret_cast<uint16_t*>(base + L.split);
+  MISA_TRY(from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, split, st)));
+  MISA_TRY(from_hip(launch_route(*shape, q, w, pooled, split, tail, h, heads, nullptr, st)));
   if (k_prime == 0)
     return run_select(*shape, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st);
   // the k' candidates are a set: the re-rank and the final top-k do not depend on their order

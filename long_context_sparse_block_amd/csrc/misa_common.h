@@ -66,6 +66,13 @@ __device__ __forceinline__ float quad_chain(const f32x4 x, float w0, float w1, f
   return p;
 }
 
+// Two fp32 -> packed bf16 (element 0 in the low half), round to nearest even
+// (gfx950's packed converter).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2_t));
+}
+
 // Number of set bits of m below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -10,11 +10,16 @@
 
 namespace misa {
 
+// split (nullable): also write the pooled keys' bf16 hi rows [n_seq][N/B][128]
+// followed by the lo rows (pooled - hi), for launch_route
 hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const float* k_scale,
-                       float* pooled, float* tail, hipStream_t st);
+                       float* pooled, float* tail, uint16_t* split, hipStream_t st);
 
+// split (nullable): launch_pool's hi/lo rows, staged directly instead of
+// splitting `pooled` in every workgroup (same values)
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
-                        const float* tail, int h, int32_t* heads, float* scores, hipStream_t st);
+                        const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
+                        hipStream_t st);
 
 // heads == nullptr: all H heads (dense DSA indexer); otherwise h routed heads per query.
 hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,

@@ -36,6 +36,7 @@ template <int KDT>
 __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restrict__ kptr,
                                                              const float* __restrict__ kscale,
                                                              float* __restrict__ pooled, float* __restrict__ tail,
+                                                             uint32_t* __restrict__ split,
                                                              int64_t N, int64_t q_pos0, int M, int B,
                                                              int64_t n_blk_total, int64_t n_full) {
   __shared__ f32x2 s_part[kPoolWaves][kWave];
@@ -73,8 +74,15 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
       t0 += s_part[v][lane].x;
       t1 += s_part[v][lane].y;
     }
-    reinterpret_cast<float2*>(pooled)[((int64_t)b * n_full + m) * (kD / 2) + lane] =
-        make_float2(t0 / (float)B, t1 / (float)B);
+    const float p0 = t0 / (float)B, p1 = t1 / (float)B;
+    const int64_t o = ((int64_t)b * n_full + m) * (kD / 2) + lane;
+    reinterpret_cast<float2*>(pooled)[o] = make_float2(p0, p1);
+    if (split != nullptr) {   // bf16 hi rows, then lo rows (p - hi is exact in fp32)
+      const uint32_t h01 = pk_bf16(p0, p1);
+      split[o] = h01;
+      split[(int64_t)gridDim.y * n_full * (kD / 2) + o] =
+          pk_bf16(p0 - __uint_as_float(h01 << 16), p1 - __uint_as_float(h01 & 0xFFFF0000u));
+    }
   }
   if (!has_query) return;
   // tails: running prefix from the sum of the slices before this one
@@ -106,18 +114,18 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
 }
 
 hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const float* k_scale,
-                       float* pooled, float* tail, hipStream_t st) {
+                       float* pooled, float* tail, uint16_t* split, hipStream_t st) {
   const int64_t N = s.n_keys;
   const int B = s.block;
   const int64_t n_blk_total = (N + B - 1) / B;
   const int64_t n_full = N / B;
   dim3 grid((unsigned)n_blk_total, (unsigned)s.n_seq);
   if (kdtype == MISA_K_BF16)
-    hipLaunchKernelGGL(k_pool<MISA_K_BF16>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail, N,
-                       s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
+    hipLaunchKernelGGL(k_pool<MISA_K_BF16>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
+                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
   else
     hipLaunchKernelGGL(k_pool<MISA_K_FP8_E4M3>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
-                       N, s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
+                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
   return hipGetLastError();
 }
 

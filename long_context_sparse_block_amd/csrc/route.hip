@@ -34,15 +34,15 @@ constexpr int kRowBytes = kD * 2;           // bf16 LDS row (256 bytes), 16-byte
 // byte offset of 16-byte chunk c of staged row j
 __device__ __forceinline__ uint32_t rt_off(int j, int c) { return (uint32_t)j * kRowBytes + (uint32_t)((c ^ (j & 15)) << 4); }
 
-// two fp32 -> packed bf16 (element 0 in the low half), round to nearest even
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2_t));
-}
 
-template <int NHC>  // 16-head chunks per query group (= ceil(H/16))
+// NHC: 16-head chunks per query group (= ceil(H/16)).  PRESPLIT: the pooled
+// keys' bf16 hi and lo rows come precomputed (`split`: hi rows of every
+// sequence, then lo rows; the pooling kernel writes them with the same
+// conversion) and are staged by direct global -> LDS loads.
+template <int NHC, bool PRESPLIT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
                                                const float* __restrict__ pooled,
+                                               const uint16_t* __restrict__ split,
                                                const float* __restrict__ tail,
                                                int32_t* __restrict__ heads, float* __restrict__ scores,
                                                int64_t q_pos0, int M, int H, int B, int h,
@@ -100,6 +100,26 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   const float* pool_b = pooled + (int64_t)b * n_full_total * kD;
   for (int64_t cbase = 0; cbase < nfull_wg; cbase += kRouteChunk) {
     // stage pooled rows [cbase, cbase+64) as bf16 hi/lo
+    if (PRESPLIT) {
+      // load u of the 32 (16 of hi rows, 16 of lo rows) fills rows r0 .. r0+3:
+      // lane l writes slot l % 16 of row r0 + l / 16, i.e. chunk
+      // (l % 16) ^ (row % 16) of that row (the rt_off layout)
+      typedef __attribute__((address_space(3))) void* lds_ptr;
+      const int64_t nrows = min((int64_t)kRouteChunk, nfull_wg - cbase);
+      const uint16_t* hb = split + ((int64_t)b * n_full_total + cbase) * kD;
+      const int64_t lo_off = (int64_t)gridDim.y * n_full_total * kD;
+      const __amdgpu_buffer_rsrc_t rh = uniform_rsrc(hb, (uint32_t)nrows * kRowBytes);
+      const __amdgpu_buffer_rsrc_t rl = uniform_rsrc(hb + lo_off, (uint32_t)nrows * kRowBytes);
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      for (int u = wv; u < 2 * (kRouteChunk / 4); u += NW) {
+        const int part = u / (kRouteChunk / 4), r0 = (u % (kRouteChunk / 4)) * 4;
+        const int j = r0 + (lane >> 4);
+        const int c = (lane & 15) ^ (j & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(part ? rl : rh, (lds_ptr)((part ? s_lo : s_hi) + r0 * kRowBytes), 16,
+                                                 (uint32_t)(j * kRowBytes + c * 16), 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
     constexpr int kTotal = kRouteChunk * (kD / 4);                 // float4 of a chunk
     constexpr int kPer = (kTotal + NW * 64 - 1) / (NW * 64);       // per thread (3 waves: ragged)
     constexpr int kBatch = NW == 4 ? 4 : 2;   // loads in flight per batch (3 waves: ragged, fewer registers)
@@ -127,6 +147,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
         *reinterpret_cast<uint2*>(&s_hi[o]) = make_uint2(h01, h23);
         *reinterpret_cast<uint2*>(&s_lo[o]) = make_uint2(l01, l23);
       }
+    }
     }
     __syncthreads();
 #pragma unroll
@@ -235,7 +256,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 }
 
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
-                        const float* tail, int h, int32_t* heads, float* scores, hipStream_t st) {
+                        const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
+                        hipStream_t st) {
   const int H = s.n_heads;
   const int nhc = (H + 15) / 16;
   const int qg = (nhc == 1) ? 4 : (nhc == 2 ? 2 : 1);
@@ -243,9 +265,13 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
   const int64_t n_full_total = s.n_keys / s.block;
   dim3 grid((unsigned)((s.q_per_seq + qwg - 1) / qwg), (unsigned)s.n_seq);
   dim3 block((unsigned)(64 * nhc * qg));
-#define MISA_ROUTE_LAUNCH(NHC_)                                                                   \
-  hipLaunchKernelGGL(k_route<NHC_>, grid, block, 0, st, q, w, pooled, tail, heads, scores, s.q_pos0, \
-                     s.q_per_seq, H, s.block, h, n_full_total)
+#define MISA_ROUTE_LAUNCH(NHC_)                                                                          \
+  if (split != nullptr)                                                                                   \
+    hipLaunchKernelGGL((k_route<NHC_, true>), grid, block, 0, st, q, w, pooled, split, tail, heads, scores, \
+                       s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total);                              \
+  else                                                                                                    \
+    hipLaunchKernelGGL((k_route<NHC_, false>), grid, block, 0, st, q, w, pooled, split, tail, heads,      \
+                       scores, s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total)
   switch (nhc) {
     case 1: MISA_ROUTE_LAUNCH(1); break;
     case 2: MISA_ROUTE_LAUNCH(2); break;
