@@ -277,16 +277,18 @@ __device__ __forceinline__ void bitonic_write(uint64_t* buf, uint32_t cnt, int k
 // Order the first cnt (<= CAP/2) raw entries of buf by composite and write the
 // top k of them, then the padding.  Counting sort into 2048 buckets of the
 // composite span (stored in buf[CAP/2 ...]), then each candidate's rank inside
-// its bucket by direct comparison.
+// its bucket by direct comparison (skipped for buckets that start at or past
+// rank k).  have_mm: the caller already holds the composites' min and max.
 template <int CAP, int NT>
 __device__ __forceinline__ void rank_write(uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out, float* val_out,
-                           uint32_t* s_hist, uint32_t* s_wave, uint64_t* s_red) {
+                           uint32_t* s_hist, uint32_t* s_wave, uint64_t* s_red, bool have_mm = false,
+                           uint64_t mm_lo = 0, uint64_t mm_hi = 0) {
   const int tid = threadIdx.x;
   constexpr int BPT = kHistBins / NT;
   uint64_t* sorted = buf + CAP / 2;
   if (cnt > 0) {
-    uint64_t cmin, cmax;
-    block_minmax<NT>(buf, cnt, s_red, &cmin, &cmax);
+    uint64_t cmin = mm_lo, cmax = mm_hi;
+    if (!have_mm) block_minmax<NT>(buf, cnt, s_red, &cmin, &cmax);
     const int nb = bit_width64(cmax - cmin);
     const int shift = nb > kDigit ? nb - kDigit : 0;
     for (int e = tid; e < kHistBins; e += NT) s_hist[e] = 0;
@@ -329,6 +331,7 @@ __device__ __forceinline__ void rank_write(uint64_t* buf, uint32_t cnt, int k, i
         const uint64_t c = sorted[e];
         const uint32_t d = (uint32_t)((c - cmin) >> shift);
         const uint32_t b0 = (d + 1 < (uint32_t)kHistBins) ? s_hist[d + 1] : 0;
+        if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
         const uint32_t b1 = s_hist[d];
         uint32_t r = b0;
         for (uint32_t q = b0; q < b1; ++q) r += sorted[q] > c;
@@ -746,10 +749,11 @@ __global__ void __launch_bounds__(NT) k_topk_filter(const float* __restrict__ lo
 // sh.buf, written to the row's outputs.
 template <int CAP, int NT>
 __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
-                                            int32_t* __restrict__ idx_out, float* __restrict__ val_out, int sorted) {
+                                            int32_t* __restrict__ idx_out, float* __restrict__ val_out, int sorted,
+                                            bool have_mm = false, uint64_t mm_lo = 0, uint64_t mm_hi = 0) {
   const int tid = threadIdx.x;
   if (sorted && cnt <= (uint32_t)(CAP / 2)) {   // rank every candidate; ranks >= k are not written
-    rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
+    rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red, have_mm, mm_lo, mm_hi);
     return;
   }
   const uint32_t kk = min((uint32_t)k, cnt);
@@ -944,9 +948,11 @@ __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, i
     if (tid == 0) flag[row] = 1;
     return;
   }
-  // every group of every region, flat: U groups per thread loaded together
-  constexpr int U = 4;
+  // every group of every region, flat: U groups per thread loaded together;
+  // the min and max composite kept are tracked for the rank
+  constexpr int U = 8;
   const uint32_t total = s_start[n_splits];
+  uint64_t mm_lo = ~0ull, mm_hi = 0;
   for (uint32_t e0 = 0; e0 < total; e0 += U * NT) {
     f32x4 v[U];
     int32_t key[U];
@@ -986,10 +992,24 @@ __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, i
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (f[j]) {
-          if (pos < (uint32_t)CAP) sh.buf[pos] = pack_raw(v[u][j], key[u] + j);
+          const uint64_t raw = pack_raw(v[u][j], key[u] + j);
+          const uint64_t c = raw_to_comp(raw);
+          mm_lo = c < mm_lo ? c : mm_lo;
+          mm_hi = c > mm_hi ? c : mm_hi;
+          if (pos < (uint32_t)CAP) sh.buf[pos] = raw;
           ++pos;
         }
     }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t a = shfl_xor_u64(mm_lo, o), b2 = shfl_xor_u64(mm_hi, o);
+    mm_lo = a < mm_lo ? a : mm_lo;
+    mm_hi = b2 > mm_hi ? b2 : mm_hi;
+  }
+  if (lane == 0) {
+    sh.red[2 * (tid >> 6)] = mm_lo;
+    sh.red[2 * (tid >> 6) + 1] = mm_hi;
   }
   __syncthreads();
   const uint32_t tot = sh.count;
@@ -997,7 +1017,15 @@ __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, i
     if (tid == 0) flag[row] = 1;
     return;
   }
-  finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted);
+  mm_lo = ~0ull;
+  mm_hi = 0;
+#pragma unroll
+  for (int wv = 0; wv < NT / 64; ++wv) {
+    mm_lo = sh.red[2 * wv] < mm_lo ? sh.red[2 * wv] : mm_lo;
+    mm_hi = sh.red[2 * wv + 1] > mm_hi ? sh.red[2 * wv + 1] : mm_hi;
+  }
+  __syncthreads();   // sh.red is reused by the select
+  finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, true, mm_lo, mm_hi);
 }
 
 // Whole-row top-k of the flagged rows from full logits; a fixed grid walks
