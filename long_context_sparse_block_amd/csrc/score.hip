@@ -770,7 +770,9 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   p.kstride = (int)std::max<int64_t>(32, (N + 4095) / 4096);   // <= 4096 sampled keys per row
   p.n_sample = (N + p.kstride - 1) / p.kstride;
   p.ld_sample = (p.n_sample + 3) / 4 * 4;
-  p.cap_list = k <= 4096 ? 8192 : 16384;               // the list select kernel's buffer
+  // the region select's list capacity (its LDS variant: 4096 in the compact
+  // one that fits three workgroups per CU)
+  p.cap_list = k <= 2048 ? 4096 : (k <= 4096 ? 8192 : 16384);
   p.target = std::min(3 * k / 2, (k + p.cap_list) / 2);
   int nks;
   int64_t KR;

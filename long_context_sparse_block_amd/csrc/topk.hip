@@ -41,6 +41,8 @@
 // buffering and compaction work is done.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "misa_common.h"
 #include "misa_launch.h"
 
@@ -358,6 +360,88 @@ struct TopkShared {
   uint32_t sel[3];
   uint32_t count;
 };
+
+// LDS of the region select for lists of up to CAP candidates: the candidates
+// and their order by bucket as 16-bit indices (instead of a second copy of
+// the composites), so three 512-thread workgroups fit per CU.
+template <int CAP, int NT>
+struct TopkSharedIdx {
+  static_assert(CAP <= 65536, "16-bit indices");
+  uint64_t buf[CAP];
+  uint16_t order[CAP];
+  uint32_t hist[kHistBins];
+  uint32_t wave[NT / 64];
+  uint64_t red[2 * (NT / 64)];
+  uint32_t sel[3];
+  uint32_t count;
+};
+
+// rank_write over all cnt (<= CAP) raw entries of sh.buf, given their min and
+// max composite: the counting sort scatters indices into sh.order, and each
+// candidate's rank inside its bucket is found by comparing through them.
+template <int CAP, int NT>
+__device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
+                                               int32_t* idx_out, float* val_out, uint64_t cmin, uint64_t cmax) {
+  static_assert(CAP <= 8 * NT, "the bitonic fallback holds 8 entries per thread");
+  const int tid = threadIdx.x;
+  constexpr int BPT = kHistBins / NT;
+  if (cnt > 0) {
+    const int nb = bit_width64(cmax - cmin);
+    const int shift = nb > kDigit ? nb - kDigit : 0;
+    for (int e = tid; e < kHistBins; e += NT) sh.hist[e] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < cnt; e += NT)
+      atomicAdd(&sh.hist[(uint32_t)((raw_to_comp(sh.buf[e]) - cmin) >> shift)], 1u);
+    __syncthreads();
+    // bucket starts, highest bucket first: thread owns buckets 2047-BPT*tid-u
+    uint32_t hv[BPT], ls = 0, big = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      hv[u] = sh.hist[kHistBins - 1 - (BPT * tid + u)];
+      ls += hv[u];
+      big = hv[u] > big ? hv[u] : big;
+    }
+    uint32_t total;
+    uint32_t start = block_exclusive_scan<NT>(ls, sh.wave, &total);
+    const uint32_t n_big = __syncthreads_or(big > kMaxRankBucket);
+    if (n_big) {
+      if (cnt <= (uint32_t)NT) bitonic_write<NT, 1>(sh.buf, cnt, k, row, idx_out, val_out);
+      else if (cnt <= 2u * NT) bitonic_write<NT, 2>(sh.buf, cnt, k, row, idx_out, val_out);
+      else if (cnt <= 4u * NT) bitonic_write<NT, 4>(sh.buf, cnt, k, row, idx_out, val_out);
+      else bitonic_write<NT, 8>(sh.buf, cnt, k, row, idx_out, val_out);
+    } else {
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        sh.hist[kHistBins - 1 - (BPT * tid + u)] = start;   // cursor = bucket start
+        start += hv[u];
+      }
+      __syncthreads();
+      for (uint32_t e = tid; e < cnt; e += NT) {
+        const uint32_t d = (uint32_t)((raw_to_comp(sh.buf[e]) - cmin) >> shift);
+        sh.order[atomicAdd(&sh.hist[d], 1u)] = (uint16_t)e;
+      }
+      __syncthreads();
+      // sh.hist[d] is now the end of bucket d; bucket d spans [end(d+1), end(d))
+      for (uint32_t e = tid; e < cnt; e += NT) {
+        const uint64_t c = raw_to_comp(sh.buf[sh.order[e]]);
+        const uint32_t d = (uint32_t)((c - cmin) >> shift);
+        const uint32_t b0 = (d + 1 < (uint32_t)kHistBins) ? sh.hist[d + 1] : 0;
+        if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
+        const uint32_t b1 = sh.hist[d];
+        uint32_t r = b0;
+        for (uint32_t q = b0; q < b1; ++q) r += raw_to_comp(sh.buf[sh.order[q]]) > c;
+        if (r < (uint32_t)k) {
+          idx_out[row * k + r] = comp_id(c);
+          if (val_out) val_out[row * k + r] = comp_val(c);
+        }
+      }
+    }
+  }
+  for (uint32_t p = cnt + tid; p < (uint32_t)k; p += NT) {
+    idx_out[row * k + p] = -1;
+    if (val_out) val_out[row * k + p] = -__builtin_inff();
+  }
+}
 
 template <int CAP, int NT>
 __device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, int i, int b, const float* __restrict__ logits,
@@ -779,6 +863,35 @@ __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cn
   rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
 }
 
+// finish_list for the compact LDS: sorted output ranks every candidate;
+// the set alone is an exact select to k and a compaction.
+template <int CAP, int NT>
+__device__ __forceinline__ void finish_list_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
+                                                int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                                                int sorted, uint64_t mm_lo, uint64_t mm_hi) {
+  const int tid = threadIdx.x;
+  if (sorted) {
+    rank_write_idx<CAP, NT>(sh, cnt, k, row, idx_out, val_out, mm_lo, mm_hi);
+    return;
+  }
+  const uint32_t kk = min((uint32_t)k, cnt);
+  if (cnt > kk) {
+    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red);
+    cnt = compact<NT>(sh.buf, cnt, Tk, sh.wave);
+  }
+  for (int e = tid; e < k; e += NT) {
+    int32_t id = -1;
+    float v = -__builtin_inff();
+    if ((uint32_t)e < cnt) {
+      const uint64_t cc = raw_to_comp(sh.buf[e]);
+      id = comp_id(cc);
+      v = comp_val(cc);
+    }
+    idx_out[row * k + e] = id;
+    if (val_out) val_out[row * k + e] = v;
+  }
+}
+
 // Exact top-k of a row's candidate list (every element at or above the row's
 // threshold).  A row whose list overflowed or came up short of k is done by
 // the whole-row path instead, in the same workgroup, so the result is exact
@@ -905,15 +1018,15 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const 
 // threshold (clamped finite, as the scoring pass used it) are kept.  A row
 // with an overflowed region, more candidates than the buffer holds, or fewer
 // than k is flagged (and left for the re-scoring path).
-template <int CAP, int NT>
-__global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, int64_t q_pos0, int M, int n_splits,
+template <int CAP, int NT, bool IDX>
+__global__ void __launch_bounds__(NT, IDX ? 3 : 2) k_topk_regions(int64_t n_keys, int k, int64_t q_pos0, int M, int n_splits,
                                                         int cap_region, int cap_list, const float* __restrict__ thr,
                                                         const f32x4* __restrict__ gvals,
                                                         const int32_t* __restrict__ gkeys,
                                                         const uint32_t* __restrict__ rcount,
                                                         uint32_t* __restrict__ flag, int32_t* __restrict__ idx_out,
                                                         float* __restrict__ val_out, int sorted) {
-  __shared__ TopkShared<CAP, NT> sh;
+  __shared__ std::conditional_t<IDX, TopkSharedIdx<CAP, NT>, TopkShared<CAP, NT>> sh;
   __shared__ uint32_t s_start[kMaxRegionSplits + 1];   // first flat group of each region
   __shared__ uint32_t s_bad;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1025,7 +1138,10 @@ __global__ void __launch_bounds__(NT, 2) k_topk_regions(int64_t n_keys, int k, i
     mm_hi = sh.red[2 * wv + 1] > mm_hi ? sh.red[2 * wv + 1] : mm_hi;
   }
   __syncthreads();   // sh.red is reused by the select
-  finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, true, mm_lo, mm_hi);
+  if constexpr (IDX)
+    finish_list_idx<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, mm_lo, mm_hi);
+  else
+    finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, true, mm_lo, mm_hi);
 }
 
 // Whole-row top-k of the flagged rows from full logits; a fixed grid walks
@@ -1059,14 +1175,17 @@ hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, c
                                int32_t* idx, float* vals, bool sorted, hipStream_t st) {
   dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
   const f32x4* gv = reinterpret_cast<const f32x4*>(gvals);
-  if (k <= 4096)
-    hipLaunchKernelGGL((k_topk_regions<8192, 512>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0, s.q_per_seq,
-                       p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, vals,
-                       (int)sorted);
+#define MISA_REGIONS_LAUNCH(CAP_, IDX_)                                                                      \
+  hipLaunchKernelGGL((k_topk_regions<CAP_, 512, IDX_>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0,       \
+                     s.q_per_seq, p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, \
+                     vals, (int)sorted)
+  if (p.cap_list <= 4096)
+    MISA_REGIONS_LAUNCH(4096, true);
+  else if (p.cap_list <= 8192)
+    MISA_REGIONS_LAUNCH(8192, false);
   else
-    hipLaunchKernelGGL((k_topk_regions<16384, 512>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0, s.q_per_seq,
-                       p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, vals,
-                       (int)sorted);
+    MISA_REGIONS_LAUNCH(16384, false);
+#undef MISA_REGIONS_LAUNCH
   return hipGetLastError();
 }
 
