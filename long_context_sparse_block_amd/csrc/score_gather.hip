@@ -8,10 +8,11 @@
 //   D[t,c] = sum_{j<H} w[t,j] * ReLU(q[t,j] . k[cand[t,c]]) * sigma[cand[t,c]]
 //
 // Each query has its own candidate keys, so nothing is shared across queries:
-// one wave owns one query and a run of its candidates.  Its 64 head rows stay
-// in registers as four 16x16x32 MFMA row blocks (row r = head 16*grp + r);
-// candidate keys are gathered straight from memory (K is small enough to stay
-// in the last-level cache) as the B operand.  The D layout gives lane group
+// one wave owns one query and a run of 512 of its candidates.  Its 64 head
+// rows stay in registers as four 16x16x32 MFMA row blocks (row r = head
+// 16*grp + r); candidate keys are gathered straight from memory (K is small
+// enough to stay in the last-level cache) as the B operand, one 16-candidate
+// group ahead of the one being scored, with the run's ids read once into LDS.  The D layout gives lane group
 // g = l/16 the head quad g of each 16-head group, so the quad partials are
 // lane-local and the group sum (P0+P1)+(P2+P3) is two butterfly adds across
 // lane groups.  The summation order is the one of k_score_c16, so every D is
@@ -21,7 +22,13 @@
 
 namespace misa {
 
-constexpr int kGatherCands = 256;  // candidates per wave
+constexpr int kGatherCands = 512;  // candidates per wave
+
+// A run's 16-candidate group as loaded (codes or bf16 bits; fp8 uses x, y)
+struct GatherRaw {
+  uint4 r[kKSteps];
+  float sc;
+};
 
 template <int KDT>
 __global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict__ q,
@@ -31,6 +38,7 @@ __global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict
                                                       const int32_t* __restrict__ cand, int n_cand,
                                                       float* __restrict__ logits, int64_t ld, int64_t N,
                                                       int M, int H, int chunks_per_query) {
+  __shared__ int32_t s_id[4][kGatherCands];   // each wave's candidate ids
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, p16 = lane & 15;
   const int b = blockIdx.y;
@@ -43,6 +51,14 @@ __global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict
   if (c_begin >= c_end) return;
   const int64_t row = (int64_t)b * M + qi;
   const int n_grp = (H + 15) / 16;
+
+  // the run's ids, once (a wave's own LDS writes and reads happen in order)
+  const int32_t* crow = cand + row * (int64_t)n_cand;
+  int32_t* sid = s_id[wave];
+  for (int e = lane; e < kGatherCands; e += 64) {
+    const int c = c_begin + e;
+    sid[e] = (c < c_end) ? crow[c] : -1;
+  }
 
   // A: row block grp, row r -> head 16*grp + r
   bf16x8 afr[4][kKSteps];
@@ -61,30 +77,50 @@ __global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict
     }
   }
 
-  const int32_t* crow = cand + row * (int64_t)n_cand;
-  const float ninf = -__builtin_inff();
-  for (int c0 = c_begin; c0 < c_end; c0 += 16) {
-    const int c = c0 + p16;
-    const int id = (c < c_end) ? crow[c] : -1;
-    // ids are a documented precondition (in [0, t]); clamp so a bad one cannot fault
+  // group it's key rows: ids are a documented precondition (in [0, t]);
+  // clamped so a bad one cannot fault.  Loads are unconditional, so waiting
+  // for one group never waits for the next group's loads.
+  auto load_group = [&](int it, GatherRaw& o) {
+    const int id = sid[16 * it + p16];
     const int64_t kid = (id >= 0) ? (id < N ? id : N - 1) : 0;
-    bf16x8 bfr[kKSteps];
-    float sc = 1.f;
     if (KDT == MISA_K_BF16) {
       const uint4* kr = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(kptr) +
                                                        ((int64_t)b * N + kid) * kD);
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) bfr[ks] = as_bf16x8(kr[ks * 4 + g]);
+      for (int ks = 0; ks < kKSteps; ++ks) o.r[ks] = kr[ks * 4 + g];
+      o.sc = 1.f;
     } else {
       const uint2* kr = reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kptr) +
                                                        ((int64_t)b * N + kid) * kD);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         const uint2 cv = kr[ks * 4 + g];     // 8 codes: d = 32*ks + 8*g .. +7
-        const uint2 lo = e4m3x4_to_bf16x4(cv.x), hi = e4m3x4_to_bf16x4(cv.y);
+        o.r[ks] = make_uint4(cv.x, cv.y, 0u, 0u);
+      }
+      o.sc = kscale[(int64_t)b * N + kid];
+    }
+  };
+  // the run's scores through a descriptor ending at the run's end (stores of
+  // candidates past it are dropped)
+  const __amdgpu_buffer_rsrc_t orsrc = uniform_rsrc(logits + row * ld, (uint32_t)c_end * 4u);
+
+  const float ninf = -__builtin_inff();
+  const int n_it = (c_end - c_begin + 15) / 16;
+  GatherRaw cur, nxt;
+  load_group(0, cur);
+  for (int it = 0; it < n_it; ++it) {
+    load_group(min(it + 1, n_it - 1), nxt);
+    const int c = c_begin + 16 * it + p16;
+    const int id = sid[16 * it + p16];
+    bf16x8 bfr[kKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (KDT == MISA_K_BF16) {
+        bfr[ks] = as_bf16x8(cur.r[ks]);
+      } else {
+        const uint2 lo = e4m3x4_to_bf16x4(cur.r[ks].x), hi = e4m3x4_to_bf16x4(cur.r[ks].y);
         bfr[ks] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
-      sc = kscale[(int64_t)b * N + kid];
     }
     float s = 0.f;
 #pragma unroll
@@ -98,9 +134,11 @@ __global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict
       const float T = v + __shfl_xor(v, 32);       // (P0+P1)+(P2+P3)
       s = s + T;
     }
-    if (KDT == MISA_K_FP8_E4M3) s *= sc;
+    if (KDT == MISA_K_FP8_E4M3) s *= cur.sc;
     if (id < 0) s = ninf;
-    if (g == 0 && c < c_end) logits[row * ld + c] = s;
+    // the 4 lane groups hold the same score: every lane stores it
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), orsrc, (int)((uint32_t)c * 4u), 0, 0);
+    cur = nxt;
   }
 }
 
