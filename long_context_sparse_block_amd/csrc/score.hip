@@ -8,25 +8,25 @@
 // head sum.)
 //
 // Design (gfx950).  The (query, head) x key products are a dense contraction
-// on v_mfma_f32_16x16x32_bf16.  A 16-row MFMA block holds 4 queries x 4 heads
-// (row r = query r/4, head r%4 of a head quad), so the D layout hands each lane
-// all four heads of one (query, key): the ReLU / weight / head sum epilogue is
-// lane-local fp32 with no shuffles, and a lane ends with one finished logit per
-// 16-key column block.  q fragments are gathered by routed head straight from
-// HBM into registers once; K tiles of 64 (or 128) keys are staged in LDS once per
-// workgroup (fp8 codes widened to bf16 on the way in: exact), double buffered,
-// and shared by the workgroup's four waves.  Rows are padded by 16 bytes in LDS
-// so the per-lane 16-byte B reads hit distinct banks.  Workgroups are (query
-// tile x key range); the key-range split is mapped so that each XCD sweeps one
-// key range, keeping that slice of K resident in the XCD's L2.
+// on v_mfma_f32_16x16x32_bf16.  K tiles of 64 keys are staged in LDS once per
+// workgroup in a swizzled layout (fp8 codes widened to bf16 on the way in:
+// exact), double buffered, and shared by the workgroup's waves; q fragments
+// sit in registers for the whole key range.  Workgroups are (query tile x key
+// range); the key-range split is mapped so that each XCD sweeps one key range,
+// keeping that slice of K resident in the XCD's L2.
+//   k_score_h8 (h <= 8): a 16-row MFMA block holds 4 queries x 4 heads, so
+//     each lane gets all four heads of one (query, key) and the epilogue is
+//     lane-local with no shuffles.
+//   k_score_q64 (h > 8, and the dense indexer's H heads): one query per wave,
+//     all its head rows resident as 16-head row blocks.
 //
 // Summation order (fixed; every kernel that must agree bitwise uses it):
 //   quad partial  P = fma chain over the quad's 4 heads in ascending order, from 0
 //   16-head group T = (P0 + P1) + (P2 + P3)
 //   total         s = (((0 + T_0) + T_1) + ...) over 16-head groups ascending
 //   then s *= sigma (fp8).
-// k_score_c16 (h > 8, and all heads) follows it exactly; k_score_h8 (h <= 8)
-// uses s = P0 + P1 (its own order; compared to the oracle within tolerance).
+// k_score_q64 and the re-rank gather follow it exactly; k_score_h8 (h <= 8)
+// uses s = P0 + P1, which is the same value (the missing quads are exact zeros).
 #include <algorithm>
 #include <type_traits>
 
@@ -35,62 +35,9 @@
 
 namespace misa {
 
-constexpr int kKRow = kD + 8;   // bf16 elements per staged key row (272 B)
-
 // Head ids are a documented precondition (in [0, H)); clamping keeps a bad id
 // from turning into an out-of-bounds load.
 __device__ __forceinline__ int clamp_head(int j, int H) { return j < 0 ? 0 : (j >= H ? H - 1 : j); }
-
-// ---------------------------------------------------------------------------
-// K tile staging: global (bf16 or fp8) -> registers -> LDS (bf16)
-// ---------------------------------------------------------------------------
-template <int KDT, int KT, int NT>
-struct KStage {
-  // bf16: KT keys * 16 uint4 per key; fp8: KT keys * 8 uint4 per key
-  static constexpr int kVecPerKey = (KDT == MISA_K_BF16) ? 16 : 8;
-  static constexpr int kRowBytes = kVecPerKey * 16;
-  static constexpr int kPerThread = KT * kVecPerKey / NT;
-  static_assert(KT * kVecPerKey % NT == 0, "tile not divisible");
-  uint4 r[kPerThread];
-  float sc;
-
-  // Keys [key0, key0 + KT) through buffer descriptors based at the tile and
-  // bounded by N: rows past N read as zeros (their logits are never stored).
-  // The loads are unconditional and need no clamping, so waiting for this
-  // prefetch never becomes a full memory wait inside the compute it overlaps.
-  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int tid) {
-    const int rem = max(0, min(KT, N - key0));
-    const __amdgpu_buffer_rsrc_t kr =
-        uniform_rsrc(static_cast<const char*>(kbase) + (int64_t)key0 * kRowBytes, (uint32_t)(rem * kRowBytes));
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int e = tid + u * NT;   // 16-byte chunk e of the (contiguous) tile
-      r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, e * 16, 0, 0));
-    }
-    if (KDT == MISA_K_FP8_E4M3) {
-      const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + key0, (uint32_t)(rem * 4));
-      sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, (tid % KT) * 4, 0, 0));
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* s_k, float* s_sc, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int e = tid + u * NT;
-      const int key = e / kVecPerKey;
-      const int c = e % kVecPerKey;
-      if (KDT == MISA_K_BF16) {
-        *reinterpret_cast<uint4*>(&s_k[key * kKRow + c * 8]) = r[u];
-      } else {
-        uint2 a = e4m3x4_to_bf16x4(r[u].x), b2 = e4m3x4_to_bf16x4(r[u].y);
-        uint2 c2 = e4m3x4_to_bf16x4(r[u].z), d2 = e4m3x4_to_bf16x4(r[u].w);
-        *reinterpret_cast<uint4*>(&s_k[key * kKRow + c * 16]) = make_uint4(a.x, a.y, b2.x, b2.y);
-        *reinterpret_cast<uint4*>(&s_k[key * kKRow + c * 16 + 8]) = make_uint4(c2.x, c2.y, d2.x, d2.y);
-      }
-    }
-    if (KDT == MISA_K_FP8_E4M3 && tid < KT) s_sc[tid] = sc;
-  }
-};
 
 struct TileCoords {
   int qt;            // query tile
@@ -562,131 +509,140 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
 }
 
 // ---------------------------------------------------------------------------
-// General head count (h > 8, or all H heads): 4 queries per wave, one 16-head
-// group per pass (4 MFMA row blocks = 4 head quads), q fragments re-read per
-// group, running per-(query,key) sums in registers.  16 queries per
-// workgroup, 128-key tiles.  HEADS = true gathers routed heads, false = all.
+// Any head count up to 64 (routed h > 8, or the dense indexer's H heads):
+// one query per wave with every head row resident in registers, as NG row
+// blocks of 16 heads (row r of block grp = head slot 16 grp + r), so the A
+// operand is read once per query.  A workgroup is 8 waves = 8 queries over
+// one key range (NT = 512; 4 with NT = 256), with the 64-key swizzled
+// tiles of k_score_h8 (register
+// staging, fp8 widened exactly on the way in).  In the D layout lane group g
+// holds head quad g of each block, so a quad's terms are lane-local and the
+// group sum (P0+P1)+(P2+P3) is two butterfly adds; groups are added in order:
+// the canonical head order of every scoring kernel here.  After a tile each
+// lane holds 4 consecutive logits (keys 4 p16 .. +3); lane group 0 stores them.
 // ---------------------------------------------------------------------------
-template <int KDT, bool HEADS>
-__global__ void __launch_bounds__(256) k_score_c16(const uint16_t* __restrict__ q,
-                                                   const float* __restrict__ w,
-                                                   const void* __restrict__ kptr,
-                                                   const float* __restrict__ kscale,
-                                                   const int32_t* __restrict__ heads, int h,
-                                                   float* __restrict__ logits, int64_t ld, int64_t N,
-                                                   int64_t q_pos0, int M, int H, int n_qtiles,
-                                                   int n_ksplits, int64_t KR) {
-  constexpr int NT = 256, KT = 128, QT = 16, NKB = KT / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KT * kKRow];
-  __shared__ float s_sc[2][KT];
-  __shared__ int s_head[QT][64];
-  __shared__ float s_w[QT][64];
+constexpr int kQ64Threads = 256;   // 4 queries per workgroup, 3 workgroups per CU
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int KDT, bool HEADS, int NG, int NT>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 3 : 2)))
+k_score_q64(const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ kptr,
+            const float* __restrict__ kscale, const int32_t* __restrict__ heads, int h,
+            float* __restrict__ logits, int64_t ld, int64_t N64, int64_t q_pos0_64, int M, int H, int n_qtiles,
+            int n_ksplits, int64_t KR) {
+  constexpr int KT = kSwKT, QT = NT / 64;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[2 * kSwTileBytes];
+  __shared__ float s_sc[2][KT];
+
+  const int Nk = (int)N64, q_pos0 = (int)q_pos0_64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, p16 = lane & 15;
   const int b = blockIdx.y;
-  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, Nk);
+  const int k0 = (int)tc.k0, k1 = (int)tc.k1;
   const int qa = tc.qt * QT;
   const int qb = min(qa + QT, M);
-  const int64_t t_last = q_pos0 + qb - 1;
-  const int64_t kend = min(tc.k1, t_last + 1);
-  const int n_tiles = kend > tc.k0 ? (int)((kend - tc.k0 + KT - 1) / KT) : 0;
-  const int n_grp = (h + 15) / 16;
+  const int t_last = q_pos0 + qb - 1;
+  const int kend = min(k1, t_last + 1);   // keys past kend are masked for every query
+  const int n_tiles = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
 
-  // head ids and weights of the tile's queries (slot order), padded with w = 0
-  for (int e = tid; e < QT * 64; e += NT) {
-    const int ql = e / 64, sl = e % 64;
-    const int qi = qa + ql;
-    int j = 0;
-    float wj = 0.f;
-    if (qi < qb && sl < h) {
-      j = HEADS ? clamp_head(heads[((int64_t)b * M + qi) * h + sl], H) : sl;
-      wj = w[((int64_t)b * M + qi) * H + j];
+  const int qi = qa + wave;
+  const bool live = qi < qb;                      // wave-uniform
+  const int tq = live ? q_pos0 + qi : -1;
+  const int64_t row = (int64_t)b * M + min(qi, M - 1);
+
+  // A fragments and the weights of the D rows each lane holds; every load is
+  // unconditional (clamped in range) and masked afterwards
+  bf16x8 afr[NG][kKSteps];
+  float wq[NG][4];
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+    const int sl = grp * 16 + p16;
+    const bool ok = live && sl < h;
+    const int j = HEADS ? clamp_head(heads[row * h + min(sl, h - 1)], H) : min(sl, H - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(q + (row * H + j) * kD);
+    const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const uint4 v = src[ks * 4 + g];
+      afr[grp][ks] = as_bf16x8(make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep));
     }
-    s_head[ql][sl] = j;
-    s_w[ql][sl] = wj;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl2 = grp * 16 + 4 * g + i;
+      const int j2 = HEADS ? clamp_head(heads[row * h + min(sl2, h - 1)], H) : min(sl2, H - 1);
+      wq[grp][i] = w[row * H + j2] * ((live && sl2 < h) ? 1.f : 0.f);
+    }
   }
-
-  const int q0w = qa + wave * 4;
-  const int qo = q0w + g;
-  const int64_t tq = (qo < qb) ? q_pos0 + qo : -1;
-  int64_t wmax = tq;
-  for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, (int64_t)__shfl_xor((long long)wmax, o));
 
   const void* kb_ptr = (KDT == MISA_K_BF16)
-                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * N * kD)
-                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * N * kD);
-  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * N : nullptr;
+                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * Nk * kD)
+                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * Nk * kD);
+  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * Nk : nullptr;
+  const __amdgpu_buffer_rsrc_t orsrc = uniform_rsrc(logits + row * ld, live ? (uint32_t)ld * 4u : 0u);
+  uint32_t rd[kKSteps];
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) rd[ks] = sw_off(p16, 4 * ks + g);
 
-  KStage<KDT, KT, NT> stg;
-  if (n_tiles > 0) {
-    stg.load(kb_ptr, sc_ptr, (int)tc.k0, (int)N, tid);
-    stg.store(s_k[0], s_sc[0], tid);
-  }
+  KStageSw<KDT, NT> stg;
+  stg.load(kb_ptr, sc_ptr, k0, Nk, 1, tid);
+  stg.store(s_k, s_sc[0], tid);
   __builtin_amdgcn_s_waitcnt(0);   // as in k_score_h8
   __syncthreads();
   const float ninf = -__builtin_inff();
+  constexpr uint32_t kDrop = 0x80000000u;
 
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int buf = jt & 1;
-    const int64_t key0 = tc.k0 + (int64_t)jt * KT;
-    if (jt + 1 < n_tiles) stg.load(kb_ptr, sc_ptr, (int)key0 + KT, (int)N, tid);
-    if (q0w < qb) {
-      float run[NKB];
+  auto tile = [&](auto buf_tag, int key0) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const unsigned char* sk = s_k + BUF * kSwTileBytes;
+    const int kg = key0 + 4 * p16;
+    f32x4 out = {ninf, ninf, ninf, ninf};
+    if (key0 <= tq) {   // wave-uniform
+      const bool diag = key0 + KT - 1 > tq;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) run[kb] = 0.f;
-      for (int grp = 0; grp < n_grp; ++grp) {
-        // A: row block qd, row r -> query q0w + r/4, slot grp*16 + 4*qd + r%4
-        bf16x8 afr[4][kKSteps];
-        {
-          const int ql = wave * 4 + (p16 >> 2);
-          const int qi = qa + ql;
+      for (int kb = 0; kb < KT / 16; ++kb) {
+        f32x4 acc[NG];
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int sl = grp * 16 + 4 * qd + (p16 & 3);
-            const bool ok = (qi < qb) && (sl < h);
-            const int j = s_head[ql][sl & 63];
-            const uint4* src = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + (ok ? qi : 0)) * H + (ok ? j : 0)) * kD);
+        for (int grp = 0; grp < NG; ++grp) acc[grp] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) afr[qd][ks] = as_bf16x8(ok ? src[ks * 4 + g] : make_uint4(0, 0, 0, 0));
-          }
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kb * 16 * kSwRowBytes + rd[ks]));
+#pragma unroll
+          for (int grp = 0; grp < NG; ++grp) acc[grp] = mfma16(afr[grp][ks], bf, acc[grp]);
         }
-        float wq[16];
-        const int qlo = wave * 4 + g;
+        float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) wq[e] = s_w[qlo][grp * 16 + e];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          if (key0 + kb * 16 > wmax) continue;
-          bf16x8 bfr[kKSteps];
-          const uint16_t* rowp = &s_k[buf][(kb * 16 + p16) * kKRow + g * 8];
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) bfr[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + ks * 32));
-          float P[4];
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) acc = mfma16(afr[qd][ks], bfr[ks], acc);
-            P[qd] = quad_chain(acc, wq[4 * qd], wq[4 * qd + 1], wq[4 * qd + 2], wq[4 * qd + 3]);
-          }
-          const float T = (P[0] + P[1]) + (P[2] + P[3]);
-          run[kb] = run[kb] + T;
+        for (int grp = 0; grp < NG; ++grp) {
+          const float P = quad_chain(acc[grp], wq[grp][0], wq[grp][1], wq[grp][2], wq[grp][3]);
+          const float v = P + __shfl_xor(P, 16);   // P0+P1 on lane groups 0/1, P2+P3 on 2/3
+          const float T = v + __shfl_xor(v, 32);   // (P0+P1)+(P2+P3)
+          s = s + T;
         }
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int64_t kpos = key0 + kb * 16 + p16;
-        float s = run[kb];
-        if (KDT == MISA_K_FP8_E4M3) s *= s_sc[buf][kb * 16 + p16];
-        if (kpos > tq) s = ninf;
-        if (tq >= 0 && kpos < N) logits[((int64_t)b * M + qo) * ld + kpos] = s;
+        if (KDT == MISA_K_FP8_E4M3) s *= s_sc[BUF][kb * 16 + p16];
+        if (diag && kg + kb > tq) s = ninf;
+        out[kb] = s;
       }
     }
-    if (jt + 1 < n_tiles) stg.store(s_k[buf ^ 1], s_sc[buf ^ 1], tid);
+    store_f32x4(orsrc, (g == 0 && kg < Nk) ? (uint32_t)kg * 4u : kDrop, out);
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    const int key0 = k0 + jt * KT;
+    stg.load(kb_ptr, sc_ptr, key0 + KT, Nk, 1, tid);   // tile jt+1 (zeros past N)
+    tile(B0{}, key0);
+    stg.store(s_k + kSwTileBytes, s_sc[1], tid);
     __syncthreads();
+    if (jt + 1 < n_tiles) {
+      stg.load(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, 1, tid);   // tile jt+2
+      tile(B1{}, key0 + KT);
+      stg.store(s_k, s_sc[0], tid);
+      __syncthreads();
+    }
   }
-  fill_neg_inf(logits, ld, b, M, qa, qb, tc.k0 + (int64_t)n_tiles * KT, tc.k1, tid, NT);
+  // keys of this range after the last computed tile: -inf for every query
+  fill_neg_inf(logits, ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
 }
 
 // ---------------------------------------------------------------------------
@@ -735,26 +691,30 @@ hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, 
     return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
   }
   const int hh = heads ? h : H;
-  const int n_qtiles = (M + 15) / 16;
+  constexpr int kQT = kQ64Threads / 64;   // queries per workgroup
+  const int n_qtiles = (M + kQT - 1) / kQT;
   int nks;
   int64_t KR;
-  plan_split(N, s.n_seq, n_qtiles, 128, &nks, &KR);
+  plan_split(N, s.n_seq, n_qtiles, 64, &nks, &KR);
   dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
-  if (kdtype == MISA_K_BF16) {
-    if (heads)
-      hipLaunchKernelGGL((k_score_c16<MISA_K_BF16, true>), grid, dim3(256), 0, st, q, w, k, k_scale,
-                         heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
-    else
-      hipLaunchKernelGGL((k_score_c16<MISA_K_BF16, false>), grid, dim3(256), 0, st, q, w, k, k_scale,
-                         heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
-  } else {
-    if (heads)
-      hipLaunchKernelGGL((k_score_c16<MISA_K_FP8_E4M3, true>), grid, dim3(256), 0, st, q, w, k,
-                         k_scale, heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
-    else
-      hipLaunchKernelGGL((k_score_c16<MISA_K_FP8_E4M3, false>), grid, dim3(256), 0, st, q, w, k,
-                         k_scale, heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR);
+  const int ng = (hh + 15) / 16;
+#define MISA_Q64(KDT_, HEADS_, NG_)                                                                          \
+  hipLaunchKernelGGL((k_score_q64<KDT_, HEADS_, NG_, kQ64Threads>), grid, dim3(kQ64Threads), 0, st, q, w, k,  \
+                     k_scale, heads, hh, logits, ld, N, s.q_pos0, M, H, n_qtiles, nks, KR)
+#define MISA_Q64_NG(KDT_, HEADS_)   \
+  switch (ng) {                     \
+    case 1: MISA_Q64(KDT_, HEADS_, 1); break; \
+    case 2: MISA_Q64(KDT_, HEADS_, 2); break; \
+    case 3: MISA_Q64(KDT_, HEADS_, 3); break; \
+    default: MISA_Q64(KDT_, HEADS_, 4); break; \
   }
+  if (kdtype == MISA_K_BF16) {
+    if (heads) { MISA_Q64_NG(MISA_K_BF16, true) } else { MISA_Q64_NG(MISA_K_BF16, false) }
+  } else {
+    if (heads) { MISA_Q64_NG(MISA_K_FP8_E4M3, true) } else { MISA_Q64_NG(MISA_K_FP8_E4M3, false) }
+  }
+#undef MISA_Q64_NG
+#undef MISA_Q64
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@
 // group ahead of the one being scored, with the run's ids read once into LDS.  The D layout gives lane group
 // g = l/16 the head quad g of each 16-head group, so the quad partials are
 // lane-local and the group sum (P0+P1)+(P2+P3) is two butterfly adds across
-// lane groups.  The summation order is the one of k_score_c16, so every D is
+// lane groups.  The summation order is the one of k_score_q64, so every D is
 // bitwise equal to the all-keys dense logit of the same (query, token).
 #include "misa_common.h"
 #include "misa_launch.h"
