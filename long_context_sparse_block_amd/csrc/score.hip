@@ -28,6 +28,7 @@
 // k_score_q64 and the re-rank gather follow it exactly; k_score_h8 (h <= 8)
 // uses s = P0 + P1, which is the same value (the missing quads are exact zeros).
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "misa_common.h"
@@ -733,7 +734,11 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   // the region select's list capacity (its LDS variant: 4096 in the compact
   // one that fits three workgroups per CU)
   p.cap_list = k <= 2048 ? 4096 : (k <= 4096 ? 8192 : 16384);
-  p.target = std::min(3 * k / 2, (k + p.cap_list) / 2);
+  // candidates aimed for: k plus a margin of 4 standard deviations of the
+  // sampled threshold's error (about k / kstride sampled keys lie above it,
+  // relative spread 1/sqrt of that), at most k/2
+  const double margin = std::min(0.5, 4.0 / std::sqrt(std::max(1.0, (double)k / p.kstride)));
+  p.target = std::min((int)(k * (1.0 + margin)), (k + p.cap_list) / 2);
   int nks;
   int64_t KR;
   plan_split(N, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);

@@ -375,6 +375,24 @@ def test_fused_indexer_equals_stages_and_oracle(case):
     assert np.mean(recs) >= 0.999, np.mean(recs)
 
 
+@pytest.mark.parametrize("topk", [3000, 6000])
+def test_fused_selection_larger_k_equals_logits_topk(topk):
+    """k above 2048 takes the region selects with 8192- and 16384-candidate
+    lists (the MISA-dagger candidate pass uses the latter): sorted result
+    bitwise equal to logits + top-k, unsorted the same set, and each row's
+    set checked against the oracle's top-k of the same logits."""
+    say("fused selection, k =", topk)
+    cfg = gen.small_config(name=f"fused_k{topk}", m=40, n=40000, hh=16, b=64, h=8, k=topk,
+                           kdtype=gen.KDTYPE_FP8, seed=45)
+    inp = gen.generate(cfg)
+    st = run_stages(inp)
+    _check_sparse_head_topk(inp, st)
+    fi, fv = lcsb.misa_sparse_head_topk(st["sh"], st["t"]["q"], st["t"]["w"], st["t"]["k"], st["heads"], topk,
+                                        k_scale=st["t"]["k_scale"])
+    torch.cuda.synchronize()
+    check_topk_exact(inp, st["logits"], topk, fi, fv)
+
+
 def test_fused_indexer_rows_the_sample_misjudges():
     """Every sampled key position (multiples of the sampling stride, 32 here)
     gets a huge score, so the sampled threshold admits far fewer than k
