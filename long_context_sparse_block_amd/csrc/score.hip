@@ -179,10 +179,6 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
   }
 }
 
-// s_waitcnt immediate: wait until at most n vector-memory operations of the
-// wave are outstanding (the export and LDS/scalar counters are not waited on)
-constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
-
 // Four consecutive logits through a uniform_rsrc descriptor (offsets past its
 // size are dropped).  The store takes raw 32-bit patterns.
 __device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
