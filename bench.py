@@ -174,8 +174,9 @@ def main():
         per = {}
         for j, (name, _) in enumerate(stages):
             per[name] = float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(steps)]))
-        step_ev = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
-        return per, step_ev, wall
+        samples = [evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]
+        run_timed.samples = samples   # per-step ms of the last call
+        return per, float(np.mean(samples)), wall
 
     misa_stages = [
         ("pool", lambda: lcsb.misa_pool_keys(sh, k, ks, pooled=pooled, tail=tail)),
@@ -189,8 +190,23 @@ def main():
     _, step_ms, wall_ms = run_timed([("indexer", lambda: lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks, idx=idx,
                                                                            vals=vals, ws=ix_ws))],
                                     args.steps, args.warmup)
+    warm_pct = [float(np.percentile(run_timed.samples, p)) for p in (10, 50, 90)]
+    # cold: a 1 GiB write before each sample evicts L2 and the 256 MB last-level cache
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(10):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks, idx=idx, vals=vals, ws=ix_ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold_pct = [float(np.percentile(cold, p)) for p in (10, 50, 90)]
     del ix_ws
-    print(f"[bench] MISA step (misa_indexer) {step_ms:.3f} ms (wall {wall_ms:.3f})", file=sys.stderr, flush=True)
+    print(f"[bench] MISA step (misa_indexer) {step_ms:.3f} ms (wall {wall_ms:.3f}); warm p10/p50/p90 "
+          f"{warm_pct}; cold (1 GiB flush before each) p10/p50/p90 {cold_pct}", file=sys.stderr, flush=True)
     # the same path as separate calls, for the time split by stage
     per, calls_ms, _ = run_timed(misa_stages, args.steps, args.warmup)
     print(f"[bench] as separate calls {calls_ms:.3f} ms {per}", file=sys.stderr, flush=True)
@@ -281,6 +297,8 @@ def main():
         "stages": stages_out,
         "step": "one misa_indexer call: pool, route, fused routed scoring + top-k",
         "separate_calls_ms": calls_ms,
+        "step_ms_p10_p50_p90": warm_pct,
+        "cold_step_ms_p10_p50_p90": cold_pct,
         "cpu_baseline": cpu,
     }
     line.update(extras)
