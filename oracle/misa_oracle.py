@@ -79,6 +79,57 @@ def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     return out
 
 
+def f32_to_e4m3fn_rne(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3fn code, round to nearest, ties to the even code.
+
+    Written from the format: below 2^-6 the step is 2^-9 (subnormals, codes
+    0..8, code 8 being the first normal 2^-6); in binade [2^E, 2^(E+1)) the
+    step is 2^(E-3) and the code is ((E+7) << 3) | (mantissa steps - 8).
+    Magnitudes past 448 (the largest finite value) saturate to it.  Every
+    operation here is exact in float64 (power-of-two scaling of a float32)
+    except the half-even rounding itself.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    a = np.abs(x)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    code = np.where(sub, np.rint(a / 2.0 ** -9).astype(np.int64), code)      # 0..8
+    _, e2 = np.frexp(np.where(sub, 1.0, a))                                 # a = f * 2^e2, f in [0.5, 1)
+    E = e2 - 1                                                              # a in [2^E, 2^(E+1))
+    steps = np.rint(np.where(sub, 8.0, a) / np.ldexp(1.0, E - 3)).astype(np.int64)   # 8..16
+    E = np.where(steps == 16, E + 1, E)
+    steps = np.where(steps == 16, 8, steps)
+    normal = ((E + 7) << 3) | (steps - 8)
+    code = np.where(sub, code, normal)
+    code = np.minimum(code, 0x7E)                                           # saturate at 448
+    return (code | sign).astype(np.uint8)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def quantize_q_e4m3(q_bits: np.ndarray):
+    """Per-row fp8 quantisation of bf16 indexer queries (rows = the last axis).
+
+    Scale s = fp32(amax / 448), amax = max |q| over the row (s = 1 for an
+    all-zero row); code = e4m3fn round-to-nearest-even of fp32(q / s), both
+    divisions correctly rounded float32 operations.  The dequantised query is
+    code * s.  Returns (codes uint8, same shape; scales float32, shape[:-1]).
+    """
+    q = bf16_bits_to_f32(q_bits)
+    amax = np.abs(q).max(axis=-1)
+    s = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0)).astype(np.float32)
+    x = (q / s[..., None]).astype(np.float32)
+    return f32_to_e4m3fn_rne(x), s
+
+
+def dequantize_q_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    return e4m3fn_to_f64(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
 def seq_keys(inp, b: int) -> np.ndarray:
     """Keys of sequence b as float64 [N, d]: bf16 widened, or fp8 decoded times scale."""
     if inp.k_scale is None:
@@ -215,12 +266,14 @@ def topk_prefix(I_row: np.ndarray, t: int, k: int):
 class SeqContext:
     """Widened inputs of one sequence plus its pooled keys."""
 
-    def __init__(self, inp, b: int):
+    def __init__(self, inp, b: int, q8: bool = False):
+        """q8: the queries as the fp8 path sees them (quantize_q_e4m3, then
+        dequantised): every step below then follows that path."""
         cfg = inp.cfg
         self.B = cfg.block
         self.q_pos0 = inp.q_pos0
         self.keys = seq_keys(inp, b)
-        self.q = seq_queries(inp, b)
+        self.q = dequantize_q_e4m3(*quantize_q_e4m3(inp.q[b])) if q8 else seq_queries(inp, b)
         self.w = seq_weights(inp, b)
         self.pooled = pool_full_blocks(self.keys, self.B)
 
