@@ -207,6 +207,38 @@ misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, co
 size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk);
 
 /*
+ * fp8 path.  The pages' indexer runs on fp8 inputs, and the GitHub issue on
+ * the vLLM kernel ("Clarification on the Figure 3 baseline and plans for an
+ * optimized vLLM MISA kernel", second question) asks for an fp8 MISA kernel
+ * that avoids widening fp8 to bf16.  These calls score with fp8 queries and
+ * fp8 keys on the fp8 matrix cores; the result is the routed score of the
+ * dequantised inputs (within the scoring tolerance: the fp8 MFMA accumulates
+ * at slightly less than fp32 precision).
+ *
+ * misa_quantize_q: per (query, head) row of 128 values,
+ *   q_scale = fp32(amax / 448), amax = max |q| over the row (1 for a zero row),
+ *   q8      = e4m3fn round-to-nearest-even of fp32(q / q_scale),
+ * both divisions correctly rounded (448 is the largest finite e4m3fn value).
+ * q: bf16 [n_seq][M][H][128] (16-byte aligned); q8: uint8 [n_seq][M][H][128]
+ * (16-byte aligned); q_scale: float [n_seq][M][H].
+ */
+misa_status misa_quantize_q(const misa_shape* shape, const uint16_t* q, uint8_t* q8, float* q_scale,
+                            void* stream);
+
+/*
+ * misa_sparse_head_logits on fp8 queries (misa_quantize_q's q8 and q_scale):
+ *   I[t,s] = sigma[s] * sum_{j in heads(t)} w[t,j] * q_scale[t,j] * ReLU(q8[t,j] . k8[s])
+ * for s <= t, -inf after (the q and key codes taken as e4m3fn values).
+ * kdtype must be MISA_K_FP8_E4M3 (MISA_ERR_UNSUPPORTED otherwise), and
+ * 1 <= h <= 8 (MISA_ERR_UNSUPPORTED above 8).  Other arguments as
+ * misa_sparse_head_logits; columns N .. roundup4(N)-1 may be set to -inf.
+ */
+misa_status misa_sparse_head_logits_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale,
+                                       const float* w, const void* k, misa_kdtype kdtype, const float* k_scale,
+                                       const int32_t* heads, int32_t h, float* logits, int64_t ld,
+                                       void* stream);
+
+/*
  * The whole indexer on the caller's stream: pool -> route -> routed scoring ->
  * top-k (k_prime == 0, MISA), or pool -> route -> routed scoring -> top-k' ->
  * all-head re-rank of the k' candidates -> top-k (k_prime >= topk, MISA-dagger;

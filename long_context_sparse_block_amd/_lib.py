@@ -28,7 +28,8 @@ MAX_TOPK = 8192
 
 EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_sparse_head_logits",
             "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_sparse_head_topk",
-            "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes")
+            "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes",
+            "misa_quantize_q", "misa_sparse_head_logits_q8")
 
 
 class MisaShape(ctypes.Structure):
@@ -68,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_topk": [S, P, i64, P, i32, i32, i32, P, P, P, sz, P],
         "misa_sparse_head_topk": [S, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
+        "misa_quantize_q": [S, P, P, P, P],
+        "misa_sparse_head_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -265,6 +268,38 @@ def misa_sparse_head_topk(shape: MisaShape, q, w, k, heads, topk: int, k_scale=N
                                       _ptr(ws), int(ws.numel()), _stream(stream))
     _check(st, "misa_sparse_head_topk")
     return idx, vals
+
+
+def misa_quantize_q(shape: MisaShape, q, q8=None, q_scale=None, stream=None):
+    """Per-(query, head) fp8 queries: e4m3fn codes [n_seq, M, H, 128] (uint8) and
+    fp32 scales [n_seq, M, H]."""
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    if q8 is None:
+        q8 = torch.empty((shape.n_seq, M, H, HEAD_DIM), dtype=torch.uint8, device=q.device)
+    if q_scale is None:
+        q_scale = torch.empty((shape.n_seq, M, H), dtype=torch.float32, device=q.device)
+    st = load().misa_quantize_q(ctypes.byref(shape), _ptr(q), _ptr(q8), _ptr(q_scale), _stream(stream))
+    _check(st, "misa_quantize_q")
+    return q8, q_scale
+
+
+def misa_sparse_head_logits_q8(shape: MisaShape, q8, q_scale, w, k, heads, k_scale, logits=None, stream=None):
+    """Routed-head logits [n_seq, M, ld] from fp8 queries and fp8 keys (h <= 8)."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q8, torch.uint8, (shape.n_seq, M, H, HEAD_DIM), "q8")
+    _need(q_scale, torch.float32, (shape.n_seq, M, H), "q_scale")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    h = heads.shape[-1]
+    _need(heads, torch.int32, (shape.n_seq, M, h), "heads")
+    if logits is None:
+        logits = torch.empty((shape.n_seq, M, _ld(shape.n_keys)), dtype=torch.float32, device=q8.device)
+    st = load().misa_sparse_head_logits_q8(ctypes.byref(shape), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k), kd,
+                                           _ptr(k_scale), _ptr(heads), int(h), _ptr(logits),
+                                           int(logits.shape[-1]), _stream(stream))
+    _check(st, "misa_sparse_head_logits_q8")
+    return logits
 
 
 def misa_indexer_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:

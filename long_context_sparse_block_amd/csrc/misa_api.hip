@@ -185,6 +185,33 @@ misa_status misa_pool_keys(const misa_shape* shape, const void* k, misa_kdtype k
   return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, nullptr, (hipStream_t)stream));
 }
 
+misa_status misa_quantize_q(const misa_shape* shape, const uint16_t* q, uint8_t* q8, float* q_scale,
+                            void* stream) {
+  MISA_TRY(check_shape(shape));
+  if (q == nullptr || !aligned16(q) || q8 == nullptr || !aligned16(q8) || q_scale == nullptr)
+    return MISA_ERR_INVALID_ARG;
+  return from_hip(misa::launch_quant_q(*shape, q, q8, q_scale, (hipStream_t)stream));
+}
+
+misa_status misa_sparse_head_logits_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale,
+                                       const float* w, const void* k, misa_kdtype kdtype, const float* k_scale,
+                                       const int32_t* heads, int32_t h, float* logits, int64_t ld,
+                                       void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (kdtype != MISA_K_FP8_E4M3) return MISA_ERR_UNSUPPORTED;   // the fp8 MFMA takes fp8 on both sides
+  if (q8 == nullptr || !aligned16(q8) || q_scale == nullptr || w == nullptr || heads == nullptr ||
+      logits == nullptr || !aligned16(logits))
+    return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (h > 8) return MISA_ERR_UNSUPPORTED;
+  if (ld < shape->n_keys || ld % 4 != 0) return MISA_ERR_INVALID_ARG;
+  if (ld > kMaxLogitLd) return MISA_ERR_UNSUPPORTED;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return from_hip(misa::launch_score_q8(*shape, q8, q_scale, w, static_cast<const uint8_t*>(k), k_scale, heads, h,
+                                        logits, ld, (hipStream_t)stream));
+}
+
 misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const float* w,
                              const float* pooled, const float* tail, int32_t h, int32_t* heads,
                              float* scores, void* stream) {

@@ -21,6 +21,18 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
                         const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
                         hipStream_t st);
 
+// Key-range split of a scoring grid: n_ksplits ranges of KR keys (a multiple
+// of the tile KT), enough workgroups to fill the chip.
+void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR);
+
+// Per-(query, head) fp8 quantisation of q: q8 codes [n_seq][M][H][128] and
+// scales q_scale [n_seq][M][H].
+hipError_t launch_quant_q(const misa_shape& s, const uint16_t* q, uint8_t* q8, float* q_scale, hipStream_t st);
+// Routed-head logits from fp8 queries and fp8 keys (h <= 8).
+hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                          const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
+                          int64_t ld, hipStream_t st);
+
 // heads == nullptr: all H heads (dense DSA indexer); otherwise h routed heads per query.
 hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                         int kdtype, const float* k_scale, const int32_t* heads, int h,

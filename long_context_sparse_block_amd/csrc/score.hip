@@ -645,7 +645,7 @@ k_score_q64(const uint16_t* __restrict__ q, const float* __restrict__ w, const v
 // ---------------------------------------------------------------------------
 // Launch: pick the kernel, the key-range split and the grid.
 // ---------------------------------------------------------------------------
-static void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR) {
+void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR) {
   const int64_t n_ktiles = (N + KT - 1) / KT;
   const int64_t target = 2048;   // workgroups: several per CU on 256 CUs
   int64_t ns = (target + (int64_t)n_seq * n_qtiles - 1) / ((int64_t)n_seq * n_qtiles);

@@ -1,0 +1,233 @@
+// Routed-head token scoring with fp8 queries and fp8 keys (h <= 8).
+//
+//   I[t,s] = sum_{j in heads(t)} w[t,j] * ReLU(sq[t,j] qc[t,j] . kc[s]) * sigma[s]
+//          = sigma[s] * sum_j (w[t,j] sq[t,j]) * ReLU(qc[t,j] . kc[s])      (sq, sigma > 0)
+// with qc / sq the e4m3fn codes and scale of misa_quantize_q and kc / sigma
+// those of the fp8 key cache: the MISA scoring of item 2 of "Metodologia:
+// MISA" (gist.science summary) on the fp8 inputs the pages' indexer uses, as
+// the GitHub issue on the vLLM kernel asks (no fp8 -> bf16 widening).
+//
+// Design (gfx950): v_mfma_f32_16x16x128_f8f6f4 takes a whole 128-long dot
+// product in one instruction (lane l holds bytes 32 (l/16) .. +31 of row
+// l % 16 of A, and of column l % 16 of B).  As in k_score_h8, a 16-row block
+// is 4 queries x 4 head slots, so all heads of one (query, key) land in one
+// lane and the epilogue is lane-local; a wave owns 8 queries (2 groups x 2
+// head quads), a workgroup 32 queries, and 64-key tiles pass through LDS
+// (double buffered) in the column order of k_score_h8, so a lane ends a tile
+// with 4 consecutive logits.  The tiles are the fp8 codes themselves (128-byte
+// rows), staged by direct global -> LDS loads; chunk c (16 bytes) of row j
+// sits at slot c ^ (((j >> 1) & 1) | (j & 4)), which makes the B-fragment
+// reads (2 x 16 bytes per lane) free of bank conflicts on gfx950.  The query
+// scale is folded into the head weight.  This MFMA accumulates at slightly
+// less than fp32 precision (about 2^-14 of the sum of |products| measured),
+// well inside the scoring tolerance.
+#include <type_traits>
+
+#include "misa_common.h"
+#include "misa_launch.h"
+
+namespace misa {
+
+namespace {
+
+constexpr int kQ8KT = 64;          // keys per tile
+constexpr int kQ8Row = kD;         // bytes per fp8 key row
+constexpr int kQ8Tile = kQ8KT * kQ8Row;
+
+__device__ __forceinline__ int q8_tile_key(int j) { return (j & 15) * 4 + (j >> 4); }
+__device__ __forceinline__ int q8_swz(int j) { return ((j >> 1) & 1) | (j & 4); }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f8(const i32x8& a, const i32x8& b) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ int clamp_head8(int j, int H) { return j < 0 ? 0 : (j >= H ? H - 1 : j); }
+
+// four consecutive logits through a uniform_rsrc descriptor (offsets past its
+// size are dropped); raw 32-bit patterns
+__device__ __forceinline__ void store_f32x4_q8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
+}
+
+// tile keys [key0, key0+64) of the sequence 0, ks, 2ks, ... into LDS (rows past
+// N read as zeros); every wave also loads the tile's 64 scales (same data)
+__device__ __forceinline__ void q8_stage(const uint8_t* kbase, const float* sbase, int key0, int N, int ks,
+                                         int lane, int wave, unsigned char* s_dst, float* s_sc) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int64_t first = (int64_t)key0 * ks;
+  const int rem = (int)max((int64_t)0, min((int64_t)kQ8KT * ks, (int64_t)N - first));
+  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + first * kQ8Row, (uint32_t)rem * kQ8Row);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {   // 8 loads of 8 rows (1 KB) per tile, 2 per wave
+    const int r0 = (u * 4 + wave) * 8;
+    const int j = r0 + (lane >> 3);
+    const int c = (lane & 7) ^ q8_swz(j);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)(s_dst + r0 * kQ8Row), 16,
+                                             (uint32_t)(q8_tile_key(j) * ks) * kQ8Row + c * 16, 0, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + first, (uint32_t)rem * 4u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr)s_sc, 4, (uint32_t)(q8_tile_key(lane) * ks) * 4u, 0, 0, 0);
+}
+
+}  // namespace
+
+// logits[row][u] for key index u of the sequence 0, ks, 2ks, ...; -inf past
+// each query's prefix; columns N .. roundup4(N)-1 may be set to -inf.
+__global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
+                                                  const float* __restrict__ w, const uint8_t* __restrict__ kptr,
+                                                  const float* __restrict__ kscale,
+                                                  const int32_t* __restrict__ heads, int h,
+                                                  float* __restrict__ logits, int64_t ld, int64_t N64, int kstride,
+                                                  int64_t q_pos0_64, int M, int H, int n_qtiles, int n_ksplits,
+                                                  int64_t KR) {
+  constexpr int NT = 256, KT = kQ8KT, QT = 32;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k0[kQ8Tile], s_k1[kQ8Tile];
+  __shared__ float s_sc0[KT], s_sc1[KT];
+
+  const int Nk = (int)N64, q_pos0 = (int)q_pos0_64;
+  const int N = (Nk + kstride - 1) / kstride;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, p16 = lane & 15;
+  const int b = blockIdx.y;
+  const int64_t total = (int64_t)n_qtiles * n_ksplits;
+  const int64_t T = xcd_remap(blockIdx.x, total);
+  const int qt = (int)(T % n_qtiles);
+  const int k0 = (int)((T / n_qtiles) * KR);
+  const int k1 = (int)min((int64_t)k0 + KR, (int64_t)N);
+  const int qa = qt * QT, qb = min(qa + QT, M);
+  const int64_t qrow0 = (int64_t)b * M;
+  const int t_last = (q_pos0 + qb - 1) / kstride;
+  const int kend = min(k1, t_last + 1);
+  const int n_tiles = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
+  const int q0w = qa + wave * 8;
+  const int t_lo = (q_pos0 + q0w) / kstride;
+  const int t_hi = (q0w < qb) ? (q_pos0 + min(q0w + 8, qb) - 1) / kstride : -1;
+
+  // A fragments: block 2G+qd, row r -> query q0w + 4G + r/4, head slot 4qd + r%4;
+  // lane (g, p16) holds bytes 32g .. 32g+31 of its row
+  i32x8 afr[4];
+  float wv[2][8];
+  int tq[2];
+  __amdgpu_buffer_rsrc_t orsrc[2];
+  const uint32_t row_bytes = (uint32_t)ld * 4u;
+  const uint32_t lane_row_off = (uint32_t)g * row_bytes;
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    const int qg0 = q0w + 4 * G;
+    const int nrows = max(0, min(4, qb - qg0));
+    const int qo = qg0 + g;
+    tq[G] = (qo < qb) ? (q_pos0 + qo) / kstride : -1;
+    const int qoc = min(qo, M - 1);
+    orsrc[G] = uniform_rsrc(logits + (qrow0 + min(qg0, M - 1)) * ld, (uint32_t)nrows * row_bytes);
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int j = clamp_head8(heads[(qrow0 + qoc) * h + min(sl, h - 1)], H);
+      const int64_t r = (qrow0 + qoc) * H + j;
+      wv[G][sl] = w[r] * q_scale[r] * ((qo < qb && sl < h) ? 1.f : 0.f);
+    }
+    const int qi = qg0 + (p16 >> 2);
+    const int qic = min(qi, M - 1);
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) {
+      const int sl = 4 * qd + (p16 & 3);
+      const bool ok = (qi < qb) && (sl < h);
+      const int j = clamp_head8(heads[(qrow0 + qic) * h + min(sl, h - 1)], H);
+      const uint4* src = reinterpret_cast<const uint4*>(q8 + ((qrow0 + qic) * H + j) * kD + 32 * g);
+      const uint4 v0 = src[0], v1 = src[1];
+      const int keep = ok ? -1 : 0;
+      afr[2 * G + qd] = i32x8{(int)v0.x & keep, (int)v0.y & keep, (int)v0.z & keep, (int)v0.w & keep,
+                              (int)v1.x & keep, (int)v1.y & keep, (int)v1.z & keep, (int)v1.w & keep};
+    }
+  }
+
+  const uint8_t* kb_ptr = kptr + (int64_t)b * Nk * kD;
+  const float* sc_ptr = kscale + (int64_t)b * Nk;
+  // lane's B-fragment byte offsets inside a column block: chunks 2g, 2g+1 of row p16
+  const uint32_t rd0 = (uint32_t)p16 * kQ8Row + (uint32_t)(((2 * g) ^ q8_swz(p16)) << 4);
+  const uint32_t rd1 = (uint32_t)p16 * kQ8Row + (uint32_t)(((2 * g + 1) ^ q8_swz(p16)) << 4);
+
+  q8_stage(kb_ptr, sc_ptr, k0, Nk, kstride, lane, wave, s_k0, s_sc0);
+  __builtin_amdgcn_s_waitcnt(0);   // prologue loads (q, w, heads) and the first tile
+  __syncthreads();
+  const float ninf = -__builtin_inff();
+  constexpr uint32_t kDrop = 0x80000000u;
+
+  auto tile = [&](auto buf_tag, int key0) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const unsigned char* sk = BUF ? s_k1 : s_k0;
+    const float* ssc = BUF ? s_sc1 : s_sc0;
+    const int kg = key0 + 4 * p16;
+    f32x4 out[2];
+    if (key0 > t_hi) {
+      out[0] = f32x4{ninf, ninf, ninf, ninf};
+      out[1] = out[0];
+    } else {
+      const bool diag = key0 + KT - 1 > t_lo;
+#pragma unroll
+      for (int kb = 0; kb < KT / 16; ++kb) {
+        const uint4 b0 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd0);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd1);
+        const i32x8 bf = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        const float sc = ssc[kb * 16 + p16];
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+          const f32x4 a0 = mfma_f8(afr[2 * G], bf);
+          const f32x4 a1 = mfma_f8(afr[2 * G + 1], bf);
+          const float P0 = quad_chain(a0, wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
+          const float P1 = quad_chain(a1, wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
+          float s = (P0 + P1) * sc;
+          if (diag && kg + kb > tq[G]) s = ninf;
+          out[G][kb] = s;
+        }
+      }
+    }
+    const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
+    store_f32x4_q8(orsrc[0], off, out[0]);
+    store_f32x4_q8(orsrc[1], off, out[1]);
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    const int key0 = k0 + jt * KT;
+    q8_stage(kb_ptr, sc_ptr, key0 + KT, Nk, kstride, lane, wave, s_k1, s_sc1);   // tile jt+1
+    tile(B0{}, key0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));   // this wave's loads of tile jt+1 (the 2 stores may fly)
+    __syncthreads();
+    if (jt + 1 < n_tiles) {
+      q8_stage(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, kstride, lane, wave, s_k0, s_sc0);   // tile jt+2
+      tile(B1{}, key0 + KT);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+      __syncthreads();
+    }
+  }
+  // keys of this range after the last computed tile: -inf for every query
+  const int64_t from = k0 + (int64_t)n_tiles * KT;
+  if (from < k1) {
+    for (int qi = qa; qi < qb; ++qi) {
+      float* rowp = logits + (qrow0 + qi) * ld;
+      for (int64_t e = from + tid; e < k1; e += NT) rowp[e] = ninf;
+    }
+  }
+}
+
+hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                          const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
+                          int64_t ld, hipStream_t st) {
+  const int M = s.q_per_seq;
+  const int n_qtiles = (M + 31) / 32;
+  int nks;
+  int64_t KR;
+  plan_split(s.n_keys, s.n_seq, n_qtiles, kQ8KT, &nks, &KR);
+  dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  hipLaunchKernelGGL(k_score_q8, grid, dim3(256), 0, st, q8, q_scale, w, k, k_scale, heads, h, logits, ld,
+                     s.n_keys, 1, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+  return hipGetLastError();
+}
+
+}  // namespace misa
