@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, TFLOP/s
 METRIC = "indexer ms per chunk & G(query·key·head)/s at M=8192,N=131K; MFMA util %"
 UNIT = "G(query·key·head)/s"
 
@@ -265,6 +266,20 @@ def main():
                                / PEAK_BF16_TFLOPS,
                                misa_speedup=nstep / step_ms)
         print(f"[bench] dagger {dstep:.3f} ms {dper}; dense {nstep:.3f} ms {nper}", file=sys.stderr, flush=True)
+        if cfg.kdtype == 1:
+            # the fp8 query path: per-row quantisation, then routed scoring on the fp8 matrix cores
+            q8, qs = lcsb.misa_quantize_q(sh, q)
+            q8_stages = [
+                ("quantize_q", lambda: lcsb.misa_quantize_q(sh, q, q8=q8, q_scale=qs)),
+                ("score_q8", lambda: lcsb.misa_sparse_head_logits_q8(sh, q8, qs, w, k, heads, ks, logits=logits)),
+            ]
+            qper, qstep, _ = run_timed(q8_stages, max(3, args.steps // 2), 2)
+            extras["fp8_query_path"] = dict(
+                ms=qstep, stage_ms=qper,
+                score_q8_TFLOPs=W["score_flops"] / (qper["score_q8"] * 1e-3) / 1e12,
+                score_q8_frac_of_fp8_peak=W["score_flops"] / (qper["score_q8"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                vs_bf16_score=sper["staged_score"] / qper["score_q8"])
+            print(f"[bench] fp8 query path {qstep:.3f} ms {qper}", file=sys.stderr, flush=True)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB

@@ -73,6 +73,10 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2_t));
 }
 
+// Cache-policy operand of a buffer store: non-temporal (gfx950's nt bit), for
+// data written once and not read again while it could still be cached.
+constexpr int kStream = 2;
+
 // s_waitcnt immediate: wait until at most n vector-memory operations of the
 // wave are outstanding (the export and LDS/scalar counters are not waited on)
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }

@@ -180,10 +180,16 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
 }
 
 // Four consecutive logits through a uniform_rsrc descriptor (offsets past its
-// size are dropped).  The store takes raw 32-bit patterns.
-__device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+// size are dropped).  The store takes raw 32-bit patterns.  POLICY kStream
+// marks it non-temporal: full logits rows are far larger than L2 and the
+// last-level cache, and streaming them out keeps the key tiles, which every
+// query tile re-reads, resident in L2.
+__device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v, int policy = 0) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
+  if (policy == kStream)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, kStream);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
 }
 __device__ __forceinline__ void store_i32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, int v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)byte_off, 0, 0);
@@ -458,8 +464,10 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
     }
     if (MODE == kLogits) {
       const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
-      store_f32x4(orsrc[0], off, out[0]);
-      store_f32x4(orsrc[1], off, out[1]);
+      // full rows stream out; the sampled pass's rows are re-read at once
+      const int pol = kstride == 1 ? kStream : 0;
+      store_f32x4(orsrc[0], off, out[0], pol);
+      store_f32x4(orsrc[1], off, out[1], pol);
     } else {
       // every lane issues its stores (dropped unless the group qualifies and
       // the region has room), so the wait for the next tile's prefetch,
@@ -620,7 +628,7 @@ k_score_q64(const uint16_t* __restrict__ q, const float* __restrict__ w, const v
         out[kb] = s;
       }
     }
-    store_f32x4(orsrc, (g == 0 && kg < Nk) ? (uint32_t)kg * 4u : kDrop, out);
+    store_f32x4(orsrc, (g == 0 && kg < Nk) ? (uint32_t)kg * 4u : kDrop, out, kStream);
   };
 
   using B0 = std::integral_constant<int, 0>;

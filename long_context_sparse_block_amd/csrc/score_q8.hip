@@ -47,10 +47,11 @@ __device__ __forceinline__ f32x4 mfma_f8(const i32x8& a, const i32x8& b) {
 __device__ __forceinline__ int clamp_head8(int j, int H) { return j < 0 ? 0 : (j >= H ? H - 1 : j); }
 
 // four consecutive logits through a uniform_rsrc descriptor (offsets past its
-// size are dropped); raw 32-bit patterns
+// size are dropped); raw 32-bit patterns, non-temporal (full logits rows
+// stream out rather than evict the key tiles from L2)
 __device__ __forceinline__ void store_f32x4_q8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, kStream);
 }
 
 // tile keys [key0, key0+64) of the sequence 0, ks, 2ks, ... into LDS (rows past
