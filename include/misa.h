@@ -239,6 +239,22 @@ misa_status misa_sparse_head_logits_q8(const misa_shape* shape, const uint8_t* q
                                        void* stream);
 
 /*
+ * misa_sparse_head_topk on fp8 queries: exactly
+ * misa_topk(misa_sparse_head_logits_q8(...), topk) (ids, values and order;
+ * the set when sorted == 0), through the same fused path (logits only for
+ * the rows the candidates cannot settle).  The second question of the GitHub
+ * issue asks for an fp8 MISA kernel with the top-k overhead cut; this is it.
+ * kdtype must be MISA_K_FP8_E4M3 and 1 <= h <= 8 (MISA_ERR_UNSUPPORTED
+ * otherwise).  The workspace is misa_sparse_head_topk_workspace_bytes(shape,
+ * h, topk) bytes (16-byte aligned).  Other arguments as
+ * misa_sparse_head_topk.
+ */
+misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale,
+                                     const float* w, const void* k, misa_kdtype kdtype, const float* k_scale,
+                                     const int32_t* heads, int32_t h, int32_t topk, int32_t sorted, int32_t* idx,
+                                     float* vals, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * The whole indexer on the caller's stream: pool -> route -> routed scoring ->
  * top-k (k_prime == 0, MISA), or pool -> route -> routed scoring -> top-k' ->
  * all-head re-rank of the k' candidates -> top-k (k_prime >= topk, MISA-dagger;

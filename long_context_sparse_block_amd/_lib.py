@@ -29,7 +29,7 @@ MAX_TOPK = 8192
 EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_sparse_head_logits",
             "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_sparse_head_topk",
             "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes",
-            "misa_quantize_q", "misa_sparse_head_logits_q8")
+            "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8")
 
 
 class MisaShape(ctypes.Structure):
@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_indexer": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
         "misa_quantize_q": [S, P, P, P, P],
         "misa_sparse_head_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
+        "misa_sparse_head_topk_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -300,6 +301,31 @@ def misa_sparse_head_logits_q8(shape: MisaShape, q8, q_scale, w, k, heads, k_sca
                                            int(logits.shape[-1]), _stream(stream))
     _check(st, "misa_sparse_head_logits_q8")
     return logits
+
+
+def misa_sparse_head_topk_q8(shape: MisaShape, q8, q_scale, w, k, heads, topk: int, k_scale, sorted=True, idx=None,
+                             vals=None, want_vals=True, ws=None, stream=None):
+    """misa_sparse_head_topk on fp8 queries and fp8 keys (h <= 8): the same
+    result as misa_topk(misa_sparse_head_logits_q8(...), topk)."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q8, torch.uint8, (shape.n_seq, M, H, HEAD_DIM), "q8")
+    _need(q_scale, torch.float32, (shape.n_seq, M, H), "q_scale")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    h = heads.shape[-1]
+    _need(heads, torch.int32, (shape.n_seq, M, h), "heads")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q8.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q8.device)
+    if ws is None:
+        ws = torch.empty(max(misa_sparse_head_topk_workspace_bytes(shape, h, topk), 1), dtype=torch.uint8,
+                         device=q8.device)
+    st = load().misa_sparse_head_topk_q8(ctypes.byref(shape), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k), kd,
+                                         _ptr(k_scale), _ptr(heads), int(h), int(topk), int(bool(sorted)),
+                                         _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel()), _stream(stream))
+    _check(st, "misa_sparse_head_topk_q8")
+    return idx, vals
 
 
 def misa_indexer_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:

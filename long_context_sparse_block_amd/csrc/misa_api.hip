@@ -92,13 +92,25 @@ SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off) {
   return L;
 }
 
-// Routed scoring + exact top-k (see misa_sparse_head_topk).
+// fp8 queries (misa_quantize_q's codes and scales): the selection scores with
+// fp8 x fp8 matrix cores instead of bf16 q
+struct QuantQ {
+  const uint8_t* q8;
+  const float* q_scale;
+};
+
+// Routed scoring + exact top-k (see misa_sparse_head_topk); qq != nullptr:
+// fp8 queries and fp8 keys (misa_sparse_head_topk_q8).
 misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, const uint16_t* q, const float* w,
                        const void* k, int kdtype, const float* k_scale, const int32_t* heads, int h, int topk,
-                       bool sorted, int32_t* idx, float* vals, hipStream_t st) {
+                       bool sorted, int32_t* idx, float* vals, hipStream_t st, const QuantQ* qq = nullptr) {
   float* logits = reinterpret_cast<float*>(base + L.logits);
+  const uint8_t* k8 = static_cast<const uint8_t*>(k);
   if (!L.fused.ok) {
-    MISA_TRY(from_hip(launch_score(s, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, st)));
+    if (qq != nullptr)
+      MISA_TRY(from_hip(misa::launch_score_q8(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, logits, L.ld, st)));
+    else
+      MISA_TRY(from_hip(launch_score(s, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, st)));
     return from_hip(launch_topk(s, logits, L.ld, nullptr, (int)s.n_keys, topk, idx, vals, base + L.topk_ws,
                                 L.end - L.topk_ws, st, sorted));
   }
@@ -109,6 +121,17 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   uint32_t* rcount = reinterpret_cast<uint32_t*>(base + L.rcount);
   float* gvals = reinterpret_cast<float*>(base + L.gvals);
   int32_t* gkeys = reinterpret_cast<int32_t*>(base + L.gkeys);
+  if (qq != nullptr) {
+    MISA_TRY(from_hip(misa::launch_score_q8_sampled(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, p, sample, st)));
+    MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
+    MISA_TRY(from_hip(misa::launch_score_q8_cands(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, p, thr, gvals,
+                                                  gkeys, rcount, st)));
+    MISA_TRY(
+        from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
+    MISA_TRY(from_hip(
+        misa::launch_score_q8(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, logits, L.ld, st, flag)));
+    return from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st));
+  }
   // the scoring launches stage bf16 keys by direct loads into LDS
   const void* kb = k;
   if (kdtype == MISA_K_FP8_E4M3) {
@@ -336,6 +359,26 @@ misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, co
   if (shape->q_per_seq == 0) return MISA_OK;
   return run_select(*shape, L, static_cast<char*>(ws), q, w, k, kdtype, k_scale, heads, h, topk, sorted != 0, idx,
                     vals, (hipStream_t)stream);
+}
+
+misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale,
+                                     const float* w, const void* k, misa_kdtype kdtype, const float* k_scale,
+                                     const int32_t* heads, int32_t h, int32_t topk, int32_t sorted, int32_t* idx,
+                                     float* vals, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (kdtype != MISA_K_FP8_E4M3) return MISA_ERR_UNSUPPORTED;   // the fp8 MFMA takes fp8 on both sides
+  if (q8 == nullptr || !aligned16(q8) || q_scale == nullptr || w == nullptr || heads == nullptr || idx == nullptr)
+    return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (h > 8) return MISA_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
+  const SelectLayout L = select_layout(*shape, h, topk, 0);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < L.end) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  const QuantQ qq{q8, q_scale};
+  return run_select(*shape, L, static_cast<char*>(ws), nullptr, w, k, kdtype, k_scale, heads, h, topk, sorted != 0,
+                    idx, vals, (hipStream_t)stream, &qq);
 }
 
 size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk) {

@@ -28,10 +28,11 @@ void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int6
 // Per-(query, head) fp8 quantisation of q: q8 codes [n_seq][M][H][128] and
 // scales q_scale [n_seq][M][H].
 hipError_t launch_quant_q(const misa_shape& s, const uint16_t* q, uint8_t* q8, float* q_scale, hipStream_t st);
-// Routed-head logits from fp8 queries and fp8 keys (h <= 8).
+// Routed-head logits from fp8 queries and fp8 keys (h <= 8); row_flag: only
+// the workgroups holding a flagged row run (re-scoring after a fused pass).
 hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
                           const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
-                          int64_t ld, hipStream_t st);
+                          int64_t ld, hipStream_t st, const uint32_t* row_flag = nullptr);
 
 // heads == nullptr: all H heads (dense DSA indexer); otherwise h routed heads per query.
 hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
@@ -98,6 +99,14 @@ hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, co
 hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const float* thr,
                                const float* gvals, const int32_t* gkeys, const uint32_t* rcount, uint32_t* row_flag,
                                int32_t* idx, float* vals, bool sorted, hipStream_t st);
+// the fp8-query versions of the two scoring passes above (fp8 keys, h <= 8)
+hipError_t launch_score_q8_sampled(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                                   const uint8_t* k, const float* k_scale, const int32_t* heads, int h,
+                                   const FusedPlan& p, float* sample_logits, hipStream_t st);
+hipError_t launch_score_q8_cands(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                                 const uint8_t* k, const float* k_scale, const int32_t* heads, int h,
+                                 const FusedPlan& p, const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount,
+                                 hipStream_t st);
 // whole-row top-k of the flagged rows from full logits
 hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* logits, int64_t ld,
                                const uint32_t* row_flag, int32_t* idx, float* vals, bool sorted, hipStream_t st);

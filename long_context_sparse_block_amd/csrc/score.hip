@@ -33,44 +33,9 @@
 
 #include "misa_common.h"
 #include "misa_launch.h"
+#include "score_shared.h"
 
 namespace misa {
-
-// Head ids are a documented precondition (in [0, H)); clamping keeps a bad id
-// from turning into an out-of-bounds load.
-__device__ __forceinline__ int clamp_head(int j, int H) { return j < 0 ? 0 : (j >= H ? H - 1 : j); }
-
-struct TileCoords {
-  int qt;            // query tile
-  int64_t k0, k1;    // key range [k0, k1)
-};
-
-__device__ __forceinline__ TileCoords tile_coords(int n_qtiles, int n_ksplits, int64_t KR, int64_t N) {
-  const int64_t total = (int64_t)n_qtiles * n_ksplits;
-  const int64_t T = xcd_remap(blockIdx.x, total);
-  TileCoords c;
-  c.qt = (int)(T % n_qtiles);
-  const int64_t ks = T / n_qtiles;
-  c.k0 = ks * KR;
-  c.k1 = c.k0 + KR < N ? c.k0 + KR : N;
-  return c;
-}
-
-// -inf for keys [from, to) of queries [qa, qb) (all of them lie after every query)
-__device__ __forceinline__ void fill_neg_inf(float* logits, int64_t ld, int b, int M, int qa, int qb,
-                                             int64_t from, int64_t to, int tid, int nt) {
-  if (from >= to) return;
-  const float ninf = -__builtin_inff();
-  const int64_t span = to - from;
-  for (int qi = qa; qi < qb; ++qi) {
-    float* row = logits + ((int64_t)b * M + qi) * ld;
-    // from is a multiple of 4 (tile aligned) and ld % 4 == 0
-    const int64_t n4 = span / 4;
-    for (int64_t e = tid; e < n4; e += nt)
-      __builtin_nontemporal_store(f32x4{ninf, ninf, ninf, ninf}, reinterpret_cast<f32x4*>(row + from) + e);
-    for (int64_t e = n4 * 4 + tid; e < span; e += nt) row[from + e] = ninf;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Swizzled K tile for k_score_h8 (64 keys, bf16 rows of 256 bytes).
@@ -179,45 +144,6 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
   }
 }
 
-// Four consecutive logits through a uniform_rsrc descriptor (offsets past its
-// size are dropped).  The store takes raw 32-bit patterns.  POLICY kStream
-// marks it non-temporal: full logits rows are far larger than L2 and the
-// last-level cache, and streaming them out keeps the key tiles, which every
-// query tile re-reads, resident in L2.
-__device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v, int policy = 0) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  if (policy == kStream)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, kStream);
-  else
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
-}
-__device__ __forceinline__ void store_i32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, int v) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)byte_off, 0, 0);
-}
-
-// Where a k_score_h8 pass puts its results.
-//  MODE kLogits: logits[row][u] for key u of the scored key sequence (u ks).
-//  MODE kCands: no logits; every group of 4 consecutive keys (4c .. 4c+3)
-//    holding a score >= thr[row] (a finite threshold, so masked -inf scores
-//    never qualify) is appended to the region of that row and of the
-//    workgroup's key range, region (row * n_splits + split) of `cap` groups:
-//    its 4 scores to gvals, its first key to gkeys.  rcount[row * n_splits +
-//    split] receives the number of groups found (more than cap: the region
-//    overflowed and holds only the first cap).
-//  row_flag != nullptr: only workgroups holding a row with row_flag[row] != 0
-//    run (re-scoring of the rows a candidate pass could not settle).
-struct ScoreOut {
-  float* logits;
-  int64_t ld;
-  const float* thr;
-  f32x4* gvals;
-  int32_t* gkeys;
-  uint32_t* rcount;
-  int cap;
-  const uint32_t* row_flag;
-};
-constexpr int kLogits = 0;
-constexpr int kCands = 1;
 
 // ---------------------------------------------------------------------------
 // h <= 8: 8 queries per wave (2 groups x 2 head quads = 4 MFMA row blocks),
@@ -299,14 +225,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   const uint32_t row_bytes = (uint32_t)out_spec.ld * 4u;
   const uint32_t lane_row_off = (uint32_t)g * row_bytes;
   const int split = (int)(k0 / KR);
-  if (MODE == kCands) {
-    // regions of rows qa..qb-1 in this key range: row r's starts (r - qa) *
-    // n_ksplits * cap groups after row qa's (fits 31 bits: checked on the host)
-    const int64_t g0 = ((qrow0 + qa) * n_ksplits + split) * (int64_t)out_spec.cap;
-    const uint32_t span = (uint32_t)(((int64_t)(qb - 1 - qa) * n_ksplits + 1) * out_spec.cap);
-    orsrc[0] = uniform_rsrc(out_spec.gvals + g0, span * 16u);
-    orsrc[1] = uniform_rsrc(out_spec.gkeys + g0, span * 4u);
-  }
+  if (MODE == kCands) cand_rsrc(out_spec, qrow0, qa, qb, n_ksplits, split, orsrc);
   int hw[2][8], ha[2][2];
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
@@ -319,10 +238,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
       orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld,
                               (uint32_t)nrows * row_bytes);
     } else {
-      // finite, so masked -inf scores never qualify; +inf for lanes past the
-      // last query, whose scores belong to no row
-      thr[G] = (qo < qb) ? __builtin_fmaxf(out_spec.thr[qrow0 + qoc], -__FLT_MAX__) : __builtin_inff();
-      reg[G] = (uint32_t)(qoc - qa) * (uint32_t)n_ksplits * (uint32_t)out_spec.cap;
+      cand_lane(out_spec, qrow0, qa, qb, qo, qoc, n_ksplits, thr[G], reg[G]);
     }
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) hw[G][sl] = heads[(qrow0 + qoc) * h + min(sl, h - 1)];
@@ -391,7 +307,6 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const float ninf = -__builtin_inff();
-  constexpr uint32_t kDrop = 0x80000000u;   // a byte offset past every store resource
 
   uint32_t run[2] = {0u, 0u};   // kCands: groups found for the lane's query so far
   const uint64_t gmask = 0xFFFFull << (16 * g);
@@ -469,20 +384,10 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
       store_f32x4(orsrc[0], off, out[0], pol);
       store_f32x4(orsrc[1], off, out[1], pol);
     } else {
-      // every lane issues its stores (dropped unless the group qualifies and
-      // the region has room), so the wait for the next tile's prefetch,
-      // issued before them, is a fixed count
+      // every lane issues its stores, so the wait for the next tile's
+      // prefetch, issued before them, is a fixed count
 #pragma unroll
-      for (int G = 0; G < 2; ++G) {
-        const float vmax = __builtin_fmaxf(__builtin_fmaxf(out[G][0], out[G][1]), __builtin_fmaxf(out[G][2], out[G][3]));
-        const bool pass = vmax >= thr[G];
-        const uint64_t m = __ballot(pass) & gmask;
-        const uint32_t pos = run[G] + lanes_below(m);
-        run[G] += (uint32_t)__popcll(m);
-        const bool put = pass && pos < (uint32_t)out_spec.cap;
-        store_f32x4(orsrc[0], put ? (reg[G] + pos) * 16u : kDrop, out[G]);
-        store_i32(orsrc[1], put ? (reg[G] + pos) * 4u : kDrop, kg);
-      }
+      for (int G = 0; G < 2; ++G) append_group(orsrc, out[G], thr[G], gmask, run[G], reg[G], out_spec.cap, kg);
     }
   };
 
@@ -595,7 +500,6 @@ k_score_q64(const uint16_t* __restrict__ q, const float* __restrict__ w, const v
   __builtin_amdgcn_s_waitcnt(0);   // as in k_score_h8
   __syncthreads();
   const float ninf = -__builtin_inff();
-  constexpr uint32_t kDrop = 0x80000000u;
 
   auto tile = [&](auto buf_tag, int key0) {
     constexpr int BUF = decltype(buf_tag)::value;

@@ -25,6 +25,7 @@
 
 #include "misa_common.h"
 #include "misa_launch.h"
+#include "score_shared.h"
 
 namespace misa {
 
@@ -42,16 +43,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mfma_f8(const i32x8& a, const i32x8& b) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
-}
-
-__device__ __forceinline__ int clamp_head8(int j, int H) { return j < 0 ? 0 : (j >= H ? H - 1 : j); }
-
-// four consecutive logits through a uniform_rsrc descriptor (offsets past its
-// size are dropped); raw 32-bit patterns, non-temporal (full logits rows
-// stream out rather than evict the key tiles from L2)
-__device__ __forceinline__ void store_f32x4_q8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, kStream);
 }
 
 // tile keys [key0, key0+64) of the sequence 0, ks, 2ks, ... into LDS (rows past
@@ -76,16 +67,21 @@ __device__ __forceinline__ void q8_stage(const uint8_t* kbase, const float* sbas
 
 }  // namespace
 
-// logits[row][u] for key index u of the sequence 0, ks, 2ks, ...; -inf past
-// each query's prefix; columns N .. roundup4(N)-1 may be set to -inf.
+// One scoring pass over the key sequence 0, ks, 2ks, ... (key index u is
+// key u ks); MODE and out_spec as for k_score_h8 (score_shared.h):
+//   kLogits: logits[row][u], -inf past each query's prefix (columns N ..
+//   roundup4(N)-1 may be set to -inf); full rows (ks = 1) stream out
+//   non-temporally, sampled rows stay cacheable (they are read at once);
+//   kCands: groups of 4 consecutive scores with one at or above the row's
+//   threshold appended to the (row, key range) regions, no logits.
+template <int MODE>
 __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
                                                   const float* __restrict__ w, const uint8_t* __restrict__ kptr,
                                                   const float* __restrict__ kscale,
-                                                  const int32_t* __restrict__ heads, int h,
-                                                  float* __restrict__ logits, int64_t ld, int64_t N64, int kstride,
-                                                  int64_t q_pos0_64, int M, int H, int n_qtiles, int n_ksplits,
-                                                  int64_t KR) {
-  constexpr int NT = 256, KT = kQ8KT, QT = 32;
+                                                  const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
+                                                  int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
+                                                  int n_qtiles, int n_ksplits, int64_t KR) {
+  constexpr int KT = kQ8KT, QT = 32;
   __shared__ __attribute__((aligned(16))) unsigned char s_k0[kQ8Tile], s_k1[kQ8Tile];
   __shared__ float s_sc0[KT], s_sc1[KT];
 
@@ -95,28 +91,34 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, p16 = lane & 15;
   const int b = blockIdx.y;
-  const int64_t total = (int64_t)n_qtiles * n_ksplits;
-  const int64_t T = xcd_remap(blockIdx.x, total);
-  const int qt = (int)(T % n_qtiles);
-  const int k0 = (int)((T / n_qtiles) * KR);
-  const int k1 = (int)min((int64_t)k0 + KR, (int64_t)N);
-  const int qa = qt * QT, qb = min(qa + QT, M);
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const int k0 = (int)tc.k0, k1 = (int)tc.k1;
+  const int qa = tc.qt * QT, qb = min(qa + QT, M);
   const int64_t qrow0 = (int64_t)b * M;
+  if (out_spec.row_flag != nullptr) {
+    bool any = false;
+    for (int i = qa; i < qb; ++i) any |= out_spec.row_flag[qrow0 + i] != 0;
+    if (!any) return;   // uniform over the workgroup
+  }
   const int t_last = (q_pos0 + qb - 1) / kstride;
   const int kend = min(k1, t_last + 1);
   const int n_tiles = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
   const int q0w = qa + wave * 8;
   const int t_lo = (q_pos0 + q0w) / kstride;
   const int t_hi = (q0w < qb) ? (q_pos0 + min(q0w + 8, qb) - 1) / kstride : -1;
+  const int split = (int)(k0 / KR);
 
   // A fragments: block 2G+qd, row r -> query q0w + 4G + r/4, head slot 4qd + r%4;
   // lane (g, p16) holds bytes 32g .. 32g+31 of its row
   i32x8 afr[4];
   float wv[2][8];
   int tq[2];
-  __amdgpu_buffer_rsrc_t orsrc[2];
-  const uint32_t row_bytes = (uint32_t)ld * 4u;
+  __amdgpu_buffer_rsrc_t orsrc[2];   // kLogits: the two groups' rows; kCands: gvals, gkeys
+  float thr[2];
+  uint32_t reg[2];
+  const uint32_t row_bytes = (uint32_t)out_spec.ld * 4u;
   const uint32_t lane_row_off = (uint32_t)g * row_bytes;
+  if (MODE == kCands) cand_rsrc(out_spec, qrow0, qa, qb, n_ksplits, split, orsrc);
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
     const int qg0 = q0w + 4 * G;
@@ -124,10 +126,13 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
     const int qo = qg0 + g;
     tq[G] = (qo < qb) ? (q_pos0 + qo) / kstride : -1;
     const int qoc = min(qo, M - 1);
-    orsrc[G] = uniform_rsrc(logits + (qrow0 + min(qg0, M - 1)) * ld, (uint32_t)nrows * row_bytes);
+    if (MODE == kLogits)
+      orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld, (uint32_t)nrows * row_bytes);
+    else
+      cand_lane(out_spec, qrow0, qa, qb, qo, qoc, n_ksplits, thr[G], reg[G]);
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      const int j = clamp_head8(heads[(qrow0 + qoc) * h + min(sl, h - 1)], H);
+      const int j = clamp_head(heads[(qrow0 + qoc) * h + min(sl, h - 1)], H);
       const int64_t r = (qrow0 + qoc) * H + j;
       wv[G][sl] = w[r] * q_scale[r] * ((qo < qb && sl < h) ? 1.f : 0.f);
     }
@@ -137,7 +142,7 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
     for (int qd = 0; qd < 2; ++qd) {
       const int sl = 4 * qd + (p16 & 3);
       const bool ok = (qi < qb) && (sl < h);
-      const int j = clamp_head8(heads[(qrow0 + qic) * h + min(sl, h - 1)], H);
+      const int j = clamp_head(heads[(qrow0 + qic) * h + min(sl, h - 1)], H);
       const uint4* src = reinterpret_cast<const uint4*>(q8 + ((qrow0 + qic) * H + j) * kD + 32 * g);
       const uint4 v0 = src[0], v1 = src[1];
       const int keep = ok ? -1 : 0;
@@ -156,7 +161,12 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
   __builtin_amdgcn_s_waitcnt(0);   // prologue loads (q, w, heads) and the first tile
   __syncthreads();
   const float ninf = -__builtin_inff();
-  constexpr uint32_t kDrop = 0x80000000u;
+  const int pol = kstride == 1 ? kStream : 0;
+  uint32_t run[2] = {0u, 0u};   // kCands: groups found for the lane's query so far
+  const uint64_t gmask = 0xFFFFull << (16 * g);
+  // stores a wave issues per tile (issued after the next tile's loads, which
+  // the wait before each barrier must cover)
+  constexpr int kTileStores = MODE == kLogits ? 2 : 4;
 
   auto tile = [&](auto buf_tag, int key0) {
     constexpr int BUF = decltype(buf_tag)::value;
@@ -187,9 +197,14 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
         }
       }
     }
-    const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
-    store_f32x4_q8(orsrc[0], off, out[0]);
-    store_f32x4_q8(orsrc[1], off, out[1]);
+    if (MODE == kLogits) {
+      const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
+      store_f32x4(orsrc[0], off, out[0], pol);
+      store_f32x4(orsrc[1], off, out[1], pol);
+    } else {
+#pragma unroll
+      for (int G = 0; G < 2; ++G) append_group(orsrc, out[G], thr[G], gmask, run[G], reg[G], out_spec.cap, kg);
+    }
   };
 
   using B0 = std::integral_constant<int, 0>;
@@ -198,37 +213,66 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
     const int key0 = k0 + jt * KT;
     q8_stage(kb_ptr, sc_ptr, key0 + KT, Nk, kstride, lane, wave, s_k1, s_sc1);   // tile jt+1
     tile(B0{}, key0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));   // this wave's loads of tile jt+1 (the 2 stores may fly)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kTileStores));   // this wave's loads of tile jt+1 (its stores may fly)
     __syncthreads();
     if (jt + 1 < n_tiles) {
       q8_stage(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, kstride, lane, wave, s_k0, s_sc0);   // tile jt+2
       tile(B1{}, key0 + KT);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kTileStores));
       __syncthreads();
     }
   }
-  // keys of this range after the last computed tile: -inf for every query
-  const int64_t from = k0 + (int64_t)n_tiles * KT;
-  if (from < k1) {
-    for (int qi = qa; qi < qb; ++qi) {
-      float* rowp = logits + (qrow0 + qi) * ld;
-      for (int64_t e = from + tid; e < k1; e += NT) rowp[e] = ninf;
+  if (MODE == kLogits) {
+    // keys of this range after the last computed tile: -inf for every query
+    fill_neg_inf(out_spec.logits, out_spec.ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, 256);
+  } else {
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const int qo = q0w + 4 * G + g;
+      if (qo < qb && p16 == 0) out_spec.rcount[(qrow0 + qo) * n_ksplits + split] = run[G];
     }
   }
 }
 
-hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
-                          const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
-                          int64_t ld, hipStream_t st) {
+template <int MODE>
+static hipError_t launch_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                            const uint8_t* k, const float* k_scale, const int32_t* heads, int h, const ScoreOut& o,
+                            int kstride, int nks, int64_t KR, hipStream_t st) {
   const int M = s.q_per_seq;
   const int n_qtiles = (M + 31) / 32;
+  dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  hipLaunchKernelGGL(k_score_q8<MODE>, grid, dim3(256), 0, st, q8, q_scale, w, k, k_scale, heads, h, o, s.n_keys,
+                     kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                          const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
+                          int64_t ld, hipStream_t st, const uint32_t* row_flag) {
   int nks;
   int64_t KR;
-  plan_split(s.n_keys, s.n_seq, n_qtiles, kQ8KT, &nks, &KR);
-  dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
-  hipLaunchKernelGGL(k_score_q8, grid, dim3(256), 0, st, q8, q_scale, w, k, k_scale, heads, h, logits, ld,
-                     s.n_keys, 1, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
-  return hipGetLastError();
+  plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, kQ8KT, &nks, &KR);
+  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
+  return launch_q8<kLogits>(s, q8, q_scale, w, k, k_scale, heads, h, o, 1, nks, KR, st);
+}
+
+hipError_t launch_score_q8_sampled(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                                   const uint8_t* k, const float* k_scale, const int32_t* heads, int h,
+                                   const FusedPlan& p, float* sample_logits, hipStream_t st) {
+  int nks;
+  int64_t KR;
+  plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, kQ8KT, &nks, &KR);
+  const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+  return launch_q8<kLogits>(s, q8, q_scale, w, k, k_scale, heads, h, o, p.kstride, nks, KR, st);
+}
+
+hipError_t launch_score_q8_cands(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                                 const uint8_t* k, const float* k_scale, const int32_t* heads, int h,
+                                 const FusedPlan& p, const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount,
+                                 hipStream_t st) {
+  static_assert(kQ8KT == 64, "the fused plan's key ranges are multiples of 64 keys");
+  const ScoreOut o{nullptr, 0, thr, reinterpret_cast<f32x4*>(gvals), gkeys, rcount, p.cap_region, nullptr};
+  return launch_q8<kCands>(s, q8, q_scale, w, k, k_scale, heads, h, o, 1, p.n_splits, p.key_range, st);
 }
 
 }  // namespace misa

@@ -143,6 +143,31 @@ def test_sparse_head_topk_checks_and_workspace(lib):
                      + 8192 * 8 * 1536 * 20)
 
 
+def test_fp8_query_calls_check_their_arguments(lib):
+    s = shape()
+    # quantisation: null or misaligned pointers
+    assert lib.misa_quantize_q(ctypes.byref(s), None, FAKE, FAKE, None) == -1
+    assert lib.misa_quantize_q(ctypes.byref(s), FAKE, ctypes.c_void_p(0x10004), FAKE, None) == -1
+    assert lib.misa_quantize_q(ctypes.byref(s), FAKE, FAKE, None, None) == -1
+    lq = lib.misa_sparse_head_logits_q8
+    # bf16 keys are refused (the fp8 MFMA takes fp8 on both sides), h above 8 too
+    assert lq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 64, None) == -2
+    assert lq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 9, FAKE, 64, None) == -1   # h > H
+    s16 = shape(n_heads=16)
+    assert lq(ctypes.byref(s16), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 9, FAKE, 64, None) == -2
+    assert lq(ctypes.byref(s), FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, 2, FAKE, 64, None) == -1   # no q scale
+    assert lq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, FAKE, 62, None) == -1   # ld < N
+    tq = lib.misa_sparse_head_topk_q8
+    need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 2, 4)
+    assert tq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, FAKE, need, None) == -2
+    assert tq(ctypes.byref(s16), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 9, 4, 1, FAKE, None, FAKE, 1 << 30,
+              None) == -2
+    assert tq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 0, 1, FAKE, None, FAKE, need, None) == -1
+    assert tq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, 2, 4, 1, FAKE, None, FAKE, need, None) == -1
+    assert tq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 4, 1, FAKE, None, FAKE, need - 1,
+              None) == -3
+
+
 def test_empty_query_set_is_a_no_op(lib):
     s = shape(q_per_seq=0, q_pos0=64)
     assert lib.misa_sparse_head_logits(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 64,

@@ -6,7 +6,13 @@
   * fp8 scoring: every logit against the oracle's routed score of the
     dequantised queries and keys, within the scoring tolerance (the fp8 matrix
     cores accumulate at slightly less than fp32 precision);
-  * the top-k of those logits against the oracle's, up to the tolerance band.
+  * the top-k of those logits against the oracle's, up to the tolerance band;
+  * the fused selection (misa_sparse_head_topk_q8) bit for bit against its
+    staged form (fp8 logits, then misa_topk): ids, values and order, the set
+    when unsorted; the staged top-k exactly against the oracle's top-k of
+    the same logits; inputs that defeat the sampled threshold (every row
+    re-scored), all-negative weights with a ragged query tile, k up to 6000,
+    decode, prefixes too short for the fused path, and the full-size chunk.
 """
 import numpy as np
 import pytest
@@ -14,7 +20,7 @@ import torch
 
 import long_context_sparse_block_amd as lcsb
 import oracle
-from gpu_helpers import band_check, logits_close, say, shape_of, upload
+from gpu_helpers import band_check, check_topk_exact, logits_close, sample_rows, say, shape_of, upload
 from long_context_sparse_block_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
@@ -90,3 +96,124 @@ def test_q8_logits_and_topk_against_oracle(case):
             ok, _ = band_check(o[:T + 1], np.arange(T + 1), gi[b, i], cfg.topk)
             assert ok, f"fp8 top-k seq {b} query {i}"
     say(f"  worst relative logit error {worst:.2e}")
+
+
+def q8_stages(inp):
+    """pool -> route (bf16 q) -> fp8 quantisation -> fp8 logits, all on the GPU."""
+    cfg = inp.cfg
+    t = upload(inp)
+    sh = shape_of(inp)
+    pooled, tail = lcsb.misa_pool_keys(sh, t["k"], t["k_scale"])
+    heads = lcsb.misa_route_heads(sh, t["q"], t["w"], pooled, tail, cfg.h)
+    q8, qs = lcsb.misa_quantize_q(sh, t["q"])
+    logits = lcsb.misa_sparse_head_logits_q8(sh, q8, qs, t["w"], t["k"], heads, t["k_scale"])
+    return dict(t=t, sh=sh, heads=heads, q8=q8, qs=qs, logits=logits)
+
+
+def check_q8_selection(inp, st, k):
+    """fused == staged, bit for bit (sorted), and the same set (unsorted)."""
+    t, sh = st["t"], st["sh"]
+    si, sv = lcsb.misa_topk(sh, st["logits"], k)
+    fi, fv = lcsb.misa_sparse_head_topk_q8(sh, st["q8"], st["qs"], t["w"], t["k"], st["heads"], k, t["k_scale"])
+    ui, _ = lcsb.misa_sparse_head_topk_q8(sh, st["q8"], st["qs"], t["w"], t["k"], st["heads"], k, t["k_scale"],
+                                          sorted=False, want_vals=False)
+    torch.cuda.synchronize()
+    assert torch.equal(fi, si) and torch.equal(fv, sv), "fused fp8 selection != fp8 logits + top-k"
+    assert torch.equal(torch.sort(ui, dim=-1)[0], torch.sort(si, dim=-1)[0]), "unsorted: not the same set"
+    return fi, fv
+
+
+def fp8_keys_from(inp, kf):
+    """Re-encode float keys [n_seq, N, 128] as the inputs' fp8 keys (per-key
+    scale amax / 448, e4m3fn codes of k / scale)."""
+    amax = np.abs(kf).max(axis=-1)
+    sc = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    inp.k[...] = gen.to_e4m3_codes(kf / sc[..., None])
+    inp.k_scale[...] = sc
+
+
+FUSED_Q8_CASES = [
+    dict(name="q8_fused_h8_ragged", n_seq=1, m=72, n=40000, hh=32, b=64, h=8, k=2048),
+    dict(name="q8_fused_h5", n_seq=1, m=40, n=36001, hh=48, b=128, h=5, k=1000),
+    dict(name="q8_fused_decode", n_seq=6, m=1, n=50000, hh=32, b=64, h=8, k=2048),
+    dict(name="q8_fused_k6000", n_seq=1, m=40, n=40000, hh=16, b=64, h=8, k=6000),
+    dict(name="q8_short_prefix", n_seq=1, m=64, n=4100, hh=32, b=128, h=8, k=512),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_Q8_CASES, ids=lambda c: c["name"])
+def test_q8_fused_selection_equals_staged_and_oracle(case):
+    c = dict(case)
+    name = c.pop("name")
+    say("fused fp8 selection", name)
+    cfg = gen.small_config(name=name, kdtype=gen.KDTYPE_FP8, seed=48, **c)
+    inp = gen.generate(cfg)
+    st = q8_stages(inp)
+    fi, fv = check_q8_selection(inp, st, cfg.topk)
+    rows = sample_rows(cfg.q_per_seq, 6)
+    check_topk_exact(inp, st["logits"], cfg.topk, fi, fv, rows=rows)
+    gh = st["heads"].cpu().numpy()
+    gi = fi.cpu().numpy()
+    for b in range(cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b, q8=True)
+        for i in rows:
+            o = ctx.score(i, gh[b, i])
+            T = ctx.t(i)
+            ok, _ = band_check(o[:T + 1], np.arange(T + 1), gi[b, i], cfg.topk)
+            assert ok, f"fp8 fused top-k seq {b} query {i}"
+
+
+def test_q8_fused_rows_the_sample_misjudges():
+    """Every key at a multiple of the sampling stride (32) gets a huge score,
+    so the sampled threshold admits far fewer than k candidates: every row is
+    flagged, re-scored into fp8 logits and selected from them."""
+    say("fused fp8 selection: threshold defeated")
+    cfg = gen.small_config(name="q8_adv", m=48, n=40000, hh=16, b=64, h=8, k=2048, kdtype=gen.KDTYPE_FP8,
+                           seed=49, plant=False)
+    inp = gen.generate(cfg)
+    q = oracle.bf16_bits_to_f64(inp.q).astype(np.float32)
+    kf = oracle.e4m3fn_to_f64(inp.k).astype(np.float32) * inp.k_scale[..., None]
+    u = np.ones(128, np.float32) / np.sqrt(128.0)
+    q += 4.0 * u
+    kf[:, ::32, :] += 40.0 * u
+    inp.q[...] = gen.to_bf16_bits(q)
+    fp8_keys_from(inp, kf)
+    inp.w[...] = np.abs(inp.w)
+    st = q8_stages(inp)
+    fi, fv = check_q8_selection(inp, st, cfg.topk)
+    check_topk_exact(inp, st["logits"], cfg.topk, fi, fv)
+
+
+def test_q8_fused_nonpositive_scores_ragged_query_tile():
+    """All head weights negative: scores <= 0, many exactly 0, thresholds <= 0;
+    M = 37 leaves padding lanes whose zero scores must reach no row."""
+    say("fused fp8 selection: scores <= 0, ragged query tile")
+    cfg = gen.small_config(name="q8_neg", m=37, n=40000, hh=16, b=64, h=4, k=256, kdtype=gen.KDTYPE_FP8,
+                           seed=50, plant=False)
+    inp = gen.generate(cfg)
+    inp.w[...] = -np.abs(inp.w)
+    st = q8_stages(inp)
+    fi, fv = check_q8_selection(inp, st, cfg.topk)
+    assert float(fv.max()) <= 0.0 and int((fv == 0).sum()) > 0
+    check_topk_exact(inp, st["logits"], cfg.topk, fi, fv)
+
+
+def test_q8_fused_selection_full_size():
+    """The benchmark's chunk (M = 8192, N = 131072, fp8 keys, H = 64, B = 128,
+    top-2048): fused == staged on every row, the staged top-k exact on
+    sampled rows, and sampled rows within the band of the oracle's scores."""
+    cfg = gen.CONFIGS["final_chunk_m8k_n128k_fp8"]
+    say("fused fp8 selection, full size", cfg.name)
+    inp = gen.generate(cfg)
+    st = q8_stages(inp)
+    fi, fv = check_q8_selection(inp, st, cfg.topk)
+    rows = sample_rows(cfg.q_per_seq, 24)
+    check_topk_exact(inp, st["logits"], cfg.topk, fi, fv, rows=rows)
+    gh = st["heads"].cpu().numpy()
+    gi = fi.cpu().numpy()
+    ctx = oracle.SeqContext(inp, 0, q8=True)
+    for i in rows[::3]:
+        o = ctx.score(i, gh[0, i])
+        T = ctx.t(i)
+        ok, _ = band_check(o[:T + 1], np.arange(T + 1), gi[0, i], cfg.topk)
+        assert ok, f"fp8 fused top-k query {i}"
