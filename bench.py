@@ -279,6 +279,13 @@ def main():
             qper, qstep, _ = run_timed(q8_stages, max(3, args.steps // 2), 2)
             lper, _, _ = run_timed([("score_q8", lambda: lcsb.misa_sparse_head_logits_q8(
                 sh, q8, qs, w, k, heads, ks, logits=logits))], max(3, args.steps // 4), 2)
+            # the fp8-query dense comparator: quantisation, all-head fp8 logits, top-k
+            dq_stages = [
+                ("quantize_q", lambda: lcsb.misa_quantize_q(sh, q, q8=q8, q_scale=qs)),
+                ("dense_score_q8", lambda: lcsb.dsa_dense_logits_q8(sh, q8, qs, w, k, ks, logits=logits)),
+                ("topk", lambda: lcsb.misa_topk(sh, logits, K, idx=idx, vals=vals, ws=tk_ws)),
+            ]
+            dqper, dqstep, _ = run_timed(dq_stages, max(3, args.steps // 4), 2)
             extras["fp8_query_path"] = dict(
                 ms_per_step=qstep, stage_ms=qper, vs_bf16_step=step_ms / qstep,
                 triples_G_per_s=W["triples"] / (qstep * 1e-3) / 1e9,
@@ -286,9 +293,14 @@ def main():
                 score_q8_ms=lper["score_q8"],
                 score_q8_TFLOPs=W["score_flops"] / (lper["score_q8"] * 1e-3) / 1e12,
                 score_q8_frac_of_fp8_peak=W["score_flops"] / (lper["score_q8"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                vs_bf16_score=sper["staged_score"] / lper["score_q8"])
-            print(f"[bench] fp8 query path {qstep:.3f} ms {qper}; fp8 logits {lper['score_q8']:.3f} ms",
-                  file=sys.stderr, flush=True)
+                vs_bf16_score=sper["staged_score"] / lper["score_q8"],
+                dense_q8_ms_per_step=dqstep, dense_q8_stage_ms=dqper,
+                dense_score_q8_TFLOPs=W["dense_flops"] / (dqper["dense_score_q8"] * 1e-3) / 1e12,
+                dense_score_q8_frac_of_fp8_peak=W["dense_flops"] / (dqper["dense_score_q8"] * 1e-3) / 1e12
+                / PEAK_FP8_TFLOPS,
+                misa_q8_speedup_vs_dense_q8=dqstep / qstep)
+            print(f"[bench] fp8 query path {qstep:.3f} ms {qper}; fp8 logits {lper['score_q8']:.3f} ms; "
+                  f"fp8 dense {dqstep:.3f} ms {dqper}", file=sys.stderr, flush=True)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB

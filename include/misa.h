@@ -239,6 +239,19 @@ misa_status misa_sparse_head_logits_q8(const misa_shape* shape, const uint8_t* q
                                        void* stream);
 
 /*
+ * dsa_dense_logits on fp8 queries, every key (the fp8-query dense DSA
+ * indexer, the production-style comparator of the GitHub issue's Figure 3
+ * discussion, whose dense path scores fp8 queries and keys):
+ *   D[t,s] = sigma[s] * sum_{j < H} w[t,j] * q_scale[t,j] * ReLU(q8[t,j] . k8[s])
+ * for s <= t, -inf after.  kdtype must be MISA_K_FP8_E4M3
+ * (MISA_ERR_UNSUPPORTED otherwise).  logits: float [n_seq][M][ld], ld >= N,
+ * ld % 4 == 0, 16-byte aligned; columns N .. roundup4(N)-1 may be set to -inf.
+ */
+misa_status dsa_dense_logits_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale, const float* w,
+                                const void* k, misa_kdtype kdtype, const float* k_scale, float* logits, int64_t ld,
+                                void* stream);
+
+/*
  * misa_sparse_head_topk on fp8 queries: exactly
  * misa_topk(misa_sparse_head_logits_q8(...), topk) (ids, values and order;
  * the set when sorted == 0), through the same fused path (logits only for

@@ -8,5 +8,6 @@ from ._lib import (  # noqa: F401
     EXPORTED, MAX_TOPK, MisaError, MisaShape, dsa_dense_logits, load, make_shape, misa_indexer,
     misa_indexer_workspace_bytes, misa_pool_keys, misa_route_heads, misa_sparse_head_logits, misa_topk,
     misa_topk_workspace_bytes, misa_sparse_head_topk, misa_sparse_head_topk_workspace_bytes,
-    misa_quantize_q, misa_sparse_head_logits_q8, misa_sparse_head_topk_q8, status_str,
+    misa_quantize_q, misa_sparse_head_logits_q8, misa_sparse_head_topk_q8, dsa_dense_logits_q8,
+    status_str,
 )

@@ -29,7 +29,7 @@ MAX_TOPK = 8192
 EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_sparse_head_logits",
             "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_sparse_head_topk",
             "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes",
-            "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8")
+            "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8")
 
 
 class MisaShape(ctypes.Structure):
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_quantize_q": [S, P, P, P, P],
         "misa_sparse_head_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "misa_sparse_head_topk_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
+        "dsa_dense_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i64, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -326,6 +327,21 @@ def misa_sparse_head_topk_q8(shape: MisaShape, q8, q_scale, w, k, heads, topk: i
                                          _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel()), _stream(stream))
     _check(st, "misa_sparse_head_topk_q8")
     return idx, vals
+
+
+def dsa_dense_logits_q8(shape: MisaShape, q8, q_scale, w, k, k_scale, logits=None, stream=None):
+    """All-head (dense DSA) logits [n_seq, M, ld] from fp8 queries and fp8 keys."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q8, torch.uint8, (shape.n_seq, M, H, HEAD_DIM), "q8")
+    _need(q_scale, torch.float32, (shape.n_seq, M, H), "q_scale")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    if logits is None:
+        logits = torch.empty((shape.n_seq, M, _ld(shape.n_keys)), dtype=torch.float32, device=q8.device)
+    st = load().dsa_dense_logits_q8(ctypes.byref(shape), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k), kd,
+                                    _ptr(k_scale), _ptr(logits), int(logits.shape[-1]), _stream(stream))
+    _check(st, "dsa_dense_logits_q8")
+    return logits
 
 
 def misa_indexer_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:

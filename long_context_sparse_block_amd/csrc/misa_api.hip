@@ -235,6 +235,22 @@ misa_status misa_sparse_head_logits_q8(const misa_shape* shape, const uint8_t* q
                                         logits, ld, (hipStream_t)stream));
 }
 
+misa_status dsa_dense_logits_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale, const float* w,
+                                const void* k, misa_kdtype kdtype, const float* k_scale, float* logits, int64_t ld,
+                                void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (kdtype != MISA_K_FP8_E4M3) return MISA_ERR_UNSUPPORTED;   // the fp8 MFMA takes fp8 on both sides
+  if (q8 == nullptr || !aligned16(q8) || q_scale == nullptr || w == nullptr || logits == nullptr ||
+      !aligned16(logits))
+    return MISA_ERR_INVALID_ARG;
+  if (ld < shape->n_keys || ld % 4 != 0) return MISA_ERR_INVALID_ARG;
+  if (ld > kMaxLogitLd) return MISA_ERR_UNSUPPORTED;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  return from_hip(misa::launch_dense_q8(*shape, q8, q_scale, w, static_cast<const uint8_t*>(k), k_scale, logits, ld,
+                                        (hipStream_t)stream));
+}
+
 misa_status misa_route_heads(const misa_shape* shape, const uint16_t* q, const float* w,
                              const float* pooled, const float* tail, int32_t h, int32_t* heads,
                              float* scores, void* stream) {

@@ -99,6 +99,10 @@ hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, co
 hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, const float* thr,
                                const float* gvals, const int32_t* gkeys, const uint32_t* rcount, uint32_t* row_flag,
                                int32_t* idx, float* vals, bool sorted, hipStream_t st);
+// Dense (all H heads) logits from fp8 queries and fp8 keys: the fp8-query
+// DSA comparator.
+hipError_t launch_dense_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                           const uint8_t* k, const float* k_scale, float* logits, int64_t ld, hipStream_t st);
 // the fp8-query versions of the two scoring passes above (fp8 keys, h <= 8)
 hipError_t launch_score_q8_sampled(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
                                    const uint8_t* k, const float* k_scale, const int32_t* heads, int h,

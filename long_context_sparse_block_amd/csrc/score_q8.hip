@@ -234,6 +234,143 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
   }
 }
 
+// Dense (all-head) fp8 scoring, the fp8-query DSA comparator:
+//   D[t,s] = sigma[s] * sum_{j < H} w[t,j] q_scale[t,j] ReLU(q8[t,j] . k8[s]),
+// -inf after t.  One query per wave with its H head rows resident in
+// registers as NG row blocks of 16 heads (8 VGPRs each: a whole 128-byte
+// row per MFMA), 4 queries per workgroup, the 64-key fp8 tiles of
+// k_score_q8.  In the D layout lane group g holds head quad g of each block,
+// so a quad's terms are lane-local and the block sum (P0+P1)+(P2+P3) is two
+// butterfly adds; blocks add in order (the head order of the bf16 dense
+// kernel).  Lane group 0 stores a tile's 4 consecutive logits per lane.
+template <int NG>
+__global__ void __launch_bounds__(256) k_score_dense_q8(const uint8_t* __restrict__ q8,
+                                                        const float* __restrict__ q_scale,
+                                                        const float* __restrict__ w, const uint8_t* __restrict__ kptr,
+                                                        const float* __restrict__ kscale, float* __restrict__ logits,
+                                                        int64_t ld, int64_t N64, int64_t q_pos0_64, int M, int H,
+                                                        int n_qtiles, int n_ksplits, int64_t KR) {
+  constexpr int KT = kQ8KT, QT = 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k0[kQ8Tile], s_k1[kQ8Tile];
+  __shared__ float s_sc0[KT], s_sc1[KT];
+
+  const int Nk = (int)N64, q_pos0 = (int)q_pos0_64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, p16 = lane & 15;
+  const int b = blockIdx.y;
+  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, Nk);
+  const int k0 = (int)tc.k0, k1 = (int)tc.k1;
+  const int qa = tc.qt * QT, qb = min(qa + QT, M);
+  const int64_t qrow0 = (int64_t)b * M;
+  const int t_last = q_pos0 + qb - 1;
+  const int kend = min(k1, t_last + 1);
+  const int n_tiles = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
+  const int qi = qa + wave;   // this wave's query
+  const bool qok = qi < qb;
+  const int qic = min(qi, M - 1);
+  const int tq = qok ? q_pos0 + qi : -1;
+
+  i32x8 afr[NG];
+  float wq[NG][4];
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+    const int j = 16 * grp + p16;   // A row p16 of block grp
+    const int jc = min(j, H - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(q8 + ((qrow0 + qic) * H + jc) * kD + 32 * g);
+    const uint4 v0 = src[0], v1 = src[1];
+    const int keep = (qok && j < H) ? -1 : 0;
+    afr[grp] = i32x8{(int)v0.x & keep, (int)v0.y & keep, (int)v0.z & keep, (int)v0.w & keep,
+                     (int)v1.x & keep, (int)v1.y & keep, (int)v1.z & keep, (int)v1.w & keep};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // D rows 4g + i of block grp
+      const int jd = 16 * grp + 4 * g + i;
+      const int64_t r = (qrow0 + qic) * H + min(jd, H - 1);
+      wq[grp][i] = w[r] * q_scale[r] * ((qok && jd < H) ? 1.f : 0.f);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t orsrc = uniform_rsrc(logits + (qrow0 + qic) * ld, qok ? (uint32_t)ld * 4u : 0u);
+
+  const uint8_t* kb_ptr = kptr + (int64_t)b * Nk * kD;
+  const float* sc_ptr = kscale + (int64_t)b * Nk;
+  const uint32_t rd0 = (uint32_t)p16 * kQ8Row + (uint32_t)(((2 * g) ^ q8_swz(p16)) << 4);
+  const uint32_t rd1 = (uint32_t)p16 * kQ8Row + (uint32_t)(((2 * g + 1) ^ q8_swz(p16)) << 4);
+
+  q8_stage(kb_ptr, sc_ptr, k0, Nk, 1, lane, wave, s_k0, s_sc0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const float ninf = -__builtin_inff();
+
+  auto tile = [&](auto buf_tag, int key0) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const unsigned char* sk = BUF ? s_k1 : s_k0;
+    const float* ssc = BUF ? s_sc1 : s_sc0;
+    const int kg = key0 + 4 * p16;
+    f32x4 out = {ninf, ninf, ninf, ninf};
+    if (key0 <= tq) {
+      const bool diag = key0 + KT - 1 > tq;
+#pragma unroll
+      for (int kb = 0; kb < KT / 16; ++kb) {
+        const uint4 b0 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd0);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd1);
+        const i32x8 bf = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        float s = 0.f;
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp) {
+          const f32x4 acc = mfma_f8(afr[grp], bf);
+          const float P = quad_chain(acc, wq[grp][0], wq[grp][1], wq[grp][2], wq[grp][3]);
+          const float v = P + __shfl_xor(P, 16);   // P0+P1 on lane groups 0/1, P2+P3 on 2/3
+          const float T = v + __shfl_xor(v, 32);   // (P0+P1)+(P2+P3)
+          s = s + T;
+        }
+        s *= ssc[kb * 16 + p16];
+        if (diag && kg + kb > tq) s = ninf;
+        out[kb] = s;
+      }
+    }
+    store_f32x4(orsrc, (g == 0 && kg < Nk) ? (uint32_t)kg * 4u : kDrop, out, kStream);
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    const int key0 = k0 + jt * KT;
+    q8_stage(kb_ptr, sc_ptr, key0 + KT, Nk, 1, lane, wave, s_k1, s_sc1);   // tile jt+1
+    tile(B0{}, key0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(1));   // this wave's loads of tile jt+1 (its store may fly)
+    __syncthreads();
+    if (jt + 1 < n_tiles) {
+      q8_stage(kb_ptr, sc_ptr, key0 + 2 * KT, Nk, 1, lane, wave, s_k0, s_sc0);   // tile jt+2
+      tile(B1{}, key0 + KT);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(1));
+      __syncthreads();
+    }
+  }
+  fill_neg_inf(logits, ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, 256);
+}
+
+hipError_t launch_dense_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
+                           const uint8_t* k, const float* k_scale, float* logits, int64_t ld, hipStream_t st) {
+  const int M = s.q_per_seq;
+  const int n_qtiles = (M + 3) / 4;
+  int nks;
+  int64_t KR;
+  plan_split(s.n_keys, s.n_seq, n_qtiles, kQ8KT, &nks, &KR);
+  dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  const int ng = (s.n_heads + 15) / 16;
+#define MISA_DQ8(NG_)                                                                                       \
+  hipLaunchKernelGGL(k_score_dense_q8<NG_>, grid, dim3(256), 0, st, q8, q_scale, w, k, k_scale, logits, ld, \
+                     s.n_keys, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR)
+  switch (ng) {
+    case 1: MISA_DQ8(1); break;
+    case 2: MISA_DQ8(2); break;
+    case 3: MISA_DQ8(3); break;
+    default: MISA_DQ8(4); break;
+  }
+#undef MISA_DQ8
+  return hipGetLastError();
+}
+
 template <int MODE>
 static hipError_t launch_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
                             const uint8_t* k, const float* k_scale, const int32_t* heads, int h, const ScoreOut& o,

