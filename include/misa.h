@@ -285,6 +285,65 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
 size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk,
                                     int32_t k_prime);
 
+/*
+ * Pooled-key cache (chunked prefill and decode).  The GitHub issue measures
+ * the indexer at a per-layer boundary that includes cache handling, under
+ * chunked prefill of 8192 tokens up to a 128K prompt ("Clarification on the
+ * Figure 3 baseline ...", the measured configuration).  Block means of keys
+ * already pooled do not change as the sequence grows, so a caller-owned
+ * cache keeps them across calls and each call pools only the blocks that
+ * have become complete since (decode then reads K once per step instead of
+ * twice).
+ *
+ * The cache of a shape's n_seq sequences, caller-owned device memory:
+ *   pooled:       float    [n_seq][cap_blocks][128]     block means
+ *   pooled_split: uint16_t [n_seq][2][cap_blocks][128]  their bf16 hi rows, then
+ *                 lo rows (pooled - hi), which the router stages directly
+ * both 16-byte aligned, cap_blocks >= n_keys / block.  n_cached: the number of
+ * leading complete blocks whose rows already hold the means of these keys
+ * (0 for an empty cache; after a call with n_keys keys the cache holds
+ * n_keys / block blocks).  0 <= n_cached <= n_keys / block, else
+ * MISA_ERR_INVALID_ARG.  The keys of the cached blocks are not read again,
+ * so they must be the keys the cache was built from.
+ */
+
+/* misa_pool_keys into the cache: pools complete blocks [n_cached, N/B) and
+ * the tails of the shape's queries (tail: float [n_seq][M][128], may be NULL
+ * when M == 0). */
+misa_status misa_pool_keys_cached(const misa_shape* shape, const void* k, misa_kdtype kdtype,
+                                  const float* k_scale, int64_t n_cached, float* pooled,
+                                  uint16_t* pooled_split, int64_t cap_blocks, float* tail, void* stream);
+
+/* misa_indexer with the pooled keys in the cache (brought up to date first).
+ * The result is exactly misa_indexer's on the same arguments.  ws: at least
+ * misa_indexer_cached_workspace_bytes() bytes.  With M == 0 it only updates
+ * the cache. */
+misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
+                                int32_t k_prime, int64_t n_cached, float* pooled, uint16_t* pooled_split,
+                                int64_t cap_blocks, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
+                                void* stream);
+
+size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk,
+                                           int32_t k_prime);
+
+/* Chunked prefill driver: the indexer over the shape's M queries (positions
+ * q_pos0 .. q_pos0+M-1 of each sequence) in chunks of `chunk` queries, the way
+ * a serving engine prefills a long prompt: chunk c sees the keys through its
+ * own last query, and the pooled-key cache (kept in the workspace) grows from
+ * chunk to chunk.  Sequences are processed one after another.  idx / vals as
+ * misa_indexer over the whole shape, and equal to it: each query's top-k
+ * depends only on its own prefix.  ws: at least misa_prefill_workspace_bytes()
+ * bytes (the cache of one sequence plus the largest chunk's indexer
+ * workspace).  chunk >= 1, else MISA_ERR_INVALID_ARG. */
+misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                 misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
+                                 int32_t k_prime, int32_t chunk, int32_t* idx, float* vals, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+size_t misa_prefill_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime,
+                                    int32_t chunk);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,9 @@ MAX_TOPK = 8192
 EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_sparse_head_logits",
             "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_sparse_head_topk",
             "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes",
-            "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8")
+            "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8",
+            "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
+            "misa_prefill_chunked", "misa_prefill_workspace_bytes")
 
 
 class MisaShape(ctypes.Structure):
@@ -73,6 +75,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_sparse_head_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "misa_sparse_head_topk_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
         "dsa_dense_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i64, P],
+        "misa_pool_keys_cached": [S, P, ctypes.c_int, P, i64, P, P, i64, P, P],
+        "misa_indexer_cached": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i64, P, P, i64, P, P, P, sz, P],
+        "misa_prefill_chunked": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, P, P, P, sz, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -84,6 +89,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.misa_sparse_head_topk_workspace_bytes.restype = sz
     lib.misa_indexer_workspace_bytes.argtypes = [S, i32, i32, i32]
     lib.misa_indexer_workspace_bytes.restype = sz
+    lib.misa_indexer_cached_workspace_bytes.argtypes = [S, i32, i32, i32]
+    lib.misa_indexer_cached_workspace_bytes.restype = sz
+    lib.misa_prefill_workspace_bytes.argtypes = [S, i32, i32, i32, i32]
+    lib.misa_prefill_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -366,4 +375,85 @@ def misa_indexer(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: int = 0,
                              int(topk), int(k_prime), _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel()),
                              _stream(stream))
     _check(st, "misa_indexer")
+    return idx, vals
+
+
+class PooledCache:
+    """Caller-owned pooled-key cache of n_seq sequences (misa.h): block means
+    [n_seq, cap_blocks, 128] fp32 and their bf16 hi/lo rows
+    [n_seq, 2, cap_blocks, 128]; n_cached counts the valid leading blocks."""
+
+    def __init__(self, n_seq: int, cap_blocks: int, device="cuda"):
+        self.pooled = torch.empty((n_seq, cap_blocks, HEAD_DIM), dtype=torch.float32, device=device)
+        self.split = torch.empty((n_seq, 2, cap_blocks, HEAD_DIM), dtype=torch.int16, device=device)
+        self.cap_blocks = int(cap_blocks)
+        self.n_cached = 0
+
+
+def misa_pool_keys_cached(shape: MisaShape, k, cache: PooledCache, k_scale=None, tail=None, stream=None):
+    """Pool the blocks completed since the cache was last brought up to date
+    (and the shape's query tails); returns tail [n_seq, M, 128]."""
+    kd = _check_keys(shape, k, k_scale)
+    if tail is None:
+        tail = torch.empty((shape.n_seq, max(shape.q_per_seq, 1), HEAD_DIM), dtype=torch.float32, device=k.device)
+    st = load().misa_pool_keys_cached(ctypes.byref(shape), _ptr(k), kd, _ptr(k_scale), int(cache.n_cached),
+                                      _ptr(cache.pooled), _ptr(cache.split), cache.cap_blocks, _ptr(tail),
+                                      _stream(stream))
+    _check(st, "misa_pool_keys_cached")
+    cache.n_cached = shape.n_keys // shape.block
+    return tail
+
+
+def misa_indexer_cached_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:
+    return int(load().misa_indexer_cached_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime)))
+
+
+def misa_indexer_cached(shape: MisaShape, q, w, k, h: int, topk: int, cache: PooledCache, k_prime: int = 0,
+                        k_scale=None, idx=None, vals=None, want_vals=True, ws=None, stream=None):
+    """misa_indexer with the pooled keys kept in `cache` across calls (the
+    cache is brought up to date first; same result as misa_indexer)."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(misa_indexer_cached_workspace_bytes(shape, h, topk, k_prime), 1), dtype=torch.uint8,
+                         device=q.device)
+    st = load().misa_indexer_cached(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
+                                    int(topk), int(k_prime), int(cache.n_cached), _ptr(cache.pooled),
+                                    _ptr(cache.split), cache.cap_blocks, _ptr(idx), _ptr(vals), _ptr(ws),
+                                    int(ws.numel()), _stream(stream))
+    _check(st, "misa_indexer_cached")
+    cache.n_cached = shape.n_keys // shape.block
+    return idx, vals
+
+
+def misa_prefill_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0, chunk: int = 8192) -> int:
+    return int(load().misa_prefill_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime),
+                                                   int(chunk)))
+
+
+def misa_prefill_chunked(shape: MisaShape, q, w, k, h: int, topk: int, chunk: int = 8192, k_prime: int = 0,
+                         k_scale=None, idx=None, vals=None, want_vals=True, ws=None, stream=None):
+    """The indexer over a whole prompt in chunks of `chunk` queries with an
+    incremental pooled-key cache (same result as one misa_indexer call)."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(misa_prefill_workspace_bytes(shape, h, topk, k_prime, chunk), 1), dtype=torch.uint8,
+                         device=q.device)
+    st = load().misa_prefill_chunked(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
+                                     int(topk), int(k_prime), int(chunk), _ptr(idx), _ptr(vals), _ptr(ws),
+                                     int(ws.numel()), _stream(stream))
+    _check(st, "misa_prefill_chunked")
     return idx, vals

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "misa.h"
 #include "misa_launch.h"
 
@@ -154,16 +156,20 @@ struct IndexerLayout {
   SelectLayout sel;
 };
 
-IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime) {
+// own_pool: the pooled keys (and their bf16 hi/lo rows) live in the
+// workspace; otherwise in a caller-owned cache (misa_indexer_cached)
+IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, bool own_pool = true) {
   IndexerLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   const int64_t n_full = s.n_keys / s.block;
   L.ld_d = (k_prime + 3) / 4 * 4;
   size_t off = 0;
-  L.pooled = off;
-  off += align_up((size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(float));
-  L.split = off;   // bf16 hi and lo rows of the pooled keys, for the router
-  off += align_up(2 * (size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(uint16_t));
+  if (own_pool) {
+    L.pooled = off;
+    off += align_up((size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(float));
+    L.split = off;   // bf16 hi and lo rows of the pooled keys, for the router
+    off += align_up(2 * (size_t)s.n_seq * (size_t)(n_full > 0 ? n_full : 1) * MISA_HEAD_DIM * sizeof(uint16_t));
+  }
   L.tail = off;
   off += align_up((size_t)rows * MISA_HEAD_DIM * sizeof(float));
   L.heads = off;
@@ -179,6 +185,78 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime) 
   // the final top-k of MISA-dagger runs over k' candidate columns
   if (k_prime > 0) off += align_up(misa::topk_workspace_bytes(s, k_prime, topk));
   L.total = off;
+  return L;
+}
+
+// pool (from block n_cached on) -> route -> select (-> MISA-dagger re-rank)
+misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base, const uint16_t* q, const float* w,
+                        const void* k, int kdtype, const float* k_scale, int h, int topk, int k_prime,
+                        float* pooled, uint16_t* split, int64_t n_cached, int64_t ld_blk, int32_t* idx,
+                        float* vals, hipStream_t st) {
+  float* tail = reinterpret_cast<float*>(base + L.tail);
+  int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
+  MISA_TRY(from_hip(launch_pool(s, k, kdtype, k_scale, pooled, tail, split, st, n_cached, ld_blk)));
+  MISA_TRY(from_hip(launch_route(s, q, w, pooled, split, tail, h, heads, nullptr, st, ld_blk)));
+  if (k_prime == 0) return run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st);
+  // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
+  int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
+  float* dlog = reinterpret_cast<float*>(base + L.dlog);
+  MISA_TRY(run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, k_prime, false, cand, nullptr, st));
+  MISA_TRY(from_hip(launch_score_gather(s, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
+  return from_hip(launch_topk(s, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
+                              L.total - L.sel.end, st));
+}
+
+misa_status check_indexer_args(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                               misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
+                               const int32_t* idx) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  if (q == nullptr || !aligned16(q) || w == nullptr || idx == nullptr) return MISA_ERR_INVALID_ARG;
+  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
+  if (k_prime != 0 && (k_prime < topk || k_prime > MISA_MAX_TOPK)) return MISA_ERR_INVALID_ARG;
+  return MISA_OK;
+}
+
+// the caller's pooled-key cache for a shape
+misa_status check_cache(const misa_shape* shape, int64_t n_cached, const float* pooled, const uint16_t* split,
+                        int64_t cap_blocks) {
+  const int64_t n_full = shape->n_keys / shape->block;
+  if (cap_blocks < n_full || cap_blocks < 1 || n_cached < 0 || n_cached > n_full) return MISA_ERR_INVALID_ARG;
+  if (pooled == nullptr || !aligned16(pooled) || split == nullptr || !aligned16(split)) return MISA_ERR_INVALID_ARG;
+  return MISA_OK;
+}
+
+// chunk c of a chunked prefill of sequence b: its queries, keys through its last query
+misa_shape chunk_shape(const misa_shape& s, int c, int chunk) {
+  misa_shape sc = s;
+  sc.n_seq = 1;
+  sc.q_pos0 = s.q_pos0 + (int64_t)c * chunk;
+  sc.q_per_seq = (int32_t)std::min<int64_t>(chunk, s.q_per_seq - (int64_t)c * chunk);
+  sc.n_keys = sc.q_pos0 + sc.q_per_seq;
+  return sc;
+}
+
+struct PrefillLayout {
+  size_t pooled, split, ixws, total;
+  int64_t cap;
+};
+
+PrefillLayout prefill_layout(const misa_shape& s, int h, int topk, int k_prime, int chunk) {
+  PrefillLayout L{};
+  L.cap = std::max<int64_t>(1, (s.q_pos0 + s.q_per_seq) / s.block);
+  size_t off = 0;
+  L.pooled = off;
+  off += align_up((size_t)L.cap * MISA_HEAD_DIM * sizeof(float));
+  L.split = off;
+  off += align_up(2 * (size_t)L.cap * MISA_HEAD_DIM * sizeof(uint16_t));
+  L.ixws = off;
+  size_t most = 0;
+  const int n_chunks = (int)((s.q_per_seq + chunk - 1) / chunk);
+  for (int c = 0; c < n_chunks; ++c)
+    most = std::max(most, indexer_layout(chunk_shape(s, c, chunk), h, topk, k_prime, false).total);
+  L.total = off + most;
   return L;
 }
 
@@ -332,32 +410,84 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
                          misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
                          int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
                          void* stream) {
-  MISA_TRY(check_shape(shape));
-  MISA_TRY(check_keys(k, kdtype, k_scale));
-  if (q == nullptr || !aligned16(q) || w == nullptr || idx == nullptr) return MISA_ERR_INVALID_ARG;
-  if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
-  if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
-  if (k_prime != 0 && (k_prime < topk || k_prime > MISA_MAX_TOPK)) return MISA_ERR_INVALID_ARG;
+  MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
-  hipStream_t st = (hipStream_t)stream;
   char* base = static_cast<char*>(ws);
-  float* pooled = reinterpret_cast<float*>(base + L.pooled);
-  float* tail = reinterpret_cast<float*>(base + L.tail);
-  int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
-  uint16_t* split = reinterpret_cast<uint16_t*>(base + L.split);
-  MISA_TRY(from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, split, st)));
-  MISA_TRY(from_hip(launch_route(*shape, q, w, pooled, split, tail, h, heads, nullptr, st)));
-  if (k_prime == 0)
-    return run_select(*shape, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st);
-  // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
-  int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
-  float* dlog = reinterpret_cast<float*>(base + L.dlog);
-  MISA_TRY(run_select(*shape, L.sel, base, q, w, k, kdtype, k_scale, heads, h, k_prime, false, cand, nullptr, st));
-  MISA_TRY(from_hip(launch_score_gather(*shape, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
-  return from_hip(launch_topk(*shape, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
-                              L.total - L.sel.end, st));
+  return run_indexer(*shape, L, base, q, w, k, kdtype, k_scale, h, topk, k_prime,
+                     reinterpret_cast<float*>(base + L.pooled), reinterpret_cast<uint16_t*>(base + L.split), 0,
+                     shape->n_keys / shape->block, idx, vals, (hipStream_t)stream);
+}
+
+misa_status misa_pool_keys_cached(const misa_shape* shape, const void* k, misa_kdtype kdtype, const float* k_scale,
+                                  int64_t n_cached, float* pooled, uint16_t* pooled_split, int64_t cap_blocks,
+                                  float* tail, void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k, kdtype, k_scale));
+  MISA_TRY(check_cache(shape, n_cached, pooled, pooled_split, cap_blocks));
+  if (shape->q_per_seq > 0 && (tail == nullptr || !aligned16(tail))) return MISA_ERR_INVALID_ARG;
+  return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, pooled_split, (hipStream_t)stream,
+                              n_cached, cap_blocks));
+}
+
+size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
+  return indexer_layout(*shape, h, topk, k_prime, false).total;
+}
+
+misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
+                                int64_t n_cached, float* pooled, uint16_t* pooled_split, int64_t cap_blocks,
+                                int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
+  MISA_TRY(check_cache(shape, n_cached, pooled, pooled_split, cap_blocks));
+  const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime, false);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0)   // no queries: only bring the cache up to date
+    return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, nullptr, pooled_split, (hipStream_t)stream,
+                                n_cached, cap_blocks));
+  return run_indexer(*shape, L, static_cast<char*>(ws), q, w, k, kdtype, k_scale, h, topk, k_prime, pooled,
+                     pooled_split, n_cached, cap_blocks, idx, vals, (hipStream_t)stream);
+}
+
+size_t misa_prefill_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime,
+                                    int32_t chunk) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0 || chunk < 1) return 0;
+  return prefill_layout(*shape, h, topk, k_prime, chunk).total;
+}
+
+misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                 misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
+                                 int32_t chunk, int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
+  if (chunk < 1) return MISA_ERR_INVALID_ARG;
+  const PrefillLayout P = prefill_layout(*shape, h, topk, k_prime, chunk);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < P.total) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  char* base = static_cast<char*>(ws);
+  float* pooled = reinterpret_cast<float*>(base + P.pooled);
+  uint16_t* split = reinterpret_cast<uint16_t*>(base + P.split);
+  const int64_t M = shape->q_per_seq, N = shape->n_keys, H = shape->n_heads;
+  const size_t key_bytes = kdtype == MISA_K_BF16 ? MISA_HEAD_DIM * 2 : MISA_HEAD_DIM;
+  const int n_chunks = (int)((M + chunk - 1) / chunk);
+  // sequences one after another on the stream, each through its chunks in
+  // order; the pooled-key cache (one sequence's) carries over between chunks
+  for (int b = 0; b < shape->n_seq; ++b) {
+    int64_t n_cached = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const misa_shape sc = chunk_shape(*shape, c, chunk);
+      const int64_t r0 = (int64_t)b * M + (int64_t)c * chunk;   // first query row of the chunk
+      const IndexerLayout L = indexer_layout(sc, h, topk, k_prime, false);
+      MISA_TRY(run_indexer(sc, L, base + P.ixws, q + r0 * H * MISA_HEAD_DIM, w + r0 * H,
+                           static_cast<const char*>(k) + (size_t)b * N * key_bytes, kdtype,
+                           k_scale != nullptr ? k_scale + (size_t)b * N : nullptr, h, topk, k_prime, pooled, split,
+                           n_cached, P.cap, idx + r0 * topk, vals != nullptr ? vals + r0 * topk : nullptr,
+                           (hipStream_t)stream));
+      n_cached = sc.n_keys / sc.block;
+    }
+  }
+  return MISA_OK;
 }
 
 misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,

@@ -10,16 +10,20 @@
 
 namespace misa {
 
-// split (nullable): also write the pooled keys' bf16 hi rows [n_seq][N/B][128]
-// followed by the lo rows (pooled - hi), for launch_route
+// pooled: [n_seq][ld_blk][128] block means (ld_blk < 0: N/B).  split
+// (nullable): also write the pooled keys' bf16 hi and lo (pooled - hi) rows,
+// per sequence ld_blk hi rows then ld_blk lo rows, for launch_route.
+// n_cached: block rows [0, n_cached) already hold these keys' means (an
+// incremental cache); only later complete blocks are pooled.
 hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const float* k_scale,
-                       float* pooled, float* tail, uint16_t* split, hipStream_t st);
+                       float* pooled, float* tail, uint16_t* split, hipStream_t st, int64_t n_cached = 0,
+                       int64_t ld_blk = -1);
 
 // split (nullable): launch_pool's hi/lo rows, staged directly instead of
-// splitting `pooled` in every workgroup (same values)
+// splitting `pooled` in every workgroup (same values); ld_blk as launch_pool
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
                         const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
-                        hipStream_t st);
+                        hipStream_t st, int64_t ld_blk = -1);
 
 // Key-range split of a scoring grid: n_ksplits ranges of KR keys (a multiple
 // of the tile KT), enough workgroups to fill the chip.

@@ -12,6 +12,14 @@
 // queries walk their slice a second time (an L2 hit) with the running sum
 // started at the sum of the slices before it: that running sum is the prefix
 // sum the tails of those queries need.  HBM-bound: one pass over K.
+//
+// Incremental use (chunked prefill, decode): block rows [0, n_cached) of the
+// caller's cache already hold the means of the same keys, so only blocks
+// from min(n_cached, first query block) on are visited, and of those only
+// the complete blocks at or past n_cached are pooled.  Cache rows are
+// ld_blk blocks apart per sequence.
+#include <algorithm>
+
 #include "misa_common.h"
 #include "misa_launch.h"
 
@@ -38,16 +46,17 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
                                                              float* __restrict__ pooled, float* __restrict__ tail,
                                                              uint32_t* __restrict__ split,
                                                              int64_t N, int64_t q_pos0, int M, int B,
-                                                             int64_t n_blk_total, int64_t n_full) {
+                                                             int64_t n_full, int64_t m_first, int64_t n_cached,
+                                                             int64_t ld_blk) {
   __shared__ f32x2 s_part[kPoolWaves][kWave];
-  const int64_t m = blockIdx.x;
+  const int64_t m = m_first + blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t s0 = m * B;
   const int64_t s1 = (s0 + B < N) ? s0 + B : N;
   // only blocks that are complete or hold a query need any work
   const int64_t q_lo = q_pos0, q_hi = q_pos0 + M;  // queries occupy [q_lo, q_hi)
-  const bool full = (s0 + B <= N);
+  const bool full = (s0 + B <= N) && m >= n_cached;   // a complete block not pooled yet
   const bool has_query = (s1 > q_lo) && (s0 < q_hi);
   if (!full && !has_query) return;   // uniform over the workgroup
   const int64_t per = (s1 - s0 + kPoolWaves - 1) / kPoolWaves;
@@ -67,7 +76,7 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
   }
   s_part[w][lane] = f32x2{a0, a1};
   __syncthreads();
-  if (full && m < n_full && w == 0) {
+  if (full && w == 0) {
     float t0 = 0.f, t1 = 0.f;
 #pragma unroll
     for (int v = 0; v < kPoolWaves; ++v) {
@@ -75,12 +84,12 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
       t1 += s_part[v][lane].y;
     }
     const float p0 = t0 / (float)B, p1 = t1 / (float)B;
-    const int64_t o = ((int64_t)b * n_full + m) * (kD / 2) + lane;
-    reinterpret_cast<float2*>(pooled)[o] = make_float2(p0, p1);
-    if (split != nullptr) {   // bf16 hi rows, then lo rows (p - hi is exact in fp32)
+    reinterpret_cast<float2*>(pooled)[((int64_t)b * ld_blk + m) * (kD / 2) + lane] = make_float2(p0, p1);
+    if (split != nullptr) {   // per sequence: bf16 hi rows, then lo rows (p - hi is exact in fp32)
+      const int64_t o = ((int64_t)b * 2 * ld_blk + m) * (kD / 2) + lane;
       const uint32_t h01 = pk_bf16(p0, p1);
       split[o] = h01;
-      split[(int64_t)gridDim.y * n_full * (kD / 2) + o] =
+      split[o + ld_blk * (kD / 2)] =
           pk_bf16(p0 - __uint_as_float(h01 << 16), p1 - __uint_as_float(h01 & 0xFFFF0000u));
     }
   }
@@ -114,18 +123,25 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
 }
 
 hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const float* k_scale,
-                       float* pooled, float* tail, uint16_t* split, hipStream_t st) {
+                       float* pooled, float* tail, uint16_t* split, hipStream_t st, int64_t n_cached,
+                       int64_t ld_blk) {
   const int64_t N = s.n_keys;
   const int B = s.block;
   const int64_t n_blk_total = (N + B - 1) / B;
   const int64_t n_full = N / B;
-  dim3 grid((unsigned)n_blk_total, (unsigned)s.n_seq);
+  if (ld_blk < 0) ld_blk = n_full;
+  // first block with work: the first one not pooled yet, or the first holding a query
+  int64_t m_first = s.q_per_seq > 0 ? std::min(n_cached, s.q_pos0 / B) : n_cached;
+  if (m_first >= n_blk_total) return hipSuccess;
+  dim3 grid((unsigned)(n_blk_total - m_first), (unsigned)s.n_seq);
   if (kdtype == MISA_K_BF16)
     hipLaunchKernelGGL(k_pool<MISA_K_BF16>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
-                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
+                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_full, m_first, n_cached,
+                       ld_blk);
   else
     hipLaunchKernelGGL(k_pool<MISA_K_FP8_E4M3>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
-                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_blk_total, n_full);
+                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_full, m_first, n_cached,
+                       ld_blk);
   return hipGetLastError();
 }
 

@@ -36,9 +36,11 @@ __device__ __forceinline__ uint32_t rt_off(int j, int c) { return (uint32_t)j * 
 
 
 // NHC: 16-head chunks per query group (= ceil(H/16)).  PRESPLIT: the pooled
-// keys' bf16 hi and lo rows come precomputed (`split`: hi rows of every
-// sequence, then lo rows; the pooling kernel writes them with the same
-// conversion) and are staged by direct global -> LDS loads.
+// keys' bf16 hi and lo rows come precomputed (`split`: per sequence, ld_blk
+// hi rows then ld_blk lo rows; the pooling kernel writes them with the same
+// conversion) and are staged by direct global -> LDS loads.  Pooled rows are
+// ld_blk blocks apart per sequence (a cache may hold more than this call's
+// complete blocks).
 template <int NHC, bool PRESPLIT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_route(const uint16_t* __restrict__ q, const float* __restrict__ w,
                                                const float* __restrict__ pooled,
@@ -46,7 +48,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
                                                const float* __restrict__ tail,
                                                int32_t* __restrict__ heads, float* __restrict__ scores,
                                                int64_t q_pos0, int M, int H, int B, int h,
-                                               int64_t n_full_total) {
+                                               int64_t ld_blk) {
   constexpr int QG = (NHC == 1) ? 4 : (NHC == 2 ? 2 : 1);  // query groups per workgroup
   constexpr int NW = NHC * QG;                              // waves per workgroup
   constexpr int QWG = 4 * QG;                               // queries per workgroup
@@ -97,7 +99,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[rb][i] = 0.f;
 
-  const float* pool_b = pooled + (int64_t)b * n_full_total * kD;
+  const float* pool_b = pooled + (int64_t)b * ld_blk * kD;
   for (int64_t cbase = 0; cbase < nfull_wg; cbase += kRouteChunk) {
     // stage pooled rows [cbase, cbase+64) as bf16 hi/lo
     if (PRESPLIT) {
@@ -106,8 +108,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
       // (l % 16) ^ (row % 16) of that row (the rt_off layout)
       typedef __attribute__((address_space(3))) void* lds_ptr;
       const int64_t nrows = min((int64_t)kRouteChunk, nfull_wg - cbase);
-      const uint16_t* hb = split + ((int64_t)b * n_full_total + cbase) * kD;
-      const int64_t lo_off = (int64_t)gridDim.y * n_full_total * kD;
+      const uint16_t* hb = split + ((int64_t)b * 2 * ld_blk + cbase) * kD;
+      const int64_t lo_off = ld_blk * kD;
       const __amdgpu_buffer_rsrc_t rh = uniform_rsrc(hb, (uint32_t)nrows * kRowBytes);
       const __amdgpu_buffer_rsrc_t rl = uniform_rsrc(hb + lo_off, (uint32_t)nrows * kRowBytes);
       const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -257,12 +259,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
                         const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
-                        hipStream_t st) {
+                        hipStream_t st, int64_t ld_blk) {
   const int H = s.n_heads;
   const int nhc = (H + 15) / 16;
   const int qg = (nhc == 1) ? 4 : (nhc == 2 ? 2 : 1);
   const int qwg = 4 * qg;
-  const int64_t n_full_total = s.n_keys / s.block;
+  const int64_t n_full_total = ld_blk < 0 ? s.n_keys / s.block : ld_blk;
   dim3 grid((unsigned)((s.q_per_seq + qwg - 1) / qwg), (unsigned)s.n_seq);
   dim3 block((unsigned)(64 * nhc * qg));
 #define MISA_ROUTE_LAUNCH(NHC_)                                                                          \

@@ -71,8 +71,8 @@ def _cfg(name, n_seq, m, n, hh, b, h, k, kdtype=KDTYPE_BF16, kp=0, seed=0):
                   plant_a=_plant_scale(n, b))
 
 
-# The five workloads (tiny chunk, DeepSeek-V3.2 chunk, 128K final chunk with fp8
-# keys, GLM-5 decode batch, MISA-dagger prefill).
+# The workloads (tiny chunk, DeepSeek-V3.2 chunk, 128K final chunk with fp8
+# keys, GLM-5 decode batch, MISA-dagger prefill, GLM-5 64K prompt).
 CONFIGS = {
     "tiny_prefill_m256_n4k": _cfg("tiny_prefill_m256_n4k", 1, 256, 4096, 64, 64, 8, 256, seed=101),
     "dsv32_prefill_m8k_n32k": _cfg("dsv32_prefill_m8k_n32k", 1, 8192, 32768, 64, 64, 8, 2048, seed=102),
@@ -81,6 +81,11 @@ CONFIGS = {
     "glm5_decode_64x1_n128k": _cfg("glm5_decode_64x1_n128k", 64, 1, 131072, 32, 64, 8, 2048, seed=104),
     "dagger_prefill_m4k_n128k": _cfg("dagger_prefill_m4k_n128k", 1, 4096, 131072, 64, 64, 8, 2048,
                                      kp=8192, seed=105),
+    # a whole GLM-5-shaped prompt (H = 32) from its first token, for the
+    # chunked-prefill driver (chunks of 8192; no block lies before the first
+    # query, so nothing is planted)
+    "glm5_prompt_m64k_h32_fp8": _cfg("glm5_prompt_m64k_h32_fp8", 1, 65536, 65536, 32, 64, 8, 2048,
+                                     kdtype=KDTYPE_FP8, seed=106),
 }
 
 

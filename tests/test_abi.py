@@ -173,6 +173,44 @@ def test_fp8_query_calls_check_their_arguments(lib):
               None) == -3
 
 
+def test_pooled_cache_calls_check_their_arguments(lib):
+    s = shape()   # 64 keys, block 16: 4 complete blocks
+    pc = lib.misa_pool_keys_cached
+    assert pc(ctypes.byref(s), FAKE, 0, None, 0, FAKE, FAKE, 3, FAKE, None) == -1     # cap < N / B
+    assert pc(ctypes.byref(s), FAKE, 0, None, 5, FAKE, FAKE, 4, FAKE, None) == -1     # n_cached > N / B
+    assert pc(ctypes.byref(s), FAKE, 0, None, -1, FAKE, FAKE, 4, FAKE, None) == -1    # n_cached < 0
+    assert pc(ctypes.byref(s), FAKE, 0, None, 0, None, FAKE, 4, FAKE, None) == -1     # no pooled rows
+    assert pc(ctypes.byref(s), FAKE, 0, None, 0, FAKE, None, 4, FAKE, None) == -1     # no hi/lo rows
+    assert pc(ctypes.byref(s), FAKE, 0, None, 0, FAKE, FAKE, 4, None, None) == -1     # queries need tails
+    ic = lib.misa_indexer_cached
+    need = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(s), 2, 4, 0)
+    full = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 0)
+    assert 0 < need < full   # the pooled keys live in the cache, not the workspace
+    assert ic(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 0, FAKE, FAKE, 3, FAKE, None, FAKE, need,
+              None) == -1
+    assert ic(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 9, 4, 0, 0, FAKE, FAKE, 4, FAKE, None, FAKE, need,
+              None) == -1
+    assert ic(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 0, FAKE, FAKE, 4, FAKE, None, FAKE, need - 1,
+              None) == -3
+    pf = lib.misa_prefill_chunked
+    pneed = lib.misa_prefill_workspace_bytes(ctypes.byref(s), 2, 4, 0, 2)
+    assert pneed > 0 and lib.misa_prefill_workspace_bytes(ctypes.byref(s), 2, 4, 0, 0) == 0
+    assert pf(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 0, FAKE, None, FAKE, pneed, None) == -1
+    assert pf(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 2, FAKE, None, FAKE, pneed - 1, None) == -3
+    assert pf(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 3, 2, FAKE, None, FAKE, pneed, None) == -1
+
+
+def test_prefill_workspace_of_a_128k_prompt(lib):
+    # 16 chunks of 8192: the one-sequence cache (1024 blocks of 128: 0.5 MB of
+    # means + 0.5 MB of bf16 hi/lo rows) plus the last chunk's indexer
+    # workspace, the largest (the full-prefix chunk of the benchmark)
+    s = lcsb.make_shape(1, 131072, 131072, 0, 64, 128)
+    need = lib.misa_prefill_workspace_bytes(ctypes.byref(s), 8, 2048, 0, 8192)
+    last = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
+    ix = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(last), 8, 2048, 0)
+    assert need == 1024 * 128 * 4 + 2 * 1024 * 128 * 2 + ix
+
+
 def test_empty_query_set_is_a_no_op(lib):
     s = shape(q_per_seq=0, q_pos0=64)
     assert lib.misa_sparse_head_logits(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, FAKE, 64,
