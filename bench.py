@@ -302,6 +302,32 @@ def main():
             print(f"[bench] fp8 query path {qstep:.3f} ms {qper}; fp8 logits {lper['score_q8']:.3f} ms; "
                   f"fp8 dense {dqstep:.3f} ms {dqper}", file=sys.stderr, flush=True)
 
+    if not args.no_extras and cfg.n_seq == 1 and inp.q_pos0 + M == N:
+        # the whole prompt this chunk ends: N queries from the first token in
+        # chunks of M, with the pooled-key cache carried across chunks (the
+        # earlier chunks' queries drawn on the GPU, same distribution; the
+        # keys are the chunk's)
+        gq = torch.Generator(device=dev).manual_seed(cfg.seed + 1000)
+        qp = torch.randn((1, N, H, 128), generator=gq, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        wp = torch.randn((1, N, H), generator=gq, device=dev, dtype=torch.float32) / 8
+        qp[:, N - M:] = q
+        wp[:, N - M:] = w
+        shp = lcsb.make_shape(1, N, N, 0, H, B)
+        idxp = torch.empty((1, N, K), dtype=torch.int32, device=dev)
+        valp = torch.empty((1, N, K), dtype=torch.float32, device=dev)
+        pf_ws = torch.empty(lcsb.misa_prefill_workspace_bytes(shp, h, K, 0, M), dtype=torch.uint8, device=dev)
+        pper, pstep, _ = run_timed([("prefill", lambda: lcsb.misa_prefill_chunked(
+            shp, qp, wp, k, h, K, chunk=M, k_scale=ks, idx=idxp, vals=valp, ws=pf_ws))], 3, 1)
+        ref_idx, _ = lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks)   # the step's own result
+        extras["chunked_prefill"] = dict(
+            prompt_tokens=N, chunk=M, n_chunks=N // M, ms=pstep,
+            triples_G_per_s=cfg.h * (N * (N + 1) / 2) / (pstep * 1e-3) / 1e9,
+            last_chunk_equals_step=bool(torch.equal(idxp[:, N - M:], ref_idx)))
+        del ref_idx
+        print(f"[bench] chunked prefill of {N} tokens in chunks of {M}: {pstep:.2f} ms", file=sys.stderr,
+              flush=True)
+        del qp, wp, idxp, valp, pf_ws
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
