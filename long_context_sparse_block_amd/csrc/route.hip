@@ -28,7 +28,8 @@
 
 namespace misa {
 
-constexpr int kRouteChunk = 64;            // pooled rows staged per step
+constexpr int kRouteChunk = 64;            // pooled rows staged per step (register staging)
+constexpr int kPreChunk = 32;              // rows per buffer of the direct-load staging
 constexpr int kRowBytes = kD * 2;           // bf16 LDS row (256 bytes), 16-byte chunks XOR-swizzled
 
 // byte offset of 16-byte chunk c of staged row j
@@ -52,8 +53,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   constexpr int QG = (NHC == 1) ? 4 : (NHC == 2 ? 2 : 1);  // query groups per workgroup
   constexpr int NW = NHC * QG;                              // waves per workgroup
   constexpr int QWG = 4 * QG;                               // queries per workgroup
-  __shared__ __attribute__((aligned(16))) unsigned char s_hi[kRouteChunk * kRowBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char s_lo[kRouteChunk * kRowBytes];
+  // register staging: one 64-row chunk; direct loads (PRESPLIT): two buffers
+  // of 32 rows, separate arrays so the compiler sees that loads into one never
+  // alias reads of the other
+  __shared__ __attribute__((aligned(16))) unsigned char s_hi[PRESPLIT ? 1 : kRouteChunk * kRowBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_lo[PRESPLIT ? 1 : kRouteChunk * kRowBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_h0[PRESPLIT ? kPreChunk * kRowBytes : 1];
+  __shared__ __attribute__((aligned(16))) unsigned char s_l0[PRESPLIT ? kPreChunk * kRowBytes : 1];
+  __shared__ __attribute__((aligned(16))) unsigned char s_h1[PRESPLIT ? kPreChunk * kRowBytes : 1];
+  __shared__ __attribute__((aligned(16))) unsigned char s_l1[PRESPLIT ? kPreChunk * kRowBytes : 1];
   __shared__ float s_r[QWG][64];
 
   const int tid = threadIdx.x;
@@ -99,29 +107,87 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[rb][i] = 0.f;
 
+  // column block cb (16 pooled rows from row cbase + 16 cb of the chunk) of a
+  // staged chunk: hi/lo fragments from LDS, 8 MFMAs per row block, ReLU and
+  // the block sum in registers
+  auto chunk_blocks = [&](const unsigned char* sh, const unsigned char* sl, int64_t cbase, int ncb) {
+#pragma unroll
+    for (int cb = 0; cb < ncb; ++cb) {
+      const int64_t col0 = cbase + cb * 16;
+      if (col0 < nfull_w) {
+        bf16x8 bh[kKSteps], bl[kKSteps];
+        const int row = cb * 16 + p16;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh[rt_off(row, ks * 4 + g)]));
+          bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&sl[rt_off(row, ks * 4 + g)]));
+        }
+        // only column blocks reaching past the wave's first query's complete
+        // blocks need the per-lane mask
+        auto accumulate = [&](auto mask_tag) {
+          constexpr bool MASK = decltype(mask_tag)::value;
+          const bool valid = !MASK || (col0 + p16) < nfull_g;
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) {
+              acc = mfma16(afr[rb][ks], bh[ks], acc);
+              acc = mfma16(afr[rb][ks], bl[ks], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[rb][i] += (MASK && !valid) ? 0.f : relu(acc[i]);
+          }
+        };
+        if (col0 + 16 <= nfull_lo)
+          accumulate(std::false_type{});
+        else
+          accumulate(std::true_type{});
+      }
+    }
+  };
+
+  if (PRESPLIT) {
+    // 32-row chunks of the hi/lo rows by direct global -> LDS loads, the next
+    // chunk in flight while this one is scored: load u of a chunk's 16 (8 of
+    // hi rows, 8 of lo rows) fills rows r0 .. r0+3, lane l writing slot l % 16
+    // of row r0 + l / 16, i.e. chunk (l % 16) ^ (row % 16) of that row (the
+    // rt_off layout)
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const uint16_t* hb0 = split + (int64_t)b * 2 * ld_blk * kD;
+    const int64_t lo_off = ld_blk * kD;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto stage = [&](int64_t cbase, unsigned char* sh, unsigned char* sl) {
+      const int64_t nrows = max((int64_t)0, min((int64_t)kPreChunk, nfull_wg - cbase));   // zeros past it
+      const __amdgpu_buffer_rsrc_t rh = uniform_rsrc(hb0 + cbase * kD, (uint32_t)nrows * kRowBytes);
+      const __amdgpu_buffer_rsrc_t rl = uniform_rsrc(hb0 + lo_off + cbase * kD, (uint32_t)nrows * kRowBytes);
+      for (int u = wv; u < 2 * (kPreChunk / 4); u += NW) {
+        const int part = u / (kPreChunk / 4), r0 = (u % (kPreChunk / 4)) * 4;
+        const int j = r0 + (lane >> 4);
+        const int c = (lane & 15) ^ (j & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(part ? rl : rh, (lds_ptr)((part ? sl : sh) + r0 * kRowBytes), 16,
+                                                 (uint32_t)(j * kRowBytes + c * 16), 0, 0, 0);
+      }
+    };
+    stage(0, s_h0, s_l0);
+    __builtin_amdgcn_s_waitcnt(0);   // (also the q fragments)
+    __syncthreads();
+    for (int64_t cbase = 0; cbase < nfull_wg; cbase += 2 * kPreChunk) {
+      stage(cbase + kPreChunk, s_h1, s_l1);   // rows past nfull_wg: an empty range, no data
+      chunk_blocks(s_h0, s_l0, cbase, kPreChunk / 16);
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next chunk (no other memory ops in flight)
+      __syncthreads();
+      if (cbase + kPreChunk < nfull_wg) {
+        stage(cbase + 2 * kPreChunk, s_h0, s_l0);
+        chunk_blocks(s_h1, s_l1, cbase + kPreChunk, kPreChunk / 16);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  } else {
   const float* pool_b = pooled + (int64_t)b * ld_blk * kD;
   for (int64_t cbase = 0; cbase < nfull_wg; cbase += kRouteChunk) {
     // stage pooled rows [cbase, cbase+64) as bf16 hi/lo
-    if (PRESPLIT) {
-      // load u of the 32 (16 of hi rows, 16 of lo rows) fills rows r0 .. r0+3:
-      // lane l writes slot l % 16 of row r0 + l / 16, i.e. chunk
-      // (l % 16) ^ (row % 16) of that row (the rt_off layout)
-      typedef __attribute__((address_space(3))) void* lds_ptr;
-      const int64_t nrows = min((int64_t)kRouteChunk, nfull_wg - cbase);
-      const uint16_t* hb = split + ((int64_t)b * 2 * ld_blk + cbase) * kD;
-      const int64_t lo_off = ld_blk * kD;
-      const __amdgpu_buffer_rsrc_t rh = uniform_rsrc(hb, (uint32_t)nrows * kRowBytes);
-      const __amdgpu_buffer_rsrc_t rl = uniform_rsrc(hb + lo_off, (uint32_t)nrows * kRowBytes);
-      const int wv = __builtin_amdgcn_readfirstlane(wave);
-      for (int u = wv; u < 2 * (kRouteChunk / 4); u += NW) {
-        const int part = u / (kRouteChunk / 4), r0 = (u % (kRouteChunk / 4)) * 4;
-        const int j = r0 + (lane >> 4);
-        const int c = (lane & 15) ^ (j & 15);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(part ? rl : rh, (lds_ptr)((part ? s_lo : s_hi) + r0 * kRowBytes), 16,
-                                                 (uint32_t)(j * kRowBytes + c * 16), 0, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-    } else {
     constexpr int kTotal = kRouteChunk * (kD / 4);                 // float4 of a chunk
     constexpr int kPer = (kTotal + NW * 64 - 1) / (NW * 64);       // per thread (3 waves: ragged)
     constexpr int kBatch = NW == 4 ? 4 : 2;   // loads in flight per batch (3 waves: ragged, fewer registers)
@@ -150,43 +216,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
         *reinterpret_cast<uint2*>(&s_lo[o]) = make_uint2(l01, l23);
       }
     }
-    }
     __syncthreads();
-#pragma unroll
-    for (int cb = 0; cb < kRouteChunk / 16; ++cb) {
-      const int64_t col0 = cbase + cb * 16;
-      if (col0 < nfull_w) {
-        bf16x8 bh[kKSteps], bl[kKSteps];
-        const int row = cb * 16 + p16;
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_hi[rt_off(row, ks * 4 + g)]));
-          bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_lo[rt_off(row, ks * 4 + g)]));
-        }
-        // only column blocks reaching past the wave's first query's complete
-        // blocks need the per-lane mask
-        auto accumulate = [&](auto mask_tag) {
-          constexpr bool MASK = decltype(mask_tag)::value;
-          const bool valid = !MASK || (col0 + p16) < nfull_g;
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) {
-              acc = mfma16(afr[rb][ks], bh[ks], acc);
-              acc = mfma16(afr[rb][ks], bl[ks], acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[rb][i] += (MASK && !valid) ? 0.f : __builtin_fmaxf(acc[i], 0.f);
-          }
-        };
-        if (col0 + 16 <= nfull_lo)
-          accumulate(std::false_type{});
-        else
-          accumulate(std::true_type{});
-      }
-    }
+    chunk_blocks(s_hi, s_lo, cbase, kRouteChunk / 16);
     __syncthreads();
+  }
   }
 
   // sum over the 16 block columns held by the 16 lanes of a row group
