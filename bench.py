@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--workload", default="final_chunk_m8k_n128k_fp8")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the MISA-dagger and dense timings")
+    p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill timing")
     p.add_argument("--cpu-queries", type=int, default=1536, help="queries in the oracle timing sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
@@ -302,7 +303,7 @@ def main():
             print(f"[bench] fp8 query path {qstep:.3f} ms {qper}; fp8 logits {lper['score_q8']:.3f} ms; "
                   f"fp8 dense {dqstep:.3f} ms {dqper}", file=sys.stderr, flush=True)
 
-    if not args.no_extras and cfg.n_seq == 1 and inp.q_pos0 + M == N:
+    if not args.no_extras and not args.no_prefill and cfg.n_seq == 1 and inp.q_pos0 + M == N:
         # the whole prompt this chunk ends: N queries from the first token in
         # chunks of M, with the pooled-key cache carried across chunks (the
         # earlier chunks' queries drawn on the GPU, same distribution; the

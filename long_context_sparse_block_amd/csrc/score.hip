@@ -125,9 +125,10 @@ template <int KDT, int NT>
 __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sbase, int key0, int N, int ks,
                                          int lane, int wave, unsigned char* s_dst, float* s_sc_dst) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  const int64_t first = (int64_t)key0 * ks;
-  const int rem = (int)max((int64_t)0, min((int64_t)kSwKT * ks, (int64_t)N - first));
-  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + first * kD, (uint32_t)rem * kSwRowBytes);
+  // 32-bit scalar arithmetic: N < 2^26 keys (the ABI checks it)
+  const int first = key0 * ks;
+  const int rem = max(0, min(kSwKT * ks, N - first));
+  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + (int64_t)first * kD, (uint32_t)rem * kSwRowBytes);
   constexpr int kLoads = kSwKT / 4 / (NT / 64);
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {

@@ -50,9 +50,10 @@ __device__ __forceinline__ f32x4 mfma_f8(const i32x8& a, const i32x8& b) {
 __device__ __forceinline__ void q8_stage(const uint8_t* kbase, const float* sbase, int key0, int N, int ks,
                                          int lane, int wave, unsigned char* s_dst, float* s_sc) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  const int64_t first = (int64_t)key0 * ks;
-  const int rem = (int)max((int64_t)0, min((int64_t)kQ8KT * ks, (int64_t)N - first));
-  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + first * kQ8Row, (uint32_t)rem * kQ8Row);
+  // 32-bit scalar arithmetic: N < 2^26 keys (the ABI checks it)
+  const int first = key0 * ks;
+  const int rem = max(0, min(kQ8KT * ks, N - first));
+  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + (int64_t)first * kQ8Row, (uint32_t)rem * kQ8Row);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {   // 8 loads of 8 rows (1 KB) per tile, 2 per wave
     const int r0 = (u * 4 + wave) * 8;
