@@ -277,7 +277,12 @@ def main():
                 ("select_q8", lambda: lcsb.misa_sparse_head_topk_q8(sh, q8, qs, w, k, heads, K, ks, idx=idx,
                                                                     vals=vals, ws=sel_ws)),
             ]
-            qper, qstep, _ = run_timed(q8_stages, max(3, args.steps // 2), 2)
+            qper, qcalls, _ = run_timed(q8_stages, max(3, args.steps // 2), 2)
+            iq_ws = torch.empty(lcsb.misa_indexer_q8_workspace_bytes(sh, h, K), dtype=torch.uint8, device=dev)
+            _, qstep, _ = run_timed([("indexer_q8", lambda: lcsb.misa_indexer_q8(sh, q, w, k, h, K, ks, idx=idx,
+                                                                                 vals=vals, ws=iq_ws))],
+                                    max(3, args.steps // 2), 2)
+            del iq_ws
             lper, _, _ = run_timed([("score_q8", lambda: lcsb.misa_sparse_head_logits_q8(
                 sh, q8, qs, w, k, heads, ks, logits=logits))], max(3, args.steps // 4), 2)
             # the fp8-query dense comparator: quantisation, all-head fp8 logits, top-k
@@ -288,7 +293,7 @@ def main():
             ]
             dqper, dqstep, _ = run_timed(dq_stages, max(3, args.steps // 4), 2)
             extras["fp8_query_path"] = dict(
-                ms_per_step=qstep, stage_ms=qper, vs_bf16_step=step_ms / qstep,
+                ms_per_step=qstep, separate_calls_ms=qcalls, stage_ms=qper, vs_bf16_step=step_ms / qstep,
                 triples_G_per_s=W["triples"] / (qstep * 1e-3) / 1e9,
                 select_q8_TFLOPs=W["score_flops"] / (qper["select_q8"] * 1e-3) / 1e12,
                 score_q8_ms=lper["score_q8"],
@@ -300,7 +305,8 @@ def main():
                 dense_score_q8_frac_of_fp8_peak=W["dense_flops"] / (dqper["dense_score_q8"] * 1e-3) / 1e12
                 / PEAK_FP8_TFLOPS,
                 misa_q8_speedup_vs_dense_q8=dqstep / qstep)
-            print(f"[bench] fp8 query path {qstep:.3f} ms {qper}; fp8 logits {lper['score_q8']:.3f} ms; "
+            print(f"[bench] fp8 query path: misa_indexer_q8 {qstep:.3f} ms, as calls {qcalls:.3f} ms {qper}; "
+                  f"fp8 logits {lper['score_q8']:.3f} ms; "
                   f"fp8 dense {dqstep:.3f} ms {dqper}", file=sys.stderr, flush=True)
 
     if not args.no_extras and not args.no_prefill and cfg.n_seq == 1 and inp.q_pos0 + M == N:

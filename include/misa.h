@@ -286,6 +286,21 @@ size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t 
                                     int32_t k_prime);
 
 /*
+ * misa_indexer with fp8 queries for the routed scoring: pool -> route (bf16
+ * q) -> misa_quantize_q into the workspace -> misa_sparse_head_topk_q8 (the
+ * k' candidates when k_prime > 0, then the MISA-dagger re-rank with bf16 q
+ * and all heads, as misa_indexer).  The result is exactly that sequence of
+ * calls.  kdtype must be MISA_K_FP8_E4M3 and 1 <= h <= 8
+ * (MISA_ERR_UNSUPPORTED otherwise); other arguments as misa_indexer; ws: at
+ * least misa_indexer_q8_workspace_bytes() bytes.
+ */
+misa_status misa_indexer_q8(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                            misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
+                            int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream);
+
+size_t misa_indexer_q8_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime);
+
+/*
  * Pooled-key cache (chunked prefill and decode).  The GitHub issue measures
  * the indexer at a per-layer boundary that includes cache handling, under
  * chunked prefill of 8192 tokens up to a 128K prompt ("Clarification on the

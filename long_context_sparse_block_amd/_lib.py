@@ -31,7 +31,8 @@ EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_spars
             "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes",
             "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8",
             "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
-            "misa_prefill_chunked", "misa_prefill_workspace_bytes")
+            "misa_prefill_chunked", "misa_prefill_workspace_bytes", "misa_indexer_q8",
+            "misa_indexer_q8_workspace_bytes")
 
 
 class MisaShape(ctypes.Structure):
@@ -78,6 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_pool_keys_cached": [S, P, ctypes.c_int, P, i64, P, P, i64, P, P],
         "misa_indexer_cached": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i64, P, P, i64, P, P, P, sz, P],
         "misa_prefill_chunked": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, P, P, P, sz, P],
+        "misa_indexer_q8": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -91,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.misa_indexer_workspace_bytes.restype = sz
     lib.misa_indexer_cached_workspace_bytes.argtypes = [S, i32, i32, i32]
     lib.misa_indexer_cached_workspace_bytes.restype = sz
+    lib.misa_indexer_q8_workspace_bytes.argtypes = [S, i32, i32, i32]
+    lib.misa_indexer_q8_workspace_bytes.restype = sz
     lib.misa_prefill_workspace_bytes.argtypes = [S, i32, i32, i32, i32]
     lib.misa_prefill_workspace_bytes.restype = sz
     _lib = lib
@@ -456,4 +460,29 @@ def misa_prefill_chunked(shape: MisaShape, q, w, k, h: int, topk: int, chunk: in
                                      int(topk), int(k_prime), int(chunk), _ptr(idx), _ptr(vals), _ptr(ws),
                                      int(ws.numel()), _stream(stream))
     _check(st, "misa_prefill_chunked")
+    return idx, vals
+
+
+def misa_indexer_q8_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:
+    return int(load().misa_indexer_q8_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime)))
+
+
+def misa_indexer_q8(shape: MisaShape, q, w, k, h: int, topk: int, k_scale, k_prime: int = 0, idx=None, vals=None,
+                    want_vals=True, ws=None, stream=None):
+    """misa_indexer with the routed scoring on fp8 queries (fp8 keys, h <= 8)."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(misa_indexer_q8_workspace_bytes(shape, h, topk, k_prime), 1), dtype=torch.uint8,
+                         device=q.device)
+    st = load().misa_indexer_q8(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
+                                int(topk), int(k_prime), _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel()),
+                                _stream(stream))
+    _check(st, "misa_indexer_q8")
     return idx, vals

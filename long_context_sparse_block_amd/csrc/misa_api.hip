@@ -151,14 +151,15 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
 }
 
 struct IndexerLayout {
-  size_t pooled, split, tail, heads, cand, dlog, total;
+  size_t pooled, split, tail, heads, q8, qscale, cand, dlog, total;
   int64_t ld_d;
   SelectLayout sel;
 };
 
 // own_pool: the pooled keys (and their bf16 hi/lo rows) live in the
 // workspace; otherwise in a caller-owned cache (misa_indexer_cached)
-IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, bool own_pool = true) {
+IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, bool own_pool = true,
+                             bool quant_q = false) {
   IndexerLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   const int64_t n_full = s.n_keys / s.block;
@@ -174,6 +175,12 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, 
   off += align_up((size_t)rows * MISA_HEAD_DIM * sizeof(float));
   L.heads = off;
   off += align_up((size_t)rows * h * sizeof(int32_t));
+  if (quant_q) {   // fp8 queries and their scales (misa_indexer_q8)
+    L.q8 = off;
+    off += align_up((size_t)rows * s.n_heads * MISA_HEAD_DIM);
+    L.qscale = off;
+    off += align_up((size_t)rows * s.n_heads * sizeof(float));
+  }
   if (k_prime > 0) {
     L.cand = off;
     off += align_up((size_t)rows * k_prime * sizeof(int32_t));
@@ -189,19 +196,26 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, 
 }
 
 // pool (from block n_cached on) -> route -> select (-> MISA-dagger re-rank)
+// quant_q: the routed scoring runs on fp8 queries (quantised into the
+// workspace after routing); routing and the MISA-dagger re-rank keep bf16 q
 misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base, const uint16_t* q, const float* w,
                         const void* k, int kdtype, const float* k_scale, int h, int topk, int k_prime,
                         float* pooled, uint16_t* split, int64_t n_cached, int64_t ld_blk, int32_t* idx,
-                        float* vals, hipStream_t st) {
+                        float* vals, hipStream_t st, bool quant_q = false) {
   float* tail = reinterpret_cast<float*>(base + L.tail);
   int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
   MISA_TRY(from_hip(launch_pool(s, k, kdtype, k_scale, pooled, tail, split, st, n_cached, ld_blk)));
   MISA_TRY(from_hip(launch_route(s, q, w, pooled, split, tail, h, heads, nullptr, st, ld_blk)));
-  if (k_prime == 0) return run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st);
+  QuantQ qq{reinterpret_cast<uint8_t*>(base + L.q8), reinterpret_cast<float*>(base + L.qscale)};
+  if (quant_q)
+    MISA_TRY(from_hip(misa::launch_quant_q(s, q, const_cast<uint8_t*>(qq.q8), const_cast<float*>(qq.q_scale), st)));
+  const QuantQ* qp = quant_q ? &qq : nullptr;
+  if (k_prime == 0)
+    return run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st, qp);
   // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
   float* dlog = reinterpret_cast<float*>(base + L.dlog);
-  MISA_TRY(run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, k_prime, false, cand, nullptr, st));
+  MISA_TRY(run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, k_prime, false, cand, nullptr, st, qp));
   MISA_TRY(from_hip(launch_score_gather(s, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
   return from_hip(launch_topk(s, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
                               L.total - L.sel.end, st));
@@ -418,6 +432,25 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
   return run_indexer(*shape, L, base, q, w, k, kdtype, k_scale, h, topk, k_prime,
                      reinterpret_cast<float*>(base + L.pooled), reinterpret_cast<uint16_t*>(base + L.split), 0,
                      shape->n_keys / shape->block, idx, vals, (hipStream_t)stream);
+}
+
+size_t misa_indexer_q8_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
+  return indexer_layout(*shape, h, topk, k_prime, true, true).total;
+}
+
+misa_status misa_indexer_q8(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                            misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
+                            int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
+  if (kdtype != MISA_K_FP8_E4M3 || h > 8) return MISA_ERR_UNSUPPORTED;   // the fp8 x fp8 routed kernels
+  const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime, true, true);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  char* base = static_cast<char*>(ws);
+  return run_indexer(*shape, L, base, q, w, k, kdtype, k_scale, h, topk, k_prime,
+                     reinterpret_cast<float*>(base + L.pooled), reinterpret_cast<uint16_t*>(base + L.split), 0,
+                     shape->n_keys / shape->block, idx, vals, (hipStream_t)stream, true);
 }
 
 misa_status misa_pool_keys_cached(const misa_shape* shape, const void* k, misa_kdtype kdtype, const float* k_scale,

@@ -173,6 +173,18 @@ def test_fp8_query_calls_check_their_arguments(lib):
               None) == -3
 
 
+def test_fp8_indexer_checks(lib):
+    s = shape()
+    f = lib.misa_indexer_q8
+    need = lib.misa_indexer_q8_workspace_bytes(ctypes.byref(s), 2, 4, 0)
+    assert need > lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 0)   # + fp8 q and its scales
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, FAKE, None, FAKE, need, None) == -2   # bf16 keys
+    s16 = shape(n_heads=16)
+    assert f(ctypes.byref(s16), FAKE, FAKE, FAKE, 1, FAKE, 9, 16, 0, FAKE, None, FAKE, 1 << 30, None) == -2
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 1, FAKE, 2, 4, 2, FAKE, None, FAKE, 1 << 30, None) == -1   # k' < k
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 1, FAKE, 2, 4, 0, FAKE, None, FAKE, need - 1, None) == -3
+
+
 def test_pooled_cache_calls_check_their_arguments(lib):
     s = shape()   # 64 keys, block 16: 4 complete blocks
     pc = lib.misa_pool_keys_cached

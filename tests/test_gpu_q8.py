@@ -14,6 +14,9 @@
     the same logits; inputs that defeat the sampled threshold (every row
     re-scored), all-negative weights with a ragged query tile, k up to 6000,
     decode, prefixes too short for the fused path, and the full-size chunk;
+  * the fp8-query indexer (misa_indexer_q8, MISA and MISA-dagger) bit for bit
+    against the same steps as separate calls, and its ids against the
+    oracle's fp8-query indexer (recall);
   * the fp8-query dense comparator (dsa_dense_logits_q8): every logit against
     the oracle's all-head score of the dequantised inputs within the derived
     fp8 bound (64 signed head terms cancel far more than 8, so the 1e-2
@@ -27,8 +30,8 @@ import torch
 
 import long_context_sparse_block_amd as lcsb
 import oracle
-from gpu_helpers import (band_check, check_topk_exact, fp8_mfma_close, logits_close, sample_rows, say, shape_of,
-                         upload)
+from gpu_helpers import (band_check, check_topk_exact, fp8_mfma_close, logits_close, recall, sample_rows, say,
+                         shape_of, upload)
 from long_context_sparse_block_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
@@ -284,3 +287,50 @@ def test_dense_q8_full_size_rows():
     for n, i in enumerate(rows):
         ok, wb = fp8_mfma_close(g[n], ctx, i, np.arange(cfg.n_heads))
         assert ok, f"fp8 dense logits query {i}: {wb} of the fp8 bound"
+
+
+INDEXER_Q8_CASES = [
+    dict(name="iq8_fused", n_seq=1, m=40, n=40000, hh=32, b=64, h=8, k=2048),
+    dict(name="iq8_dagger", n_seq=1, m=48, n=36000, hh=32, b=64, h=8, k=1024, kp=4096),
+    dict(name="iq8_short_decode", n_seq=3, m=1, n=3000, hh=16, b=64, h=5, k=256),
+]
+
+
+@pytest.mark.parametrize("case", INDEXER_Q8_CASES, ids=lambda c: c["name"])
+def test_fp8_indexer_equals_its_steps_and_oracle(case):
+    c = dict(case)
+    name, kp = c.pop("name"), c.pop("kp", 0)
+    say("fp8-query indexer", name)
+    cfg = gen.small_config(name=name, kdtype=gen.KDTYPE_FP8, seed=53, kp=kp, **c)
+    inp = gen.generate(cfg)
+    st = q8_stages(inp)
+    t, sh = st["t"], st["sh"]
+    ii, iv = lcsb.misa_indexer_q8(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, t["k_scale"], k_prime=kp)
+    if kp == 0:
+        si, sv = lcsb.misa_sparse_head_topk_q8(sh, st["q8"], st["qs"], t["w"], t["k"], st["heads"], cfg.topk,
+                                               t["k_scale"])
+    else:
+        cand, _ = lcsb.misa_sparse_head_topk_q8(sh, st["q8"], st["qs"], t["w"], t["k"], st["heads"], kp,
+                                                t["k_scale"], sorted=False, want_vals=False)
+        dl = lcsb.dsa_dense_logits(sh, t["q"], t["w"], t["k"], k_scale=t["k_scale"], cand=cand)
+        si, sv = lcsb.misa_topk(sh, dl, cfg.topk, cand=cand)
+    torch.cuda.synchronize()
+    assert torch.equal(ii, si) and torch.equal(iv, sv), "misa_indexer_q8 != its steps"
+    gi = ii.cpu().numpy()
+    recs = []
+    for b in range(cfg.n_seq):
+        ctx = oracle.SeqContext(inp, b, q8=True)
+        ctx_bf16 = oracle.SeqContext(inp, b)
+        for i in sample_rows(cfg.q_per_seq, 6):
+            # routing on bf16 q, routed scoring on the fp8 queries
+            heads = ctx_bf16.route(i, cfg.h)[2]
+            I = ctx.score(i, heads)
+            if kp:
+                # the k' candidates re-ranked with bf16 q and every head
+                cand_o = oracle.topk_prefix(I, ctx.t(i), kp)[0]
+                D = oracle.score_candidates(ctx_bf16.q[i], ctx_bf16.w[i], ctx_bf16.keys, cand_o)
+                ref = oracle.topk_row(D, cand_o, cfg.topk)[0]
+            else:
+                ref = oracle.topk_prefix(I, ctx.t(i), cfg.topk)[0]
+            recs.append(recall(gi[b, i], ref))
+    assert np.mean(recs) >= 0.999, np.mean(recs)
