@@ -179,24 +179,32 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
       out[0] = f32x4{ninf, ninf, ninf, ninf};
       out[1] = out[0];
     } else {
-      const bool diag = key0 + KT - 1 > t_lo;
+      // DIAG: some key of the tile may lie after some query of the wave; only
+      // those tiles pay for the causal mask
+      auto scores = [&](auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
 #pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd0);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd1);
-        const i32x8 bf = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        const float sc = ssc[kb * 16 + p16];
+        for (int kb = 0; kb < KT / 16; ++kb) {
+          const uint4 b0 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd0);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(sk + kb * 16 * kQ8Row + rd1);
+          const i32x8 bf = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          const float sc = ssc[kb * 16 + p16];
 #pragma unroll
-        for (int G = 0; G < 2; ++G) {
-          const f32x4 a0 = mfma_f8(afr[2 * G], bf);
-          const f32x4 a1 = mfma_f8(afr[2 * G + 1], bf);
-          const float P0 = quad_chain(a0, wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
-          const float P1 = quad_chain(a1, wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
-          float s = (P0 + P1) * sc;
-          if (diag && kg + kb > tq[G]) s = ninf;
-          out[G][kb] = s;
+          for (int G = 0; G < 2; ++G) {
+            const f32x4 a0 = mfma_f8(afr[2 * G], bf);
+            const f32x4 a1 = mfma_f8(afr[2 * G + 1], bf);
+            const float P0 = quad_chain(a0, wv[G][0], wv[G][1], wv[G][2], wv[G][3]);
+            const float P1 = quad_chain(a1, wv[G][4], wv[G][5], wv[G][6], wv[G][7]);
+            float s = (P0 + P1) * sc;
+            if (DIAG && kg + kb > tq[G]) s = ninf;
+            out[G][kb] = s;
+          }
         }
-      }
+      };
+      if (key0 + KT - 1 > t_lo)
+        scores(std::true_type{});
+      else
+        scores(std::false_type{});
     }
     if (MODE == kLogits) {
       const uint32_t off = (kg < N) ? lane_row_off + (uint32_t)kg * 4u : kDrop;
