@@ -301,6 +301,24 @@ misa_status misa_indexer_q8(const misa_shape* shape, const uint16_t* q, const fl
 size_t misa_indexer_q8_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime);
 
 /*
+ * Paged key cache -> the contiguous keys every call here reads.  Serving
+ * engines keep the indexer keys in pages of page_keys keys named by a
+ * per-sequence block table (the GitHub issue's per-layer boundary includes
+ * this cache handling).  Key s of sequence b is row s % page_keys of page
+ * block_table[b * max_pages + s / page_keys]; the call writes keys
+ * [0, n_keys) of every sequence to k_out [n_seq][n_keys][128] (16-byte
+ * aligned) and, for fp8, their scales to scale_out [n_seq][n_keys].
+ * k_pages: [n_pages][page_keys][128] bf16 or e4m3 codes (16-byte aligned),
+ * scale_pages: [n_pages][page_keys] (fp8 only).  max_pages >=
+ * ceil(n_keys / page_keys).  Page ids outside [0, n_pages) are a
+ * precondition violation: those keys are written as zeros (scale 1), never
+ * read.  HBM-bound: 2 x the keys' bytes.
+ */
+misa_status misa_gather_keys_paged(const misa_shape* shape, const void* k_pages, misa_kdtype kdtype,
+                                   const float* scale_pages, const int32_t* block_table, int64_t max_pages,
+                                   int64_t n_pages, int32_t page_keys, void* k_out, float* scale_out, void* stream);
+
+/*
  * Pooled-key cache (chunked prefill and decode).  The GitHub issue measures
  * the indexer at a per-layer boundary that includes cache handling, under
  * chunked prefill of 8192 tokens up to a 128K prompt ("Clarification on the

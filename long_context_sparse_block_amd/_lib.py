@@ -32,7 +32,7 @@ EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_spars
             "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8",
             "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
             "misa_prefill_chunked", "misa_prefill_workspace_bytes", "misa_indexer_q8",
-            "misa_indexer_q8_workspace_bytes")
+            "misa_indexer_q8_workspace_bytes", "misa_gather_keys_paged")
 
 
 class MisaShape(ctypes.Structure):
@@ -80,6 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_indexer_cached": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i64, P, P, i64, P, P, P, sz, P],
         "misa_prefill_chunked": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer_q8": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
+        "misa_gather_keys_paged": [S, P, ctypes.c_int, P, P, i64, i64, i32, P, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -486,3 +487,25 @@ def misa_indexer_q8(shape: MisaShape, q, w, k, h: int, topk: int, k_scale, k_pri
                                 _stream(stream))
     _check(st, "misa_indexer_q8")
     return idx, vals
+
+
+def misa_gather_keys_paged(shape: MisaShape, k_pages, block_table, scale_pages=None, k_out=None, scale_out=None,
+                           stream=None):
+    """Contiguous keys [n_seq, n_keys, 128] (and fp8 scales [n_seq, n_keys]) from
+    a paged cache: k_pages [n_pages, page_keys, 128], block_table int32
+    [n_seq, max_pages]."""
+    kd = _kdtype(k_pages)
+    n_pages, page_keys = int(k_pages.shape[0]), int(k_pages.shape[1])
+    _need(k_pages, k_pages.dtype, (n_pages, page_keys, HEAD_DIM), "k_pages")
+    if kd == MISA_K_FP8_E4M3:
+        _need(scale_pages, torch.float32, (n_pages, page_keys), "scale_pages")
+    _need(block_table, torch.int32, (shape.n_seq, block_table.shape[-1]), "block_table")
+    if k_out is None:
+        k_out = torch.empty((shape.n_seq, shape.n_keys, HEAD_DIM), dtype=k_pages.dtype, device=k_pages.device)
+    if scale_out is None and kd == MISA_K_FP8_E4M3:
+        scale_out = torch.empty((shape.n_seq, shape.n_keys), dtype=torch.float32, device=k_pages.device)
+    st = load().misa_gather_keys_paged(ctypes.byref(shape), _ptr(k_pages), kd, _ptr(scale_pages), _ptr(block_table),
+                                       int(block_table.shape[-1]), n_pages, page_keys, _ptr(k_out), _ptr(scale_out),
+                                       _stream(stream))
+    _check(st, "misa_gather_keys_paged")
+    return k_out, scale_out

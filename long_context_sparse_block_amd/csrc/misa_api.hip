@@ -300,6 +300,19 @@ misa_status misa_pool_keys(const misa_shape* shape, const void* k, misa_kdtype k
   return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, tail, nullptr, (hipStream_t)stream));
 }
 
+misa_status misa_gather_keys_paged(const misa_shape* shape, const void* k_pages, misa_kdtype kdtype,
+                                   const float* scale_pages, const int32_t* block_table, int64_t max_pages,
+                                   int64_t n_pages, int32_t page_keys, void* k_out, float* scale_out, void* stream) {
+  MISA_TRY(check_shape(shape));
+  MISA_TRY(check_keys(k_pages, kdtype, scale_pages));
+  if (block_table == nullptr || k_out == nullptr || !aligned16(k_out) || page_keys < 1 || n_pages < 1)
+    return MISA_ERR_INVALID_ARG;
+  if (kdtype == MISA_K_FP8_E4M3 && scale_out == nullptr) return MISA_ERR_INVALID_ARG;
+  if (max_pages < (shape->n_keys + page_keys - 1) / page_keys) return MISA_ERR_INVALID_ARG;
+  return from_hip(misa::launch_gather_pages(*shape, k_pages, kdtype, scale_pages, block_table, max_pages, n_pages,
+                                            page_keys, k_out, scale_out, (hipStream_t)stream));
+}
+
 misa_status misa_quantize_q(const misa_shape* shape, const uint16_t* q, uint8_t* q8, float* q_scale,
                             void* stream) {
   MISA_TRY(check_shape(shape));

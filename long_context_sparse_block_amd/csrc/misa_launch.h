@@ -29,6 +29,11 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
 // of the tile KT), enough workgroups to fill the chip.
 void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR);
 
+// Paged key cache -> contiguous [n_seq][N][128] keys (and fp8 scales [n_seq][N]).
+hipError_t launch_gather_pages(const misa_shape& s, const void* pages, int kdtype, const float* page_scales,
+                               const int32_t* table, int64_t max_pages, int64_t n_pages, int page_keys, void* out,
+                               float* out_scale, hipStream_t st);
+
 // Per-(query, head) fp8 quantisation of q: q8 codes [n_seq][M][H][128] and
 // scales q_scale [n_seq][M][H].
 hipError_t launch_quant_q(const misa_shape& s, const uint16_t* q, uint8_t* q8, float* q_scale, hipStream_t st);

@@ -185,6 +185,16 @@ def test_fp8_indexer_checks(lib):
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 1, FAKE, 2, 4, 0, FAKE, None, FAKE, need - 1, None) == -3
 
 
+def test_paged_gather_checks(lib):
+    s = shape()   # 64 keys
+    g = lib.misa_gather_keys_paged
+    assert g(ctypes.byref(s), FAKE, 0, None, None, 4, 8, 16, FAKE, None, None) == -1       # no block table
+    assert g(ctypes.byref(s), FAKE, 0, None, FAKE, 3, 8, 16, FAKE, None, None) == -1       # 3 pages < 64 / 16
+    assert g(ctypes.byref(s), FAKE, 0, None, FAKE, 4, 8, 0, FAKE, None, None) == -1        # empty pages
+    assert g(ctypes.byref(s), FAKE, 1, FAKE, FAKE, 4, 8, 16, FAKE, None, None) == -1       # fp8 needs scale_out
+    assert g(ctypes.byref(s), FAKE, 1, None, FAKE, 4, 8, 16, FAKE, FAKE, None) == -1       # fp8 needs page scales
+
+
 def test_pooled_cache_calls_check_their_arguments(lib):
     s = shape()   # 64 keys, block 16: 4 complete blocks
     pc = lib.misa_pool_keys_cached

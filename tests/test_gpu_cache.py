@@ -9,7 +9,10 @@ must equal the one-call indexer bit for bit (ids and values):
     misa_indexer_cached and misa_pool_keys_cached) == misa_indexer from
     scratch at every step, across block boundaries;
   * the GLM-5-shaped 64K prompt (H = 32) in chunks of 8192, with sampled
-    rows against the oracle.
+    rows against the oracle;
+  * a paged key cache (shuffled pages, spare pages, a partial last page)
+    gathered back bit for bit, an out-of-range page id giving zero keys, and
+    the indexer on the gathered keys equal to the indexer on the originals.
 """
 import numpy as np
 import pytest
@@ -117,3 +120,57 @@ def test_glm5_prompt_chunked_prefill():
     for i in sample_rows(cfg.q_per_seq, 10):
         recs.append(recall(gi[0, i], ctx.misa(i, cfg.h, cfg.topk)["idx"]))
     assert np.mean(recs) >= 0.999, np.mean(recs)
+
+
+@pytest.mark.parametrize("kdtype,page_keys", [(gen.KDTYPE_FP8, 64), (gen.KDTYPE_BF16, 48)])
+def test_paged_keys_gather(kdtype, page_keys):
+    say("paged key cache", kdtype, page_keys)
+    cfg = gen.small_config(name="paged", n_seq=3, m=16, n=5000, hh=16, b=64, h=4, k=128, kdtype=kdtype, seed=63)
+    inp = gen.generate(cfg)
+    S, N = cfg.n_seq, cfg.n_keys
+    per_seq = -(-N // page_keys)
+    max_pages = per_seq + 2
+    n_pages = S * per_seq + 7
+    rng = np.random.default_rng(64)
+    ids = rng.permutation(n_pages)[:S * per_seq].reshape(S, per_seq).astype(np.int32)
+    table = np.full((S, max_pages), -1, np.int32)
+    table[:, :per_seq] = ids
+    kdt = inp.k.dtype
+    pages = np.zeros((n_pages, page_keys, 128), kdt)
+    pscale = np.zeros((n_pages, page_keys), np.float32)
+    for b in range(S):
+        for p in range(per_seq):
+            rows = inp.k[b, p * page_keys:(p + 1) * page_keys]
+            pages[ids[b, p], :len(rows)] = rows
+            if inp.k_scale is not None:
+                pscale[ids[b, p], :len(rows)] = inp.k_scale[b, p * page_keys:(p + 1) * page_keys]
+    dev = "cuda"
+    if kdtype == gen.KDTYPE_FP8:
+        kp = torch.from_numpy(pages).to(dev)
+        sp = torch.from_numpy(pscale).to(dev)
+    else:
+        kp = torch.from_numpy(pages.view(np.int16)).to(dev).view(torch.bfloat16)
+        sp = None
+    tt = torch.from_numpy(table).to(dev)
+    sh = shape_of(inp)
+    kg, sg = lcsb.misa_gather_keys_paged(sh, kp, tt, scale_pages=sp)
+    st = staged(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(kg.view(torch.uint8), st["t"]["k"].view(torch.uint8))
+    if sg is not None:
+        assert torch.equal(sg, st["t"]["k_scale"])
+    t = st["t"]
+    ia, va = lcsb.misa_indexer(sh, t["q"], t["w"], kg, cfg.h, cfg.topk, k_scale=sg)
+    ib, vb = whole(st, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(ia, ib) and torch.equal(va, vb)
+    # an out-of-range page id: its keys come back as zeros (scale 1), nothing read
+    bad = tt.clone()
+    bad[1, 2] = n_pages
+    kb, sb = lcsb.misa_gather_keys_paged(sh, kp, bad, scale_pages=sp)
+    torch.cuda.synchronize()
+    lo, hi = 2 * page_keys, min(3 * page_keys, N)
+    assert not bool(kb[1, lo:hi].view(torch.uint8).any())
+    if sb is not None:
+        assert bool((sb[1, lo:hi] == 1.0).all())
+    assert torch.equal(kb[0], kg[0]) and torch.equal(kb[1, :lo], kg[1, :lo])
