@@ -335,6 +335,42 @@ def main():
               flush=True)
         del qp, wp, idxp, valp, pf_ws
 
+    if not args.no_extras and not args.no_prefill:
+        # decode: the GLM-5-shaped batch of 64 sequences x 1 query over 131072
+        # keys each (bf16 keys, H = 32, B = 64), drawn on the GPU with the
+        # same distributions; from scratch, and with the pooled-key cache of
+        # the previous step (only the new key's block is pooled, K is read once)
+        dc = gen.CONFIGS["glm5_decode_64x1_n128k"]
+        gd = torch.Generator(device=dev).manual_seed(dc.seed)
+        Sd, Nd, Hd, Bd = dc.n_seq, dc.n_keys, dc.n_heads, dc.block
+        kd_ = torch.randn((Sd, Nd, 128), generator=gd, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        qd_ = torch.randn((Sd, 1, Hd, 128), generator=gd, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        wd_ = torch.randn((Sd, 1, Hd), generator=gd, device=dev, dtype=torch.float32) / 8
+        shd = lcsb.make_shape(Sd, 1, Nd, Nd - 1, Hd, Bd)
+        idd = torch.empty((Sd, 1, dc.topk), dtype=torch.int32, device=dev)
+        vad = torch.empty((Sd, 1, dc.topk), dtype=torch.float32, device=dev)
+        wsd = torch.empty(lcsb.misa_indexer_workspace_bytes(shd, dc.h, dc.topk), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(lcsb.misa_indexer_cached_workspace_bytes(shd, dc.h, dc.topk), dtype=torch.uint8,
+                          device=dev)
+        cache = lcsb.PooledCache(Sd, Nd // Bd)
+        prev = lcsb.make_shape(Sd, 0, Nd - 1, Nd - 1, Hd, Bd)
+        lcsb.misa_pool_keys_cached(prev, kd_[:, :Nd - 1].contiguous(), cache)   # the previous step's cache
+
+        def cached_step():
+            cache.n_cached = (Nd - 1) // Bd
+            lcsb.misa_indexer_cached(shd, qd_, wd_, kd_, dc.h, dc.topk, cache, idx=idd, vals=vad, ws=wsc)
+
+        dper, _, _ = run_timed([("scratch", lambda: lcsb.misa_indexer(shd, qd_, wd_, kd_, dc.h, dc.topk, idx=idd,
+                                                                       vals=vad, ws=wsd)),
+                                ("cached", cached_step)], 5, 2)
+        kbytes = Sd * Nd * 256
+        extras["decode"] = dict(workload=dc.name, ms_from_scratch=dper["scratch"], ms_with_pooled_cache=dper["cached"],
+                                key_bytes=kbytes,
+                                cached_key_read_GBs=kbytes / (dper["cached"] * 1e-3) / 1e9)
+        print(f"[bench] decode {dc.name}: {dper['scratch']:.3f} ms from scratch, {dper['cached']:.3f} ms with the "
+              f"pooled-key cache", file=sys.stderr, flush=True)
+        del kd_, qd_, wd_, wsd, wsc, cache
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
