@@ -1019,7 +1019,7 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const 
 // with an overflowed region, more candidates than the buffer holds, or fewer
 // than k is flagged (and left for the re-scoring path).
 template <int CAP, int NT, bool IDX>
-__global__ void __launch_bounds__(NT, IDX ? 3 : 2) k_topk_regions(int64_t n_keys, int k, int64_t q_pos0, int M, int n_splits,
+__global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int64_t q_pos0, int M, int n_splits,
                                                         int cap_region, int cap_list, const float* __restrict__ thr,
                                                         const f32x4* __restrict__ gvals,
                                                         const int32_t* __restrict__ gkeys,
@@ -1183,8 +1183,11 @@ hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, c
     MISA_REGIONS_LAUNCH(4096, true);
   else if (p.cap_list <= 8192)
     MISA_REGIONS_LAUNCH(8192, false);
-  else
-    MISA_REGIONS_LAUNCH(16384, false);
+  else {
+    hipLaunchKernelGGL((k_topk_regions<16384, 1024, false>), grid, dim3(1024), 0, st, s.n_keys, k, s.q_pos0,
+                       s.q_per_seq, p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx,
+                       vals, (int)sorted);
+  }
 #undef MISA_REGIONS_LAUNCH
   return hipGetLastError();
 }
