@@ -267,6 +267,30 @@ def main():
                                / PEAK_BF16_TFLOPS,
                                misa_speedup=nstep / step_ms)
         print(f"[bench] dagger {dstep:.3f} ms {dper}; dense {nstep:.3f} ms {nper}", file=sys.stderr, flush=True)
+        # selection quality on every row (reported, not a pass/fail): the share
+        # of the dense indexer's top-k that MISA and MISA-dagger recover
+        dense_idx, _ = lcsb.misa_topk(sh, logits, K, want_vals=False, ws=tk_ws)   # logits: the dense ones
+        misa_idx, _ = lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks, want_vals=False)
+        dag_idx, _ = lcsb.misa_indexer(sh, q, w, k, h, K, k_prime=kp, k_scale=ks, want_vals=False)
+
+        def recovered(a, ref):
+            s_, _ = torch.sort(torch.cat([a, ref], dim=-1), dim=-1)
+            both = ((s_[..., 1:] == s_[..., :-1]) & (s_[..., 1:] >= 0)).sum(-1).float()
+            return both / (ref >= 0).sum(-1).clamp(min=1).float()
+
+        sels = [("misa", misa_idx), ("misa_dagger", dag_idx)]
+        if cfg.kdtype == 1:
+            sels.append(("misa_fp8_query", lcsb.misa_indexer_q8(sh, q, w, k, h, K, ks, want_vals=False)[0]))
+        quality = {}
+        for name, sel in sels:
+            r = recovered(sel, dense_idx)
+            quality[name] = dict(mean=float(r.mean()), min=float(r.min()))
+        if cfg.kdtype == 1:   # fp8 queries against bf16 queries, same routing
+            r = recovered(sels[2][1], misa_idx)
+            quality["misa_fp8_query_vs_misa"] = dict(mean=float(r.mean()), min=float(r.min()))
+        extras["recall_vs_dense_topk"] = quality
+        print(f"[bench] recall vs the dense top-k {quality}", file=sys.stderr, flush=True)
+        del dense_idx, misa_idx, dag_idx, sels
         if cfg.kdtype == 1:
             # the fp8 query path: per-row quantisation, then routed scoring on
             # the fp8 matrix cores, fused with the selection (the step) and as
