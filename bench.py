@@ -206,9 +206,21 @@ def main():
         cold.append(e0.elapsed_time(e1))
     del flush
     cold_pct = [float(np.percentile(cold, p)) for p in (10, 50, 90)]
-    del ix_ws
+    # the same call captured in a HIP graph and replayed (no launch gaps
+    # between its kernels; the library allocates and synchronises nothing)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph):
+            lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks, idx=idx, vals=vals, ws=ix_ws)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    _, graph_ms, _ = run_timed([("graph", graph.replay)], args.steps, args.warmup)
+    del graph, ix_ws
     print(f"[bench] MISA step (misa_indexer) {step_ms:.3f} ms (wall {wall_ms:.3f}); warm p10/p50/p90 "
-          f"{warm_pct}; cold (1 GiB flush before each) p10/p50/p90 {cold_pct}", file=sys.stderr, flush=True)
+          f"{warm_pct}; cold (1 GiB flush before each) p10/p50/p90 {cold_pct}; graph replay {graph_ms:.3f} ms",
+          file=sys.stderr, flush=True)
     # the same path as separate calls, for the time split by stage
     per, calls_ms, _ = run_timed(misa_stages, args.steps, args.warmup)
     print(f"[bench] as separate calls {calls_ms:.3f} ms {per}", file=sys.stderr, flush=True)
@@ -428,6 +440,7 @@ def main():
         "separate_calls_ms": calls_ms,
         "step_ms_p10_p50_p90": warm_pct,
         "cold_step_ms_p10_p50_p90": cold_pct,
+        "graph_replay_ms": graph_ms,
         "cpu_baseline": cpu,
     }
     line.update(extras)
