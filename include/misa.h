@@ -187,7 +187,8 @@ size_t misa_topk_workspace_bytes(const misa_shape* shape, int32_t n_cols, int32_
  * top-k the GitHub issue asks for as a "fused MISA kernel").  The result is
  * exactly misa_topk(misa_sparse_head_logits(...), topk, sorted): same ids,
  * same values, same order (sorted != 0) or the same set (sorted == 0).
- * When every query's prefix has at least 32768 keys and h <= 8, the scores of
+ * When h <= 8, topk <= 8192 and every query's prefix has at least
+ * max(16384, 4 topk) keys, the scores of
  * a key sample (every kstride-th key, kstride >= 32) give each row a
  * threshold; the routed scoring keeps only the scores at or above it, as
  * candidates, and the exact top-k is taken over them.  A row whose

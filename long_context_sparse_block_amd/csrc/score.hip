@@ -635,7 +635,10 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   FusedPlan p{};
   const int64_t N = s.n_keys;
   const int64_t n_min = s.q_pos0 + 1;   // shortest prefix of the chunk
-  p.ok = h <= 8 && k <= 8192 && n_min >= 32768 && s.q_per_seq > 0;
+  // prefixes long enough that the candidates are a small share of each row
+  // (k at most a quarter of the shortest prefix; below 16384 keys the
+  // materialised logits are cheap anyway)
+  p.ok = h <= 8 && k <= 8192 && n_min >= std::max<int64_t>(16384, 4 * (int64_t)k) && s.q_per_seq > 0;
   if (!p.ok) return p;
   p.kstride = (int)std::max<int64_t>(32, (N + 4095) / 4096);   // <= 4096 sampled keys per row
   p.n_sample = (N + p.kstride - 1) / p.kstride;

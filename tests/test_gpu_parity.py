@@ -348,6 +348,7 @@ FUSED_CASES = [
          kdtype=gen.KDTYPE_BF16),
     dict(name="fused_decode", n_seq=6, m=1, n=50000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_BF16),
     dict(name="fused_2seq_fp8", n_seq=2, m=70, n=38000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_FP8),
+    dict(name="fused_mid_prefix", n_seq=1, m=64, n=20000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_BF16),
 ]
 
 
