@@ -121,7 +121,9 @@ struct KStageSw {
 // tile key sw_tile_key(row) -- the layout KStageSw writes.  With fp8 scales,
 // every wave loads the tile's 64 scales (256 bytes) into the same LDS floats
 // (identical data).  Rows past N read as zeros.
-template <int KDT, int NT>
+// AUX: cache policy of the loads (kStream when each key is read by one
+// workgroup only: decode, one query tile per sequence)
+template <int KDT, int NT, int AUX = 0>
 __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sbase, int key0, int N, int ks,
                                          int lane, int wave, unsigned char* s_dst, float* s_sc_dst) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -136,12 +138,12 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
     const int j = r0 + (lane >> 4);
     const int c = (lane & 15) ^ (j & 15);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)(s_dst + r0 * kSwRowBytes), 16,
-                                             (uint32_t)(sw_tile_key(j) * ks) * kSwRowBytes + c * 16, 0, 0, 0);
+                                             (uint32_t)(sw_tile_key(j) * ks) * kSwRowBytes + c * 16, 0, 0, AUX);
   }
   if (KDT == MISA_K_FP8_E4M3) {
     const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + first, (uint32_t)rem * 4u);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr)s_sc_dst, 4, (uint32_t)(sw_tile_key(lane) * ks) * 4u, 0,
-                                             0, 0);
+                                             0, AUX);
   }
 }
 
@@ -287,10 +289,20 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   // staging of tile `key` into LDS buffer `buf`: issued before the current
   // tile's compute, completed (stage_done) after it, before the barrier
   KStageSw<KDT, NT> stg;
+  // with one query tile per sequence (decode) every key is read once: the
+  // key tiles stream past the caches (same-box: 392 -> 337 us for 64
+  // sequences x 131072 keys; with many query tiles the keys are re-read and
+  // must stay cached)
+  const bool stream_keys = n_qtiles == 1;
   auto stage_issue = [&](int key, int buf) {
-    if (DMA)
-      dma_tile<KDT, NT>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
-                        buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0);
+    if (DMA) {
+      if (stream_keys)
+        dma_tile<KDT, NT, kStream>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
+                                   buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0);
+      else
+        dma_tile<KDT, NT>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
+                          buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0);
+    }
     else
       stg.load(kb_ptr, sc_ptr, key, Nk, kstride, tid);
   };
