@@ -151,7 +151,7 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
 }
 
 struct IndexerLayout {
-  size_t pooled, split, tail, heads, q8, qscale, cand, dlog, total;
+  size_t pooled, split, tail, heads, rpart, q8, qscale, cand, dlog, total;
   int64_t ld_d;
   SelectLayout sel;
 };
@@ -175,6 +175,9 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, 
   off += align_up((size_t)rows * MISA_HEAD_DIM * sizeof(float));
   L.heads = off;
   off += align_up((size_t)rows * h * sizeof(int32_t));
+  const int n_parts = misa::route_parts(s);
+  L.rpart = n_parts > 1 ? off : SIZE_MAX;   // the router's partial block sums (few queries)
+  if (n_parts > 1) off += align_up((size_t)rows * n_parts * s.n_heads * sizeof(float));
   if (quant_q) {   // fp8 queries and their scales (misa_indexer_q8)
     L.q8 = off;
     off += align_up((size_t)rows * s.n_heads * MISA_HEAD_DIM);
@@ -205,7 +208,8 @@ misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base,
   float* tail = reinterpret_cast<float*>(base + L.tail);
   int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
   MISA_TRY(from_hip(launch_pool(s, k, kdtype, k_scale, pooled, tail, split, st, n_cached, ld_blk)));
-  MISA_TRY(from_hip(launch_route(s, q, w, pooled, split, tail, h, heads, nullptr, st, ld_blk)));
+  float* rpart = L.rpart == SIZE_MAX ? nullptr : reinterpret_cast<float*>(base + L.rpart);
+  MISA_TRY(from_hip(launch_route(s, q, w, pooled, split, tail, h, heads, nullptr, st, ld_blk, rpart)));
   QuantQ qq{reinterpret_cast<uint8_t*>(base + L.q8), reinterpret_cast<float*>(base + L.qscale)};
   if (quant_q)
     MISA_TRY(from_hip(misa::launch_quant_q(s, q, const_cast<uint8_t*>(qq.q8), const_cast<float*>(qq.q_scale), st)));

@@ -20,10 +20,14 @@ hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const flo
                        int64_t ld_blk = -1);
 
 // split (nullable): launch_pool's hi/lo rows, staged directly instead of
-// splitting `pooled` in every workgroup (same values); ld_blk as launch_pool
+// splitting `pooled` in every workgroup (same values); ld_blk as launch_pool.
+// part_ws (nullable, with split): [rows][route_parts(s)][H] floats that let a
+// launch with few workgroups (decode) split each block sum over more of them.
+constexpr int kMaxRouteParts = 8;
+int route_parts(const misa_shape& s);   // 1: no split
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
                         const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
-                        hipStream_t st, int64_t ld_blk = -1);
+                        hipStream_t st, int64_t ld_blk = -1, float* part_ws = nullptr);
 
 // Key-range split of a scoring grid: n_ksplits ranges of KR keys (a multiple
 // of the tile KT), enough workgroups to fill the chip.

@@ -23,6 +23,9 @@
 // block mask and the block sum stay in registers; the tail term is an fp32 dot
 // per (query, head); the top-h selection is a rank count over <= 64 values,
 // one wave per query.
+#include <algorithm>
+#include <type_traits>
+
 #include "misa_common.h"
 #include "misa_launch.h"
 
@@ -35,6 +38,48 @@ constexpr int kRowBytes = kD * 2;           // bf16 LDS row (256 bytes), 16-byte
 // byte offset of 16-byte chunk c of staged row j
 __device__ __forceinline__ uint32_t rt_off(int j, int c) { return (uint32_t)j * kRowBytes + (uint32_t)((c ^ (j & 15)) << 4); }
 
+
+// ReLU(q[row, j] . tail[row]) (fp32 dot over bf16 q), 0 when query t's prefix
+// ends on a block boundary (no partial block)
+__device__ __forceinline__ float tail_term(const uint16_t* __restrict__ q, const float* __restrict__ tail, int64_t row,
+                                           int64_t t, int B, int H, int j) {
+  if (((t + 1) % B) == 0) return 0.f;
+  const uint4* qr = reinterpret_cast<const uint4*>(q + (row * H + j) * kD);
+  const float4* tr = reinterpret_cast<const float4*>(tail + row * kD);
+  float dot = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < kD / 8; ++c) {
+    uint4 qv = qr[c];
+    float4 t0 = tr[2 * c], t1 = tr[2 * c + 1];
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.x & 0xFFFF), t0.x, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.x >> 16), t0.y, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.y & 0xFFFF), t0.z, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.y >> 16), t0.w, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.z & 0xFFFF), t1.x, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.z >> 16), t1.y, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.w & 0xFFFF), t1.z, dot);
+    dot = __builtin_fmaf(bf16_bits_to_f32(qv.w >> 16), t1.w, dot);
+  }
+  return __builtin_fmaxf(dot, 0.f);
+}
+
+// top-h of one query's r (lane j holds r_j, the wave's LDS row sr holds all
+// of them) by rank counting, ties -> lower head id, stored ascending
+__device__ __forceinline__ void select_heads(const float* sr, int H, int h, int64_t row, int32_t* heads,
+                                             float* scores) {
+  const int j = threadIdx.x & 63;
+  const float rj = (j < H) ? sr[j] : 0.f;
+  int cnt = 0;
+  for (int jj = 0; jj < H; ++jj) {
+    const float rv = sr[jj];
+    cnt += (rv > rj) || (rv == rj && jj < j);
+  }
+  const bool sel = (j < H) && (cnt < h);
+  const uint64_t mask = __ballot(sel);
+  const int pos = __popcll(mask & ((1ull << j) - 1ull));
+  if (sel) heads[row * h + pos] = j;
+  if (scores != nullptr && j < H) scores[row * H + j] = rj;
+}
 
 // NHC: 16-head chunks per query group (= ceil(H/16)).  PRESPLIT: the pooled
 // keys' bf16 hi and lo rows come precomputed (`split`: per sequence, ld_blk
@@ -49,7 +94,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
                                                const float* __restrict__ tail,
                                                int32_t* __restrict__ heads, float* __restrict__ scores,
                                                int64_t q_pos0, int M, int H, int B, int h,
-                                               int64_t ld_blk) {
+                                               int64_t ld_blk, int n_parts, float* __restrict__ part_out) {
   constexpr int QG = (NHC == 1) ? 4 : (NHC == 2 ? 2 : 1);  // query groups per workgroup
   constexpr int NW = NHC * QG;                              // waves per workgroup
   constexpr int QWG = 4 * QG;                               // queries per workgroup
@@ -157,8 +202,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     const uint16_t* hb0 = split + (int64_t)b * 2 * ld_blk * kD;
     const int64_t lo_off = ld_blk * kD;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // part blockIdx.z of n_parts covers the blocks [c_lo, c_hi)
+    const int64_t per = ((nfull_wg + n_parts - 1) / n_parts + 2 * kPreChunk - 1) / (2 * kPreChunk) * (2 * kPreChunk);
+    const int64_t c_lo = (int64_t)blockIdx.z * per, c_hi = min(nfull_wg, c_lo + per);
     auto stage = [&](int64_t cbase, unsigned char* sh, unsigned char* sl) {
-      const int64_t nrows = max((int64_t)0, min((int64_t)kPreChunk, nfull_wg - cbase));   // zeros past it
+      const int64_t nrows = max((int64_t)0, min((int64_t)kPreChunk, c_hi - cbase));   // zeros past it
       const __amdgpu_buffer_rsrc_t rh = uniform_rsrc(hb0 + cbase * kD, (uint32_t)nrows * kRowBytes);
       const __amdgpu_buffer_rsrc_t rl = uniform_rsrc(hb0 + lo_off + cbase * kD, (uint32_t)nrows * kRowBytes);
       for (int u = wv; u < 2 * (kPreChunk / 4); u += NW) {
@@ -169,15 +217,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
                                                  (uint32_t)(j * kRowBytes + c * 16), 0, 0, 0);
       }
     };
-    stage(0, s_h0, s_l0);
+    stage(c_lo, s_h0, s_l0);
     __builtin_amdgcn_s_waitcnt(0);   // (also the q fragments)
     __syncthreads();
-    for (int64_t cbase = 0; cbase < nfull_wg; cbase += 2 * kPreChunk) {
-      stage(cbase + kPreChunk, s_h1, s_l1);   // rows past nfull_wg: an empty range, no data
+    for (int64_t cbase = c_lo; cbase < c_hi; cbase += 2 * kPreChunk) {
+      stage(cbase + kPreChunk, s_h1, s_l1);   // rows past c_hi: an empty range, no data
       chunk_blocks(s_h0, s_l0, cbase, kPreChunk / 16);
       __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next chunk (no other memory ops in flight)
       __syncthreads();
-      if (cbase + kPreChunk < nfull_wg) {
+      if (cbase + kPreChunk < c_hi) {
         stage(cbase + 2 * kPreChunk, s_h0, s_l0);
         chunk_blocks(s_h1, s_l1, cbase + kPreChunk, kPreChunk / 16);
         __builtin_amdgcn_s_waitcnt(0);
@@ -241,31 +289,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (p16 == rb * 4 + i) s_sel = S[rb][i];
+  if (n_parts > 1) {
+    // one part of the block sum: k_route_finish adds the parts (in order) and the tail
+    const int qi = q0w + g;
+    const int j = hc * 16 + p16;
+    if (qi < M && j < H) part_out[(((int64_t)b * M + qi) * n_parts + blockIdx.z) * H + j] = s_sel;
+    return;   // uniform over the workgroup
+  }
   {
     const int qi = q0w + g;
     const int j = hc * 16 + p16;
     if (qi < M && j < H) {
-      const int64_t t = q_pos0 + qi;
-      if (((t + 1) % B) != 0) {
-        const uint4* qr = reinterpret_cast<const uint4*>(q + (((int64_t)b * M + qi) * H + j) * kD);
-        const float4* tr = reinterpret_cast<const float4*>(tail + ((int64_t)b * M + qi) * kD);
-        float dot = 0.f;
-#pragma unroll 4
-        for (int c = 0; c < kD / 8; ++c) {
-          uint4 qv = qr[c];
-          float4 t0 = tr[2 * c], t1 = tr[2 * c + 1];
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.x & 0xFFFF), t0.x, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.x >> 16), t0.y, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.y & 0xFFFF), t0.z, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.y >> 16), t0.w, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.z & 0xFFFF), t1.x, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.z >> 16), t1.y, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.w & 0xFFFF), t1.z, dot);
-          dot = __builtin_fmaf(bf16_bits_to_f32(qv.w >> 16), t1.w, dot);
-        }
-        s_sel += __builtin_fmaxf(dot, 0.f);
-      }
-      s_r[qg * 4 + g][j] = w[((int64_t)b * M + qi) * H + j] * s_sel;
+      const int64_t row = (int64_t)b * M + qi;
+      s_sel += tail_term(q, tail, row, q_pos0 + qi, B, H, j);
+      s_r[qg * 4 + g][j] = w[row * H + j] * s_sel;
     }
   }
   __syncthreads();
@@ -274,39 +311,65 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   for (int ql = wave; ql < QWG; ql += NW) {
     const int qi = q0_wg + ql;
     if (qi >= M) continue;
-    const int j = lane;
-    const float rj = (j < H) ? s_r[ql][j] : 0.f;
-    int cnt = 0;
-    for (int jj = 0; jj < H; ++jj) {
-      const float rv = s_r[ql][jj];
-      cnt += (rv > rj) || (rv == rj && jj < j);
-    }
-    const bool sel = (j < H) && (cnt < h);
-    const uint64_t mask = __ballot(sel);
-    const int pos = __popcll(mask & ((1ull << j) - 1ull));
-    const int64_t row = (int64_t)b * M + qi;
-    if (sel) heads[row * h + pos] = j;
-    if (scores != nullptr && j < H) scores[row * H + j] = rj;
+    select_heads(s_r[ql], H, h, (int64_t)b * M + qi, heads, scores);
   }
+}
+
+// Parts of a split block sum (few queries: decode) -> S, r and the top-h: one
+// wave per query, lane j the head; the parts are added in order, then the
+// tail term, as the unsplit kernel adds its running sum and the tail.
+__global__ void __launch_bounds__(256) k_route_finish(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                      const float* __restrict__ tail,
+                                                      const float* __restrict__ part, int n_parts,
+                                                      int32_t* __restrict__ heads, float* __restrict__ scores,
+                                                      int64_t q_pos0, int M, int H, int B, int h, int64_t rows) {
+  __shared__ float s_r[4][64];
+  const int wave = threadIdx.x >> 6, j = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;   // uniform over the wave; no workgroup barrier below
+  const int qi = (int)(row % M);
+  float r = 0.f;
+  if (j < H) {
+    float S = 0.f;
+    for (int p = 0; p < n_parts; ++p) S += part[(row * n_parts + p) * H + j];
+    S += tail_term(q, tail, row, q_pos0 + qi, B, H, j);
+    r = w[row * H + j] * S;
+  }
+  s_r[wave][j] = r;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  select_heads(s_r[wave], H, h, row, heads, scores);
+}
+
+int route_parts(const misa_shape& s) {
+  const int nhc = (s.n_heads + 15) / 16;
+  const int qwg = 4 * ((nhc == 1) ? 4 : (nhc == 2 ? 2 : 1));
+  const int64_t wgs = (int64_t)((s.q_per_seq + qwg - 1) / qwg) * s.n_seq;
+  const int64_t nfull_max = (s.q_pos0 + s.q_per_seq) / s.block;
+  if (wgs >= 256 || nfull_max < 256) return 1;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxRouteParts, (512 + wgs - 1) / wgs, nfull_max / 128}));
 }
 
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,
                         const uint16_t* split, const float* tail, int h, int32_t* heads, float* scores,
-                        hipStream_t st, int64_t ld_blk) {
+                        hipStream_t st, int64_t ld_blk, float* part_ws) {
   const int H = s.n_heads;
   const int nhc = (H + 15) / 16;
   const int qg = (nhc == 1) ? 4 : (nhc == 2 ? 2 : 1);
   const int qwg = 4 * qg;
   const int64_t n_full_total = ld_blk < 0 ? s.n_keys / s.block : ld_blk;
-  dim3 grid((unsigned)((s.q_per_seq + qwg - 1) / qwg), (unsigned)s.n_seq);
+  // few workgroups (decode) and long prefixes: split each workgroup's block
+  // sum into parts over more workgroups, then a finishing kernel
+  const int n_parts = (part_ws != nullptr && split != nullptr) ? route_parts(s) : 1;
+  dim3 grid((unsigned)((s.q_per_seq + qwg - 1) / qwg), (unsigned)s.n_seq, (unsigned)n_parts);
   dim3 block((unsigned)(64 * nhc * qg));
 #define MISA_ROUTE_LAUNCH(NHC_)                                                                          \
   if (split != nullptr)                                                                                   \
     hipLaunchKernelGGL((k_route<NHC_, true>), grid, block, 0, st, q, w, pooled, split, tail, heads, scores, \
-                       s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total);                              \
+                       s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total, n_parts, part_ws);            \
   else                                                                                                    \
     hipLaunchKernelGGL((k_route<NHC_, false>), grid, block, 0, st, q, w, pooled, split, tail, heads,      \
-                       scores, s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total)
+                       scores, s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total, 1, nullptr)
   switch (nhc) {
     case 1: MISA_ROUTE_LAUNCH(1); break;
     case 2: MISA_ROUTE_LAUNCH(2); break;
@@ -314,6 +377,13 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
     default: MISA_ROUTE_LAUNCH(4); break;
   }
 #undef MISA_ROUTE_LAUNCH
+  if (n_parts > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+    hipLaunchKernelGGL(k_route_finish, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q, w, tail, part_ws,
+                       n_parts, heads, scores, s.q_pos0, s.q_per_seq, H, s.block, h, rows);
+  }
   return hipGetLastError();
 }
 
