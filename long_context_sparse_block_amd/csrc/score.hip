@@ -204,10 +204,9 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   const int qa = tc.qt * QT;
   const int qb = min(qa + QT, M);
   const int64_t qrow0 = (int64_t)b * M;
-  if (out_spec.row_flag != nullptr) {
-    bool any = false;
-    for (int i = qa; i < qb; ++i) any |= out_spec.row_flag[qrow0 + i] != 0;
-    if (!any) return;   // uniform over the workgroup
+  if (out_spec.row_flag != nullptr) {   // one flag per thread (QT <= 256), loaded together
+    const bool mine = tid < qb - qa && out_spec.row_flag[qrow0 + qa + tid] != 0;
+    if (!__syncthreads_or(mine)) return;   // uniform over the workgroup
   }
   const int t_last = (q_pos0 + qb - 1) / kstride;
   const int kend = min(k1, t_last + 1);   // key indices past kend are masked for every query

@@ -1153,6 +1153,12 @@ __global__ void __launch_bounds__(NT, 2) k_topk_flagged(const float* __restrict_
                                                         int32_t* __restrict__ idx_out, float* __restrict__ val_out,
                                                         int sorted) {
   __shared__ TopkShared<CAP, NT> sh;
+  {   // the workgroup's flags loaded together: most calls have none
+    uint32_t mine = 0;
+    for (int64_t r = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; r < rows; r += (int64_t)NT * gridDim.x)
+      mine |= flag[r];
+    if (!__syncthreads_or(mine != 0)) return;   // uniform over the workgroup
+  }
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     if (flag[r] == 0) continue;   // uniform over the workgroup
     topk_row<CAP, NT>(sh, (int)(r % M), (int)(r / M), logits, ld, nullptr, (int)n_keys, k, q_pos0, M, idx_out,
