@@ -361,14 +361,12 @@ struct TopkShared {
   uint32_t count;
 };
 
-// LDS of the region select for lists of up to CAP candidates: the candidates
-// and their order by bucket as 16-bit indices (instead of a second copy of
-// the composites), so three 512-thread workgroups fit per CU.
+// LDS of the region select for lists of up to CAP candidates: one copy of
+// the candidates, sorted by bucket in place (through registers), so three
+// 512-thread workgroups fit per CU.
 template <int CAP, int NT>
 struct TopkSharedIdx {
-  static_assert(CAP <= 65536, "16-bit indices");
   uint64_t buf[CAP];
-  uint16_t order[CAP];
   uint32_t hist[kHistBins];
   uint32_t wave[NT / 64];
   uint64_t red[2 * (NT / 64)];
@@ -377,12 +375,15 @@ struct TopkSharedIdx {
 };
 
 // rank_write over all cnt (<= CAP) raw entries of sh.buf, given their min and
-// max composite: the counting sort scatters indices into sh.order, and each
-// candidate's rank inside its bucket is found by comparing through them.
+// max composite: each thread holds its entries' composites in registers, the
+// counting sort scatters them back into sh.buf (now bucket-sorted
+// composites), and each candidate's rank inside its bucket is found by
+// comparing with the bucket's other entries.
 template <int CAP, int NT>
 __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
                                                int32_t* idx_out, float* val_out, uint64_t cmin, uint64_t cmax) {
   static_assert(CAP <= 8 * NT, "the bitonic fallback holds 8 entries per thread");
+  constexpr int EPT = CAP / NT;   // entries per thread
   const int tid = threadIdx.x;
   constexpr int BPT = kHistBins / NT;
   if (cnt > 0) {
@@ -415,21 +416,26 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
         sh.hist[kHistBins - 1 - (BPT * tid + u)] = start;   // cursor = bucket start
         start += hv[u];
       }
-      __syncthreads();
-      for (uint32_t e = tid; e < cnt; e += NT) {
-        const uint32_t d = (uint32_t)((raw_to_comp(sh.buf[e]) - cmin) >> shift);
-        sh.order[atomicAdd(&sh.hist[d], 1u)] = (uint16_t)e;
+      uint64_t mine[EPT];   // this thread's entries, read before any is overwritten
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const uint32_t e = tid + j * NT;
+        mine[j] = e < cnt ? raw_to_comp(sh.buf[e]) : 0;
       }
+      __syncthreads();   // (the cursors, and every thread's reads of sh.buf)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        if (tid + j * NT < cnt) sh.buf[atomicAdd(&sh.hist[(uint32_t)((mine[j] - cmin) >> shift)], 1u)] = mine[j];
       __syncthreads();
       // sh.hist[d] is now the end of bucket d; bucket d spans [end(d+1), end(d))
       for (uint32_t e = tid; e < cnt; e += NT) {
-        const uint64_t c = raw_to_comp(sh.buf[sh.order[e]]);
+        const uint64_t c = sh.buf[e];
         const uint32_t d = (uint32_t)((c - cmin) >> shift);
         const uint32_t b0 = (d + 1 < (uint32_t)kHistBins) ? sh.hist[d + 1] : 0;
         if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
         const uint32_t b1 = sh.hist[d];
         uint32_t r = b0;
-        for (uint32_t q = b0; q < b1; ++q) r += raw_to_comp(sh.buf[sh.order[q]]) > c;
+        for (uint32_t q = b0; q < b1; ++q) r += sh.buf[q] > c;
         if (r < (uint32_t)k) {
           idx_out[row * k + r] = comp_id(c);
           if (val_out) val_out[row * k + r] = comp_val(c);
