@@ -51,6 +51,8 @@ namespace misa {
 constexpr int kDigit = 11;                 // radix digit width
 constexpr int kHistBins = 1 << kDigit;
 constexpr uint32_t kMaxRankBucket = 64;    // larger buckets -> bitonic fallback
+constexpr int kDigitIdx = 12;              // the region select's rank buckets
+constexpr int kHistBinsIdx = 1 << kDigitIdx;
 
 __device__ __forceinline__ uint64_t pack_raw(float v, int32_t id) {
   return ((uint64_t)(uint32_t)id << 32) | (uint64_t)__float_as_uint(v);
@@ -367,7 +369,7 @@ struct TopkShared {
 template <int CAP, int NT>
 struct TopkSharedIdx {
   uint64_t buf[CAP];
-  uint32_t hist[kHistBins];
+  uint32_t hist[kHistBinsIdx];
   uint32_t wave[NT / 64];
   uint64_t red[2 * (NT / 64)];
   uint32_t sel[3];
@@ -385,20 +387,21 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
   static_assert(CAP <= 8 * NT, "the bitonic fallback holds 8 entries per thread");
   constexpr int EPT = CAP / NT;   // entries per thread
   const int tid = threadIdx.x;
-  constexpr int BPT = kHistBins / NT;
+  constexpr int HB = kHistBinsIdx;   // finer buckets than rank_write: fewer in-bucket comparisons
+  constexpr int BPT = HB / NT;
   if (cnt > 0) {
     const int nb = bit_width64(cmax - cmin);
-    const int shift = nb > kDigit ? nb - kDigit : 0;
-    for (int e = tid; e < kHistBins; e += NT) sh.hist[e] = 0;
+    const int shift = nb > kDigitIdx ? nb - kDigitIdx : 0;
+    for (int e = tid; e < HB; e += NT) sh.hist[e] = 0;
     __syncthreads();
     for (uint32_t e = tid; e < cnt; e += NT)
       atomicAdd(&sh.hist[(uint32_t)((raw_to_comp(sh.buf[e]) - cmin) >> shift)], 1u);
     __syncthreads();
-    // bucket starts, highest bucket first: thread owns buckets 2047-BPT*tid-u
+    // bucket starts, highest bucket first: thread owns buckets HB-1-BPT*tid-u
     uint32_t hv[BPT], ls = 0, big = 0;
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      hv[u] = sh.hist[kHistBins - 1 - (BPT * tid + u)];
+      hv[u] = sh.hist[HB - 1 - (BPT * tid + u)];
       ls += hv[u];
       big = hv[u] > big ? hv[u] : big;
     }
@@ -413,7 +416,7 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
     } else {
 #pragma unroll
       for (int u = 0; u < BPT; ++u) {
-        sh.hist[kHistBins - 1 - (BPT * tid + u)] = start;   // cursor = bucket start
+        sh.hist[HB - 1 - (BPT * tid + u)] = start;   // cursor = bucket start
         start += hv[u];
       }
       uint64_t mine[EPT];   // this thread's entries, read before any is overwritten
@@ -431,7 +434,7 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
       for (uint32_t e = tid; e < cnt; e += NT) {
         const uint64_t c = sh.buf[e];
         const uint32_t d = (uint32_t)((c - cmin) >> shift);
-        const uint32_t b0 = (d + 1 < (uint32_t)kHistBins) ? sh.hist[d + 1] : 0;
+        const uint32_t b0 = (d + 1 < (uint32_t)HB) ? sh.hist[d + 1] : 0;
         if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
         const uint32_t b1 = sh.hist[d];
         uint32_t r = b0;
