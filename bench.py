@@ -90,8 +90,8 @@ def src_hash(*names):
 
 
 KERNEL_SOURCES = {
-    "select": ("score.hip", "topk.hip", "misa_common.h"),
-    "staged_score": ("score.hip", "misa_common.h"),
+    "select": ("score.hip", "score_shared.h", "topk.hip", "misa_common.h"),
+    "staged_score": ("score.hip", "score_shared.h", "misa_common.h"),
     "staged_topk": ("topk.hip", "misa_common.h"),
     "route": ("route.hip", "misa_common.h"),
     "pool": ("pool.hip", "misa_common.h"),
