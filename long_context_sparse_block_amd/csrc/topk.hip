@@ -132,13 +132,15 @@ __device__ __forceinline__ int bit_width64(uint64_t x) { return x ? 64 - __clzll
 // threshold T with need <= #{c >= T} <= limit (the upper bound can only fail
 // for duplicate entries); with limit == need it selects exactly the need
 // largest.  Requires 1 <= need <= n.  Every thread of the workgroup must call it.
+// have_mm: the caller already holds the composites' min and max.
 template <int NT>
 __device__ __forceinline__ uint64_t select_threshold(const uint64_t* buf, uint32_t n, uint32_t need, uint32_t limit,
-                                     uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint64_t* s_red) {
+                                     uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint64_t* s_red,
+                                     bool have_mm = false, uint64_t mm_lo = 0, uint64_t mm_hi = 0) {
   const int tid = threadIdx.x;
   constexpr int BPT = kHistBins / NT;  // bins per thread
-  uint64_t cmin, cmax;
-  block_minmax<NT>(buf, n, s_red, &cmin, &cmax);
+  uint64_t cmin = mm_lo, cmax = mm_hi;
+  if (!have_mm) block_minmax<NT>(buf, n, s_red, &cmin, &cmax);
   const int nb = bit_width64(cmax - cmin);
   if (nb == 0) return cmin;
   // digits over x = c - cmin, from the highest bit in which the composites differ
@@ -851,7 +853,8 @@ __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cn
   }
   const uint32_t kk = min((uint32_t)k, cnt);
   if (cnt > kk) {
-    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red);
+    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red, have_mm, mm_lo,
+                                             mm_hi);
     cnt = compact<NT>(sh.buf, cnt, Tk, sh.wave);
   }
   cnt = min(cnt, (uint32_t)(CAP / 2));
@@ -885,7 +888,8 @@ __device__ __forceinline__ void finish_list_idx(TopkSharedIdx<CAP, NT>& sh, uint
   }
   const uint32_t kk = min((uint32_t)k, cnt);
   if (cnt > kk) {
-    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red);
+    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red, true, mm_lo,
+                                             mm_hi);
     cnt = compact<NT>(sh.buf, cnt, Tk, sh.wave);
   }
   for (int e = tid; e < k; e += NT) {
