@@ -226,6 +226,57 @@ __device__ __forceinline__ uint32_t compact(uint64_t* buf, uint32_t n, uint64_t 
   return base;
 }
 
+// The entries of buf whose composite is >= T written straight to the row's
+// outputs (a set: buffer order), at most k of them; returns how many.
+template <int NT>
+__device__ __forceinline__ uint32_t compact_write(const uint64_t* buf, uint32_t n, uint64_t T, uint32_t* s_wave,
+                                                  int64_t row, int k, int32_t* idx_out, float* val_out) {
+  const int tid = threadIdx.x;
+  uint32_t base = 0;
+  for (uint32_t c0 = 0; c0 < n; c0 += 4 * NT) {
+    uint64_t c[4];
+    bool keep[4];
+    uint32_t nk = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t e = c0 + tid + u * NT;
+      c[u] = (e < n) ? raw_to_comp(buf[e]) : 0;
+      keep[u] = (e < n) && c[u] >= T;
+      nk += keep[u];
+    }
+    uint32_t total;
+    uint32_t pos = base + block_exclusive_scan<NT>(nk, s_wave, &total);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (keep[u]) {
+        if (pos < (uint32_t)k) {
+          idx_out[row * k + pos] = comp_id(c[u]);
+          if (val_out) val_out[row * k + pos] = comp_val(c[u]);
+        }
+        ++pos;
+      }
+    base += total;
+    __syncthreads();   // s_wave is reused by the next chunk's scan
+  }
+  return base < (uint32_t)k ? base : (uint32_t)k;
+}
+
+// the set of the top kk of buf's cnt entries (radix select, then written
+// straight out), padded to k
+template <int NT>
+__device__ __forceinline__ void write_set(const uint64_t* buf, uint32_t cnt, int k, int64_t row, int32_t* idx_out,
+                                          float* val_out, uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel,
+                                          uint64_t* s_red, bool have_mm, uint64_t mm_lo, uint64_t mm_hi) {
+  const uint32_t kk = min((uint32_t)k, cnt);
+  const uint64_t Tk =
+      cnt > kk ? select_threshold<NT>(buf, cnt, kk, kk, s_hist, s_wave, s_sel, s_red, have_mm, mm_lo, mm_hi) : 0;
+  const uint32_t w = compact_write<NT>(buf, cnt, Tk, s_wave, row, k, idx_out, val_out);
+  for (uint32_t p = w + threadIdx.x; p < (uint32_t)k; p += NT) {
+    idx_out[row * k + p] = -1;
+    if (val_out) val_out[row * k + p] = -__builtin_inff();
+  }
+}
+
 // Bitonic sort of the composites of the first cnt raw entries of buf held in
 // registers (E consecutive network positions per thread; strides below E are
 // in-thread, below 64E lane shuffles, wider ones go through LDS), then the
@@ -851,6 +902,10 @@ __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cn
     rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red, have_mm, mm_lo, mm_hi);
     return;
   }
+  if (!sorted) {
+    write_set<NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.sel, sh.red, have_mm, mm_lo, mm_hi);
+    return;
+  }
   const uint32_t kk = min((uint32_t)k, cnt);
   if (cnt > kk) {
     const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red, have_mm, mm_lo,
@@ -858,20 +913,6 @@ __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cn
     cnt = compact<NT>(sh.buf, cnt, Tk, sh.wave);
   }
   cnt = min(cnt, (uint32_t)(CAP / 2));
-  if (!sorted) {
-    for (int e = tid; e < k; e += NT) {
-      int32_t id = -1;
-      float v = -__builtin_inff();
-      if ((uint32_t)e < cnt) {
-        const uint64_t cc = raw_to_comp(sh.buf[e]);
-        id = comp_id(cc);
-        v = comp_val(cc);
-      }
-      idx_out[row * k + e] = id;
-      if (val_out) val_out[row * k + e] = v;
-    }
-    return;
-  }
   rank_write<CAP, NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.red);
 }
 
@@ -886,23 +927,7 @@ __device__ __forceinline__ void finish_list_idx(TopkSharedIdx<CAP, NT>& sh, uint
     rank_write_idx<CAP, NT>(sh, cnt, k, row, idx_out, val_out, mm_lo, mm_hi);
     return;
   }
-  const uint32_t kk = min((uint32_t)k, cnt);
-  if (cnt > kk) {
-    const uint64_t Tk = select_threshold<NT>(sh.buf, cnt, kk, kk, sh.hist, sh.wave, sh.sel, sh.red, true, mm_lo,
-                                             mm_hi);
-    cnt = compact<NT>(sh.buf, cnt, Tk, sh.wave);
-  }
-  for (int e = tid; e < k; e += NT) {
-    int32_t id = -1;
-    float v = -__builtin_inff();
-    if ((uint32_t)e < cnt) {
-      const uint64_t cc = raw_to_comp(sh.buf[e]);
-      id = comp_id(cc);
-      v = comp_val(cc);
-    }
-    idx_out[row * k + e] = id;
-    if (val_out) val_out[row * k + e] = v;
-  }
+  write_set<NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.sel, sh.red, true, mm_lo, mm_hi);
 }
 
 // Exact top-k of a row's candidate list (every element at or above the row's
