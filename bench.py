@@ -435,6 +435,10 @@ def main():
         "config": {"workload": cfg.name, "n_seq": S, "M": M, "N": N, "H_I": H, "h": h, "B": B, "topk": K,
                    "k_dtype": "fp8_e4m3" if cfg.kdtype == 1 else "bf16", "head_dim": 128},
         "roofline": roofline,
+        # the metric's MFMA utilisation: the dominant call's algorithmic flops
+        # over its measured time and the bf16 dense peak (the hardware
+        # MFMA-busy counters per kernel are in the committed profiles)
+        "mfma_util_pct": round(100.0 * roofline["frac"], 1) if roofline.get("frac") is not None else None,
         "stages": stages_out,
         "step": "one misa_indexer call: pool, route, fused routed scoring + top-k",
         "separate_calls_ms": calls_ms,
