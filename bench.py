@@ -154,8 +154,9 @@ def main():
     tk_ws_bytes = max(lcsb.misa_topk_workspace_bytes(sh, N, K), lcsb.misa_topk_workspace_bytes(sh, N, kp),
                       lcsb.misa_topk_workspace_bytes(sh, kp, K), 1)
     tk_ws = torch.empty(tk_ws_bytes, dtype=torch.uint8, device=dev)   # top-k scratch, allocated once
-    sel_ws = torch.empty(max(lcsb.misa_sparse_head_topk_workspace_bytes(sh, h, K),
-                             lcsb.misa_sparse_head_topk_workspace_bytes(sh, h, kp)), dtype=torch.uint8, device=dev)
+    sel_ws = torch.empty(max(lcsb.misa_sparse_head_topk_workspace_bytes(sh, cfg.kdtype, h, K),
+                             lcsb.misa_sparse_head_topk_workspace_bytes(sh, cfg.kdtype, h, kp)), dtype=torch.uint8,
+                         device=dev)
 
     def run_timed(stages, steps, warmup):
         """stages: list of (name, fn).  Returns per-stage mean ms and step ms."""
@@ -188,7 +189,7 @@ def main():
     ]
     # the step: the whole indexer as one C call (pool, route, fused selection;
     # the router stages pooled keys the pooling kernel has already split)
-    ix_ws = torch.empty(lcsb.misa_indexer_workspace_bytes(sh, h, K), dtype=torch.uint8, device=dev)
+    ix_ws = torch.empty(lcsb.misa_indexer_workspace_bytes(sh, cfg.kdtype, h, K), dtype=torch.uint8, device=dev)
     _, step_ms, wall_ms = run_timed([("indexer", lambda: lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks, idx=idx,
                                                                            vals=vals, ws=ix_ws))],
                                     args.steps, args.warmup)
@@ -358,7 +359,7 @@ def main():
         shp = lcsb.make_shape(1, N, N, 0, H, B)
         idxp = torch.empty((1, N, K), dtype=torch.int32, device=dev)
         valp = torch.empty((1, N, K), dtype=torch.float32, device=dev)
-        pf_ws = torch.empty(lcsb.misa_prefill_workspace_bytes(shp, h, K, 0, M), dtype=torch.uint8, device=dev)
+        pf_ws = torch.empty(lcsb.misa_prefill_workspace_bytes(shp, cfg.kdtype, h, K, 0, M), dtype=torch.uint8, device=dev)
         pper, pstep, _ = run_timed([("prefill", lambda: lcsb.misa_prefill_chunked(
             shp, qp, wp, k, h, K, chunk=M, k_scale=ks, idx=idxp, vals=valp, ws=pf_ws))], 3, 1)
         ref_idx, _ = lcsb.misa_indexer(sh, q, w, k, h, K, k_scale=ks)   # the step's own result
@@ -385,8 +386,8 @@ def main():
         shd = lcsb.make_shape(Sd, 1, Nd, Nd - 1, Hd, Bd)
         idd = torch.empty((Sd, 1, dc.topk), dtype=torch.int32, device=dev)
         vad = torch.empty((Sd, 1, dc.topk), dtype=torch.float32, device=dev)
-        wsd = torch.empty(lcsb.misa_indexer_workspace_bytes(shd, dc.h, dc.topk), dtype=torch.uint8, device=dev)
-        wsc = torch.empty(lcsb.misa_indexer_cached_workspace_bytes(shd, dc.h, dc.topk), dtype=torch.uint8,
+        wsd = torch.empty(lcsb.misa_indexer_workspace_bytes(shd, dc.kdtype, dc.h, dc.topk), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(lcsb.misa_indexer_cached_workspace_bytes(shd, dc.kdtype, dc.h, dc.topk), dtype=torch.uint8,
                           device=dev)
         cache = lcsb.PooledCache(Sd, Nd // Bd)
         prev = lcsb.make_shape(Sd, 0, Nd - 1, Nd - 1, Hd, Bd)

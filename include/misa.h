@@ -205,7 +205,11 @@ misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, co
                                   const int32_t* heads, int32_t h, int32_t topk, int32_t sorted,
                                   int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream);
 
-size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk);
+/* Workspace of misa_sparse_head_topk for keys of type kdtype (fp8 keys add a
+ * bf16 copy of the keys, widened exactly once per call for the scoring's
+ * direct global -> LDS staging); 0 for an invalid shape. */
+size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h,
+                                             int32_t topk);
 
 /*
  * fp8 path.  The pages' indexer runs on fp8 inputs, and the GitHub issue on
@@ -260,8 +264,9 @@ misa_status dsa_dense_logits_q8(const misa_shape* shape, const uint8_t* q8, cons
  * issue asks for an fp8 MISA kernel with the top-k overhead cut; this is it.
  * kdtype must be MISA_K_FP8_E4M3 and 1 <= h <= 8 (MISA_ERR_UNSUPPORTED
  * otherwise).  The workspace is misa_sparse_head_topk_workspace_bytes(shape,
- * h, topk) bytes (16-byte aligned).  Other arguments as
- * misa_sparse_head_topk.
+ * MISA_K_FP8_E4M3, h, topk) bytes (16-byte aligned; the fp8 keys feed the
+ * fp8 matrix cores as they are, so part of it stays unused).  Other arguments
+ * as misa_sparse_head_topk.
  */
 misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8, const float* q_scale,
                                      const float* w, const void* k, misa_kdtype kdtype, const float* k_scale,
@@ -283,7 +288,8 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
                          int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
                          void* stream);
 
-size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk,
+/* Workspace of misa_indexer for keys of type kdtype; 0 for an invalid shape. */
+size_t misa_indexer_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
                                     int32_t k_prime);
 
 /*
@@ -358,8 +364,8 @@ misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, cons
                                 int64_t cap_blocks, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
                                 void* stream);
 
-size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk,
-                                           int32_t k_prime);
+size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h,
+                                           int32_t topk, int32_t k_prime);
 
 /* Chunked prefill driver: the indexer over the shape's M queries (positions
  * q_pos0 .. q_pos0+M-1 of each sequence) in chunks of `chunk` queries, the way
@@ -375,8 +381,8 @@ misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, con
                                  int32_t k_prime, int32_t chunk, int32_t* idx, float* vals, void* ws,
                                  size_t ws_bytes, void* stream);
 
-size_t misa_prefill_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime,
-                                    int32_t chunk);
+size_t misa_prefill_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
+                                    int32_t k_prime, int32_t chunk);
 
 #ifdef __cplusplus
 }

@@ -88,15 +88,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.misa_topk_workspace_bytes.argtypes = [S, i32, i32]
     lib.misa_topk_workspace_bytes.restype = sz
-    lib.misa_sparse_head_topk_workspace_bytes.argtypes = [S, i32, i32]
+    lib.misa_sparse_head_topk_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32]
     lib.misa_sparse_head_topk_workspace_bytes.restype = sz
-    lib.misa_indexer_workspace_bytes.argtypes = [S, i32, i32, i32]
+    lib.misa_indexer_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32]
     lib.misa_indexer_workspace_bytes.restype = sz
-    lib.misa_indexer_cached_workspace_bytes.argtypes = [S, i32, i32, i32]
+    lib.misa_indexer_cached_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32]
     lib.misa_indexer_cached_workspace_bytes.restype = sz
     lib.misa_indexer_q8_workspace_bytes.argtypes = [S, i32, i32, i32]
     lib.misa_indexer_q8_workspace_bytes.restype = sz
-    lib.misa_prefill_workspace_bytes.argtypes = [S, i32, i32, i32, i32]
+    lib.misa_prefill_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32, i32]
     lib.misa_prefill_workspace_bytes.restype = sz
     _lib = lib
     return lib
@@ -258,8 +258,9 @@ def misa_topk_workspace_bytes(shape: MisaShape, n_cols: int, k: int) -> int:
     return int(load().misa_topk_workspace_bytes(ctypes.byref(shape), int(n_cols), int(k)))
 
 
-def misa_sparse_head_topk_workspace_bytes(shape: MisaShape, h: int, topk: int) -> int:
-    return int(load().misa_sparse_head_topk_workspace_bytes(ctypes.byref(shape), int(h), int(topk)))
+def misa_sparse_head_topk_workspace_bytes(shape: MisaShape, kdtype: int, h: int, topk: int) -> int:
+    """kdtype: MISA_K_BF16 or MISA_K_FP8_E4M3 (the key type of the call)."""
+    return int(load().misa_sparse_head_topk_workspace_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk)))
 
 
 def misa_sparse_head_topk(shape: MisaShape, q, w, k, heads, topk: int, k_scale=None, sorted=True, idx=None,
@@ -277,7 +278,7 @@ def misa_sparse_head_topk(shape: MisaShape, q, w, k, heads, topk: int, k_scale=N
     if vals is None and want_vals:
         vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = torch.empty(max(misa_sparse_head_topk_workspace_bytes(shape, h, topk), 1), dtype=torch.uint8,
+        ws = torch.empty(max(misa_sparse_head_topk_workspace_bytes(shape, kd, h, topk), 1), dtype=torch.uint8,
                          device=q.device)
     st = load().misa_sparse_head_topk(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale),
                                       _ptr(heads), int(h), int(topk), int(bool(sorted)), _ptr(idx), _ptr(vals),
@@ -334,7 +335,7 @@ def misa_sparse_head_topk_q8(shape: MisaShape, q8, q_scale, w, k, heads, topk: i
     if vals is None and want_vals:
         vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q8.device)
     if ws is None:
-        ws = torch.empty(max(misa_sparse_head_topk_workspace_bytes(shape, h, topk), 1), dtype=torch.uint8,
+        ws = torch.empty(max(misa_sparse_head_topk_workspace_bytes(shape, kd, h, topk), 1), dtype=torch.uint8,
                          device=q8.device)
     st = load().misa_sparse_head_topk_q8(ctypes.byref(shape), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k), kd,
                                          _ptr(k_scale), _ptr(heads), int(h), int(topk), int(bool(sorted)),
@@ -358,8 +359,9 @@ def dsa_dense_logits_q8(shape: MisaShape, q8, q_scale, w, k, k_scale, logits=Non
     return logits
 
 
-def misa_indexer_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:
-    return int(load().misa_indexer_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime)))
+def misa_indexer_workspace_bytes(shape: MisaShape, kdtype: int, h: int, topk: int, k_prime: int = 0) -> int:
+    return int(load().misa_indexer_workspace_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk),
+                                                   int(k_prime)))
 
 
 def misa_indexer(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: int = 0, k_scale=None,
@@ -373,7 +375,7 @@ def misa_indexer(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: int = 0,
         idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
     if vals is None and want_vals:
         vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
-    need = misa_indexer_workspace_bytes(shape, h, topk, k_prime)
+    need = misa_indexer_workspace_bytes(shape, kd, h, topk, k_prime)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = load().misa_indexer(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
@@ -409,8 +411,9 @@ def misa_pool_keys_cached(shape: MisaShape, k, cache: PooledCache, k_scale=None,
     return tail
 
 
-def misa_indexer_cached_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0) -> int:
-    return int(load().misa_indexer_cached_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime)))
+def misa_indexer_cached_workspace_bytes(shape: MisaShape, kdtype: int, h: int, topk: int, k_prime: int = 0) -> int:
+    return int(load().misa_indexer_cached_workspace_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk),
+                                                          int(k_prime)))
 
 
 def misa_indexer_cached(shape: MisaShape, q, w, k, h: int, topk: int, cache: PooledCache, k_prime: int = 0,
@@ -426,8 +429,8 @@ def misa_indexer_cached(shape: MisaShape, q, w, k, h: int, topk: int, cache: Poo
     if vals is None and want_vals:
         vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = torch.empty(max(misa_indexer_cached_workspace_bytes(shape, h, topk, k_prime), 1), dtype=torch.uint8,
-                         device=q.device)
+        ws = torch.empty(max(misa_indexer_cached_workspace_bytes(shape, kd, h, topk, k_prime), 1),
+                         dtype=torch.uint8, device=q.device)
     st = load().misa_indexer_cached(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
                                     int(topk), int(k_prime), int(cache.n_cached), _ptr(cache.pooled),
                                     _ptr(cache.split), cache.cap_blocks, _ptr(idx), _ptr(vals), _ptr(ws),
@@ -437,9 +440,10 @@ def misa_indexer_cached(shape: MisaShape, q, w, k, h: int, topk: int, cache: Poo
     return idx, vals
 
 
-def misa_prefill_workspace_bytes(shape: MisaShape, h: int, topk: int, k_prime: int = 0, chunk: int = 8192) -> int:
-    return int(load().misa_prefill_workspace_bytes(ctypes.byref(shape), int(h), int(topk), int(k_prime),
-                                                   int(chunk)))
+def misa_prefill_workspace_bytes(shape: MisaShape, kdtype: int, h: int, topk: int, k_prime: int = 0,
+                                 chunk: int = 8192) -> int:
+    return int(load().misa_prefill_workspace_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk),
+                                                   int(k_prime), int(chunk)))
 
 
 def misa_prefill_chunked(shape: MisaShape, q, w, k, h: int, topk: int, chunk: int = 8192, k_prime: int = 0,
@@ -455,8 +459,8 @@ def misa_prefill_chunked(shape: MisaShape, q, w, k, h: int, topk: int, chunk: in
     if vals is None and want_vals:
         vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = torch.empty(max(misa_prefill_workspace_bytes(shape, h, topk, k_prime, chunk), 1), dtype=torch.uint8,
-                         device=q.device)
+        ws = torch.empty(max(misa_prefill_workspace_bytes(shape, kd, h, topk, k_prime, chunk), 1),
+                         dtype=torch.uint8, device=q.device)
     st = load().misa_prefill_chunked(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
                                      int(topk), int(k_prime), int(chunk), _ptr(idx), _ptr(vals), _ptr(ws),
                                      int(ws.numel()), _stream(stream))

@@ -62,7 +62,9 @@ struct SelectLayout {
   misa::FusedPlan fused;
 };
 
-SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off) {
+// wide_keys: reserve the bf16 copy of fp8 keys that the direct-load staging
+// of the bf16-query scoring reads (fp8 keys, bf16 queries)
+SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off, bool wide_keys) {
   SelectLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   L.ld = (s.n_keys + 3) / 4 * 4;
@@ -71,8 +73,8 @@ SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off) {
   L.fused = misa::plan_fused(s, h, k);
   if (L.fused.ok) {
     const misa::FusedPlan& p = L.fused;
-    L.kwide = off;   // bf16 copy of fp8 keys (reserved for either key type)
-    off += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128 (shape check)
+    L.kwide = off;   // bf16 copy of fp8 keys
+    if (wide_keys) off += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128
     L.sample = off;
     off += align_up((size_t)rows * (size_t)p.ld_sample * sizeof(float));
     L.thr = off;
@@ -158,7 +160,7 @@ struct IndexerLayout {
 
 // own_pool: the pooled keys (and their bf16 hi/lo rows) live in the
 // workspace; otherwise in a caller-owned cache (misa_indexer_cached)
-IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, bool own_pool = true,
+IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, int k_prime, bool own_pool = true,
                              bool quant_q = false) {
   IndexerLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
@@ -190,7 +192,7 @@ IndexerLayout indexer_layout(const misa_shape& s, int h, int topk, int k_prime, 
     L.dlog = off;
     off += align_up((size_t)rows * (size_t)L.ld_d * sizeof(float));
   }
-  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off);
+  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off, kdtype == MISA_K_FP8_E4M3 && !quant_q);
   off = L.sel.end;
   // the final top-k of MISA-dagger runs over k' candidate columns
   if (k_prime > 0) off += align_up(misa::topk_workspace_bytes(s, k_prime, topk));
@@ -261,7 +263,7 @@ struct PrefillLayout {
   int64_t cap;
 };
 
-PrefillLayout prefill_layout(const misa_shape& s, int h, int topk, int k_prime, int chunk) {
+PrefillLayout prefill_layout(const misa_shape& s, int kdtype, int h, int topk, int k_prime, int chunk) {
   PrefillLayout L{};
   L.cap = std::max<int64_t>(1, (s.q_pos0 + s.q_per_seq) / s.block);
   size_t off = 0;
@@ -273,7 +275,7 @@ PrefillLayout prefill_layout(const misa_shape& s, int h, int topk, int k_prime, 
   size_t most = 0;
   const int n_chunks = (int)((s.q_per_seq + chunk - 1) / chunk);
   for (int c = 0; c < n_chunks; ++c)
-    most = std::max(most, indexer_layout(chunk_shape(s, c, chunk), h, topk, k_prime, false).total);
+    most = std::max(most, indexer_layout(chunk_shape(s, c, chunk), kdtype, h, topk, k_prime, false).total);
   L.total = off + most;
   return L;
 }
@@ -432,9 +434,10 @@ misa_status misa_topk(const misa_shape* shape, const float* logits, int64_t ld, 
                               (hipStream_t)stream, sorted != 0));
 }
 
-size_t misa_indexer_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
+size_t misa_indexer_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
+                                    int32_t k_prime) {
   if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
-  return indexer_layout(*shape, h, topk, k_prime).total;
+  return indexer_layout(*shape, kdtype, h, topk, k_prime).total;
 }
 
 misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
@@ -442,7 +445,7 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
                          int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
                          void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
-  const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
@@ -453,7 +456,7 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
 
 size_t misa_indexer_q8_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
   if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
-  return indexer_layout(*shape, h, topk, k_prime, true, true).total;
+  return indexer_layout(*shape, MISA_K_FP8_E4M3, h, topk, k_prime, true, true).total;
 }
 
 misa_status misa_indexer_q8(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
@@ -461,7 +464,7 @@ misa_status misa_indexer_q8(const misa_shape* shape, const uint16_t* q, const fl
                             int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   if (kdtype != MISA_K_FP8_E4M3 || h > 8) return MISA_ERR_UNSUPPORTED;   // the fp8 x fp8 routed kernels
-  const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime, true, true);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, true, true);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
@@ -481,9 +484,10 @@ misa_status misa_pool_keys_cached(const misa_shape* shape, const void* k, misa_k
                               n_cached, cap_blocks));
 }
 
-size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime) {
+size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
+                                           int32_t k_prime) {
   if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
-  return indexer_layout(*shape, h, topk, k_prime, false).total;
+  return indexer_layout(*shape, kdtype, h, topk, k_prime, false).total;
 }
 
 misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
@@ -492,7 +496,7 @@ misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, cons
                                 int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   MISA_TRY(check_cache(shape, n_cached, pooled, pooled_split, cap_blocks));
-  const IndexerLayout L = indexer_layout(*shape, h, topk, k_prime, false);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, false);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0)   // no queries: only bring the cache up to date
     return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, nullptr, pooled_split, (hipStream_t)stream,
@@ -501,10 +505,10 @@ misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, cons
                      pooled_split, n_cached, cap_blocks, idx, vals, (hipStream_t)stream);
 }
 
-size_t misa_prefill_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk, int32_t k_prime,
-                                    int32_t chunk) {
+size_t misa_prefill_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
+                                    int32_t k_prime, int32_t chunk) {
   if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0 || chunk < 1) return 0;
-  return prefill_layout(*shape, h, topk, k_prime, chunk).total;
+  return prefill_layout(*shape, kdtype, h, topk, k_prime, chunk).total;
 }
 
 misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
@@ -512,7 +516,7 @@ misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, con
                                  int32_t chunk, int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   if (chunk < 1) return MISA_ERR_INVALID_ARG;
-  const PrefillLayout P = prefill_layout(*shape, h, topk, k_prime, chunk);
+  const PrefillLayout P = prefill_layout(*shape, kdtype, h, topk, k_prime, chunk);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < P.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
@@ -528,7 +532,7 @@ misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, con
     for (int c = 0; c < n_chunks; ++c) {
       const misa_shape sc = chunk_shape(*shape, c, chunk);
       const int64_t r0 = (int64_t)b * M + (int64_t)c * chunk;   // first query row of the chunk
-      const IndexerLayout L = indexer_layout(sc, h, topk, k_prime, false);
+      const IndexerLayout L = indexer_layout(sc, kdtype, h, topk, k_prime, false);
       MISA_TRY(run_indexer(sc, L, base + P.ixws, q + r0 * H * MISA_HEAD_DIM, w + r0 * H,
                            static_cast<const char*>(k) + (size_t)b * N * key_bytes, kdtype,
                            k_scale != nullptr ? k_scale + (size_t)b * N : nullptr, h, topk, k_prime, pooled, split,
@@ -550,7 +554,7 @@ misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, co
     return MISA_ERR_INVALID_ARG;
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
-  const SelectLayout L = select_layout(*shape, h, topk, 0);
+  const SelectLayout L = select_layout(*shape, h, topk, 0, kdtype == MISA_K_FP8_E4M3);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.end) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   return run_select(*shape, L, static_cast<char*>(ws), q, w, k, kdtype, k_scale, heads, h, topk, sorted != 0, idx,
@@ -569,7 +573,7 @@ misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8,
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (h > 8) return MISA_ERR_UNSUPPORTED;
   if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
-  const SelectLayout L = select_layout(*shape, h, topk, 0);
+  const SelectLayout L = select_layout(*shape, h, topk, 0, false);   // fp8 keys feed the fp8 MFMA as they are
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.end) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   const QuantQ qq{q8, q_scale};
@@ -577,9 +581,9 @@ misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8,
                     idx, vals, (hipStream_t)stream, &qq);
 }
 
-size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, int32_t h, int32_t topk) {
+size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk) {
   if (check_shape(shape) != MISA_OK || h < 1 || topk < 1) return 0;
-  return select_layout(*shape, h, topk, 0).end;
+  return select_layout(*shape, h, topk, 0, kdtype == MISA_K_FP8_E4M3).end;
 }
 
 }  // extern "C"

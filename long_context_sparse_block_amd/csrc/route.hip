@@ -94,7 +94,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
                                                const float* __restrict__ tail,
                                                int32_t* __restrict__ heads, float* __restrict__ scores,
                                                int64_t q_pos0, int M, int H, int B, int h,
-                                               int64_t ld_blk, int n_parts, float* __restrict__ part_out) {
+                                               int64_t ld_blk, int n_parts, float* __restrict__ part_out,
+                                               int seq_parts) {
   constexpr int QG = (NHC == 1) ? 4 : (NHC == 2 ? 2 : 1);  // query groups per workgroup
   constexpr int NW = NHC * QG;                              // waves per workgroup
   constexpr int QWG = 4 * QG;                               // queries per workgroup
@@ -152,6 +153,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[rb][i] = 0.f;
 
+  // the block sum so far over the 16 block columns held by the 16 lanes of a
+  // row group; lane (g, p16) keeps head hc*16 + p16 of query q0w + g.  The
+  // lanes' running sums restart from 0.
+  auto fold = [&]() -> float {
+    float sel = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = S[rb][i];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        if (p16 == rb * 4 + i) sel = v;
+        S[rb][i] = 0.f;
+      }
+    return sel;
+  };
+  // A block sum split into parts (part z of n covers blocks [z per, (z+1) per),
+  // per a multiple of 64) is added part by part: over workgroups (blockIdx.z,
+  // n_parts > 1, finished by k_route_finish) or here in order (seq_parts > 1),
+  // so that both give the same sum bit for bit.
+  const int n_split = n_parts > 1 ? n_parts : seq_parts;
+  const int64_t per = ((nfull_wg + n_split - 1) / n_split + 2 * kPreChunk - 1) / (2 * kPreChunk) * (2 * kPreChunk);
+  float s_acc = 0.f;   // seq_parts > 1: the parts folded so far
+
   // column block cb (16 pooled rows from row cbase + 16 cb of the chunk) of a
   // staged chunk: hi/lo fragments from LDS, 8 MFMAs per row block, ReLU and
   // the block sum in registers
@@ -203,8 +231,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     const int64_t lo_off = ld_blk * kD;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     // part blockIdx.z of n_parts covers the blocks [c_lo, c_hi)
-    const int64_t per = ((nfull_wg + n_parts - 1) / n_parts + 2 * kPreChunk - 1) / (2 * kPreChunk) * (2 * kPreChunk);
-    const int64_t c_lo = (int64_t)blockIdx.z * per, c_hi = min(nfull_wg, c_lo + per);
+    const int64_t c_lo = n_parts > 1 ? (int64_t)blockIdx.z * per : 0;
+    const int64_t c_hi = n_parts > 1 ? min(nfull_wg, c_lo + per) : nfull_wg;
     auto stage = [&](int64_t cbase, unsigned char* sh, unsigned char* sl) {
       const int64_t nrows = max((int64_t)0, min((int64_t)kPreChunk, c_hi - cbase));   // zeros past it
       const __amdgpu_buffer_rsrc_t rh = uniform_rsrc(hb0 + cbase * kD, (uint32_t)nrows * kRowBytes);
@@ -221,6 +249,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     __builtin_amdgcn_s_waitcnt(0);   // (also the q fragments)
     __syncthreads();
     for (int64_t cbase = c_lo; cbase < c_hi; cbase += 2 * kPreChunk) {
+      if (seq_parts > 1 && cbase > 0 && cbase % per == 0) s_acc += fold();
       stage(cbase + kPreChunk, s_h1, s_l1);   // rows past c_hi: an empty range, no data
       chunk_blocks(s_h0, s_l0, cbase, kPreChunk / 16);
       __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next chunk (no other memory ops in flight)
@@ -235,6 +264,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   } else {
   const float* pool_b = pooled + (int64_t)b * ld_blk * kD;
   for (int64_t cbase = 0; cbase < nfull_wg; cbase += kRouteChunk) {
+    if (seq_parts > 1 && cbase > 0 && cbase % per == 0) s_acc += fold();
     // stage pooled rows [cbase, cbase+64) as bf16 hi/lo
     constexpr int kTotal = kRouteChunk * (kD / 4);                 // float4 of a chunk
     constexpr int kPer = (kTotal + NW * 64 - 1) / (NW * 64);       // per thread (3 waves: ragged)
@@ -270,25 +300,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   }
   }
 
-  // sum over the 16 block columns held by the 16 lanes of a row group
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = S[rb][i];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      S[rb][i] = v;
-    }
-  // lane (g, p16) now handles head hc*16 + p16 of query q0w + g
-  float s_sel = 0.f;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (p16 == rb * 4 + i) s_sel = S[rb][i];
+  // lane (g, p16) handles head hc*16 + p16 of query q0w + g
+  float s_sel = fold();
+  if (seq_parts > 1) s_sel = s_acc + s_sel;
   if (n_parts > 1) {
     // one part of the block sum: k_route_finish adds the parts (in order) and the tail
     const int qi = q0w + g;
@@ -361,15 +375,17 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
   // few workgroups (decode) and long prefixes: split each workgroup's block
   // sum into parts over more workgroups, then a finishing kernel
   const int n_parts = (part_ws != nullptr && split != nullptr) ? route_parts(s) : 1;
+  // without the part workspace, the same parts are added in order in-kernel
+  const int seq_parts = n_parts > 1 ? 1 : route_parts(s);
   dim3 grid((unsigned)((s.q_per_seq + qwg - 1) / qwg), (unsigned)s.n_seq, (unsigned)n_parts);
   dim3 block((unsigned)(64 * nhc * qg));
 #define MISA_ROUTE_LAUNCH(NHC_)                                                                          \
   if (split != nullptr)                                                                                   \
     hipLaunchKernelGGL((k_route<NHC_, true>), grid, block, 0, st, q, w, pooled, split, tail, heads, scores, \
-                       s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total, n_parts, part_ws);            \
+                       s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total, n_parts, part_ws, seq_parts); \
   else                                                                                                    \
     hipLaunchKernelGGL((k_route<NHC_, false>), grid, block, 0, st, q, w, pooled, split, tail, heads,      \
-                       scores, s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total, 1, nullptr)
+                       scores, s.q_pos0, s.q_per_seq, H, s.block, h, n_full_total, 1, nullptr, seq_parts)
   switch (nhc) {
     case 1: MISA_ROUTE_LAUNCH(1); break;
     case 2: MISA_ROUTE_LAUNCH(2); break;

@@ -675,6 +675,9 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   // expected candidates), doubled, plus room for a few clusters of large scores
   const int64_t expect = (int64_t)p.target * KR / n_min + 1;
   p.cap_region = (int)((2 * expect + 512 + 255) / 256 * 256);
+  // a key range of KR keys holds at most KR / 4 groups: short ranges (few
+  // queries spread over many ranges) never need more
+  p.cap_region = (int)std::min<int64_t>(p.cap_region, (KR + 3) / 4);
   // a workgroup's 32 rows of regions are addressed with byte offsets below 2^31
   if ((int64_t)32 * p.n_splits * p.cap_region * 16 >= ((int64_t)1 << 31)) p.ok = false;
   return p;

@@ -43,7 +43,11 @@ Parity unpinned: the router's definition (how the partial block enters and
 how the per-block affinities and the head weight combine into one head
 importance) is a reading; the pages fix no formula or worked example for it.
 Its arithmetic is pinned (brute force, the B = 1 closed form, relabelling and
-scaling invariants), its agreement with the pages is not.
+scaling invariants), its agreement with the pages is not.  The other readings
+(partial block dropped; |w| or no weight; max instead of sum over blocks) are
+available here (head_importance_reading) so that the tests can measure how
+many routed heads change between readings; the HIP path implements only the
+first.
 """
 from __future__ import annotations
 
@@ -186,6 +190,39 @@ def head_importance(qt: np.ndarray, wt: np.ndarray, pooled: np.ndarray, tail, t:
     return S, wt * S
 
 
+# Other readings of the router, for measuring how much the routed heads depend
+# on the reading (the pages say the per-head affinities against the pooled
+# block keys are aggregated along the blocks, but print no formula):
+#   tail:   "pool" (the partial last block is pooled over its visible keys:
+#           the block count ceil(L/B) includes it) | "drop" (floor(L/B)
+#           complete blocks only);
+#   weight: "signed" (r = w S) | "abs" (r = |w| S) | "none" (r = S);
+#   agg:    "sum" (S = sum over blocks of ReLU(q . pooled)) | "max" (S = the
+#           largest of those terms, 0 without any block).
+# The first of each is the reading every other function here takes.
+ROUTER_READINGS = dict(tail=("pool", "drop"), weight=("signed", "abs", "none"), agg=("sum", "max"))
+
+
+def head_importance_reading(qt, wt, pooled, tail, t, B, tail_mode="pool", weight="signed", agg="sum"):
+    """head_importance under the reading (tail_mode, weight, agg); returns (S, r)."""
+    assert tail_mode in ROUTER_READINGS["tail"] and weight in ROUTER_READINGS["weight"]
+    assert agg in ROUTER_READINGS["agg"]
+    n_full = (t + 1) // B
+    cols = [pooled[:n_full]]
+    if tail is not None and tail_mode == "pool":
+        cols.append(tail[None, :])
+    blocks = np.concatenate(cols, axis=0)                    # [n_blocks, d]
+    terms = np.maximum(qt @ blocks.T, 0.0)                   # [H, n_blocks]
+    if terms.shape[1] == 0:
+        S = np.zeros(qt.shape[0])
+    elif agg == "sum":
+        S = terms.sum(axis=1)
+    else:
+        S = terms.max(axis=1)
+    f = {"signed": wt, "abs": np.abs(wt), "none": np.ones_like(wt)}[weight]
+    return S, f * S
+
+
 def top_positions(values: np.ndarray, ids: np.ndarray, count: int) -> np.ndarray:
     """Positions of the `count` entries with the largest values; equal values ->
     lower id first.  Returned in selection order (value descending, id ascending).
@@ -203,9 +240,14 @@ def top_ids(values: np.ndarray, ids: np.ndarray, count: int) -> np.ndarray:
     return ids[top_positions(values, ids, count)]
 
 
-def route_query(qt, wt, pooled, keys, t, B, h):
+def route_query(qt, wt, pooled, keys, t, B, h, reading=None):
+    """reading: None (this repository's reading), or a dict of the keywords of
+    head_importance_reading (tail_mode, weight, agg)."""
     tail = tail_of(keys, t, B)
-    S, r = head_importance(qt, wt, pooled, tail, t, B)
+    if reading is None:
+        S, r = head_importance(qt, wt, pooled, tail, t, B)
+    else:
+        S, r = head_importance_reading(qt, wt, pooled, tail, t, B, **reading)
     heads = np.sort(top_ids(r, np.arange(qt.shape[0]), h))   # stored ascending
     return S, r, heads
 
@@ -283,8 +325,8 @@ class SeqContext:
     def tail(self, i):
         return tail_of(self.keys, self.t(i), self.B)
 
-    def route(self, i, h):
-        return route_query(self.q[i], self.w[i], self.pooled, self.keys, self.t(i), self.B, h)
+    def route(self, i, h, reading=None):
+        return route_query(self.q[i], self.w[i], self.pooled, self.keys, self.t(i), self.B, h, reading)
 
     def score(self, i, heads):
         return score_query(self.q[i], self.w[i], self.keys, self.t(i), heads)

@@ -52,20 +52,36 @@ def rank_select(values, ids, count):
     return out
 
 
-def bf_route(qt, wt, keys, t, B, h):
-    """qt: list of H vectors; keys: list of vectors.  Returns S, r, heads (ascending)."""
+def bf_route(qt, wt, keys, t, B, h, tail_mode="pool", weight="signed", agg="sum"):
+    """qt: list of H vectors; keys: list of vectors.  Returns S, r, heads (ascending).
+
+    Readings: tail_mode "pool" (the partial last block is a block too) or
+    "drop"; weight "signed" (w S), "abs" (|w| S) or "none" (S); agg "sum" or
+    "max" over the blocks (0 with no block)."""
     L = t + 1
     n_full = L // B
     blocks = [mean_rows(keys[m * B:(m + 1) * B]) for m in range(n_full)]
-    if n_full * B < L:
+    if n_full * B < L and tail_mode == "pool":
         blocks.append(mean_rows(keys[n_full * B:L]))
     S = []
     for qj in qt:
         acc = 0.0
         for kb in blocks:
-            acc += relu(dot(qj, kb))
+            term = relu(dot(qj, kb))
+            if agg == "sum":
+                acc += term
+            elif term > acc:
+                acc = term
         S.append(acc)
-    r = [wt[j] * S[j] for j in range(len(qt))]
+    r = []
+    for j in range(len(qt)):
+        if weight == "signed":
+            f = wt[j]
+        elif weight == "abs":
+            f = wt[j] if wt[j] >= 0.0 else -wt[j]
+        else:
+            f = 1.0
+        r.append(f * S[j])
     heads = sorted(rank_select(r, list(range(len(qt))), h))
     return S, r, heads, blocks
 

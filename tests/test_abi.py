@@ -111,11 +111,11 @@ def test_indexer_checks_and_workspace(lib):
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 9, 4, 0, FAKE, None, FAKE, 1 << 30, None) == -1
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 3, FAKE, None, FAKE, 1 << 30, None) == -1
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, FAKE, None, None, 0, None) == -3
-    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 0)
+    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 2, 4, 0)
     assert need > 0
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, FAKE, None, FAKE, need - 1, None) == -3
     # MISA-dagger needs room for candidates and their re-ranked scores
-    need_d = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 16)
+    need_d = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 2, 4, 16)
     assert need_d > need
 
 
@@ -127,20 +127,35 @@ def test_sparse_head_topk_checks_and_workspace(lib):
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, 0, 1, FAKE, None, FAKE, 1 << 30, None) == -1
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, None, 2, 4, 1, FAKE, None, FAKE, 1 << 30, None) == -1
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, None, 0, None) == -3
-    need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 2, 4)
+    need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 0, 2, 4)
     assert need > 0
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, FAKE, need - 1, None) == -3
     # the long-context chunk takes the fused path: sampled scores and candidate
     # regions instead of the whole-row top-k's lists, beside the full logits
     # kept for rows the candidates cannot settle
     big = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
-    fused = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(big), 8, 2048)
+    fused = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(big), 1, 8, 2048)
     # target 3072 candidates per row, 8 key ranges of 16384 keys over a shortest
     # prefix of 122881: 410 expected groups per range, doubled, + 512, rounded
     # up to 256 = 1536 groups of 4 scores (16 bytes) and their first key (4)
     # plus the bf16 copy of the keys the scoring stages by direct loads (131072 x 256)
     assert fused == (8192 * 131072 * 4 + 131072 * 256 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4
                      + 8192 * 8 * 1536 * 20)
+    # bf16 keys are staged as they are: no widened copy
+    assert lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(big), 0, 8, 2048) == fused - 131072 * 256
+
+
+def test_only_fp8_keys_reserve_a_widened_copy(lib):
+    # the decode batch: 64 sequences x 131072 keys; a bf16 copy of fp8 keys
+    # would be 64 x 131072 x 256 bytes = 2 GiB
+    s = lcsb.make_shape(64, 1, 131072, 131071, 32, 64)
+    bf = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 8, 2048, 0)
+    f8 = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 1, 8, 2048, 0)
+    assert f8 - bf == 64 * 131072 * 256
+    assert bf < (1 << 30)
+    # the fp8-query indexer feeds fp8 keys to the fp8 matrix cores directly
+    q8 = lib.misa_indexer_q8_workspace_bytes(ctypes.byref(s), 8, 2048, 0)
+    assert q8 < f8
 
 
 def test_fp8_query_calls_check_their_arguments(lib):
@@ -163,7 +178,7 @@ def test_fp8_query_calls_check_their_arguments(lib):
     assert dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 66, None) == -1    # ld % 4
     assert dq(ctypes.byref(s), FAKE, FAKE, None, FAKE, 1, FAKE, FAKE, 64, None) == -1    # no weights
     tq = lib.misa_sparse_head_topk_q8
-    need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 2, 4)
+    need = lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(s), 0, 2, 4)
     assert tq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 2, 4, 1, FAKE, None, FAKE, need, None) == -2
     assert tq(ctypes.byref(s16), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 9, 4, 1, FAKE, None, FAKE, 1 << 30,
               None) == -2
@@ -177,7 +192,7 @@ def test_fp8_indexer_checks(lib):
     s = shape()
     f = lib.misa_indexer_q8
     need = lib.misa_indexer_q8_workspace_bytes(ctypes.byref(s), 2, 4, 0)
-    assert need > lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 0)   # + fp8 q and its scales
+    assert need > lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 2, 4, 0)   # + fp8 q and its scales
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, FAKE, None, FAKE, need, None) == -2   # bf16 keys
     s16 = shape(n_heads=16)
     assert f(ctypes.byref(s16), FAKE, FAKE, FAKE, 1, FAKE, 9, 16, 0, FAKE, None, FAKE, 1 << 30, None) == -2
@@ -205,8 +220,8 @@ def test_pooled_cache_calls_check_their_arguments(lib):
     assert pc(ctypes.byref(s), FAKE, 0, None, 0, FAKE, None, 4, FAKE, None) == -1     # no hi/lo rows
     assert pc(ctypes.byref(s), FAKE, 0, None, 0, FAKE, FAKE, 4, None, None) == -1     # queries need tails
     ic = lib.misa_indexer_cached
-    need = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(s), 2, 4, 0)
-    full = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 2, 4, 0)
+    need = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(s), 0, 2, 4, 0)
+    full = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 2, 4, 0)
     assert 0 < need < full   # the pooled keys live in the cache, not the workspace
     assert ic(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 0, FAKE, FAKE, 3, FAKE, None, FAKE, need,
               None) == -1
@@ -215,8 +230,8 @@ def test_pooled_cache_calls_check_their_arguments(lib):
     assert ic(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 0, FAKE, FAKE, 4, FAKE, None, FAKE, need - 1,
               None) == -3
     pf = lib.misa_prefill_chunked
-    pneed = lib.misa_prefill_workspace_bytes(ctypes.byref(s), 2, 4, 0, 2)
-    assert pneed > 0 and lib.misa_prefill_workspace_bytes(ctypes.byref(s), 2, 4, 0, 0) == 0
+    pneed = lib.misa_prefill_workspace_bytes(ctypes.byref(s), 0, 2, 4, 0, 2)
+    assert pneed > 0 and lib.misa_prefill_workspace_bytes(ctypes.byref(s), 0, 2, 4, 0, 0) == 0
     assert pf(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 0, FAKE, None, FAKE, pneed, None) == -1
     assert pf(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 0, 2, FAKE, None, FAKE, pneed - 1, None) == -3
     assert pf(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 2, 4, 3, 2, FAKE, None, FAKE, pneed, None) == -1
@@ -227,9 +242,9 @@ def test_prefill_workspace_of_a_128k_prompt(lib):
     # means + 0.5 MB of bf16 hi/lo rows) plus the last chunk's indexer
     # workspace, the largest (the full-prefix chunk of the benchmark)
     s = lcsb.make_shape(1, 131072, 131072, 0, 64, 128)
-    need = lib.misa_prefill_workspace_bytes(ctypes.byref(s), 8, 2048, 0, 8192)
+    need = lib.misa_prefill_workspace_bytes(ctypes.byref(s), 1, 8, 2048, 0, 8192)
     last = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
-    ix = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(last), 8, 2048, 0)
+    ix = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(last), 1, 8, 2048, 0)
     assert need == 1024 * 128 * 4 + 2 * 1024 * 128 * 2 + ix
 
 
@@ -242,10 +257,19 @@ def test_empty_query_set_is_a_no_op(lib):
 
 def test_workspace_size_of_the_long_context_chunk(lib):
     s = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
-    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 8, 2048, 0)
+    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 1, 8, 2048, 0)
     # the fp32 logits of the chunk (8192 x 131072 x 4 bytes; the fused path
     # writes them only for rows its candidates cannot settle), the sampled
     # scores (8192 x 4096 x 4), the candidate regions (8192 rows x 8 key
     # ranges x 1536 groups of 4 scores and a key, 20 bytes) and the bf16 keys
     main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 1536 * 20 + 131072 * 256
     assert main <= need < main * 1.01
+
+
+def test_region_capacity_never_exceeds_a_key_range(lib):
+    # 64 queries over 32768 keys: 512 key ranges of 64 keys, each of which holds
+    # at most 16 groups of 4 keys, so no region reserves more than that
+    s = lcsb.make_shape(1, 64, 32768, 32768 - 64, 64, 64)
+    need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 8, 2048, 0)
+    assert need < (32 << 20)
+

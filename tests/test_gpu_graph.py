@@ -28,7 +28,7 @@ def test_indexer_graph_replays_equal_eager(fp8_query):
     t0 = inputs[0]
     q, w, k, ks = (t0[n].clone() for n in ("q", "w", "k", "k_scale"))
     nbytes = (lcsb.misa_indexer_q8_workspace_bytes(sh, cfg.h, cfg.topk) if fp8_query
-              else lcsb.misa_indexer_workspace_bytes(sh, cfg.h, cfg.topk))
+              else lcsb.misa_indexer_workspace_bytes(sh, cfg.kdtype, cfg.h, cfg.topk))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     idx = torch.empty((1, cfg.q_per_seq, cfg.topk), dtype=torch.int32, device=q.device)
     vals = torch.empty((1, cfg.q_per_seq, cfg.topk), dtype=torch.float32, device=q.device)

@@ -369,9 +369,9 @@ def test_fused_indexer_equals_stages_and_oracle(case):
                                   k_prime=kp, k_scale=st["t"]["k_scale"])
     sidx, svals = _staged_selection(inp, st, kp)
     torch.cuda.synchronize()
-    # (with few queries the indexer's router adds its block sum in parts, the
-    # staged misa_route_heads in one pass: equal heads unless two heads' r tie to
-    # the last bit, which these seeded inputs do not have)
+    # (with few queries the indexer's router adds its block sum in parts over
+    # several workgroups; the staged misa_route_heads adds the same parts in the
+    # same order in one workgroup, so the heads agree bit for bit)
     assert torch.equal(idx, sidx) and torch.equal(vals, svals), "fused indexer != its stages"
     _check_sparse_head_topk(inp, st)
     gi = idx.cpu().numpy()
