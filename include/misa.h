@@ -27,7 +27,8 @@
  * ---------------------------------------
  * Memory   All tensor pointers are DEVICE pointers owned by the caller.  The
  *          library never allocates, frees or synchronises; scratch space comes
- *          only from a caller-provided workspace.  Every tensor is densely
+ *          from a caller-provided workspace (misa_indexer_noalloc: from a fixed
+ *          device buffer of the library).  Every tensor is densely
  *          packed in the layout given (row-major, last index fastest) and
  *          16-byte aligned.
  * Streams  `stream` is a hipStream_t passed as void* (NULL = the default
@@ -35,8 +36,10 @@
  * Errors   Arguments are checked on the host before anything is enqueued; a
  *          bad argument returns a negative misa_status and enqueues nothing.
  *          A failed kernel launch returns MISA_ERR_HIP.  No C++ exception
- *          crosses this interface; there is no mutable global state, so calls
- *          from several host threads are safe.
+ *          crosses this interface.  The only global state is the per-device
+ *          address of misa_indexer_noalloc's fixed scratch (looked up once
+ *          under a lock), so calls from several host threads are safe, except
+ *          that misa_indexer_noalloc calls sharing one GPU must not overlap.
  * Numerics Preconditions that are documented, not checked: inputs are finite;
  *          fp8 scales are > 0.  Accumulation is fp32.
  * Shapes   A call covers n_seq independent sequences.  Sequence b has n_keys
@@ -63,7 +66,9 @@ typedef enum {
   MISA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad alignment */
   MISA_ERR_UNSUPPORTED = -2,   /* a valid request outside what is implemented */
   MISA_ERR_WORKSPACE = -3,     /* workspace missing or too small */
-  MISA_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
+  MISA_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
+  MISA_ERR_SCRATCH = -5        /* misa_indexer_noalloc: more scratch needed than
+                                  MISA_NOALLOC_SCRATCH_BYTES */
 } misa_status;
 
 typedef enum {
@@ -291,6 +296,27 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
 /* Workspace of misa_indexer for keys of type kdtype; 0 for an invalid shape. */
 size_t misa_indexer_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
                                     int32_t k_prime);
+
+/*
+ * misa_indexer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments and the same result as misa_indexer, but no workspace
+ * argument.  Its scratch is a fixed device buffer of the library,
+ * MISA_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, held until the process ends;
+ * a request whose misa_indexer_workspace_bytes() exceeds it returns
+ * MISA_ERR_SCRATCH and enqueues nothing (256 MiB holds, e.g., a decode batch
+ * of 64 sequences x 131072 keys, or a prefill chunk of 512 queries over
+ * 65536 keys).  The call allocates, frees and synchronises nothing.  All
+ * calls on one GPU share that GPU's buffer, which keeps the last call's
+ * contents: calls that may overlap on one GPU (several streams, several host
+ * threads) race, so the caller must order them (one stream, or events).
+ * The first call on a device looks up the buffer's device address; later calls
+ * reuse it.
+ */
+#define MISA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+misa_status misa_indexer_noalloc(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                 misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
+                                 int32_t k_prime, int32_t* idx, float* vals, void* stream);
 
 /*
  * misa_indexer with fp8 queries for the routed scoring: pool -> route (bf16

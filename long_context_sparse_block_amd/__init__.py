@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     misa_quantize_q, misa_sparse_head_logits_q8, misa_sparse_head_topk_q8, dsa_dense_logits_q8,
     PooledCache, misa_pool_keys_cached, misa_indexer_cached, misa_indexer_cached_workspace_bytes,
     misa_prefill_chunked, misa_prefill_workspace_bytes, misa_indexer_q8, misa_indexer_q8_workspace_bytes,
-    misa_gather_keys_paged, status_str,
+    misa_gather_keys_paged, status_str, misa_indexer_noalloc, NOALLOC_SCRATCH_BYTES, MISA_ERR_SCRATCH,
 )

@@ -32,7 +32,9 @@ EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_spars
             "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8",
             "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
             "misa_prefill_chunked", "misa_prefill_workspace_bytes", "misa_indexer_q8",
-            "misa_indexer_q8_workspace_bytes", "misa_gather_keys_paged")
+            "misa_indexer_q8_workspace_bytes", "misa_gather_keys_paged", "misa_indexer_noalloc")
+MISA_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 256 << 20   # MISA_NOALLOC_SCRATCH_BYTES of misa.h
 
 
 class MisaShape(ctypes.Structure):
@@ -72,6 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_topk": [S, P, i64, P, i32, i32, i32, P, P, P, sz, P],
         "misa_sparse_head_topk": [S, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
+        "misa_indexer_noalloc": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P],
         "misa_quantize_q": [S, P, P, P, P],
         "misa_sparse_head_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "misa_sparse_head_topk_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
@@ -382,6 +385,26 @@ def misa_indexer(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: int = 0,
                              int(topk), int(k_prime), _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel()),
                              _stream(stream))
     _check(st, "misa_indexer")
+    return idx, vals
+
+
+def misa_indexer_noalloc(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: int = 0, k_scale=None,
+                         idx=None, vals=None, want_vals=True, stream=None):
+    """misa_indexer with the library's fixed device scratch instead of a
+    workspace (for callers that cannot allocate; the outputs must still be
+    given to avoid an allocation here).  Raises MisaError (MISA_ERR_SCRATCH)
+    when the request needs more than NOALLOC_SCRATCH_BYTES."""
+    kd = _check_keys(shape, k, k_scale)
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
+    st = load().misa_indexer_noalloc(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k), kd, _ptr(k_scale), int(h),
+                                     int(topk), int(k_prime), _ptr(idx), _ptr(vals), _stream(stream))
+    _check(st, "misa_indexer_noalloc")
     return idx, vals
 
 

@@ -6,9 +6,17 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "misa.h"
 #include "misa_launch.h"
+
+// Fixed device scratch of misa_indexer_noalloc (callers that cannot allocate:
+// HIP graph capture, serving loops, harnesses that forbid allocation).  Every
+// GPU the library runs on holds one copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MISA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -258,6 +266,26 @@ misa_shape chunk_shape(const misa_shape& s, int c, int chunk) {
   return sc;
 }
 
+// Per device: the address of its copy of `scratch`, looked up on the first
+// misa_indexer_noalloc call with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+misa_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MISA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MISA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MISA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return MISA_OK;
+}
+
 struct PrefillLayout {
   size_t pooled, split, ixws, total;
   int64_t cap;
@@ -291,6 +319,9 @@ const char* misa_status_str(misa_status s) {
     case MISA_ERR_UNSUPPORTED: return "MISA_ERR_UNSUPPORTED: request outside what is implemented";
     case MISA_ERR_WORKSPACE: return "MISA_ERR_WORKSPACE: workspace missing or too small";
     case MISA_ERR_HIP: return "MISA_ERR_HIP: HIP runtime error";
+    case MISA_ERR_SCRATCH:
+      return "MISA_ERR_SCRATCH: the request needs more scratch than the library's fixed device buffer "
+             "(MISA_NOALLOC_SCRATCH_BYTES) holds";
   }
   return "MISA: unknown status";
 }
@@ -449,6 +480,22 @@ misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
+  return run_indexer(*shape, L, base, q, w, k, kdtype, k_scale, h, topk, k_prime,
+                     reinterpret_cast<float*>(base + L.pooled), reinterpret_cast<uint16_t*>(base + L.split), 0,
+                     shape->n_keys / shape->block, idx, vals, (hipStream_t)stream);
+}
+
+misa_status misa_indexer_noalloc(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
+                                 misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
+                                 int32_t* idx, float* vals, void* stream) {
+  MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime);
+  if (L.total > MISA_NOALLOC_SCRATCH_BYTES) return MISA_ERR_SCRATCH;
+  if (shape->q_per_seq == 0) return MISA_OK;
+  char* base = nullptr;
+  MISA_TRY(scratch_of_current_device(&base));
+  // every counter the kernels use is initialised by a kernel of the same call:
+  // nothing in the scratch has to start at zero
   return run_indexer(*shape, L, base, q, w, k, kdtype, k_scale, h, topk, k_prime,
                      reinterpret_cast<float*>(base + L.pooled), reinterpret_cast<uint16_t*>(base + L.split), 0,
                      shape->n_keys / shape->block, idx, vals, (hipStream_t)stream);

@@ -266,6 +266,22 @@ def test_workspace_size_of_the_long_context_chunk(lib):
     assert main <= need < main * 1.01
 
 
+def test_noalloc_indexer_refuses_requests_beyond_its_scratch(lib):
+    # argument errors first, as misa_indexer
+    s = shape()
+    f = lib.misa_indexer_noalloc
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 0, None, 9, 4, 0, FAKE, None, None) == -1
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 1, None, 2, 4, 0, FAKE, None, None) == -1   # fp8 without scales
+    # the long-context chunk needs gigabytes of scratch: refused before anything is enqueued
+    big = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
+    assert lib.misa_indexer_workspace_bytes(ctypes.byref(big), 1, 8, 2048, 0) > lcsb.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, 1, FAKE, 8, 2048, 0, FAKE, None, None) == lcsb.MISA_ERR_SCRATCH
+    assert "fixed device buffer" in lcsb.status_str(lcsb.MISA_ERR_SCRATCH)
+    # a decode batch of 64 sequences x 131072 bf16 keys fits
+    dec = lcsb.make_shape(64, 1, 131072, 131071, 32, 64)
+    assert lib.misa_indexer_workspace_bytes(ctypes.byref(dec), 0, 8, 2048, 0) <= lcsb.NOALLOC_SCRATCH_BYTES
+
+
 def test_region_capacity_never_exceeds_a_key_range(lib):
     # 64 queries over 32768 keys: 512 key ranges of 64 keys, each of which holds
     # at most 16 groups of 4 keys, so no region reserves more than that
