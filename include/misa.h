@@ -410,6 +410,37 @@ misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, con
 size_t misa_prefill_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
                                     int32_t k_prime, int32_t chunk);
 
+/*
+ * Profiling.  The stages of misa_indexer (and of the calls that run parts of
+ * it: misa_sparse_head_topk[_q8], misa_indexer_cached, misa_indexer_q8,
+ * misa_indexer_noalloc, misa_prefill_chunked) whose kernels a caller can time
+ * on their own with HIP events.  The fused-selection stages apply when that
+ * path is taken (misa_sparse_head_topk above).
+ */
+typedef enum {
+  MISA_STAGE_NONE = 0,
+  MISA_STAGE_POOL = 1,               /* block pooling (inside the indexer calls) */
+  MISA_STAGE_ROUTE = 2,              /* head routing (inside the indexer calls) */
+  MISA_STAGE_SCORE_SAMPLE = 3,       /* scores of the key sample */
+  MISA_STAGE_SAMPLE_THRESHOLD = 4,   /* per-row thresholds from the sample */
+  MISA_STAGE_SCORE_CANDIDATES = 5,   /* routed scoring that keeps the candidates */
+  MISA_STAGE_REGION_SELECT = 6,      /* exact top-k of the candidates */
+  MISA_STAGE_RESCORE = 7,            /* re-scoring and top-k of the rows the candidates could not settle */
+  MISA_STAGE_RERANK = 8,             /* MISA-dagger: all-head re-rank of the k' candidates */
+  MISA_STAGE_FINAL_TOPK = 9          /* MISA-dagger: top-k of the re-ranked candidates */
+} misa_stage;
+
+/*
+ * Until the next misa_profile_stage call on the same host thread, every call
+ * made on that thread records start_event on its stream just before it
+ * enqueues the kernels of `stage`, and stop_event just after (hipEvent_t
+ * passed as void*, created by the caller; the setting is per host thread).
+ * A call that does not run the stage records nothing.  MISA_STAGE_NONE (events
+ * may be NULL) turns it off.  An unknown stage or a null event:
+ * MISA_ERR_INVALID_ARG.
+ */
+misa_status misa_profile_stage(int32_t stage, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,10 @@ EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_spars
             "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8",
             "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
             "misa_prefill_chunked", "misa_prefill_workspace_bytes", "misa_indexer_q8",
-            "misa_indexer_q8_workspace_bytes", "misa_gather_keys_paged", "misa_indexer_noalloc")
+            "misa_indexer_q8_workspace_bytes", "misa_gather_keys_paged", "misa_indexer_noalloc",
+            "misa_profile_stage")
+STAGES = dict(pool=1, route=2, score_sample=3, sample_threshold=4, score_candidates=5, region_select=6,
+              rescore=7, rerank=8, final_topk=9)
 MISA_ERR_SCRATCH = -5
 NOALLOC_SCRATCH_BYTES = 256 << 20   # MISA_NOALLOC_SCRATCH_BYTES of misa.h
 
@@ -75,6 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_sparse_head_topk": [S, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer_noalloc": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P],
+        "misa_profile_stage": [i32, P, P],
         "misa_quantize_q": [S, P, P, P, P],
         "misa_sparse_head_logits_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, P, i64, P],
         "misa_sparse_head_topk_q8": [S, P, P, P, P, ctypes.c_int, P, P, i32, i32, i32, P, P, P, sz, P],
@@ -406,6 +410,16 @@ def misa_indexer_noalloc(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: 
                                      int(topk), int(k_prime), _ptr(idx), _ptr(vals), _stream(stream))
     _check(st, "misa_indexer_noalloc")
     return idx, vals
+
+
+def misa_profile_stage(stage, start_event=None, stop_event=None):
+    """Bracket the kernels of `stage` (a name of STAGES, or None to stop) in the
+    calls this host thread makes next with two torch.cuda.Event(enable_timing=True)."""
+    if stage is None:
+        _check(load().misa_profile_stage(0, None, None), "misa_profile_stage")
+        return
+    _check(load().misa_profile_stage(int(STAGES[stage]), ctypes.c_void_p(start_event.cuda_event),
+                                     ctypes.c_void_p(stop_event.cuda_event)), "misa_profile_stage")
 
 
 class PooledCache:

@@ -111,6 +111,23 @@ struct QuantQ {
   const float* q_scale;
 };
 
+// misa_profile_stage: per host thread, the stage whose kernels calls bracket
+// with the caller's events (MISA_STAGE_NONE: none)
+struct ProfileHook {
+  int stage;
+  hipEvent_t start, stop;
+};
+thread_local ProfileHook t_profile = {MISA_STAGE_NONE, nullptr, nullptr};
+
+inline misa_status stage_begin(int stage, hipStream_t st) {
+  if (t_profile.stage != stage) return MISA_OK;
+  return from_hip(hipEventRecord(t_profile.start, st));
+}
+inline misa_status stage_end(int stage, hipStream_t st) {
+  if (t_profile.stage != stage) return MISA_OK;
+  return from_hip(hipEventRecord(t_profile.stop, st));
+}
+
 // Routed scoring + exact top-k (see misa_sparse_head_topk); qq != nullptr:
 // fp8 queries and fp8 keys (misa_sparse_head_topk_q8).
 misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, const uint16_t* q, const float* w,
@@ -134,15 +151,25 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   float* gvals = reinterpret_cast<float*>(base + L.gvals);
   int32_t* gkeys = reinterpret_cast<int32_t*>(base + L.gkeys);
   if (qq != nullptr) {
+    MISA_TRY(stage_begin(MISA_STAGE_SCORE_SAMPLE, st));
     MISA_TRY(from_hip(misa::launch_score_q8_sampled(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, p, sample, st)));
+    MISA_TRY(stage_end(MISA_STAGE_SCORE_SAMPLE, st));
+    MISA_TRY(stage_begin(MISA_STAGE_SAMPLE_THRESHOLD, st));
     MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
+    MISA_TRY(stage_end(MISA_STAGE_SAMPLE_THRESHOLD, st));
+    MISA_TRY(stage_begin(MISA_STAGE_SCORE_CANDIDATES, st));
     MISA_TRY(from_hip(misa::launch_score_q8_cands(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, p, thr, gvals,
                                                   gkeys, rcount, st)));
+    MISA_TRY(stage_end(MISA_STAGE_SCORE_CANDIDATES, st));
+    MISA_TRY(stage_begin(MISA_STAGE_REGION_SELECT, st));
     MISA_TRY(
         from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
+    MISA_TRY(stage_end(MISA_STAGE_REGION_SELECT, st));
+    MISA_TRY(stage_begin(MISA_STAGE_RESCORE, st));
     MISA_TRY(from_hip(
         misa::launch_score_q8(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, logits, L.ld, st, flag)));
-    return from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st));
+    MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st)));
+    return stage_end(MISA_STAGE_RESCORE, st);
   }
   // the scoring launches stage bf16 keys by direct loads into LDS
   const void* kb = k;
@@ -151,13 +178,23 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
     MISA_TRY(from_hip(misa::launch_widen_fp8(s, k, kwide, st)));
     kb = kwide;
   }
+  MISA_TRY(stage_begin(MISA_STAGE_SCORE_SAMPLE, st));
   MISA_TRY(from_hip(misa::launch_score_sampled(s, q, w, kb, kdtype, k_scale, heads, h, p, sample, st)));
+  MISA_TRY(stage_end(MISA_STAGE_SCORE_SAMPLE, st));
+  MISA_TRY(stage_begin(MISA_STAGE_SAMPLE_THRESHOLD, st));
   MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
+  MISA_TRY(stage_end(MISA_STAGE_SAMPLE_THRESHOLD, st));
+  MISA_TRY(stage_begin(MISA_STAGE_SCORE_CANDIDATES, st));
   MISA_TRY(from_hip(
       misa::launch_score_cands(s, q, w, kb, kdtype, k_scale, heads, h, p, thr, gvals, gkeys, rcount, st)));
+  MISA_TRY(stage_end(MISA_STAGE_SCORE_CANDIDATES, st));
+  MISA_TRY(stage_begin(MISA_STAGE_REGION_SELECT, st));
   MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
+  MISA_TRY(stage_end(MISA_STAGE_REGION_SELECT, st));
+  MISA_TRY(stage_begin(MISA_STAGE_RESCORE, st));
   MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, kb, kdtype, k_scale, heads, h, flag, logits, L.ld, st)));
-  return from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st));
+  MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st)));
+  return stage_end(MISA_STAGE_RESCORE, st);
 }
 
 struct IndexerLayout {
@@ -187,7 +224,7 @@ IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, i
   off += align_up((size_t)rows * h * sizeof(int32_t));
   const int n_parts = misa::route_parts(s);
   L.rpart = n_parts > 1 ? off : SIZE_MAX;   // the router's partial block sums (few queries)
-  if (n_parts > 1) off += align_up((size_t)rows * n_parts * s.n_heads * sizeof(float));
+  if (n_parts > 1) off += align_up((size_t)rows * (n_parts + 1) * s.n_heads * sizeof(float));
   if (quant_q) {   // fp8 queries and their scales (misa_indexer_q8)
     L.q8 = off;
     off += align_up((size_t)rows * s.n_heads * MISA_HEAD_DIM);
@@ -217,9 +254,13 @@ misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base,
                         float* vals, hipStream_t st, bool quant_q = false) {
   float* tail = reinterpret_cast<float*>(base + L.tail);
   int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
+  MISA_TRY(stage_begin(MISA_STAGE_POOL, st));
   MISA_TRY(from_hip(launch_pool(s, k, kdtype, k_scale, pooled, tail, split, st, n_cached, ld_blk)));
+  MISA_TRY(stage_end(MISA_STAGE_POOL, st));
   float* rpart = L.rpart == SIZE_MAX ? nullptr : reinterpret_cast<float*>(base + L.rpart);
+  MISA_TRY(stage_begin(MISA_STAGE_ROUTE, st));
   MISA_TRY(from_hip(launch_route(s, q, w, pooled, split, tail, h, heads, nullptr, st, ld_blk, rpart)));
+  MISA_TRY(stage_end(MISA_STAGE_ROUTE, st));
   QuantQ qq{reinterpret_cast<uint8_t*>(base + L.q8), reinterpret_cast<float*>(base + L.qscale)};
   if (quant_q)
     MISA_TRY(from_hip(misa::launch_quant_q(s, q, const_cast<uint8_t*>(qq.q8), const_cast<float*>(qq.q_scale), st)));
@@ -230,9 +271,13 @@ misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base,
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
   float* dlog = reinterpret_cast<float*>(base + L.dlog);
   MISA_TRY(run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, k_prime, false, cand, nullptr, st, qp));
+  MISA_TRY(stage_begin(MISA_STAGE_RERANK, st));
   MISA_TRY(from_hip(launch_score_gather(s, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
-  return from_hip(launch_topk(s, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
-                              L.total - L.sel.end, st));
+  MISA_TRY(stage_end(MISA_STAGE_RERANK, st));
+  MISA_TRY(stage_begin(MISA_STAGE_FINAL_TOPK, st));
+  MISA_TRY(from_hip(launch_topk(s, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
+                                L.total - L.sel.end, st)));
+  return stage_end(MISA_STAGE_FINAL_TOPK, st);
 }
 
 misa_status check_indexer_args(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
@@ -626,6 +671,17 @@ misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8,
   const QuantQ qq{q8, q_scale};
   return run_select(*shape, L, static_cast<char*>(ws), nullptr, w, k, kdtype, k_scale, heads, h, topk, sorted != 0,
                     idx, vals, (hipStream_t)stream, &qq);
+}
+
+misa_status misa_profile_stage(int32_t stage, void* start_event, void* stop_event) {
+  if (stage == MISA_STAGE_NONE) {
+    t_profile = ProfileHook{MISA_STAGE_NONE, nullptr, nullptr};
+    return MISA_OK;
+  }
+  if (stage < MISA_STAGE_POOL || stage > MISA_STAGE_FINAL_TOPK || start_event == nullptr || stop_event == nullptr)
+    return MISA_ERR_INVALID_ARG;
+  t_profile = ProfileHook{stage, static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return MISA_OK;
 }
 
 size_t misa_sparse_head_topk_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk) {

@@ -21,8 +21,9 @@ hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const flo
 
 // split (nullable): launch_pool's hi/lo rows, staged directly instead of
 // splitting `pooled` in every workgroup (same values); ld_blk as launch_pool.
-// part_ws (nullable, with split): [rows][route_parts(s)][H] floats that let a
-// launch with few workgroups (decode) split each block sum over more of them.
+// part_ws (nullable, with split): [rows][route_parts(s) + 1][H] floats that let
+// a launch with few workgroups (decode) split each block sum over more of them
+// (the last slot holds the partial block's term).
 constexpr int kMaxRouteParts = 8;
 int route_parts(const misa_shape& s);   // 1: no split
 hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, const float* pooled,

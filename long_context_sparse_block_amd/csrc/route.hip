@@ -20,9 +20,10 @@
 // of pooled keys staged once per workgroup in LDS (XOR-swizzled 256-byte rows,
 // as in the scoring kernel, so the fragment reads are free of bank conflicts);
 // a workgroup serves 4 (H = 64) to 16 (H <= 16) queries.  ReLU, the causal
-// block mask and the block sum stay in registers; the tail term is an fp32 dot
-// per (query, head); the top-h selection is a rank count over <= 64 values,
-// one wave per query.
+// block mask and the block sum stay in registers; the partial block's term
+// runs on the same resident q fragments (the wave's 4 tails as B columns, hi
+// + lo), so q is read once; the top-h selection is a rank count over <= 64
+// values, one wave per query.
 #include <algorithm>
 #include <type_traits>
 
@@ -38,30 +39,6 @@ constexpr int kRowBytes = kD * 2;           // bf16 LDS row (256 bytes), 16-byte
 // byte offset of 16-byte chunk c of staged row j
 __device__ __forceinline__ uint32_t rt_off(int j, int c) { return (uint32_t)j * kRowBytes + (uint32_t)((c ^ (j & 15)) << 4); }
 
-
-// ReLU(q[row, j] . tail[row]) (fp32 dot over bf16 q), 0 when query t's prefix
-// ends on a block boundary (no partial block)
-__device__ __forceinline__ float tail_term(const uint16_t* __restrict__ q, const float* __restrict__ tail, int64_t row,
-                                           int64_t t, int B, int H, int j) {
-  if (((t + 1) % B) == 0) return 0.f;
-  const uint4* qr = reinterpret_cast<const uint4*>(q + (row * H + j) * kD);
-  const float4* tr = reinterpret_cast<const float4*>(tail + row * kD);
-  float dot = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < kD / 8; ++c) {
-    uint4 qv = qr[c];
-    float4 t0 = tr[2 * c], t1 = tr[2 * c + 1];
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.x & 0xFFFF), t0.x, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.x >> 16), t0.y, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.y & 0xFFFF), t0.z, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.y >> 16), t0.w, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.z & 0xFFFF), t1.x, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.z >> 16), t1.y, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.w & 0xFFFF), t1.z, dot);
-    dot = __builtin_fmaf(bf16_bits_to_f32(qv.w >> 16), t1.w, dot);
-  }
-  return __builtin_fmaxf(dot, 0.f);
-}
 
 // top-h of one query's r (lane j holds r_j, the wave's LDS row sr holds all
 // of them) by rank counting, ties -> lower head id, stored ascending
@@ -109,6 +86,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   __shared__ __attribute__((aligned(16))) unsigned char s_h1[PRESPLIT ? kPreChunk * kRowBytes : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_l1[PRESPLIT ? kPreChunk * kRowBytes : 1];
   __shared__ float s_r[QWG][64];
+  __shared__ float s_t[QWG][64];   // the partial blocks' terms
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,39 +161,46 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   // column block cb (16 pooled rows from row cbase + 16 cb of the chunk) of a
   // staged chunk: hi/lo fragments from LDS, 8 MFMAs per row block, ReLU and
   // the block sum in registers
+  auto block = [&](const unsigned char* sh, const unsigned char* sl, int cb, int64_t col0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    bf16x8 bh[kKSteps], bl[kKSteps];
+    const int row = cb * 16 + p16;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh[rt_off(row, ks * 4 + g)]));
+      bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&sl[rt_off(row, ks * 4 + g)]));
+    }
+    const bool valid = !MASK || (col0 + p16) < nfull_g;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        acc = mfma16(afr[rb][ks], bh[ks], acc);
+        acc = mfma16(afr[rb][ks], bl[ks], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[rb][i] += (MASK && !valid) ? 0.f : relu(acc[i]);
+    }
+  };
   auto chunk_blocks = [&](const unsigned char* sh, const unsigned char* sl, int64_t cbase, int ncb) {
+    if (cbase + 16 * ncb <= nfull_lo) {
+      // every block of the chunk is complete for every query of the wave: no
+      // branch between the column blocks, so their MFMAs and epilogues overlap
+#pragma unroll
+      for (int cb = 0; cb < ncb; ++cb) block(sh, sl, cb, cbase + cb * 16, std::false_type{});
+      return;
+    }
 #pragma unroll
     for (int cb = 0; cb < ncb; ++cb) {
       const int64_t col0 = cbase + cb * 16;
       if (col0 < nfull_w) {
-        bf16x8 bh[kKSteps], bl[kKSteps];
-        const int row = cb * 16 + p16;
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          bh[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh[rt_off(row, ks * 4 + g)]));
-          bl[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&sl[rt_off(row, ks * 4 + g)]));
-        }
         // only column blocks reaching past the wave's first query's complete
         // blocks need the per-lane mask
-        auto accumulate = [&](auto mask_tag) {
-          constexpr bool MASK = decltype(mask_tag)::value;
-          const bool valid = !MASK || (col0 + p16) < nfull_g;
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) {
-              acc = mfma16(afr[rb][ks], bh[ks], acc);
-              acc = mfma16(afr[rb][ks], bl[ks], acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[rb][i] += (MASK && !valid) ? 0.f : relu(acc[i]);
-          }
-        };
         if (col0 + 16 <= nfull_lo)
-          accumulate(std::false_type{});
+          block(sh, sl, cb, col0, std::false_type{});
         else
-          accumulate(std::true_type{});
+          block(sh, sl, cb, col0, std::true_type{});
       }
     }
   };
@@ -303,20 +288,63 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
   // lane (g, p16) handles head hc*16 + p16 of query q0w + g
   float s_sel = fold();
   if (seq_parts > 1) s_sel = s_acc + s_sel;
+  const int qi_o = q0w + g;
+  const int j_o = hc * 16 + p16;
+  const bool own = qi_o < M && j_o < H;
   if (n_parts > 1) {
-    // one part of the block sum: k_route_finish adds the parts (in order) and the tail
-    const int qi = q0w + g;
-    const int j = hc * 16 + p16;
-    if (qi < M && j < H) part_out[(((int64_t)b * M + qi) * n_parts + blockIdx.z) * H + j] = s_sel;
-    return;   // uniform over the workgroup
+    // one part of the block sum: k_route_finish adds the parts (in order), then
+    // the partial block's term, which part 0 also writes (slot n_parts)
+    if (own) part_out[(((int64_t)b * M + qi_o) * (n_parts + 1) + blockIdx.z) * H + j_o] = s_sel;
+    if (blockIdx.z != 0) return;   // uniform over the workgroup
   }
+  // The partial block's term ReLU(q . tail) on the resident q fragments: the
+  // wave's 4 tails (fp32, split into bf16 hi + lo like the pooled keys) are
+  // the B columns 0..3, so the product of query g's rows with column g sits in
+  // lane (g, g); it reaches the lanes that own the heads through LDS.  A query
+  // whose prefix ends on a block boundary has a zero tail: a zero term.
   {
-    const int qi = q0w + g;
-    const int j = hc * 16 + p16;
-    if (qi < M && j < H) {
-      const int64_t row = (int64_t)b * M + qi;
-      s_sel += tail_term(q, tail, row, q_pos0 + qi, B, H, j);
-      s_r[qg * 4 + g][j] = w[row * H + j] * s_sel;
+    bf16x8 th[kKSteps], tl[kKSteps];
+    const int qc = q0w + p16;
+    const bool col_ok = p16 < 4 && qc < M;
+    const float4* tr = reinterpret_cast<const float4*>(tail + ((int64_t)b * M + (col_ok ? qc : 0)) * kD);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      float4 v0 = col_ok ? tr[(ks * 32 + 8 * g) / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 v1 = col_ok ? tr[(ks * 32 + 8 * g) / 4 + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t h01 = pk_bf16(v0.x, v0.y), h23 = pk_bf16(v0.z, v0.w);
+      const uint32_t h45 = pk_bf16(v1.x, v1.y), h67 = pk_bf16(v1.z, v1.w);
+      // f - hi is exact in fp32
+      const uint32_t l01 = pk_bf16(v0.x - __uint_as_float(h01 << 16), v0.y - __uint_as_float(h01 & 0xFFFF0000u));
+      const uint32_t l23 = pk_bf16(v0.z - __uint_as_float(h23 << 16), v0.w - __uint_as_float(h23 & 0xFFFF0000u));
+      const uint32_t l45 = pk_bf16(v1.x - __uint_as_float(h45 << 16), v1.y - __uint_as_float(h45 & 0xFFFF0000u));
+      const uint32_t l67 = pk_bf16(v1.z - __uint_as_float(h67 << 16), v1.w - __uint_as_float(h67 & 0xFFFF0000u));
+      th[ks] = as_bf16x8(make_uint4(h01, h23, h45, h67));
+      tl[ks] = as_bf16x8(make_uint4(l01, l23, l45, l67));
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        acc = mfma16(afr[rb][ks], th[ks], acc);
+        acc = mfma16(afr[rb][ks], tl[ks], acc);
+      }
+      if (p16 == g) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_t[qg * 4 + g][hc * 16 + rb * 4 + i] = relu(acc[i]);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const float tterm = own ? s_t[qg * 4 + g][j_o] : 0.f;
+    if (n_parts > 1) {
+      if (own) part_out[(((int64_t)b * M + qi_o) * (n_parts + 1) + n_parts) * H + j_o] = tterm;
+      return;   // uniform over the workgroup (part 0)
+    }
+    if (own) {
+      const int64_t row = (int64_t)b * M + qi_o;
+      s_r[qg * 4 + g][j_o] = w[row * H + j_o] * (s_sel + tterm);
     }
   }
   __syncthreads();
@@ -331,22 +359,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 
 // Parts of a split block sum (few queries: decode) -> S, r and the top-h: one
 // wave per query, lane j the head; the parts are added in order, then the
-// tail term, as the unsplit kernel adds its running sum and the tail.
-__global__ void __launch_bounds__(256) k_route_finish(const uint16_t* __restrict__ q, const float* __restrict__ w,
-                                                      const float* __restrict__ tail,
-                                                      const float* __restrict__ part, int n_parts,
-                                                      int32_t* __restrict__ heads, float* __restrict__ scores,
-                                                      int64_t q_pos0, int M, int H, int B, int h, int64_t rows) {
+// partial block's term (slot n_parts, written by part 0), as the unsplit
+// kernel adds its running sum and then that term.
+__global__ void __launch_bounds__(256) k_route_finish(const float* __restrict__ w, const float* __restrict__ part,
+                                                      int n_parts, int32_t* __restrict__ heads,
+                                                      float* __restrict__ scores, int H, int h, int64_t rows) {
   __shared__ float s_r[4][64];
   const int wave = threadIdx.x >> 6, j = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= rows) return;   // uniform over the wave; no workgroup barrier below
-  const int qi = (int)(row % M);
   float r = 0.f;
   if (j < H) {
     float S = 0.f;
-    for (int p = 0; p < n_parts; ++p) S += part[(row * n_parts + p) * H + j];
-    S += tail_term(q, tail, row, q_pos0 + qi, B, H, j);
+    for (int p = 0; p < n_parts; ++p) S += part[(row * (n_parts + 1) + p) * H + j];
+    S += part[(row * (n_parts + 1) + n_parts) * H + j];   // the partial block's term
     r = w[row * H + j] * S;
   }
   s_r[wave][j] = r;
@@ -397,8 +423,8 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
-    hipLaunchKernelGGL(k_route_finish, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q, w, tail, part_ws,
-                       n_parts, heads, scores, s.q_pos0, s.q_per_seq, H, s.block, h, rows);
+    hipLaunchKernelGGL(k_route_finish, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, w, part_ws, n_parts,
+                       heads, scores, H, h, rows);
   }
   return hipGetLastError();
 }

@@ -141,7 +141,7 @@ def pool_bound(keys_abs_mean: np.ndarray, n: int) -> np.ndarray:
 #  * a pooled-key dot product: the key split into bf16 hi + lo parts (off by
 #    at most 2^-16 of |pooled|) and 256 products summed by the matrix core
 #    (2^-16 of the sum of |products|): 2^-15 of sum_i |q_i pooled_i|; the
-#    partial block's dot is an fp32 fma chain (2^-17);
+#    partial block's mean goes through the matrix core the same way;
 #  * the block sum: each lane adds n/16 terms, then 4 butterfly adds, the
 #    parts of a split sum and the partial block's term: (n/16 + 16) 2^-24 of S;
 #  * r = w S: one more rounding.
@@ -173,7 +173,7 @@ def route_bound(ctx, i: int, pooled=None, tail=None):
     tl = ctx.tail(i)
     if tl is not None:
         tl = tl if tail is None else np.asarray(tail, np.float64)
-        bound = bound + 2.0 ** -16 * (aq @ np.abs(tl))
+        bound = bound + EPS_ROUTE_DOT * (aq @ np.abs(tl))
     bound = bound + 2 * (n_full / 16 + 16) * 2.0 ** -24 * S
     return np.abs(ctx.w[i]) * bound + 2.0 ** -23 * np.abs(r) + 1e-30
 

@@ -289,3 +289,9 @@ def test_region_capacity_never_exceeds_a_key_range(lib):
     need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 8, 2048, 0)
     assert need < (32 << 20)
 
+
+def test_profile_stage_checks_its_arguments(lib):
+    assert lib.misa_profile_stage(99, FAKE, FAKE) == -1        # unknown stage
+    assert lib.misa_profile_stage(5, None, FAKE) == -1         # null event
+    assert lib.misa_profile_stage(0, None, None) == 0          # off
+
