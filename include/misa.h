@@ -285,28 +285,44 @@ misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8,
  * "Variante Hierárquica (MISA†)" of the gist.science summary).
  * idx: int32 [n_seq][M][topk], vals: float [n_seq][M][topk] or NULL.
  * 1 <= h <= H; 1 <= topk <= MISA_MAX_TOPK; k_prime == 0 or topk <= k_prime <= MISA_MAX_TOPK.
- * ws / ws_bytes: at least misa_indexer_workspace_bytes() bytes (holds the
- * pooled keys, tails, routed heads and the fp32 logits of the chunk).
+ * ws / ws_bytes: the workspace (16-byte aligned) holds the pooled keys,
+ * tails, routed heads, sampled scores, candidate regions and the logits rows
+ * of rows the candidates cannot settle.  misa_indexer_workspace_bytes() bytes
+ * is the fast plan (every such row re-scored in one pass); any size down to
+ * misa_indexer_workspace_min_bytes() also works, with the same result: the
+ * plan is taken from ws_bytes, the re-scoring then runs through a smaller
+ * logits slab, a batch of query tiles at a time (two more launches per
+ * batch), and candidate regions may be sized closer to the expected
+ * candidates.  Below the minimum: MISA_ERR_WORKSPACE, nothing enqueued.
  */
 misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
                          misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
                          int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* Workspace of misa_indexer for keys of type kdtype; 0 for an invalid shape. */
+/* Workspace of misa_indexer's fast plan for keys of type kdtype; 0 for an
+ * invalid shape. */
 size_t misa_indexer_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
                                     int32_t k_prime);
+
+/* The least workspace misa_indexer takes (its lean plan: a logits slab no
+ * larger than the sampled scores, which it shares memory with, and tighter
+ * candidate regions); 0 for an invalid shape.  E.g. about 0.94 GiB for
+ * 8192 queries over 131072 fp8 keys, h = 8, topk = 2048, against 6 GiB for
+ * the fast plan. */
+size_t misa_indexer_workspace_min_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
+                                        int32_t k_prime);
 
 /*
  * misa_indexer for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation): the
  * same arguments and the same result as misa_indexer, but no workspace
  * argument.  Its scratch is a fixed device buffer of the library,
- * MISA_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, held until the process ends;
- * a request whose misa_indexer_workspace_bytes() exceeds it returns
- * MISA_ERR_SCRATCH and enqueues nothing (256 MiB holds, e.g., a decode batch
- * of 64 sequences x 131072 keys, or a prefill chunk of 512 queries over
- * 65536 keys).  The call allocates, frees and synchronises nothing.  All
+ * MISA_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, held until the process ends,
+ * planned as a workspace of that size (see misa_indexer); a request whose
+ * misa_indexer_workspace_min_bytes() exceeds it returns MISA_ERR_SCRATCH and
+ * enqueues nothing (256 MiB holds, e.g., a decode batch of 64 sequences x
+ * 131072 keys, or a prefill chunk of 512 queries over 65536 keys).  The call allocates, frees and synchronises nothing.  All
  * calls on one GPU share that GPU's buffer, which keeps the last call's
  * contents: calls that may overlap on one GPU (several streams, several host
  * threads) race, so the caller must order them (one stream, or events).

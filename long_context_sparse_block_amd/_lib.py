@@ -29,6 +29,7 @@ MAX_TOPK = 8192
 EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_sparse_head_logits",
             "dsa_dense_logits", "misa_topk", "misa_topk_workspace_bytes", "misa_sparse_head_topk",
             "misa_sparse_head_topk_workspace_bytes", "misa_indexer", "misa_indexer_workspace_bytes",
+            "misa_indexer_workspace_min_bytes",
             "misa_quantize_q", "misa_sparse_head_logits_q8", "misa_sparse_head_topk_q8", "dsa_dense_logits_q8",
             "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
             "misa_prefill_chunked", "misa_prefill_workspace_bytes", "misa_indexer_q8",
@@ -99,6 +100,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.misa_sparse_head_topk_workspace_bytes.restype = sz
     lib.misa_indexer_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32]
     lib.misa_indexer_workspace_bytes.restype = sz
+    lib.misa_indexer_workspace_min_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32]
+    lib.misa_indexer_workspace_min_bytes.restype = sz
     lib.misa_indexer_cached_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32]
     lib.misa_indexer_cached_workspace_bytes.restype = sz
     lib.misa_indexer_q8_workspace_bytes.argtypes = [S, i32, i32, i32]
@@ -369,6 +372,13 @@ def dsa_dense_logits_q8(shape: MisaShape, q8, q_scale, w, k, k_scale, logits=Non
 def misa_indexer_workspace_bytes(shape: MisaShape, kdtype: int, h: int, topk: int, k_prime: int = 0) -> int:
     return int(load().misa_indexer_workspace_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk),
                                                    int(k_prime)))
+
+
+def misa_indexer_workspace_min_bytes(shape: MisaShape, kdtype: int, h: int, topk: int, k_prime: int = 0) -> int:
+    """The least workspace misa_indexer takes (same results, the flagged-row
+    re-scoring in batches)."""
+    return int(load().misa_indexer_workspace_min_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk),
+                                                       int(k_prime)))
 
 
 def misa_indexer(shape: MisaShape, q, w, k, h: int, topk: int, k_prime: int = 0, k_scale=None,

@@ -64,44 +64,83 @@ inline misa_status from_hip(hipError_t e) { return e == hipSuccess ? MISA_OK : M
 
 // Workspace of the routed scoring + top-k selection (misa_sparse_head_topk,
 // and the first selection of misa_indexer), placed from offset `off`.
+//
+// Fused path: the sample logits and the slab of the flagged-row re-scoring
+// share one buffer (the sample is dead once the thresholds are taken).  The
+// slab holds slab_tiles query tiles of tr rows; the re-scoring walks the
+// tiles in batches of that many.  With room for every tile (the fast plan)
+// it is one batch; a smaller workspace (down to the lean plan, whose slab
+// is no larger than the sample, and whose candidate regions are sized to the
+// expected candidates with a smaller margin) takes more batches, each a
+// scoring and a top-k launch that only flagged rows give work.
 struct SelectLayout {
   size_t logits, kwide, sample, thr, flag, rcount, gvals, gkeys, topk_ws, end;
   int64_t ld;
+  int slab_tiles, tr, n_flat;
   misa::FusedPlan fused;
 };
 
 // wide_keys: reserve the bf16 copy of fp8 keys that the direct-load staging
-// of the bf16-query scoring reads (fp8 keys, bf16 queries)
-SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off, bool wide_keys) {
+// of the bf16-query scoring reads (fp8 keys, bf16 queries).  end_limit: the
+// workspace's end (the caller's bytes); the fast plan when it fits, else the
+// largest slab that fits, else the lean plan (whose end then lies past
+// end_limit: the caller's check refuses the workspace).
+SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off, bool wide_keys,
+                           size_t end_limit = SIZE_MAX) {
   SelectLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   L.ld = (s.n_keys + 3) / 4 * 4;
-  L.logits = off;   // full logits: the unfused path, or the rows the fused path re-scores
-  off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
   L.fused = misa::plan_fused(s, h, k);
-  if (L.fused.ok) {
-    const misa::FusedPlan& p = L.fused;
-    L.kwide = off;   // bf16 copy of fp8 keys
-    if (wide_keys) off += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128
-    L.sample = off;
-    off += align_up((size_t)rows * (size_t)p.ld_sample * sizeof(float));
-    L.thr = off;
-    off += align_up((size_t)rows * sizeof(float));
-    L.flag = off;
-    off += align_up((size_t)rows * sizeof(uint32_t));
-    L.rcount = off;
-    off += align_up((size_t)rows * p.n_splits * sizeof(uint32_t));
-    const size_t groups = (size_t)rows * p.n_splits * (size_t)p.cap_region;
-    L.gvals = off;
-    off += align_up(groups * 4 * sizeof(float));
-    L.gkeys = off;
-    off += align_up(groups * sizeof(int32_t));
-  } else {
+  if (!L.fused.ok) {
+    L.logits = off;   // full logits
+    off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
     L.topk_ws = off;
     off += align_up(misa::topk_workspace_bytes(s, (int)s.n_keys, k));
+    L.end = off;
+    return L;
   }
-  L.end = off;
-  return L;
+  const int n_qtiles = (s.q_per_seq + 31) / 32;
+  L.n_flat = s.n_seq * n_qtiles;
+  L.tr = std::min(32, (int)s.q_per_seq);
+  const size_t tile_bytes = (size_t)L.tr * (size_t)L.ld * sizeof(float);
+  auto place = [&](const misa::FusedPlan& p, int64_t slab_tiles) {
+    size_t o = off;
+    L.fused = p;
+    L.kwide = o;   // bf16 copy of fp8 keys
+    if (wide_keys) o += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128
+    L.thr = o;
+    o += align_up((size_t)rows * sizeof(float));
+    L.flag = o;
+    o += align_up((size_t)rows * sizeof(uint32_t));
+    L.rcount = o;
+    o += align_up((size_t)rows * p.n_splits * sizeof(uint32_t));
+    const size_t groups = (size_t)rows * p.n_splits * (size_t)p.cap_region;
+    L.gvals = o;
+    o += align_up(groups * 4 * sizeof(float));
+    L.gkeys = o;
+    o += align_up(groups * sizeof(int32_t));
+    L.sample = L.logits = o;   // last: the part a workspace's size decides
+    const size_t sample_bytes = (size_t)rows * (size_t)p.ld_sample * sizeof(float);
+    L.slab_tiles = (int)std::max<int64_t>(1, slab_tiles);
+    o += align_up(std::max(sample_bytes, (size_t)L.slab_tiles * tile_bytes));
+    L.end = o;
+    return sample_bytes;
+  };
+  place(L.fused, L.n_flat);
+  if (L.end <= end_limit) return L;   // the fast plan: every tile in one batch
+  const misa::FusedPlan fast = L.fused;
+  for (const misa::FusedPlan& p : {fast, misa::lean_plan(fast, s)}) {
+    const size_t sample_bytes = place(p, 1);
+    const size_t fixed = L.sample;
+    // as many tiles as the workspace holds, at least those the sample's bytes hold
+    // (tiles whose bytes fit the room rounded down to the alignment still fit
+    // once rounded up)
+    const int64_t room = end_limit > fixed ? (int64_t)((end_limit - fixed) / kAlign * kAlign / tile_bytes) : 0;
+    const int64_t free_tiles = (int64_t)(sample_bytes / tile_bytes);
+    place(p, std::min<int64_t>(L.n_flat, std::max<int64_t>(room, free_tiles)));
+    if (L.end <= end_limit) return L;
+  }
+  return L;   // the lean plan at its least: end_limit is below it
 }
 
 // fp8 queries (misa_quantize_q's codes and scales): the selection scores with
@@ -166,9 +205,12 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
         from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
     MISA_TRY(stage_end(MISA_STAGE_REGION_SELECT, st));
     MISA_TRY(stage_begin(MISA_STAGE_RESCORE, st));
-    MISA_TRY(from_hip(
-        misa::launch_score_q8(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, logits, L.ld, st, flag)));
-    MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st)));
+    for (int64_t first = 0; first < L.n_flat; first += L.slab_tiles) {
+      const misa::SlabBatch sb{first, (int)std::min<int64_t>(L.slab_tiles, L.n_flat - first), L.tr};
+      MISA_TRY(from_hip(
+          misa::launch_score_q8(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, logits, L.ld, st, flag, &sb)));
+      MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, sb, flag, idx, vals, sorted, st)));
+    }
     return stage_end(MISA_STAGE_RESCORE, st);
   }
   // the scoring launches stage bf16 keys by direct loads into LDS
@@ -191,22 +233,29 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   MISA_TRY(stage_begin(MISA_STAGE_REGION_SELECT, st));
   MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
   MISA_TRY(stage_end(MISA_STAGE_REGION_SELECT, st));
+  // the rows the regions could not settle: whole logits rows through the
+  // slab, a batch of query tiles at a time
   MISA_TRY(stage_begin(MISA_STAGE_RESCORE, st));
-  MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, kb, kdtype, k_scale, heads, h, flag, logits, L.ld, st)));
-  MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, flag, idx, vals, sorted, st)));
+  for (int64_t first = 0; first < L.n_flat; first += L.slab_tiles) {
+    const misa::SlabBatch sb{first, (int)std::min<int64_t>(L.slab_tiles, L.n_flat - first), L.tr};
+    MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, kb, kdtype, k_scale, heads, h, flag, logits, L.ld, sb, st)));
+    MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, sb, flag, idx, vals, sorted, st)));
+  }
   return stage_end(MISA_STAGE_RESCORE, st);
 }
 
 struct IndexerLayout {
-  size_t pooled, split, tail, heads, rpart, q8, qscale, cand, dlog, total;
+  size_t pooled, split, tail, heads, rpart, q8, qscale, cand, dlog, ftopk, ftopk_bytes, total;
   int64_t ld_d;
   SelectLayout sel;
 };
 
 // own_pool: the pooled keys (and their bf16 hi/lo rows) live in the
-// workspace; otherwise in a caller-owned cache (misa_indexer_cached)
+// workspace; otherwise in a caller-owned cache (misa_indexer_cached).
+// end_limit: the workspace's size (the selection is planned to fit it; see
+// select_layout).
 IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, int k_prime, bool own_pool = true,
-                             bool quant_q = false) {
+                             bool quant_q = false, size_t end_limit = SIZE_MAX) {
   IndexerLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   const int64_t n_full = s.n_keys / s.block;
@@ -236,12 +285,13 @@ IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, i
     off += align_up((size_t)rows * k_prime * sizeof(int32_t));
     L.dlog = off;
     off += align_up((size_t)rows * (size_t)L.ld_d * sizeof(float));
+    L.ftopk = off;   // the final top-k of MISA-dagger runs over k' candidate columns
+    L.ftopk_bytes = align_up(misa::topk_workspace_bytes(s, k_prime, topk));
+    off += L.ftopk_bytes;
   }
-  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off, kdtype == MISA_K_FP8_E4M3 && !quant_q);
-  off = L.sel.end;
-  // the final top-k of MISA-dagger runs over k' candidate columns
-  if (k_prime > 0) off += align_up(misa::topk_workspace_bytes(s, k_prime, topk));
-  L.total = off;
+  // last: the selection takes what the workspace has left
+  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off, kdtype == MISA_K_FP8_E4M3 && !quant_q, end_limit);
+  L.total = L.sel.end;
   return L;
 }
 
@@ -275,8 +325,8 @@ misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base,
   MISA_TRY(from_hip(launch_score_gather(s, q, w, k, kdtype, k_scale, cand, k_prime, dlog, L.ld_d, st)));
   MISA_TRY(stage_end(MISA_STAGE_RERANK, st));
   MISA_TRY(stage_begin(MISA_STAGE_FINAL_TOPK, st));
-  MISA_TRY(from_hip(launch_topk(s, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.sel.end,
-                                L.total - L.sel.end, st)));
+  MISA_TRY(from_hip(launch_topk(s, dlog, L.ld_d, cand, k_prime, topk, idx, vals, base + L.ftopk, L.ftopk_bytes,
+                                st)));
   return stage_end(MISA_STAGE_FINAL_TOPK, st);
 }
 
@@ -336,7 +386,8 @@ struct PrefillLayout {
   int64_t cap;
 };
 
-PrefillLayout prefill_layout(const misa_shape& s, int kdtype, int h, int topk, int k_prime, int chunk) {
+PrefillLayout prefill_layout(const misa_shape& s, int kdtype, int h, int topk, int k_prime, int chunk,
+                             size_t end_limit = SIZE_MAX) {
   PrefillLayout L{};
   L.cap = std::max<int64_t>(1, (s.q_pos0 + s.q_per_seq) / s.block);
   size_t off = 0;
@@ -347,8 +398,10 @@ PrefillLayout prefill_layout(const misa_shape& s, int kdtype, int h, int topk, i
   L.ixws = off;
   size_t most = 0;
   const int n_chunks = (int)((s.q_per_seq + chunk - 1) / chunk);
+  const size_t limit = end_limit == SIZE_MAX ? SIZE_MAX : (end_limit > off ? end_limit - off : 0);
   for (int c = 0; c < n_chunks; ++c)
-    most = std::max(most, indexer_layout(chunk_shape(s, c, chunk), kdtype, h, topk, k_prime, false).total);
+    most = std::max(most,
+                    indexer_layout(chunk_shape(s, c, chunk), kdtype, h, topk, k_prime, false, false, limit).total);
   L.total = off + most;
   return L;
 }
@@ -516,12 +569,18 @@ size_t misa_indexer_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype,
   return indexer_layout(*shape, kdtype, h, topk, k_prime).total;
 }
 
+size_t misa_indexer_workspace_min_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
+                                        int32_t k_prime) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0) return 0;
+  return indexer_layout(*shape, kdtype, h, topk, k_prime, true, false, 0).total;
+}
+
 misa_status misa_indexer(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
                          misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
                          int32_t k_prime, int32_t* idx, float* vals, void* ws, size_t ws_bytes,
                          void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
-  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, true, false, ws_bytes);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
@@ -534,7 +593,7 @@ misa_status misa_indexer_noalloc(const misa_shape* shape, const uint16_t* q, con
                                  misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk, int32_t k_prime,
                                  int32_t* idx, float* vals, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
-  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, true, false, MISA_NOALLOC_SCRATCH_BYTES);
   if (L.total > MISA_NOALLOC_SCRATCH_BYTES) return MISA_ERR_SCRATCH;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = nullptr;
@@ -556,7 +615,7 @@ misa_status misa_indexer_q8(const misa_shape* shape, const uint16_t* q, const fl
                             int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   if (kdtype != MISA_K_FP8_E4M3 || h > 8) return MISA_ERR_UNSUPPORTED;   // the fp8 x fp8 routed kernels
-  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, true, true);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, true, true, ws_bytes);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
@@ -588,7 +647,7 @@ misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, cons
                                 int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   MISA_TRY(check_cache(shape, n_cached, pooled, pooled_split, cap_blocks));
-  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, false);
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, k_prime, false, false, ws_bytes);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0)   // no queries: only bring the cache up to date
     return from_hip(launch_pool(*shape, k, kdtype, k_scale, pooled, nullptr, pooled_split, (hipStream_t)stream,
@@ -608,7 +667,7 @@ misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, con
                                  int32_t chunk, int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
   MISA_TRY(check_indexer_args(shape, q, w, k, kdtype, k_scale, h, topk, k_prime, idx));
   if (chunk < 1) return MISA_ERR_INVALID_ARG;
-  const PrefillLayout P = prefill_layout(*shape, kdtype, h, topk, k_prime, chunk);
+  const PrefillLayout P = prefill_layout(*shape, kdtype, h, topk, k_prime, chunk, ws_bytes);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < P.total) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   char* base = static_cast<char*>(ws);
@@ -624,7 +683,7 @@ misa_status misa_prefill_chunked(const misa_shape* shape, const uint16_t* q, con
     for (int c = 0; c < n_chunks; ++c) {
       const misa_shape sc = chunk_shape(*shape, c, chunk);
       const int64_t r0 = (int64_t)b * M + (int64_t)c * chunk;   // first query row of the chunk
-      const IndexerLayout L = indexer_layout(sc, kdtype, h, topk, k_prime, false);
+      const IndexerLayout L = indexer_layout(sc, kdtype, h, topk, k_prime, false, false, ws_bytes - P.ixws);
       MISA_TRY(run_indexer(sc, L, base + P.ixws, q + r0 * H * MISA_HEAD_DIM, w + r0 * H,
                            static_cast<const char*>(k) + (size_t)b * N * key_bytes, kdtype,
                            k_scale != nullptr ? k_scale + (size_t)b * N : nullptr, h, topk, k_prime, pooled, split,
@@ -646,7 +705,7 @@ misa_status misa_sparse_head_topk(const misa_shape* shape, const uint16_t* q, co
     return MISA_ERR_INVALID_ARG;
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
-  const SelectLayout L = select_layout(*shape, h, topk, 0, kdtype == MISA_K_FP8_E4M3);
+  const SelectLayout L = select_layout(*shape, h, topk, 0, kdtype == MISA_K_FP8_E4M3, ws_bytes);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.end) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   return run_select(*shape, L, static_cast<char*>(ws), q, w, k, kdtype, k_scale, heads, h, topk, sorted != 0, idx,
@@ -665,7 +724,8 @@ misa_status misa_sparse_head_topk_q8(const misa_shape* shape, const uint8_t* q8,
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (h > 8) return MISA_ERR_UNSUPPORTED;
   if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
-  const SelectLayout L = select_layout(*shape, h, topk, 0, false);   // fp8 keys feed the fp8 MFMA as they are
+  // fp8 keys feed the fp8 MFMA as they are
+  const SelectLayout L = select_layout(*shape, h, topk, 0, false, ws_bytes);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < L.end) return MISA_ERR_WORKSPACE;
   if (shape->q_per_seq == 0) return MISA_OK;
   const QuantQ qq{q8, q_scale};

@@ -44,9 +44,18 @@ hipError_t launch_gather_pages(const misa_shape& s, const void* pages, int kdtyp
 hipError_t launch_quant_q(const misa_shape& s, const uint16_t* q, uint8_t* q8, float* q_scale, hipStream_t st);
 // Routed-head logits from fp8 queries and fp8 keys (h <= 8); row_flag: only
 // the workgroups holding a flagged row run (re-scoring after a fused pass).
+// A re-scoring batch through a logits slab: query tiles [first, first +
+// tiles) of the flattened (sequence, query tile) order, 32 queries a tile;
+// the queries of the tile in slot s go to slab rows s * tr .. s * tr + tr - 1
+// (tr = min(32, queries per sequence)).
+struct SlabBatch {
+  int64_t first;
+  int tiles, tr;
+};
 hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
                           const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
-                          int64_t ld, hipStream_t st, const uint32_t* row_flag = nullptr);
+                          int64_t ld, hipStream_t st, const uint32_t* row_flag = nullptr,
+                          const SlabBatch* slab = nullptr);
 
 // heads == nullptr: all H heads (dense DSA indexer); otherwise h routed heads per query.
 hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
@@ -89,6 +98,9 @@ struct FusedPlan {
   int cap_region;      // candidate groups of 4 keys one (row, key range) region holds
 };
 FusedPlan plan_fused(const misa_shape& s, int h, int k);
+// the fast plan with candidate regions sized closer to the expected
+// candidates (the least-workspace plan)
+FusedPlan lean_plan(const FusedPlan& fast, const misa_shape& s);
 
 // The fused path's scoring launches take bf16 keys in `k` whatever kdtype is
 // (fp8 keys widened by launch_widen_fp8; kdtype then says that k_scale
@@ -102,10 +114,12 @@ hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const fl
 hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                               const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
                               const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st);
-// full logits rows of the workgroups that hold a row with row_flag != 0
+// logits rows, into a slab batch, of the workgroups that hold a row with
+// row_flag != 0
 hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                                 int kdtype, const float* k_scale, const int32_t* heads, int h,
-                                const uint32_t* row_flag, float* logits, int64_t ld, hipStream_t st);
+                                const uint32_t* row_flag, float* slab, int64_t ld, const SlabBatch& sb,
+                                hipStream_t st);
 // thr[row] from the sample logits; row_flag[row] = 0
 hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, const float* sample_logits,
                                      float* thr, uint32_t* row_flag, hipStream_t st);
@@ -125,8 +139,8 @@ hipError_t launch_score_q8_cands(const misa_shape& s, const uint8_t* q8, const f
                                  const uint8_t* k, const float* k_scale, const int32_t* heads, int h,
                                  const FusedPlan& p, const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount,
                                  hipStream_t st);
-// whole-row top-k of the flagged rows from full logits
-hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* logits, int64_t ld,
+// whole-row top-k of the flagged rows of a slab batch
+hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* slab, int64_t ld, const SlabBatch& sb,
                                const uint32_t* row_flag, int32_t* idx, float* vals, bool sorted, hipStream_t st);
 
 }  // namespace misa

@@ -198,8 +198,9 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
   const int g = lane >> 4, p16 = lane & 15;
-  const int b = blockIdx.y;
-  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const WgTile tc = wg_tile<QT, MODE == kLogits>(out_spec, M, n_qtiles, n_ksplits, KR, N);
+  if (!tc.valid) return;   // uniform over the workgroup
+  const int b = tc.b;
   const int k0 = (int)tc.k0, k1 = (int)tc.k1;
   const int qa = tc.qt * QT;
   const int qb = min(qa + QT, M);
@@ -237,7 +238,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
     tq[G] = (qo < qb) ? (q_pos0 + qo) / kstride : -1;
     const int qoc = min(qo, M - 1);
     if (MODE == kLogits) {
-      orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld,
+      orsrc[G] = uniform_rsrc(out_spec.logits + (tc.orow0 + min(qg0, M - 1)) * out_spec.ld,
                               (uint32_t)nrows * row_bytes);
     } else {
       cand_lane(out_spec, qrow0, qa, qb, qo, qoc, n_ksplits, thr[G], reg[G]);
@@ -420,7 +421,7 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   }
   if (MODE == kLogits) {
     // keys of this range after the last computed tile: -inf for every query
-    fill_neg_inf(out_spec.logits, out_spec.ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
+    fill_neg_inf(out_spec.logits, out_spec.ld, tc.orow0, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
   } else {
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
@@ -563,7 +564,7 @@ k_score_q64(const uint16_t* __restrict__ q, const float* __restrict__ w, const v
     }
   }
   // keys of this range after the last computed tile: -inf for every query
-  fill_neg_inf(logits, ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
+  fill_neg_inf(logits, ld, (int64_t)b * M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, NT);
 }
 
 // ---------------------------------------------------------------------------
@@ -590,6 +591,7 @@ static hipError_t launch_h8(const misa_shape& s, const uint16_t* q, const float*
   const int M = s.q_per_seq;
   const int n_qtiles = (M + 31) / 32;
   dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  if (o.slab_tiles > 0) grid = dim3((unsigned)((int64_t)o.slab_tiles * nks), 1);
   if (kdtype == MISA_K_BF16)
     hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE, DMA>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
                        o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
@@ -683,6 +685,18 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   return p;
 }
 
+FusedPlan lean_plan(const FusedPlan& fast, const misa_shape& s) {
+  FusedPlan p = fast;
+  if (!p.ok) return p;
+  // the expected groups per region with a quarter more and room for one
+  // cluster of large scores: a region that overflows flags its row for the
+  // exact re-scoring, so a tighter region costs time, never results
+  const int64_t n_min = s.q_pos0 + 1;
+  const int64_t expect = (int64_t)p.target * p.key_range / n_min + 1;
+  p.cap_region = (int)std::min<int64_t>(fast.cap_region, (expect + expect / 4 + 128 + 63) / 64 * 64);
+  return p;
+}
+
 hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                                 const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
                                 float* sample_logits, hipStream_t st) {
@@ -702,11 +716,17 @@ hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const floa
 
 hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                                 int kdtype, const float* k_scale, const int32_t* heads, int h,
-                                const uint32_t* row_flag, float* logits, int64_t ld, hipStream_t st) {
+                                const uint32_t* row_flag, float* slab, int64_t ld, const SlabBatch& sb,
+                                hipStream_t st) {
   int nks;
   int64_t KR;
-  plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
-  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
+  const int n_qtiles = (s.q_per_seq + 31) / 32;
+  plan_split(s.n_keys, s.n_seq, n_qtiles, 64, &nks, &KR);   // the candidate pass's key ranges
+  ScoreOut o{slab, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
+  o.slab_tiles = sb.tiles;
+  o.slab_first = (int)sb.first;
+  o.slab_tr = sb.tr;
+  o.n_flat = s.n_seq * n_qtiles;
   return launch_h8<kLogits, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
 }
 

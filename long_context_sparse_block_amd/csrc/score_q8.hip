@@ -91,8 +91,9 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, p16 = lane & 15;
-  const int b = blockIdx.y;
-  const TileCoords tc = tile_coords(n_qtiles, n_ksplits, KR, N);
+  const WgTile tc = wg_tile<QT, MODE == kLogits>(out_spec, M, n_qtiles, n_ksplits, KR, N);
+  if (!tc.valid) return;   // uniform over the workgroup
+  const int b = tc.b;
   const int k0 = (int)tc.k0, k1 = (int)tc.k1;
   const int qa = tc.qt * QT, qb = min(qa + QT, M);
   const int64_t qrow0 = (int64_t)b * M;
@@ -127,7 +128,7 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
     tq[G] = (qo < qb) ? (q_pos0 + qo) / kstride : -1;
     const int qoc = min(qo, M - 1);
     if (MODE == kLogits)
-      orsrc[G] = uniform_rsrc(out_spec.logits + (qrow0 + min(qg0, M - 1)) * out_spec.ld, (uint32_t)nrows * row_bytes);
+      orsrc[G] = uniform_rsrc(out_spec.logits + (tc.orow0 + min(qg0, M - 1)) * out_spec.ld, (uint32_t)nrows * row_bytes);
     else
       cand_lane(out_spec, qrow0, qa, qb, qo, qoc, n_ksplits, thr[G], reg[G]);
 #pragma unroll
@@ -232,7 +233,7 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
   }
   if (MODE == kLogits) {
     // keys of this range after the last computed tile: -inf for every query
-    fill_neg_inf(out_spec.logits, out_spec.ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, 256);
+    fill_neg_inf(out_spec.logits, out_spec.ld, tc.orow0, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, 256);
   } else {
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
@@ -354,7 +355,7 @@ __global__ void __launch_bounds__(256) k_score_dense_q8(const uint8_t* __restric
       __syncthreads();
     }
   }
-  fill_neg_inf(logits, ld, b, M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, 256);
+  fill_neg_inf(logits, ld, (int64_t)b * M, qa, qb, k0 + (int64_t)n_tiles * KT, k1, tid, 256);
 }
 
 hipError_t launch_dense_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
@@ -386,6 +387,7 @@ static hipError_t launch_q8(const misa_shape& s, const uint8_t* q8, const float*
   const int M = s.q_per_seq;
   const int n_qtiles = (M + 31) / 32;
   dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
+  if (o.slab_tiles > 0) grid = dim3((unsigned)((int64_t)o.slab_tiles * nks), 1);
   hipLaunchKernelGGL(k_score_q8<MODE>, grid, dim3(256), 0, st, q8, q_scale, w, k, k_scale, heads, h, o, s.n_keys,
                      kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
   return hipGetLastError();
@@ -393,11 +395,18 @@ static hipError_t launch_q8(const misa_shape& s, const uint8_t* q8, const float*
 
 hipError_t launch_score_q8(const misa_shape& s, const uint8_t* q8, const float* q_scale, const float* w,
                           const uint8_t* k, const float* k_scale, const int32_t* heads, int h, float* logits,
-                          int64_t ld, hipStream_t st, const uint32_t* row_flag) {
+                          int64_t ld, hipStream_t st, const uint32_t* row_flag, const SlabBatch* slab) {
   int nks;
   int64_t KR;
-  plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, kQ8KT, &nks, &KR);
-  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
+  const int n_qtiles = (s.q_per_seq + 31) / 32;
+  plan_split(s.n_keys, s.n_seq, n_qtiles, kQ8KT, &nks, &KR);
+  ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
+  if (slab != nullptr) {
+    o.slab_tiles = slab->tiles;
+    o.slab_first = (int)slab->first;
+    o.slab_tr = slab->tr;
+    o.n_flat = s.n_seq * n_qtiles;
+  }
   return launch_q8<kLogits>(s, q8, q_scale, w, k, k_scale, heads, h, o, 1, nks, KR, st);
 }
 

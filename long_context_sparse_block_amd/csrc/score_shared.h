@@ -28,14 +28,15 @@ __device__ __forceinline__ TileCoords tile_coords(int n_qtiles, int n_ksplits, i
   return c;
 }
 
-// -inf for keys [from, to) of queries [qa, qb) (all of them lie after every query)
-__device__ __forceinline__ void fill_neg_inf(float* logits, int64_t ld, int b, int M, int qa, int qb,
+// -inf for keys [from, to) of queries [qa, qb) (all of them lie after every
+// query); query qi's logits row is row orow0 + qi
+__device__ __forceinline__ void fill_neg_inf(float* logits, int64_t ld, int64_t orow0, int qa, int qb,
                                              int64_t from, int64_t to, int tid, int nt) {
   if (from >= to) return;
   const float ninf = -__builtin_inff();
   const int64_t span = to - from;
   for (int qi = qa; qi < qb; ++qi) {
-    float* row = logits + ((int64_t)b * M + qi) * ld;
+    float* row = logits + (orow0 + qi) * ld;
     // from is a multiple of 4 (tile aligned) and ld % 4 == 0
     const int64_t n4 = span / 4;
     for (int64_t e = tid; e < n4; e += nt)
@@ -71,6 +72,11 @@ __device__ __forceinline__ void store_i32(__amdgpu_buffer_rsrc_t r, uint32_t byt
 //    overflowed and holds only the first cap).
 //  row_flag != nullptr: only workgroups holding a row with row_flag[row] != 0
 //    run (re-scoring of the rows a candidate pass could not settle).
+//  slab_tiles > 0 (kLogits): one batch of a re-scoring that runs through a
+//    logits slab.  The grid covers slab_tiles consecutive query tiles of the
+//    flattened (sequence, query tile) order, from tile slab_first on (tiles
+//    past n_flat have no work); query qi of the tile in slot s writes slab row
+//    s * slab_tr + (qi - first query of the tile).
 struct ScoreOut {
   float* logits;
   int64_t ld;
@@ -80,11 +86,47 @@ struct ScoreOut {
   uint32_t* rcount;
   int cap;
   const uint32_t* row_flag;
+  int slab_tiles = 0, slab_first = 0, slab_tr = 0, n_flat = 0;
 };
 constexpr int kLogits = 0;
 constexpr int kCands = 1;
 
 constexpr uint32_t kDrop = 0x80000000u;   // a byte offset past every store resource
+
+// The workgroup's sequence b, query tile (qt, QT queries a tile), key range
+// [k0, k1), and the logits row base orow0 (query qi of the tile writes row
+// orow0 + qi).  valid == false: a slab batch's slot past the last tile (no
+// work; uniform over the workgroup).  SLAB: slab batches are possible (only
+// logits passes take them).
+struct WgTile {
+  int b, qt;
+  int64_t k0, k1, orow0;
+  bool valid;
+};
+template <int QT, bool SLAB>
+__device__ __forceinline__ WgTile wg_tile(const ScoreOut& o, int M, int n_qtiles, int n_ksplits, int64_t KR,
+                                          int64_t N) {
+  WgTile t;
+  if (SLAB && o.slab_tiles > 0) {
+    const int64_t T = xcd_remap(blockIdx.x, (int64_t)o.slab_tiles * n_ksplits);
+    const int slot = (int)(T % o.slab_tiles);
+    const int64_t flat = (int64_t)o.slab_first + slot;
+    t.valid = flat < (int64_t)o.n_flat;
+    t.b = (int)(flat / n_qtiles);
+    t.qt = (int)(flat % n_qtiles);
+    t.k0 = (T / o.slab_tiles) * KR;
+    t.orow0 = (int64_t)slot * o.slab_tr - (int64_t)t.qt * QT;
+  } else {
+    const TileCoords c = tile_coords(n_qtiles, n_ksplits, KR, N);
+    t.valid = true;
+    t.b = blockIdx.y;
+    t.qt = c.qt;
+    t.k0 = c.k0;
+    t.orow0 = (int64_t)t.b * M;
+  }
+  t.k1 = t.k0 + KR < N ? t.k0 + KR : N;
+  return t;
+}
 
 // kCands set-up for the lane's output query qo (qoc = min(qo, M - 1)) of a
 // workgroup holding rows qa .. qb-1 of sequence row base qrow0: its threshold
@@ -108,6 +150,16 @@ __device__ __forceinline__ void cand_rsrc(const ScoreOut& o, int64_t qrow0, int 
   r[1] = uniform_rsrc(o.gkeys + g0, span * 4u);
 }
 
+// Largest of four scores that are finite or -inf: v_max3 and v_max without the
+// NaN-quieting operand canonicalisation that fmaxf costs (two more VALU
+// instructions per group).
+__device__ __forceinline__ float max4(f32x4 v) {
+  float m;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(v[0]), "v"(v[1]), "v"(v[2]));
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(v[3]));
+  return m;
+}
+
 // kCands epilogue of one tile: the lane holds 4 consecutive scores `v` (keys
 // kg .. kg+3) of its output query; the 16 lanes of lane group `gmask` hold one
 // query.  A group with a score at or above thr is appended whole; positions
@@ -116,14 +168,18 @@ __device__ __forceinline__ void cand_rsrc(const ScoreOut& o, int64_t qrow0, int 
 // room), so a wave's count of stores per tile is fixed.
 __device__ __forceinline__ void append_group(const __amdgpu_buffer_rsrc_t* r, f32x4 v, float thr, uint64_t gmask,
                                              uint32_t& run, uint32_t reg, int cap, int kg) {
-  const float vmax = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
+  const float vmax = max4(v);
   const bool pass = vmax >= thr;
   const uint64_t m = __ballot(pass) & gmask;
   const uint32_t pos = run + lanes_below(m);
   run += (uint32_t)__popcll(m);
   const bool put = pass && pos < (uint32_t)cap;
-  store_f32x4(r[0], put ? (reg + pos) * 16u : kDrop, v);
-  store_i32(r[1], put ? (reg + pos) * 4u : kDrop, kg);
+  // the group's slot, or one whose byte offsets lie past both descriptors:
+  // kDrop for the scores; kDrop / 4 for the keys, past their range because a
+  // workgroup's regions take fewer than 2^31 bytes of scores (4x their keys)
+  const uint32_t slot = put ? reg + pos : (kDrop >> 4);
+  store_f32x4(r[0], slot << 4, v);
+  store_i32(r[1], slot << 2, kg);
 }
 
 }  // namespace misa

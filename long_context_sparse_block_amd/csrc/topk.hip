@@ -509,7 +509,8 @@ template <int CAP, int NT>
 __device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, int i, int b, const float* __restrict__ logits,
                                          int64_t ld, const int32_t* __restrict__ cand, int n_cols, int k,
                                          int64_t q_pos0, int M, int32_t* __restrict__ idx_out,
-                                         float* __restrict__ val_out, int sorted) {
+                                         float* __restrict__ val_out, int sorted,
+                                         const float* __restrict__ lrow_in = nullptr) {
   constexpr int VPT = 2;                  // float4s per thread per lock-step (robust) step
   constexpr int STEP = 4 * VPT * NT;      // elements per lock-step step
   static_assert(CAP / 2 >= STEP, "a lock-step step must fit the free half of the buffer");
@@ -525,7 +526,7 @@ __device__ __forceinline__ void topk_row(TopkShared<CAP, NT>& sh, int i, int b, 
   const int64_t row = (int64_t)b * M + i;
   const int64_t t = q_pos0 + i;
   const int n = cand ? n_cols : (int)min((int64_t)n_cols, t + 1);
-  const float* lrow = logits + row * ld;
+  const float* lrow = lrow_in != nullptr ? lrow_in : logits + row * ld;   // the row's logits
   const int32_t* crow = cand ? cand + row * (int64_t)n_cols : nullptr;
   // float4 / int4 loads need 16-byte aligned rows: ld % 4 == 0 always, and the
   // candidate rows when n_cols % 4 == 0; otherwise every element is read singly
@@ -749,35 +750,48 @@ static SplitWs split_ws(void* ws, int64_t rows, int k) {
   return w;
 }
 
-// Per-row threshold from a sample: 1024 float4s (4096 elements) at a regular
-// stride over the row.  Sampling in 16-byte pieces keeps a cluster of large
-// scores (a block of related keys) from taking more than its share of the
+// Per-row threshold from a sample of whole 128-byte lines: 128 lines of 32
+// scores at a regular stride over the row (4096 scores, 1/32 of a
+// 131072-score row; a line costs one memory transaction whether one of its
+// scores is read or all 32, so sampling single 16-byte pieces fetched 8 times
+// the bytes it used).  A line's scores are neighbours and may be correlated
+// (a block of related keys), so each line counts at most 16 of its scores: a
+// cluster of large scores cannot take more than a bounded share of the
 // sample.  The threshold is the lower edge of the 20-bit order-key bucket
-// holding the k_s-th largest sampled element, k_s chosen so that about
-// `target` row elements are expected at or above it; rows no longer than
-// `target` keep every element (-inf).  Computed by one wave.
+// above which the capped count reaches k_s = target * 4096 / n + 2, so that
+// about `target` row elements are expected at or above it; rows too short
+// for the sample keep every element (-inf).  Computed by one wave: lane l
+// reads lines 2l and 2l + 1.
 __device__ __forceinline__ float row_threshold(const float* __restrict__ lrow, int n, int target) {
-  constexpr int L = 16;          // float4 loads per lane
-  constexpr int ns = 64 * L * 4;  // 4096 sampled elements
+  constexpr int kLines = 128, kCap = 16;  // sampled lines, scores a line can count
+  constexpr int ns = kLines * 32;         // 4096 sampled scores
   const int lane = threadIdx.x & 63;
   const uint64_t ks = (uint64_t)target * ns / (uint64_t)max(n, 1) + 2;
-  if (!(n > target && n >= 2 * ns && ks < (uint64_t)ns)) return -__builtin_inff();
-  const uint32_t n4 = (uint32_t)n / 4;                // whole float4s (16-byte aligned rows)
-  const uint32_t stride = n4 / (uint32_t)(ns / 4);    // >= 2 (n >= 2 ns)
-  uint32_t key[4 * L];
+  if (!(n > target && n >= 2 * ns && ks < (uint64_t)(kLines * kCap))) return -__builtin_inff();
+  const uint32_t stride = ((uint32_t)n / 32u) / (uint32_t)kLines;   // lines apart, >= 2 (n >= 2 ns)
+  uint32_t key[2][32];
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const f32x4 v = *(reinterpret_cast<const f32x4*>(lrow) + (uint32_t)(j * 64 + lane) * stride);
+  for (int ln = 0; ln < 2; ++ln) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(lrow + (size_t)((2 * lane + ln) * stride) * 32u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) key[4 * j + e] = order_key(v[e]);
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 v = src[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[ln][4 * j + e] = order_key(v[e]);
+    }
   }
-  // bits decided from the top: per-lane counts, one wave sum per bit
+  // bits decided from the top: capped per-line counts, one wave sum per bit
   uint32_t T = 0;
   for (int bit = 31; bit >= 12; --bit) {
     const uint32_t c = T | (1u << bit);
     uint32_t cl = 0;
 #pragma unroll
-    for (int j = 0; j < 4 * L; ++j) cl += (key[j] >= c) ? 1u : 0u;
+    for (int ln = 0; ln < 2; ++ln) {
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) cnt += (key[ln][j] >= c) ? 1u : 0u;
+      cl += min(cnt, (uint32_t)kCap);
+    }
     if (__reduce_add_sync(~0ull, cl) >= (uint32_t)ks) T = c;
   }
   const float tf = key_to_float(T);
@@ -1182,25 +1196,42 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
     finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, true, mm_lo, mm_hi);
 }
 
-// Whole-row top-k of the flagged rows from full logits; a fixed grid walks
-// the rows, so the (rare) flagged rows cost one cheap flag check each.
+// Whole-row top-k of the flagged rows from a logits slab: slab_tiles query
+// tiles (32 queries each) of the flattened (sequence, query tile) order from
+// tile slab_first on, query qi of the tile in slot s in slab row
+// s * slab_tr + (qi - first query of the tile).  A fixed grid walks the slab
+// rows, so the (rare) flagged rows cost one cheap flag check each.
+// the row (b * M + i) of slab row r of a batch (see k_topk_flagged), or -1
+__device__ __forceinline__ int64_t slab_row(int64_t r, int64_t slab_first, int slab_tr, int n_qtiles, int64_t n_flat,
+                                            int M) {
+  const int64_t flat = slab_first + r / slab_tr;
+  const int i = (int)(flat % n_qtiles) * 32 + (int)(r % slab_tr);
+  return (flat < n_flat && i < M) ? (flat / n_qtiles) * M + i : -1;
+}
+
 template <int CAP, int NT>
-__global__ void __launch_bounds__(NT, 2) k_topk_flagged(const float* __restrict__ logits, int64_t ld,
-                                                        int64_t n_keys, int k, int64_t q_pos0, int M, int64_t rows,
+__global__ void __launch_bounds__(NT, 2) k_topk_flagged(const float* __restrict__ slab, int64_t ld,
+                                                        int64_t n_keys, int k, int64_t q_pos0, int M,
+                                                        int n_qtiles, int64_t n_flat, int64_t slab_first,
+                                                        int slab_tiles, int slab_tr,
                                                         const uint32_t* __restrict__ flag,
                                                         int32_t* __restrict__ idx_out, float* __restrict__ val_out,
                                                         int sorted) {
   __shared__ TopkShared<CAP, NT> sh;
+  const int64_t n_rows = (int64_t)slab_tiles * slab_tr;
   {   // the workgroup's flags loaded together: most calls have none
     uint32_t mine = 0;
-    for (int64_t r = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; r < rows; r += (int64_t)NT * gridDim.x)
-      mine |= flag[r];
+    for (int64_t r = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; r < n_rows; r += (int64_t)NT * gridDim.x) {
+      const int64_t row = slab_row(r, slab_first, slab_tr, n_qtiles, n_flat, M);
+      if (row >= 0) mine |= flag[row];
+    }
     if (!__syncthreads_or(mine != 0)) return;   // uniform over the workgroup
   }
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    if (flag[r] == 0) continue;   // uniform over the workgroup
-    topk_row<CAP, NT>(sh, (int)(r % M), (int)(r / M), logits, ld, nullptr, (int)n_keys, k, q_pos0, M, idx_out,
-                      val_out, sorted);
+  for (int64_t r = blockIdx.x; r < n_rows; r += gridDim.x) {
+    const int64_t row = slab_row(r, slab_first, slab_tr, n_qtiles, n_flat, M);
+    if (row < 0 || flag[row] == 0) continue;   // uniform over the workgroup
+    topk_row<CAP, NT>(sh, (int)(row % M), (int)(row / M), slab, ld, nullptr, (int)n_keys, k, q_pos0, M, idx_out,
+                      val_out, sorted, slab + r * ld);
     __syncthreads();
   }
 }
@@ -1236,16 +1267,21 @@ hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, c
   return hipGetLastError();
 }
 
-hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* logits, int64_t ld,
+hipError_t launch_topk_flagged(const misa_shape& s, int k, const float* slab, int64_t ld, const SlabBatch& sb,
                                const uint32_t* row_flag, int32_t* idx, float* vals, bool sorted, hipStream_t st) {
-  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
-  const unsigned g = (unsigned)std::min<int64_t>(rows, 512);
+  const int64_t slab_first = sb.first;
+  const int slab_tiles = sb.tiles, slab_tr = sb.tr;
+  const int n_qtiles = (s.q_per_seq + 31) / 32;
+  const int64_t n_flat = (int64_t)s.n_seq * n_qtiles;
+  const unsigned g = (unsigned)std::min<int64_t>((int64_t)slab_tiles * slab_tr, 512);
   if (k <= 4096)
-    hipLaunchKernelGGL((k_topk_flagged<8192, 512>), dim3(g), dim3(512), 0, st, logits, ld, s.n_keys, k, s.q_pos0,
-                       s.q_per_seq, rows, row_flag, idx, vals, (int)sorted);
+    hipLaunchKernelGGL((k_topk_flagged<8192, 512>), dim3(g), dim3(512), 0, st, slab, ld, s.n_keys, k, s.q_pos0,
+                       s.q_per_seq, n_qtiles, n_flat, slab_first, slab_tiles, slab_tr, row_flag, idx, vals,
+                       (int)sorted);
   else
-    hipLaunchKernelGGL((k_topk_flagged<16384, 512>), dim3(g), dim3(512), 0, st, logits, ld, s.n_keys, k,
-                       s.q_pos0, s.q_per_seq, rows, row_flag, idx, vals, (int)sorted);
+    hipLaunchKernelGGL((k_topk_flagged<16384, 512>), dim3(g), dim3(512), 0, st, slab, ld, s.n_keys, k, s.q_pos0,
+                       s.q_per_seq, n_qtiles, n_flat, slab_first, slab_tiles, slab_tr, row_flag, idx, vals,
+                       (int)sorted);
   return hipGetLastError();
 }
 

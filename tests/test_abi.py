@@ -139,8 +139,8 @@ def test_sparse_head_topk_checks_and_workspace(lib):
     # prefix of 122881: 410 expected groups per range, doubled, + 512, rounded
     # up to 256 = 1536 groups of 4 scores (16 bytes) and their first key (4)
     # plus the bf16 copy of the keys the scoring stages by direct loads (131072 x 256)
-    assert fused == (8192 * 131072 * 4 + 131072 * 256 + 8192 * 4096 * 4 + 2 * 8192 * 4 + 8192 * 8 * 4
-                     + 8192 * 8 * 1536 * 20)
+    # (the sampled scores share their memory with the logits slab)
+    assert fused == (8192 * 131072 * 4 + 131072 * 256 + 2 * 8192 * 4 + 8192 * 8 * 4 + 8192 * 8 * 1536 * 20)
     # bf16 keys are staged as they are: no widened copy
     assert lib.misa_sparse_head_topk_workspace_bytes(ctypes.byref(big), 0, 8, 2048) == fused - 131072 * 256
 
@@ -259,11 +259,36 @@ def test_workspace_size_of_the_long_context_chunk(lib):
     s = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
     need = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 1, 8, 2048, 0)
     # the fp32 logits of the chunk (8192 x 131072 x 4 bytes; the fused path
-    # writes them only for rows its candidates cannot settle), the sampled
-    # scores (8192 x 4096 x 4), the candidate regions (8192 rows x 8 key
+    # writes them only for rows its candidates cannot settle, and the sampled
+    # scores share their memory), the candidate regions (8192 rows x 8 key
     # ranges x 1536 groups of 4 scores and a key, 20 bytes) and the bf16 keys
-    main = 8192 * 131072 * 4 + 8192 * 4096 * 4 + 8192 * 8 * 1536 * 20 + 131072 * 256
+    main = 8192 * 131072 * 4 + 8192 * 8 * 1536 * 20 + 131072 * 256
     assert main <= need < main * 1.01
+
+
+def test_least_workspace_of_the_long_context_chunk(lib):
+    s = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
+    full = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 1, 8, 2048, 0)
+    least = lib.misa_indexer_workspace_min_bytes(ctypes.byref(s), 1, 8, 2048, 0)
+    # the sampled scores (8192 x 4096 x 4 bytes = 128 MiB) double as the
+    # logits slab (8 query tiles of 32 rows x 131072 scores, 16 MiB each), the
+    # regions take 640 groups (410 expected + a quarter + 128, rounded up to
+    # 64), and the bf16 keys
+    main = 8192 * 4096 * 4 + 8192 * 8 * 640 * 20 + 131072 * 256
+    assert main <= least < main * 1.01
+    assert least < (1 << 30) < full
+    # a workspace below the least is refused before anything is enqueued
+    f = lib.misa_indexer
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, 1, FAKE, 8, 2048, 0, FAKE, None, FAKE, least - 1, None) == -3
+    assert lib.misa_indexer_workspace_min_bytes(ctypes.byref(s), 1, 0, 2048, 0) == 0
+
+
+def test_short_prefixes_have_no_lean_plan(lib):
+    # rows that the fused path does not take (prefixes of 1 .. 4096 keys) are
+    # selected from full logits, whatever the workspace
+    s = lcsb.make_shape(1, 4096, 4096, 0, 64, 64)
+    assert lib.misa_indexer_workspace_min_bytes(ctypes.byref(s), 0, 8, 256, 0) == \
+        lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 8, 256, 0)
 
 
 def test_noalloc_indexer_refuses_requests_beyond_its_scratch(lib):

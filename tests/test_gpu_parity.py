@@ -427,6 +427,54 @@ def test_fused_indexer_rows_the_sample_misjudges():
     _check_sparse_head_topk(inp, st)
 
 
+def _threshold_defeated(inp):
+    """Every key at a multiple of the sampling stride (32) gets a huge score,
+    so the sampled threshold admits far fewer than k candidates: every row is
+    flagged for the re-scoring."""
+    q = oracle.bf16_bits_to_f64(inp.q).astype(np.float32)
+    kf = oracle.bf16_bits_to_f64(inp.k).astype(np.float32)
+    u = np.ones(128, np.float32) / np.sqrt(128.0)
+    q += 4.0 * u
+    kf[:, ::32, :] += 40.0 * u
+    inp.q[...] = gen.to_bf16_bits(q)
+    inp.k[...] = gen.to_bf16_bits(kf)
+    inp.w[...] = np.abs(inp.w)
+    return inp
+
+
+@pytest.mark.parametrize("room", ["least", "two_tiles", "three_tiles"])
+def test_fused_indexer_in_a_smaller_workspace(room):
+    """Below the fast plan's workspace the flagged rows are re-scored through a
+    logits slab a few query tiles at a time (the least workspace: one tile,
+    and candidate regions sized closer to the expected candidates).  Two
+    sequences of 48 queries (2 tiles each, the second ragged) with every row
+    flagged: the result equals the fast plan's bit for bit, in 4, 2 and 2
+    batches."""
+    say(f"fused indexer in a smaller workspace ({room})")
+    cfg = gen.small_config(name="fused_slab", n_seq=2, m=48, n=40000, hh=16, b=64, h=8, k=2048, seed=46,
+                           plant=False)
+    inp = _threshold_defeated(gen.generate(cfg))
+    st = run_stages(inp)
+    sh, t = st["sh"], st["t"]
+    full = lcsb.misa_indexer_workspace_bytes(sh, cfg.kdtype, cfg.h, cfg.topk)
+    least = lcsb.misa_indexer_workspace_min_bytes(sh, cfg.kdtype, cfg.h, cfg.topk)
+    tile = 32 * 40000 * 4
+    # (regions of 128-key ranges hold at most 32 groups in either plan, so the
+    # least workspace is the fast one with a slab of one tile)
+    assert least == full - 3 * tile
+    size = dict(least=least, two_tiles=full - 2 * tile, three_tiles=full - tile)[room]
+    ref_i, ref_v = lcsb.misa_indexer(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk)
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+    idx, vals = lcsb.misa_indexer(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, ws=ws)
+    sidx, svals = _staged_selection(inp, st, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref_i) and torch.equal(vals, ref_v)
+    assert torch.equal(idx, sidx) and torch.equal(vals, svals)
+    with pytest.raises(lcsb.MisaError):
+        lcsb.misa_indexer(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk,
+                          ws=torch.empty(least - 256, dtype=torch.uint8, device="cuda"))
+
+
 def test_fused_indexer_nonpositive_scores_ragged_query_tile():
     """All head weights negative: every score is <= 0 and a good share of each
     row is exactly 0 (no routed head with a positive dot product), so the row

@@ -197,6 +197,40 @@ def test_q8_fused_rows_the_sample_misjudges():
     check_topk_exact(inp, st["logits"], cfg.topk, fi, fv)
 
 
+def test_q8_fused_selection_in_a_smaller_workspace():
+    """misa_sparse_head_topk_q8 and misa_indexer_q8 with room for one query tile
+    of logits (every row flagged, two sequences of 48 queries: 4 re-scoring
+    batches) give the fast plan's result bit for bit."""
+    say("fused fp8 selection in a smaller workspace")
+    cfg = gen.small_config(name="q8_slab", n_seq=2, m=48, n=40000, hh=16, b=64, h=8, k=2048, kdtype=gen.KDTYPE_FP8,
+                           seed=50, plant=False)
+    inp = gen.generate(cfg)
+    q = oracle.bf16_bits_to_f64(inp.q).astype(np.float32)
+    kf = oracle.e4m3fn_to_f64(inp.k).astype(np.float32) * inp.k_scale[..., None]
+    u = np.ones(128, np.float32) / np.sqrt(128.0)
+    q += 4.0 * u
+    kf[:, ::32, :] += 40.0 * u
+    inp.q[...] = gen.to_bf16_bits(q)
+    fp8_keys_from(inp, kf)
+    inp.w[...] = np.abs(inp.w)
+    st = q8_stages(inp)
+    t, sh = st["t"], st["sh"]
+    tile = 32 * 40000 * 4
+    si, sv = lcsb.misa_topk(sh, st["logits"], cfg.topk)
+    full = lcsb.misa_sparse_head_topk_workspace_bytes(sh, gen.KDTYPE_FP8, cfg.h, cfg.topk)
+    ws = torch.empty(full - 3 * tile, dtype=torch.uint8, device="cuda")
+    fi, fv = lcsb.misa_sparse_head_topk_q8(sh, st["q8"], st["qs"], t["w"], t["k"], st["heads"], cfg.topk,
+                                           t["k_scale"], ws=ws)
+    ii, iv = lcsb.misa_indexer_q8(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, t["k_scale"])
+    full_ix = lcsb.misa_indexer_q8_workspace_bytes(sh, cfg.h, cfg.topk)
+    ji, jv = lcsb.misa_indexer_q8(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, t["k_scale"],
+                                  ws=torch.empty(full_ix - 3 * tile, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(fi, si) and torch.equal(fv, sv)
+    assert torch.equal(ji, ii) and torch.equal(jv, iv)
+    assert torch.equal(ii, si) and torch.equal(iv, sv)
+
+
 def test_q8_fused_nonpositive_scores_ragged_query_tile():
     """All head weights negative: scores <= 0, many exactly 0, thresholds <= 0;
     M = 37 leaves padding lanes whose zero scores must reach no row."""
