@@ -331,6 +331,18 @@ __device__ __forceinline__ void bitonic_write(uint64_t* buf, uint32_t cnt, int k
   }
 }
 
+// b0 + the number of composites in sorted[b0, b1) above c: four reads in
+// flight at a time (the bucket's entries are read back to back)
+__device__ __forceinline__ uint32_t bucket_rank(const uint64_t* sorted, uint32_t b0, uint32_t b1, uint64_t c) {
+  uint32_t r = b0, q = b0;
+  for (; q + 4 <= b1; q += 4) {
+    const uint64_t a0 = sorted[q], a1 = sorted[q + 1], a2 = sorted[q + 2], a3 = sorted[q + 3];
+    r += (uint32_t)(a0 > c) + (uint32_t)(a1 > c) + (uint32_t)(a2 > c) + (uint32_t)(a3 > c);
+  }
+  for (; q < b1; ++q) r += sorted[q] > c;
+  return r;
+}
+
 // Order the first cnt (<= CAP/2) raw entries of buf by composite and write the
 // top k of them, then the padding.  Counting sort into 2048 buckets of the
 // composite span (stored in buf[CAP/2 ...]), then each candidate's rank inside
@@ -390,8 +402,7 @@ __device__ __forceinline__ void rank_write(uint64_t* buf, uint32_t cnt, int k, i
         const uint32_t b0 = (d + 1 < (uint32_t)kHistBins) ? s_hist[d + 1] : 0;
         if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
         const uint32_t b1 = s_hist[d];
-        uint32_t r = b0;
-        for (uint32_t q = b0; q < b1; ++q) r += sorted[q] > c;
+        const uint32_t r = bucket_rank(sorted, b0, b1, c);
         if (r < (uint32_t)k) {
           idx_out[row * k + r] = comp_id(c);
           if (val_out) val_out[row * k + r] = comp_val(c);
@@ -490,8 +501,7 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
         const uint32_t b0 = (d + 1 < (uint32_t)HB) ? sh.hist[d + 1] : 0;
         if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
         const uint32_t b1 = sh.hist[d];
-        uint32_t r = b0;
-        for (uint32_t q = b0; q < b1; ++q) r += sh.buf[q] > c;
+        const uint32_t r = bucket_rank(sh.buf, b0, b1, c);
         if (r < (uint32_t)k) {
           idx_out[row * k + r] = comp_id(c);
           if (val_out) val_out[row * k + r] = comp_val(c);
@@ -965,8 +975,15 @@ __global__ void __launch_bounds__(NT, 2) k_topk_list(const float* __restrict__ l
     topk_row<CAP, NT>(sh, i, b, logits, ld, nullptr, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
     return;
   }
+  // the list into LDS: every thread's loads issued together (c >= 1 here)
   const uint64_t* src = list + row * (int64_t)capg;
-  for (uint32_t e = tid; e < c; e += NT) sh.buf[e] = src[e];
+  constexpr int EPT = CAP / NT;
+  uint64_t v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = src[min((uint32_t)(tid + j * NT), c - 1)];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)
+    if ((uint32_t)(tid + j * NT) < c) sh.buf[tid + j * NT] = v[j];
   __syncthreads();
   finish_list<CAP, NT>(sh, c, k, row, idx_out, val_out, sorted);
 }
