@@ -87,6 +87,22 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 }
 
 // Order-preserving map float -> uint32 (larger float <=> larger key), with
+// (P0 + P1) + (P2 + P3) of a value P held on the four 16-lane rows of a wave,
+// on every lane: the xor-16 and xor-32 butterflies done by gfx950's
+// v_permlane16_swap / v_permlane32_swap (VALU, no LDS round trip).  The
+// 16-swap of P with itself leaves rows (0, 0, 2, 2) in one register and (1, 1,
+// 3, 3) in the other, so their sum is P0 + P1 on rows 0 and 1 and P2 + P3 on
+// rows 2 and 3; the 32-swap does the same across the two halves.  Each add
+// has the same two operands as P + shfl_xor(P, 16) and v + shfl_xor(v, 32)
+// (in some order, and float addition is commutative), so the result is
+// bitwise the same.
+__device__ __forceinline__ float sum_rows(float P) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(P), __float_as_uint(P), false, false);
+  const float v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // -0.0 folded onto +0.0.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -536,8 +536,7 @@ k_score_q64(const uint16_t* __restrict__ q, const float* __restrict__ w, const v
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp) {
           const float P = quad_chain(acc[grp], wq[grp][0], wq[grp][1], wq[grp][2], wq[grp][3]);
-          const float v = P + __shfl_xor(P, 16);   // P0+P1 on lane groups 0/1, P2+P3 on 2/3
-          const float T = v + __shfl_xor(v, 32);   // (P0+P1)+(P2+P3)
+          const float T = sum_rows(P);   // (P0+P1)+(P2+P3) on every lane
           s = s + T;
         }
         if (KDT == MISA_K_FP8_E4M3) s *= s_sc[BUF][kb * 16 + p16];

@@ -130,8 +130,7 @@ __global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) acc = mfma16(afr[grp][ks], bfr[ks], acc);
       const float P = quad_chain(acc, wq[grp][0], wq[grp][1], wq[grp][2], wq[grp][3]);
-      const float v = P + __shfl_xor(P, 16);       // P0+P1 on groups 0/1, P2+P3 on 2/3
-      const float T = v + __shfl_xor(v, 32);       // (P0+P1)+(P2+P3)
+      const float T = sum_rows(P);   // (P0+P1)+(P2+P3) on every lane
       s = s + T;
     }
     if (KDT == MISA_K_FP8_E4M3) s *= cur.sc;
@@ -308,8 +307,7 @@ __global__ void __launch_bounds__(256) k_score_gather_lds(const uint16_t* __rest
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) acc = mfma16(afr[grp][ks], bfr[ks], acc);
       const float P = quad_chain(acc, wq[grp][0], wq[grp][1], wq[grp][2], wq[grp][3]);
-      const float v = P + __shfl_xor(P, 16);
-      const float T = v + __shfl_xor(v, 32);
+      const float T = sum_rows(P);   // (P0+P1)+(P2+P3) on every lane
       s = s + T;
     }
     if (kFp8) s *= sc;

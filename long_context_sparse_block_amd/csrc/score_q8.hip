@@ -328,8 +328,7 @@ __global__ void __launch_bounds__(256) k_score_dense_q8(const uint8_t* __restric
         for (int grp = 0; grp < NG; ++grp) {
           const f32x4 acc = mfma_f8(afr[grp], bf);
           const float P = quad_chain(acc, wq[grp][0], wq[grp][1], wq[grp][2], wq[grp][3]);
-          const float v = P + __shfl_xor(P, 16);   // P0+P1 on lane groups 0/1, P2+P3 on 2/3
-          const float T = v + __shfl_xor(v, 32);   // (P0+P1)+(P2+P3)
+          const float T = sum_rows(P);   // (P0+P1)+(P2+P3) on every lane
           s = s + T;
         }
         s *= ssc[kb * 16 + p16];
