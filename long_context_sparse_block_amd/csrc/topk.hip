@@ -988,8 +988,119 @@ __global__ void __launch_bounds__(NT, 2) k_topk_list(const float* __restrict__ l
   finish_list<CAP, NT>(sh, c, k, row, idx_out, val_out, sorted);
 }
 
+// The long-row top-k (k <= 4096) in one kernel, one workgroup per row: wave 0
+// takes the row's threshold from its sampled lines (row_threshold) while the
+// other waves' first loads are in flight; the row is streamed once, each wave
+// keeping every element at or above the threshold in its own LDS region (the
+// float4s interleaved over the waves, positions from ballots of the lanes'
+// per-batch counts); the regions are gathered into one list and the exact
+// top-k is selected from it (finish_list).  A row whose regions overflow, or
+// whose candidates come short of k, takes the whole-row path in the same
+// workgroup, so the result is exact for every input.  The list never leaves
+// LDS, and the select of one row overlaps the streaming of the other
+// workgroup on the CU.
+template <int CAP, int NT>
+__global__ void __launch_bounds__(NT, 2) k_topk_fused(const float* __restrict__ logits, int64_t ld, int n_cols,
+                                                      int k, int target, int64_t q_pos0, int M,
+                                                      int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                                                      int sorted) {
+  constexpr int NW = NT / 64;
+  constexpr int WCAP = CAP / NW;   // candidates a wave's region holds
+  constexpr int U = 4;             // float4s per lane per batch (two batches in flight)
+  __shared__ TopkShared<CAP, NT> sh;
+  __shared__ float s_thr;
+  __shared__ uint32_t s_run[NW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int64_t row = (int64_t)b * M + i;
+  const int n = (int)min((int64_t)n_cols, q_pos0 + i + 1);
+  const float* lrow = logits + row * ld;
+  // float4s of the row (16-byte aligned: ld % 4 == 0), non-temporal (read
+  // once), index clamped into the row (no branch)
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(lrow);
+  const int n4 = (n + 3) / 4;
+  f32x4 va[U], vb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    va[u] = __builtin_nontemporal_load(p4 + min(tid + u * NT, n4 - 1));
+    vb[u] = __builtin_nontemporal_load(p4 + min(U * NT + tid + u * NT, n4 - 1));
+  }
+  if (wv == 0) {
+    const float t = row_threshold(lrow, n, target);
+    if (lane == 0) s_thr = t;
+  }
+  __syncthreads();
+  const float tf = s_thr;
+  uint64_t* reg = sh.buf + wv * WCAP;
+  uint32_t run = 0;   // candidates found by this wave (uniform)
+  for (int base4 = 0; base4 < n4; base4 += U * NT) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = va[u];
+      va[u] = vb[u];
+      vb[u] = __builtin_nontemporal_load(p4 + min(base4 + 2 * U * NT + tid + u * NT, n4 - 1));
+    }
+    uint32_t fl = 0;   // bit 4u+j: element j of float4 u passes
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e0 = 4 * (base4 + tid + u * NT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fl |= (uint32_t)(e0 + j < n && v[u][j] >= tf) << (4 * u + j);
+    }
+    const uint32_t cnt = __popc(fl);   // 0..16
+    const uint64_t m0 = __ballot(cnt & 1u), m1 = __ballot(cnt & 2u), m2 = __ballot(cnt & 4u),
+                   m3 = __ballot(cnt & 8u), m4 = __ballot(cnt & 16u);
+    if ((m0 | m1 | m2 | m3 | m4) == 0) continue;
+    uint32_t pos = run + lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2) + 8 * lanes_below(m3) +
+                   16 * lanes_below(m4);
+    run += __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2) + 8 * __popcll(m3) + 16 * __popcll(m4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e0 = 4 * (base4 + tid + u * NT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (fl & (1u << (4 * u + j))) {
+          if (pos < (uint32_t)WCAP) reg[pos] = pack_raw(v[u][j], e0 + j);
+          ++pos;
+        }
+    }
+  }
+  if (lane == 0) s_run[wv] = run;
+  __syncthreads();
+  uint32_t tot = 0, before = 0;
+  bool over = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = s_run[w];
+    over |= c > (uint32_t)WCAP;
+    before += (w < wv) ? c : 0u;
+    tot += c;
+  }
+  if (over || tot < (uint32_t)min(k, n)) {   // uniform over the workgroup
+    topk_row<CAP, NT>(sh, i, b, logits, ld, nullptr, n_cols, k, q_pos0, M, idx_out, val_out, sorted);
+    return;
+  }
+  // the regions gathered into sh.buf[0, tot): every thread holds its wave's
+  // entries in registers before any is written
+  {
+    constexpr int PER = WCAP / 64;
+    uint64_t e[PER];
+    const uint32_t mine = run;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) e[m] = reg[min((uint32_t)(lane + 64 * m), (uint32_t)WCAP - 1)];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+      if ((uint32_t)(lane + 64 * m) < mine) sh.buf[before + lane + 64 * m] = e[m];
+    __syncthreads();
+  }
+  finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted);
+}
+
 size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k) {
-  if (n_cols < kSplitMinCols) return 0;
+  if (n_cols < kSplitMinCols || k <= 4096) return 0;   // k <= 4096: k_topk_fused keeps its list in LDS
   return split_ws_bytes((int64_t)s.n_seq * s.q_per_seq, k);
 }
 
@@ -998,6 +1109,12 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
                        bool sorted) {
   dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  if (cand == nullptr && n_cols >= kSplitMinCols && k <= 4096) {
+    const int target = min(3 * k / 2, (k + list_cap(k)) / 2);
+    hipLaunchKernelGGL((k_topk_fused<8192, 512>), grid, dim3(512), 0, st, logits, ld, n_cols, k, target, s.q_pos0,
+                       s.q_per_seq, idx, vals, (int)sorted);
+    return hipGetLastError();
+  }
   const bool split = cand == nullptr && n_cols >= kSplitMinCols && ws != nullptr &&
                      ws_bytes >= split_ws_bytes(rows, k);
   if (split) {

@@ -568,16 +568,20 @@ def test_topk_rows_that_defeat_the_sampled_threshold(kind):
     check_topk_exact_arrays(vals, N - M, k, idx.cpu().numpy(), v.cpu().numpy())
 
 
-@pytest.mark.parametrize("n,k", [(40001, 2048), (50003, 8192), (16384, 2048)])
-def test_topk_long_rows_split_path(n, k):
-    """Rows long enough for the threshold / filter / select kernels: ragged
-    lengths, causal prefixes across chunk boundaries, repeated values."""
-    say("split top-k", n, k)
+@pytest.mark.parametrize("n,k,q0", [(40001, 2048, None), (50003, 8192, None), (16384, 2048, None),
+                                    (20000, 2048, 8170), (20000, 2048, 7000), (20000, 4096, 0)])
+def test_topk_long_rows_split_path(n, k, q0):
+    """Rows of buffers long enough for the long-row paths (the one-kernel
+    top-k for k <= 4096, the threshold / filter / list kernels above):
+    ragged lengths, causal prefixes (rows from 1 to 40 keys, rows of about
+    7000 keys that keep every element, rows crossing 8192 keys where the
+    sampled threshold starts), repeated values."""
+    say("long-row top-k", n, k, q0)
     M = 40
     rng = np.random.default_rng(n + k)
     vals = rng.standard_normal((1, M, n)).astype(np.float32)
     vals[0, :, ::7] = np.round(vals[0, :, ::7], 1)          # many exact ties
-    q_pos0 = n - M
+    q_pos0 = n - M if q0 is None else q0
     sh = lcsb.make_shape(1, M, n, q_pos0, 1, 1)
     dev = torch.device("cuda:0")
     ld = (n + 3) // 4 * 4
