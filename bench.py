@@ -550,13 +550,39 @@ def decode_leg(B_, args):
         cache.n_cached = (Nd - 1) // Bd
         lcsb.misa_indexer_cached(sh, q, w, k, dc.h, dc.topk, cache, idx=idd, vals=vad, ws=wsc)
 
+    # the same keys in a paged cache (pages of 64 keys, shuffled over a pool
+    # with spare pages), read in place by misa_indexer_paged
+    page_keys = 64
+    per_seq = Nd // page_keys
+    n_pages = Sd * per_seq + 64
+    g = torch.Generator(device="cpu").manual_seed(11)
+    ids = torch.randperm(n_pages, generator=g)[:Sd * per_seq].view(Sd, per_seq).to(torch.int32)
+    pages = torch.empty((n_pages, page_keys, 128), dtype=k.dtype, device=dev)
+    pages[ids.view(-1).to(dev).long()] = k.view(Sd * per_seq, page_keys, 128)
+    table = ids.to(dev)
+    wsp = torch.empty(lcsb.misa_indexer_paged_workspace_bytes(sh, dc.kdtype, dc.h, dc.topk), dtype=torch.uint8,
+                      device=dev)
+    cache_p = lcsb.PooledCache(Sd, Nd // Bd)
+    lcsb.misa_pool_keys_cached(prev, k[:, :Nd - 1].contiguous(), cache_p)
+    idp = torch.empty_like(idd)
+    vap = torch.empty_like(vad)
+
+    def paged_step():
+        cache_p.n_cached = (Nd - 1) // Bd
+        lcsb.misa_indexer_paged(sh, q, w, pages, table, dc.h, dc.topk, cache_p, idx=idp, vals=vap, ws=wsp)
+
     dper, _ = B_.timed([("scratch", lambda: lcsb.misa_indexer(sh, q, w, k, dc.h, dc.topk, idx=idd, vals=vad,
                                                                ws=wsd)),
-                        ("cached", cached_step)], max(5, args.steps // 2), 2)
+                        ("cached", cached_step), ("paged", paged_step)], max(5, args.steps // 2), 2)
+    same = bool(torch.equal(idp, idd) and torch.equal(vap, vad))
     kbytes = Sd * Nd * 256
     out = dict(workload=dc.name, ms_from_scratch=dper["scratch"], ms_with_pooled_cache=dper["cached"],
-               key_bytes=kbytes, cached_key_read=roof_hbm(kbytes, dper["cached"]))
-    say(f"decode {dc.name}: {dper['scratch']:.3f} ms from scratch, {dper['cached']:.3f} ms with the pooled-key cache")
+               ms_paged_in_place=dper["paged"], paged_equals_contiguous=same, page_keys=page_keys,
+               key_bytes=kbytes, cached_key_read=roof_hbm(kbytes, dper["cached"]),
+               paged_key_read=roof_hbm(kbytes, dper["paged"]),
+               stages_paged=B_.stage_ms(paged_step, ("pool", "route", "score_logits", "logits_topk"), 10))
+    say(f"decode {dc.name}: {dper['scratch']:.3f} ms from scratch, {dper['cached']:.3f} ms with the pooled-key "
+        f"cache, {dper['paged']:.3f} ms on pages read in place (same result: {same})")
     return out
 
 

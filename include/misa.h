@@ -399,7 +399,7 @@ misa_status misa_pool_keys_cached(const misa_shape* shape, const void* k, misa_k
 /* misa_indexer with the pooled keys in the cache (brought up to date first).
  * The result is exactly misa_indexer's on the same arguments.  ws: at least
  * misa_indexer_cached_workspace_bytes() bytes.  With M == 0 it only updates
- * the cache. */
+ * the cache (q, w and idx may then be NULL). */
 misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, const float* w, const void* k,
                                 misa_kdtype kdtype, const float* k_scale, int32_t h, int32_t topk,
                                 int32_t k_prime, int64_t n_cached, float* pooled, uint16_t* pooled_split,
@@ -408,6 +408,31 @@ misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, cons
 
 size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h,
                                            int32_t topk, int32_t k_prime);
+
+/* misa_indexer_cached (k_prime = 0) on keys read in place from a paged cache
+ * (the serving engine's KV pages; the GitHub issue's measured configuration
+ * counts the cache handling inside the indexer): the pooling of the new
+ * blocks and tails, and the routed scoring, read key t of sequence b from
+ * page block_table[b * max_pages + t / page_keys], row t % page_keys, of the
+ * pools k_pages (key rows of the kdtype, [n_pages][page_keys][128]) and, for
+ * fp8 keys, scale_pages (float [n_pages][page_keys]).  No copy of the keys is
+ * made.  The routed scores go to whole logits rows in the workspace and
+ * misa_topk selects from them; the result equals misa_indexer_cached's on
+ * the keys misa_gather_keys_paged would gather, bit for bit.
+ * page_keys >= 64 and a multiple of 64 (a 64-key scoring tile then lies in
+ * one page), n_pages >= 1, max_pages >= ceil(N / page_keys), else
+ * MISA_ERR_INVALID_ARG; table entries are a precondition (in [0, n_pages);
+ * out-of-range ones are clamped, never faulting); 1 <= h <= 8 (else
+ * MISA_ERR_UNSUPPORTED).  Cache arguments as misa_indexer_cached; ws: at
+ * least misa_indexer_paged_workspace_bytes() bytes.  With M == 0 it only
+ * updates the cache (q, w and idx may then be NULL). */
+misa_status misa_indexer_paged(const misa_shape* shape, const uint16_t* q, const float* w, const void* k_pages,
+                               misa_kdtype kdtype, const float* scale_pages, const int32_t* block_table,
+                               int64_t max_pages, int64_t n_pages, int32_t page_keys, int32_t h, int32_t topk,
+                               int64_t n_cached, float* pooled, uint16_t* pooled_split, int64_t cap_blocks,
+                               int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream);
+
+size_t misa_indexer_paged_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk);
 
 /* Chunked prefill driver: the indexer over the shape's M queries (positions
  * q_pos0 .. q_pos0+M-1 of each sequence) in chunks of `chunk` queries, the way
@@ -443,7 +468,9 @@ typedef enum {
   MISA_STAGE_REGION_SELECT = 6,      /* exact top-k of the candidates */
   MISA_STAGE_RESCORE = 7,            /* re-scoring and top-k of the rows the candidates could not settle */
   MISA_STAGE_RERANK = 8,             /* MISA-dagger: all-head re-rank of the k' candidates */
-  MISA_STAGE_FINAL_TOPK = 9          /* MISA-dagger: top-k of the re-ranked candidates */
+  MISA_STAGE_FINAL_TOPK = 9,         /* MISA-dagger: top-k of the re-ranked candidates */
+  MISA_STAGE_SCORE_LOGITS = 10,      /* routed scoring into whole logits rows (few queries, short prefixes, paged keys) */
+  MISA_STAGE_LOGITS_TOPK = 11        /* top-k of those logits */
 } misa_stage;
 
 /*

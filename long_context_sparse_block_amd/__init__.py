@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     PooledCache, misa_pool_keys_cached, misa_indexer_cached, misa_indexer_cached_workspace_bytes,
     misa_prefill_chunked, misa_prefill_workspace_bytes, misa_indexer_q8, misa_indexer_q8_workspace_bytes,
     misa_gather_keys_paged, status_str, misa_indexer_noalloc, NOALLOC_SCRATCH_BYTES, MISA_ERR_SCRATCH,
-    misa_profile_stage, STAGES,
+    misa_profile_stage, STAGES, misa_indexer_paged, misa_indexer_paged_workspace_bytes,
 )

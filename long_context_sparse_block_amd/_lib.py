@@ -34,9 +34,9 @@ EXPORTED = ("misa_status_str", "misa_pool_keys", "misa_route_heads", "misa_spars
             "misa_pool_keys_cached", "misa_indexer_cached", "misa_indexer_cached_workspace_bytes",
             "misa_prefill_chunked", "misa_prefill_workspace_bytes", "misa_indexer_q8",
             "misa_indexer_q8_workspace_bytes", "misa_gather_keys_paged", "misa_indexer_noalloc",
-            "misa_profile_stage")
+            "misa_profile_stage", "misa_indexer_paged", "misa_indexer_paged_workspace_bytes")
 STAGES = dict(pool=1, route=2, score_sample=3, sample_threshold=4, score_candidates=5, region_select=6,
-              rescore=7, rerank=8, final_topk=9)
+              rescore=7, rerank=8, final_topk=9, score_logits=10, logits_topk=11)
 MISA_ERR_SCRATCH = -5
 NOALLOC_SCRATCH_BYTES = 256 << 20   # MISA_NOALLOC_SCRATCH_BYTES of misa.h
 
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "misa_prefill_chunked": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, P, P, P, sz, P],
         "misa_indexer_q8": [S, P, P, P, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P],
         "misa_gather_keys_paged": [S, P, ctypes.c_int, P, P, i64, i64, i32, P, P, P],
+        "misa_indexer_paged": [S, P, P, P, ctypes.c_int, P, P, i64, i64, i32, i32, i32, i64, P, P, i64, P, P, P,
+                               sz, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -108,6 +110,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.misa_indexer_q8_workspace_bytes.restype = sz
     lib.misa_prefill_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32, i32, i32]
     lib.misa_prefill_workspace_bytes.restype = sz
+    lib.misa_indexer_paged_workspace_bytes.argtypes = [S, ctypes.c_int, i32, i32]
+    lib.misa_indexer_paged_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -560,3 +564,38 @@ def misa_gather_keys_paged(shape: MisaShape, k_pages, block_table, scale_pages=N
                                        _stream(stream))
     _check(st, "misa_gather_keys_paged")
     return k_out, scale_out
+
+
+def misa_indexer_paged_workspace_bytes(shape: MisaShape, kdtype: int, h: int, topk: int) -> int:
+    return int(load().misa_indexer_paged_workspace_bytes(ctypes.byref(shape), int(kdtype), int(h), int(topk)))
+
+
+def misa_indexer_paged(shape: MisaShape, q, w, k_pages, block_table, h: int, topk: int, cache: PooledCache,
+                       scale_pages=None, idx=None, vals=None, want_vals=True, ws=None, stream=None):
+    """misa_indexer_cached on keys read in place from a paged cache: k_pages
+    [n_pages, page_keys, 128] (bf16, or e4m3 codes with scale_pages [n_pages,
+    page_keys]), block_table int32 [n_seq, max_pages]."""
+    kd = _kdtype(k_pages)
+    n_pages, page_keys = int(k_pages.shape[0]), int(k_pages.shape[1])
+    _need(k_pages, k_pages.dtype, (n_pages, page_keys, HEAD_DIM), "k_pages")
+    if kd == MISA_K_FP8_E4M3:
+        _need(scale_pages, torch.float32, (n_pages, page_keys), "scale_pages")
+    _need(block_table, torch.int32, (shape.n_seq, block_table.shape[-1]), "block_table")
+    M, H = shape.q_per_seq, shape.n_heads
+    _need(q, torch.bfloat16, (shape.n_seq, M, H, HEAD_DIM), "q")
+    _need(w, torch.float32, (shape.n_seq, M, H), "w")
+    if idx is None:
+        idx = torch.empty((shape.n_seq, M, topk), dtype=torch.int32, device=q.device)
+    if vals is None and want_vals:
+        vals = torch.empty((shape.n_seq, M, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(misa_indexer_paged_workspace_bytes(shape, kd, h, topk), 1), dtype=torch.uint8,
+                         device=q.device)
+    st = load().misa_indexer_paged(ctypes.byref(shape), _ptr(q), _ptr(w), _ptr(k_pages), kd, _ptr(scale_pages),
+                                   _ptr(block_table), int(block_table.shape[-1]), n_pages, page_keys, int(h),
+                                   int(topk), int(cache.n_cached), _ptr(cache.pooled), _ptr(cache.split),
+                                   cache.cap_blocks, _ptr(idx), _ptr(vals), _ptr(ws), int(ws.numel()),
+                                   _stream(stream))
+    _check(st, "misa_indexer_paged")
+    cache.n_cached = shape.n_keys // shape.block
+    return idx, vals

@@ -86,11 +86,12 @@ struct SelectLayout {
 // largest slab that fits, else the lean plan (whose end then lies past
 // end_limit: the caller's check refuses the workspace).
 SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off, bool wide_keys,
-                           size_t end_limit = SIZE_MAX) {
+                           size_t end_limit = SIZE_MAX, bool paged = false) {
   SelectLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   L.ld = (s.n_keys + 3) / 4 * 4;
   L.fused = misa::plan_fused(s, h, k);
+  if (paged) L.fused.ok = false;   // paged keys: scored into whole logits rows
   if (!L.fused.ok) {
     L.logits = off;   // full logits
     off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
@@ -169,18 +170,27 @@ inline misa_status stage_end(int stage, hipStream_t st) {
 
 // Routed scoring + exact top-k (see misa_sparse_head_topk); qq != nullptr:
 // fp8 queries and fp8 keys (misa_sparse_head_topk_q8).
+// pages != nullptr: k / k_scale are page pools read through the block table
+// (the layout must be the unfused one: select_layout with paged = true).
 misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, const uint16_t* q, const float* w,
                        const void* k, int kdtype, const float* k_scale, const int32_t* heads, int h, int topk,
-                       bool sorted, int32_t* idx, float* vals, hipStream_t st, const QuantQ* qq = nullptr) {
+                       bool sorted, int32_t* idx, float* vals, hipStream_t st, const QuantQ* qq = nullptr,
+                       const misa::KeyPages* pages = nullptr) {
   float* logits = reinterpret_cast<float*>(base + L.logits);
   const uint8_t* k8 = static_cast<const uint8_t*>(k);
   if (!L.fused.ok) {
-    if (qq != nullptr)
+    MISA_TRY(stage_begin(MISA_STAGE_SCORE_LOGITS, st));
+    if (pages != nullptr)
+      MISA_TRY(from_hip(misa::launch_score_paged(s, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, *pages, st)));
+    else if (qq != nullptr)
       MISA_TRY(from_hip(misa::launch_score_q8(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, logits, L.ld, st)));
     else
       MISA_TRY(from_hip(launch_score(s, q, w, k, kdtype, k_scale, heads, h, logits, L.ld, st)));
-    return from_hip(launch_topk(s, logits, L.ld, nullptr, (int)s.n_keys, topk, idx, vals, base + L.topk_ws,
-                                L.end - L.topk_ws, st, sorted));
+    MISA_TRY(stage_end(MISA_STAGE_SCORE_LOGITS, st));
+    MISA_TRY(stage_begin(MISA_STAGE_LOGITS_TOPK, st));
+    MISA_TRY(from_hip(launch_topk(s, logits, L.ld, nullptr, (int)s.n_keys, topk, idx, vals, base + L.topk_ws,
+                                  L.end - L.topk_ws, st, sorted)));
+    return stage_end(MISA_STAGE_LOGITS_TOPK, st);
   }
   const misa::FusedPlan& p = L.fused;
   float* sample = reinterpret_cast<float*>(base + L.sample);
@@ -255,7 +265,7 @@ struct IndexerLayout {
 // end_limit: the workspace's size (the selection is planned to fit it; see
 // select_layout).
 IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, int k_prime, bool own_pool = true,
-                             bool quant_q = false, size_t end_limit = SIZE_MAX) {
+                             bool quant_q = false, size_t end_limit = SIZE_MAX, bool paged = false) {
   IndexerLayout L{};
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   const int64_t n_full = s.n_keys / s.block;
@@ -290,7 +300,8 @@ IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, i
     off += L.ftopk_bytes;
   }
   // last: the selection takes what the workspace has left
-  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off, kdtype == MISA_K_FP8_E4M3 && !quant_q, end_limit);
+  L.sel = select_layout(s, h, k_prime > 0 ? k_prime : topk, off, kdtype == MISA_K_FP8_E4M3 && !quant_q, end_limit,
+                        paged);
   L.total = L.sel.end;
   return L;
 }
@@ -301,11 +312,11 @@ IndexerLayout indexer_layout(const misa_shape& s, int kdtype, int h, int topk, i
 misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base, const uint16_t* q, const float* w,
                         const void* k, int kdtype, const float* k_scale, int h, int topk, int k_prime,
                         float* pooled, uint16_t* split, int64_t n_cached, int64_t ld_blk, int32_t* idx,
-                        float* vals, hipStream_t st, bool quant_q = false) {
+                        float* vals, hipStream_t st, bool quant_q = false, const misa::KeyPages* pages = nullptr) {
   float* tail = reinterpret_cast<float*>(base + L.tail);
   int32_t* heads = reinterpret_cast<int32_t*>(base + L.heads);
   MISA_TRY(stage_begin(MISA_STAGE_POOL, st));
-  MISA_TRY(from_hip(launch_pool(s, k, kdtype, k_scale, pooled, tail, split, st, n_cached, ld_blk)));
+  MISA_TRY(from_hip(launch_pool(s, k, kdtype, k_scale, pooled, tail, split, st, n_cached, ld_blk, pages)));
   MISA_TRY(stage_end(MISA_STAGE_POOL, st));
   float* rpart = L.rpart == SIZE_MAX ? nullptr : reinterpret_cast<float*>(base + L.rpart);
   MISA_TRY(stage_begin(MISA_STAGE_ROUTE, st));
@@ -316,7 +327,7 @@ misa_status run_indexer(const misa_shape& s, const IndexerLayout& L, char* base,
     MISA_TRY(from_hip(misa::launch_quant_q(s, q, const_cast<uint8_t*>(qq.q8), const_cast<float*>(qq.q_scale), st)));
   const QuantQ* qp = quant_q ? &qq : nullptr;
   if (k_prime == 0)
-    return run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st, qp);
+    return run_select(s, L.sel, base, q, w, k, kdtype, k_scale, heads, h, topk, true, idx, vals, st, qp, pages);
   // the k' candidates are a set: the re-rank and the final top-k do not depend on their order
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
   float* dlog = reinterpret_cast<float*>(base + L.dlog);
@@ -335,7 +346,9 @@ misa_status check_indexer_args(const misa_shape* shape, const uint16_t* q, const
                                const int32_t* idx) {
   MISA_TRY(check_shape(shape));
   MISA_TRY(check_keys(k, kdtype, k_scale));
-  if (q == nullptr || !aligned16(q) || w == nullptr || idx == nullptr) return MISA_ERR_INVALID_ARG;
+  // (no queries: the call has nothing to read or write per query)
+  if (shape->q_per_seq > 0 && (q == nullptr || !aligned16(q) || w == nullptr || idx == nullptr))
+    return MISA_ERR_INVALID_ARG;
   if (h < 1 || h > shape->n_heads) return MISA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MISA_MAX_TOPK) return MISA_ERR_INVALID_ARG;
   if (k_prime != 0 && (k_prime < topk || k_prime > MISA_MAX_TOPK)) return MISA_ERR_INVALID_ARG;
@@ -656,6 +669,32 @@ misa_status misa_indexer_cached(const misa_shape* shape, const uint16_t* q, cons
                      pooled_split, n_cached, cap_blocks, idx, vals, (hipStream_t)stream);
 }
 
+size_t misa_indexer_paged_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk) {
+  if (check_shape(shape) != MISA_OK || h < 1 || topk < 1) return 0;
+  return indexer_layout(*shape, kdtype, h, topk, 0, false, false, SIZE_MAX, true).total;
+}
+
+misa_status misa_indexer_paged(const misa_shape* shape, const uint16_t* q, const float* w, const void* k_pages,
+                               misa_kdtype kdtype, const float* scale_pages, const int32_t* block_table,
+                               int64_t max_pages, int64_t n_pages, int32_t page_keys, int32_t h, int32_t topk,
+                               int64_t n_cached, float* pooled, uint16_t* pooled_split, int64_t cap_blocks,
+                               int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_indexer_args(shape, q, w, k_pages, kdtype, scale_pages, h, topk, 0, idx));
+  MISA_TRY(check_cache(shape, n_cached, pooled, pooled_split, cap_blocks));
+  if (block_table == nullptr || n_pages < 1 || page_keys < 64 || page_keys % 64 != 0) return MISA_ERR_INVALID_ARG;
+  if (max_pages < (shape->n_keys + page_keys - 1) / page_keys) return MISA_ERR_INVALID_ARG;
+  if (!aligned16(k_pages)) return MISA_ERR_INVALID_ARG;
+  if (h > 8) return MISA_ERR_UNSUPPORTED;   // the routed kernel of h <= 8 reads the pages
+  const IndexerLayout L = indexer_layout(*shape, kdtype, h, topk, 0, false, false, ws_bytes, true);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  const misa::KeyPages pages{block_table, max_pages, n_pages, page_keys};
+  if (shape->q_per_seq == 0)   // no queries: only bring the cache up to date
+    return from_hip(launch_pool(*shape, k_pages, kdtype, scale_pages, pooled, nullptr, pooled_split,
+                                (hipStream_t)stream, n_cached, cap_blocks, &pages));
+  return run_indexer(*shape, L, static_cast<char*>(ws), q, w, k_pages, kdtype, scale_pages, h, topk, 0, pooled,
+                     pooled_split, n_cached, cap_blocks, idx, vals, (hipStream_t)stream, false, &pages);
+}
+
 size_t misa_prefill_workspace_bytes(const misa_shape* shape, misa_kdtype kdtype, int32_t h, int32_t topk,
                                     int32_t k_prime, int32_t chunk) {
   if (check_shape(shape) != MISA_OK || h < 1 || topk < 1 || k_prime < 0 || chunk < 1) return 0;
@@ -738,7 +777,7 @@ misa_status misa_profile_stage(int32_t stage, void* start_event, void* stop_even
     t_profile = ProfileHook{MISA_STAGE_NONE, nullptr, nullptr};
     return MISA_OK;
   }
-  if (stage < MISA_STAGE_POOL || stage > MISA_STAGE_FINAL_TOPK || start_event == nullptr || stop_event == nullptr)
+  if (stage < MISA_STAGE_POOL || stage > MISA_STAGE_LOGITS_TOPK || start_event == nullptr || stop_event == nullptr)
     return MISA_ERR_INVALID_ARG;
   t_profile = ProfileHook{stage, static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   return MISA_OK;

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "misa_launch.h"
+
 namespace misa {
 
 constexpr int kWave = 64;
@@ -87,6 +89,16 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 }
 
 // Order-preserving map float -> uint32 (larger float <=> larger key), with
+// The page-pool row of key t of sequence b (KeyPages).  Table entries are a
+// documented precondition (in [0, n_pages)); they are clamped so that a bad
+// one cannot fault.
+__device__ __forceinline__ int64_t paged_row(const KeyPages& pg, int b, int64_t t) {
+  const uint32_t p = (uint32_t)t / (uint32_t)pg.page_keys;   // t < 2^31 (the ABI bounds N)
+  int64_t e = pg.table[(int64_t)b * pg.max_pages + min((int64_t)p, pg.max_pages - 1)];
+  e = e < 0 ? 0 : (e >= pg.n_pages ? pg.n_pages - 1 : e);
+  return e * pg.page_keys + (t - (int64_t)p * pg.page_keys);
+}
+
 // (P0 + P1) + (P2 + P3) of a value P held on the four 16-lane rows of a wave,
 // on every lane: the xor-16 and xor-32 butterflies done by gfx950's
 // v_permlane16_swap / v_permlane32_swap (VALU, no LDS round trip).  The

@@ -15,9 +15,24 @@ namespace misa {
 // per sequence ld_blk hi rows then ld_blk lo rows, for launch_route.
 // n_cached: block rows [0, n_cached) already hold these keys' means (an
 // incremental cache); only later complete blocks are pooled.
+// Paged keys: key t of sequence b is row table[b * max_pages + t / page_keys]
+// * page_keys + t % page_keys of the page pool.  page_keys is a multiple of
+// 64, so a 64-key scoring tile never straddles two pages.
+struct KeyPages {
+  const int32_t* table;
+  int64_t max_pages, n_pages;
+  int page_keys;
+};
+
+// Routed-head logits (h <= 8, the k_score_h8 arithmetic) with the keys read in
+// place from a page pool through the block table (page_keys % 64 == 0)
+hipError_t launch_score_paged(const misa_shape& s, const uint16_t* q, const float* w, const void* k_pages,
+                              int kdtype, const float* scale_pages, const int32_t* heads, int h, float* logits,
+                              int64_t ld, const KeyPages& pages, hipStream_t st);
+// pages (nullable): k and k_scale are page pools read through the block table
 hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const float* k_scale,
                        float* pooled, float* tail, uint16_t* split, hipStream_t st, int64_t n_cached = 0,
-                       int64_t ld_blk = -1);
+                       int64_t ld_blk = -1, const KeyPages* pages = nullptr);
 
 // split (nullable): launch_pool's hi/lo rows, staged directly instead of
 // splitting `pooled` in every workgroup (same values); ld_blk as launch_pool.

@@ -18,6 +18,10 @@
 // from min(n_cached, first query block) on are visited, and of those only
 // the complete blocks at or past n_cached are pooled.  Cache rows are
 // ld_blk blocks apart per sequence.
+//
+// PAGED: the keys are read in place from a page pool (KeyPages): a wave looks
+// up the page of its slice's first key once and only looks again for a key
+// on another page.
 #include <algorithm>
 
 #include "misa_common.h"
@@ -40,14 +44,14 @@ __device__ __forceinline__ f32x2 pool_load(const void* kptr, const float* kscale
   }
 }
 
-template <int KDT>
+template <int KDT, bool PAGED = false>
 __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restrict__ kptr,
                                                              const float* __restrict__ kscale,
                                                              float* __restrict__ pooled, float* __restrict__ tail,
                                                              uint32_t* __restrict__ split,
                                                              int64_t N, int64_t q_pos0, int M, int B,
                                                              int64_t n_full, int64_t m_first, int64_t n_cached,
-                                                             int64_t ld_blk) {
+                                                             int64_t ld_blk, KeyPages pages) {
   __shared__ f32x2 s_part[kPoolWaves][kWave];
   const int64_t m = m_first + blockIdx.x;
   const int b = blockIdx.y;
@@ -61,13 +65,27 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
   if (!full && !has_query) return;   // uniform over the workgroup
   const int64_t per = (s1 - s0 + kPoolWaves - 1) / kPoolWaves;
   const int64_t w0 = min(s0 + w * per, s1), w1 = min(w0 + per, s1);   // this wave's slice
+  // the key row of key t of this sequence (t uniform over the wave)
+  int64_t pg_first = 0, pg_row = 0;   // PAGED: first key of the page looked up last, and its row
+  if (PAGED) {
+    pg_first = w0 - w0 % pages.page_keys;
+    pg_row = paged_row(pages, b, pg_first);
+  }
+  auto row_of = [&](int64_t t) -> int64_t {
+    if (!PAGED) return (int64_t)b * N + t;
+    if (t < pg_first || t >= pg_first + pages.page_keys) {
+      pg_first = t - t % pages.page_keys;
+      pg_row = paged_row(pages, b, pg_first);
+    }
+    return pg_row + (t - pg_first);
+  };
 
   constexpr int U = 8;
   float a0 = 0.f, a1 = 0.f;
   for (int64_t s = w0; s < w1; s += U) {
     f32x2 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = (s + u < w1) ? pool_load<KDT>(kptr, kscale, (int64_t)b * N + s + u, lane) : f32x2{0.f, 0.f};
+    for (int u = 0; u < U; ++u) v[u] = (s + u < w1) ? pool_load<KDT>(kptr, kscale, row_of(s + u), lane) : f32x2{0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       a0 += v[u].x;
@@ -104,7 +122,7 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
   for (int64_t s = w0; s < w1; s += U) {
     f32x2 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = (s + u < w1) ? pool_load<KDT>(kptr, kscale, (int64_t)b * N + s + u, lane) : f32x2{0.f, 0.f};
+    for (int u = 0; u < U; ++u) v[u] = (s + u < w1) ? pool_load<KDT>(kptr, kscale, row_of(s + u), lane) : f32x2{0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t ss = s + u;
@@ -124,7 +142,7 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(const void* __restr
 
 hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const float* k_scale,
                        float* pooled, float* tail, uint16_t* split, hipStream_t st, int64_t n_cached,
-                       int64_t ld_blk) {
+                       int64_t ld_blk, const KeyPages* pages) {
   const int64_t N = s.n_keys;
   const int B = s.block;
   const int64_t n_blk_total = (N + B - 1) / B;
@@ -134,14 +152,19 @@ hipError_t launch_pool(const misa_shape& s, const void* k, int kdtype, const flo
   int64_t m_first = s.q_per_seq > 0 ? std::min(n_cached, s.q_pos0 / B) : n_cached;
   if (m_first >= n_blk_total) return hipSuccess;
   dim3 grid((unsigned)(n_blk_total - m_first), (unsigned)s.n_seq);
-  if (kdtype == MISA_K_BF16)
-    hipLaunchKernelGGL(k_pool<MISA_K_BF16>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
-                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_full, m_first, n_cached,
-                       ld_blk);
-  else
-    hipLaunchKernelGGL(k_pool<MISA_K_FP8_E4M3>, grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail,
-                       reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_full, m_first, n_cached,
-                       ld_blk);
+  const KeyPages pg = pages != nullptr ? *pages : KeyPages{nullptr, 0, 0, 1};
+#define MISA_POOL(KDT_, PAGED_)                                                                              \
+  hipLaunchKernelGGL((k_pool<KDT_, PAGED_>), grid, dim3(kWave * kPoolWaves), 0, st, k, k_scale, pooled, tail, \
+                     reinterpret_cast<uint32_t*>(split), N, s.q_pos0, s.q_per_seq, B, n_full, m_first, n_cached, \
+                     ld_blk, pg)
+  if (kdtype == MISA_K_BF16) {
+    if (pages != nullptr) MISA_POOL(MISA_K_BF16, true);
+    else MISA_POOL(MISA_K_BF16, false);
+  } else {
+    if (pages != nullptr) MISA_POOL(MISA_K_FP8_E4M3, true);
+    else MISA_POOL(MISA_K_FP8_E4M3, false);
+  }
+#undef MISA_POOL
   return hipGetLastError();
 }
 

@@ -386,7 +386,7 @@ int route_parts(const misa_shape& s) {
   const int qwg = 4 * ((nhc == 1) ? 4 : (nhc == 2 ? 2 : 1));
   const int64_t wgs = (int64_t)((s.q_per_seq + qwg - 1) / qwg) * s.n_seq;
   const int64_t nfull_max = (s.q_pos0 + s.q_per_seq) / s.block;
-  if (wgs >= 256 || nfull_max < 256) return 1;
+  if (wgs == 0 || wgs >= 256 || nfull_max < 256) return 1;   // (no queries: nothing to split)
   return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxRouteParts, (512 + wgs - 1) / wgs, nfull_max / 128}));
 }
 

@@ -75,11 +75,15 @@ struct KStageSw {
   // every key) through descriptors based at the tile and bounded by the N
   // keys (rows past N read as zeros; their logits are never kept).  Thread
   // chunk e fills LDS row e / kVecPerKey, i.e. tile key sw_tile_key(row).
-  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int ks, int tid) {
+  // pages != nullptr: kbase / sbase are page pools, the tile's rows found
+  // through sequence b's block table (ks == 1; the tile lies in one page)
+  __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int ks, int tid,
+                                       const KeyPages* pages = nullptr, int b = 0) {
     const int64_t first = (int64_t)key0 * ks;   // position of the tile's first key
     const int rem = (int)max((int64_t)0, min((int64_t)kSwKT * ks, (int64_t)N - first));   // keys in range
+    const int64_t row0 = pages != nullptr ? paged_row(*pages, b, first) : first;
     const __amdgpu_buffer_rsrc_t kr =
-        uniform_rsrc(static_cast<const char*>(kbase) + first * kRowBytes, (uint32_t)rem * kRowBytes);
+        uniform_rsrc(static_cast<const char*>(kbase) + row0 * kRowBytes, (uint32_t)rem * kRowBytes);
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
       const int e = tid + u * NT;
@@ -88,7 +92,7 @@ struct KStageSw {
                                            kr, (uint32_t)(sw_tile_key(j) * ks) * kRowBytes + c * 16, 0, 0));
     }
     if (KDT == MISA_K_FP8_E4M3) {
-      const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + first, (uint32_t)rem * 4u);
+      const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + row0, (uint32_t)rem * 4u);
       sc = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(sw_tile_key(tid % kSwKT) * ks) * 4u, 0, 0));
     }
@@ -125,12 +129,15 @@ struct KStageSw {
 // workgroup only: decode, one query tile per sequence)
 template <int KDT, int NT, int AUX = 0>
 __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sbase, int key0, int N, int ks,
-                                         int lane, int wave, unsigned char* s_dst, float* s_sc_dst) {
+                                         int lane, int wave, unsigned char* s_dst, float* s_sc_dst,
+                                         const KeyPages* pages = nullptr, int b = 0) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   // 32-bit scalar arithmetic: N < 2^26 keys (the ABI checks it)
   const int first = key0 * ks;
   const int rem = max(0, min(kSwKT * ks, N - first));
-  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + (int64_t)first * kD, (uint32_t)rem * kSwRowBytes);
+  // pages: kbase / sbase are page pools (ks == 1; the tile lies in one page)
+  const int64_t row0 = pages != nullptr ? paged_row(*pages, b, first) : (int64_t)first;
+  const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(kbase + row0 * kD, (uint32_t)rem * kSwRowBytes);
   constexpr int kLoads = kSwKT / 4 / (NT / 64);
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {
@@ -141,7 +148,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
                                              (uint32_t)(sw_tile_key(j) * ks) * kSwRowBytes + c * 16, 0, 0, AUX);
   }
   if (KDT == MISA_K_FP8_E4M3) {
-    const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + first, (uint32_t)rem * 4u);
+    const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(sbase + row0, (uint32_t)rem * 4u);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr)s_sc_dst, 4, (uint32_t)(sw_tile_key(lane) * ks) * 4u, 0,
                                              0, AUX);
   }
@@ -169,14 +176,14 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
 // every key; a stride samples the keys): key index u < ceil(N / ks) is the key
 // at position u ks, and query t sees indices u <= t / ks.  N is 32-bit here.
 // ---------------------------------------------------------------------------
-template <int KDT, int MODE, bool DMA>
+template <int KDT, int MODE, bool DMA, bool PAGED = false>
 __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q,
                                                   const float* __restrict__ w,
                                                   const void* __restrict__ kptr,
                                                   const float* __restrict__ kscale,
                                                   const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
                                                   int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
-                                                  int n_qtiles, int n_ksplits, int64_t KR) {
+                                                  int n_qtiles, int n_ksplits, int64_t KR, KeyPages pages) {
   constexpr int NT = 256, KT = kSwKT, QT = 32;
   // B fragments read one column block ahead where the registers allow it
   // (16 more VGPRs; the other variants would drop to 2 waves per SIMD)
@@ -276,10 +283,13 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
 
   // DMA: kptr holds bf16 keys whatever KDT is (KDT then only says whether the
   // fp8 scales apply)
+  // PAGED: kptr / kscale are page pools (rows found per tile through b's table)
+  const int64_t seq_rows = PAGED ? 0 : (int64_t)b * Nk;
   const void* kb_ptr = (KDT == MISA_K_BF16 || DMA)
-                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + (int64_t)b * Nk * kD)
-                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + (int64_t)b * Nk * kD);
-  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + (int64_t)b * Nk : nullptr;
+                           ? (const void*)(reinterpret_cast<const uint16_t*>(kptr) + seq_rows * kD)
+                           : (const void*)(reinterpret_cast<const uint8_t*>(kptr) + seq_rows * kD);
+  const float* sc_ptr = (KDT == MISA_K_FP8_E4M3) ? kscale + seq_rows : nullptr;
+  const KeyPages* pg = PAGED ? &pages : nullptr;
 
   // lane's B-fragment byte offsets inside a tile (column block 0), one per k-step
   uint32_t rd[kKSteps];
@@ -298,13 +308,13 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
     if (DMA) {
       if (stream_keys)
         dma_tile<KDT, NT, kStream>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
-                                   buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0);
+                                   buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0, pg, b);
       else
         dma_tile<KDT, NT>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
-                          buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0);
+                          buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0, pg, b);
     }
     else
-      stg.load(kb_ptr, sc_ptr, key, Nk, kstride, tid);
+      stg.load(kb_ptr, sc_ptr, key, Nk, kstride, tid, pg, b);
   };
   auto stage_done = [&](int buf) {
     if (DMA)   // the stores issued after the loads (2 per tile, or 4 with candidates) may stay in flight
@@ -583,21 +593,36 @@ void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int6
 
 // DMA: k holds bf16 keys (for kdtype fp8: the widened copy; k_scale still
 // applies), staged by direct loads into LDS
-template <int MODE, bool DMA = false>
+template <int MODE, bool DMA = false, bool PAGED = false>
 static hipError_t launch_h8(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                             const float* k_scale, const int32_t* heads, int h, const ScoreOut& o, int kstride,
-                            int nks, int64_t KR, hipStream_t st) {
+                            int nks, int64_t KR, hipStream_t st, const KeyPages* pages = nullptr) {
   const int M = s.q_per_seq;
   const int n_qtiles = (M + 31) / 32;
   dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
   if (o.slab_tiles > 0) grid = dim3((unsigned)((int64_t)o.slab_tiles * nks), 1);
+  const KeyPages pg = pages != nullptr ? *pages : KeyPages{nullptr, 0, 0, 1};
   if (kdtype == MISA_K_BF16)
-    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE, DMA>), grid, dim3(256), 0, st, q, w, k, k_scale, heads, h,
-                       o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE, DMA, PAGED>), grid, dim3(256), 0, st, q, w, k, k_scale,
+                       heads, h, o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR, pg);
   else
-    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE, DMA>), grid, dim3(256), 0, st, q, w, k, k_scale, heads,
-                       h, o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR);
+    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE, DMA, PAGED>), grid, dim3(256), 0, st, q, w, k, k_scale,
+                       heads, h, o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR, pg);
   return hipGetLastError();
+}
+
+hipError_t launch_score_paged(const misa_shape& s, const uint16_t* q, const float* w, const void* k_pages,
+                              int kdtype, const float* scale_pages, const int32_t* heads, int h, float* logits,
+                              int64_t ld, const KeyPages& pages, hipStream_t st) {
+  int nks;
+  int64_t KR;
+  plan_split(s.n_keys, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
+  const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+  if (kdtype == MISA_K_BF16)
+    return launch_h8<kLogits, true, true>(s, q, w, k_pages, kdtype, scale_pages, heads, h, o, 1, nks, KR, st,
+                                          &pages);
+  return launch_h8<kLogits, false, true>(s, q, w, k_pages, kdtype, scale_pages, heads, h, o, 1, nks, KR, st,
+                                         &pages);
 }
 
 hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
@@ -610,6 +635,10 @@ hipError_t launch_score(const misa_shape& s, const uint16_t* q, const float* w, 
     int64_t KR;
     plan_split(N, s.n_seq, (M + 31) / 32, 64, &nks, &KR);
     const ScoreOut o{logits, ld, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+    // bf16 keys are staged by direct loads into LDS; fp8 keys through
+    // registers, where they are widened (the same bf16 tiles either way)
+    if (kdtype == MISA_K_BF16)
+      return launch_h8<kLogits, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
     return launch_h8<kLogits>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
   }
   const int hh = heads ? h : H;
@@ -651,6 +680,12 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   // (k at most a quarter of the shortest prefix; below 16384 keys the
   // materialised logits are cheap anyway)
   p.ok = h <= 8 && k <= 8192 && n_min >= std::max<int64_t>(16384, 4 * (int64_t)k) && s.q_per_seq > 0;
+  // a few queries per sequence (decode): the sampled pass, the threshold and
+  // the region select each take a launch's latency for little work, while
+  // the whole logits are small (64 sequences x 131072 keys: 33.5 MB), so
+  // scoring into logits and the one-kernel top-k take less time
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  if (s.q_per_seq < 16 && rows * N <= ((int64_t)1 << 26)) p.ok = false;
   if (!p.ok) return p;
   p.kstride = (int)std::max<int64_t>(32, (N + 4095) / 4096);   // <= 4096 sampled keys per row
   p.n_sample = (N + p.kstride - 1) / p.kstride;

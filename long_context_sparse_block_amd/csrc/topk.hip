@@ -447,19 +447,21 @@ struct TopkSharedIdx {
 // comparing with the bucket's other entries.
 template <int CAP, int NT>
 __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
-                                               int32_t* idx_out, float* val_out, uint64_t cmin, uint64_t cmax) {
+                                               int32_t* idx_out, float* val_out, uint32_t kmin, uint32_t kmax) {
   static_assert(CAP <= 8 * NT, "the bitonic fallback holds 8 entries per thread");
   constexpr int EPT = CAP / NT;   // entries per thread
   const int tid = threadIdx.x;
   constexpr int HB = kHistBinsIdx;   // finer buckets than rank_write: fewer in-bucket comparisons
   constexpr int BPT = HB / NT;
   if (cnt > 0) {
-    const int nb = bit_width64(cmax - cmin);
+    // buckets by the value's order key (the composite's high word), so
+    // equal values share a bucket and are ranked there by id
+    const int nb = kmax > kmin ? 32 - __clz((int)(kmax - kmin)) : 0;
     const int shift = nb > kDigitIdx ? nb - kDigitIdx : 0;
+    auto bucket = [&](uint64_t c) -> uint32_t { return ((uint32_t)(c >> 32) - kmin) >> shift; };
     for (int e = tid; e < HB; e += NT) sh.hist[e] = 0;
     __syncthreads();
-    for (uint32_t e = tid; e < cnt; e += NT)
-      atomicAdd(&sh.hist[(uint32_t)((raw_to_comp(sh.buf[e]) - cmin) >> shift)], 1u);
+    for (uint32_t e = tid; e < cnt; e += NT) atomicAdd(&sh.hist[bucket(raw_to_comp(sh.buf[e]))], 1u);
     __syncthreads();
     // bucket starts, highest bucket first: thread owns buckets HB-1-BPT*tid-u
     uint32_t hv[BPT], ls = 0, big = 0;
@@ -492,12 +494,12 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
       __syncthreads();   // (the cursors, and every thread's reads of sh.buf)
 #pragma unroll
       for (int j = 0; j < EPT; ++j)
-        if (tid + j * NT < cnt) sh.buf[atomicAdd(&sh.hist[(uint32_t)((mine[j] - cmin) >> shift)], 1u)] = mine[j];
+        if (tid + j * NT < cnt) sh.buf[atomicAdd(&sh.hist[bucket(mine[j])], 1u)] = mine[j];
       __syncthreads();
       // sh.hist[d] is now the end of bucket d; bucket d spans [end(d+1), end(d))
       for (uint32_t e = tid; e < cnt; e += NT) {
         const uint64_t c = sh.buf[e];
-        const uint32_t d = (uint32_t)((c - cmin) >> shift);
+        const uint32_t d = bucket(c);
         const uint32_t b0 = (d + 1 < (uint32_t)HB) ? sh.hist[d + 1] : 0;
         if (b0 >= (uint32_t)k) continue;   // every element of the bucket ranks at or past k
         const uint32_t b1 = sh.hist[d];
@@ -945,13 +947,12 @@ __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cn
 template <int CAP, int NT>
 __device__ __forceinline__ void finish_list_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
                                                 int32_t* __restrict__ idx_out, float* __restrict__ val_out,
-                                                int sorted, uint64_t mm_lo, uint64_t mm_hi) {
-  const int tid = threadIdx.x;
+                                                int sorted, uint32_t kmin, uint32_t kmax) {
   if (sorted) {
-    rank_write_idx<CAP, NT>(sh, cnt, k, row, idx_out, val_out, mm_lo, mm_hi);
+    rank_write_idx<CAP, NT>(sh, cnt, k, row, idx_out, val_out, kmin, kmax);
     return;
   }
-  write_set<NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.sel, sh.red, true, mm_lo, mm_hi);
+  write_set<NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.sel, sh.red, false, 0, 0);
 }
 
 // Exact top-k of a row's candidate list (every element at or above the row's
@@ -1247,11 +1248,14 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
     if (tid == 0) flag[row] = 1;
     return;
   }
-  // every group of every region, flat: U groups per thread loaded together;
-  // the min and max composite kept are tracked for the rank
+  // every group of every region, flat: U groups per thread loaded together.
+  // A thread's candidates of a batch are written one after another from its
+  // position (the wave-exclusive sum of the threads' counts, one LDS atomic
+  // per wave); the largest value seen bounds the rank's buckets from above,
+  // the threshold from below
   constexpr int U = 8;
   const uint32_t total = s_start[n_splits];
-  uint64_t mm_lo = ~0ull, mm_hi = 0;
+  float gmax = -__builtin_inff();
   for (uint32_t e0 = 0; e0 < total; e0 += U * NT) {
     f32x4 v[U];
     int32_t key[U];
@@ -1272,62 +1276,49 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
         key[u] = gkeys[g];
       }
     }
+    uint32_t fl = 0;   // bit 4u + j: element j of group u is a candidate
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bool f[4];
-      uint32_t cnt = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[j] = v[u][j] >= tf;
-        cnt += f[j];
-      }
-      const uint64_t m0 = __ballot(cnt & 1u), m1 = __ballot(cnt & 2u), m2 = __ballot(cnt & 4u);
-      if ((m0 | m1 | m2) == 0) continue;
-      uint32_t pos = lanes_below(m0) + 2 * lanes_below(m1) + 4 * lanes_below(m2);
-      uint32_t wbase = 0;
-      if (lane == __ffsll((unsigned long long)__ballot(1)) - 1)
-        wbase = atomicAdd(&sh.count, (uint32_t)(__popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2)));
-      pos += __builtin_amdgcn_readfirstlane(wbase);
+      for (int j = 0; j < 4; ++j) fl |= (uint32_t)(v[u][j] >= tf) << (4 * u + j);
+      const float m01 = __builtin_fmaxf(v[u][0], v[u][1]), m23 = __builtin_fmaxf(v[u][2], v[u][3]);
+      gmax = __builtin_fmaxf(gmax, __builtin_fmaxf(m01, m23));
+    }
+    const uint32_t cnt = __popc(fl);   // 0..32
+    const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u), b2 = __ballot(cnt & 4u), b3 = __ballot(cnt & 8u),
+                   b4 = __ballot(cnt & 16u), b5 = __ballot(cnt & 32u);
+    if ((b0 | b1 | b2 | b3 | b4 | b5) == 0) continue;   // uniform over the wave
+    uint32_t pos = lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3) +
+                   16 * lanes_below(b4) + 32 * lanes_below(b5);
+    const uint32_t wtot = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3) +
+                          16 * __popcll(b4) + 32 * __popcll(b5);
+    uint32_t wbase = 0;
+    if (lane == 0) wbase = atomicAdd(&sh.count, wtot);
+    pos += __builtin_amdgcn_readfirstlane(wbase);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (f[j]) {
-          const uint64_t raw = pack_raw(v[u][j], key[u] + j);
-          const uint64_t c = raw_to_comp(raw);
-          mm_lo = c < mm_lo ? c : mm_lo;
-          mm_hi = c > mm_hi ? c : mm_hi;
-          if (pos < (uint32_t)CAP) sh.buf[pos] = raw;
+        if (fl & (1u << (4 * u + j))) {
+          if (pos < (uint32_t)CAP) sh.buf[pos] = pack_raw(v[u][j], key[u] + j);
           ++pos;
         }
-    }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t a = shfl_xor_u64(mm_lo, o), b2 = shfl_xor_u64(mm_hi, o);
-    mm_lo = a < mm_lo ? a : mm_lo;
-    mm_hi = b2 > mm_hi ? b2 : mm_hi;
-  }
-  if (lane == 0) {
-    sh.red[2 * (tid >> 6)] = mm_lo;
-    sh.red[2 * (tid >> 6) + 1] = mm_hi;
-  }
+  for (int o = 32; o >= 1; o >>= 1) gmax = __builtin_fmaxf(gmax, __shfl_xor(gmax, o));
+  if (lane == 0) sh.red[tid >> 6] = __float_as_uint(gmax);
   __syncthreads();
   const uint32_t tot = sh.count;
   if (tot > (uint32_t)min(cap_list, CAP) || tot < (uint32_t)min(k, n)) {
     if (tid == 0) flag[row] = 1;
     return;
   }
-  mm_lo = ~0ull;
-  mm_hi = 0;
-#pragma unroll
-  for (int wv = 0; wv < NT / 64; ++wv) {
-    mm_lo = sh.red[2 * wv] < mm_lo ? sh.red[2 * wv] : mm_lo;
-    mm_hi = sh.red[2 * wv + 1] > mm_hi ? sh.red[2 * wv + 1] : mm_hi;
-  }
+  for (int wv = 0; wv < NT / 64; ++wv) gmax = __builtin_fmaxf(gmax, __uint_as_float((uint32_t)sh.red[wv]));
   __syncthreads();   // sh.red is reused by the select
   if constexpr (IDX)
-    finish_list_idx<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, mm_lo, mm_hi);
+    finish_list_idx<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, order_key(tf), order_key(gmax));
   else
-    finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, true, mm_lo, mm_hi);
+    finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted);
 }
 
 // Whole-row top-k of the flagged rows from a logits slab: slab_tiles query

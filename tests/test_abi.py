@@ -146,16 +146,22 @@ def test_sparse_head_topk_checks_and_workspace(lib):
 
 
 def test_only_fp8_keys_reserve_a_widened_copy(lib):
-    # the decode batch: 64 sequences x 131072 keys; a bf16 copy of fp8 keys
-    # would be 64 x 131072 x 256 bytes = 2 GiB
-    s = lcsb.make_shape(64, 1, 131072, 131071, 32, 64)
+    # a prefill chunk of 256 queries over 131072 keys takes the fused path,
+    # whose direct-load staging reads a bf16 copy of fp8 keys (131072 x 256 B)
+    s = lcsb.make_shape(1, 256, 131072, 131072 - 256, 32, 64)
     bf = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 0, 8, 2048, 0)
     f8 = lib.misa_indexer_workspace_bytes(ctypes.byref(s), 1, 8, 2048, 0)
-    assert f8 - bf == 64 * 131072 * 256
-    assert bf < (1 << 30)
+    assert f8 - bf == 131072 * 256
     # the fp8-query indexer feeds fp8 keys to the fp8 matrix cores directly
     q8 = lib.misa_indexer_q8_workspace_bytes(ctypes.byref(s), 8, 2048, 0)
     assert q8 < f8
+    # the decode batch (64 sequences x 131072 keys, one query each) scores into
+    # whole logits rows (64 x 131072 x 4 B = 32 MiB) and stages fp8 keys
+    # through registers: no copy of the keys (it would be 2 GiB)
+    d = lcsb.make_shape(64, 1, 131072, 131071, 32, 64)
+    bf = lib.misa_indexer_workspace_bytes(ctypes.byref(d), 0, 8, 2048, 0)
+    assert lib.misa_indexer_workspace_bytes(ctypes.byref(d), 1, 8, 2048, 0) == bf
+    assert 64 * 131072 * 4 <= bf < (256 << 20)
 
 
 def test_fp8_query_calls_check_their_arguments(lib):
@@ -208,6 +214,42 @@ def test_paged_gather_checks(lib):
     assert g(ctypes.byref(s), FAKE, 0, None, FAKE, 4, 8, 0, FAKE, None, None) == -1        # empty pages
     assert g(ctypes.byref(s), FAKE, 1, FAKE, FAKE, 4, 8, 16, FAKE, None, None) == -1       # fp8 needs scale_out
     assert g(ctypes.byref(s), FAKE, 1, None, FAKE, 4, 8, 16, FAKE, FAKE, None) == -1       # fp8 needs page scales
+
+
+def test_paged_indexer_checks_its_arguments(lib):
+    s = lcsb.make_shape(2, 1, 300, 299, 16, 64)   # decode: 2 sequences x 300 keys, 4 complete blocks
+    f = lib.misa_indexer_paged
+    need = lib.misa_indexer_paged_workspace_bytes(ctypes.byref(s), 0, 8, 64)
+    assert need > 0
+
+    def call(kd=0, sc=None, table=FAKE, max_pages=5, n_pages=10, page_keys=64, h=8, cap=4, ws_bytes=need):
+        return f(ctypes.byref(s), FAKE, FAKE, FAKE, kd, sc, table, max_pages, n_pages, page_keys, h, 64, 0, FAKE,
+                 FAKE, cap, FAKE, None, FAKE, ws_bytes, None)
+    assert call(table=None) == -1          # no block table
+    assert call(page_keys=48) == -1        # pages must hold whole 64-key tiles
+    assert call(page_keys=32) == -1
+    assert call(max_pages=4) == -1         # 4 pages of 64 < 300 keys
+    assert call(n_pages=0) == -1
+    assert call(kd=1) == -1                # fp8 pages need their scales
+    assert call(cap=3) == -1               # cache smaller than the 4 complete blocks
+    assert call(h=17) == -1                # more heads than the shape has
+    assert call(h=9) == -2                 # the routed kernel that reads pages takes h <= 8
+    assert call(ws_bytes=need - 1) == -3   # workspace too small
+    # no logits for rows the fused path would take: the paged path always scores whole rows
+    big = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
+    assert lib.misa_indexer_paged_workspace_bytes(ctypes.byref(big), 1, 8, 2048) >= 8192 * 131072 * 4
+
+
+def test_workspace_queries_of_a_cache_update_without_queries(lib):
+    # no queries over more than 256 complete blocks: the router's part split
+    # must not divide by its (zero) workgroup count
+    # (such a call only brings the cache up to date and needs no workspace
+    # beyond the pooled keys misa_indexer keeps in its own)
+    s = lcsb.make_shape(3, 0, 20011, 20011, 16, 64)
+    for kd in (0, 1):
+        assert lib.misa_indexer_cached_workspace_bytes(ctypes.byref(s), kd, 8, 512, 0) == 0
+        assert lib.misa_indexer_paged_workspace_bytes(ctypes.byref(s), kd, 8, 512) == 0
+        assert lib.misa_indexer_workspace_bytes(ctypes.byref(s), kd, 8, 512, 0) > 0
 
 
 def test_pooled_cache_calls_check_their_arguments(lib):

@@ -12,7 +12,10 @@ must equal the one-call indexer bit for bit (ids and values):
     rows against the oracle;
   * a paged key cache (shuffled pages, spare pages, a partial last page)
     gathered back bit for bit, an out-of-range page id giving zero keys, and
-    the indexer on the gathered keys equal to the indexer on the originals.
+    the indexer on the gathered keys equal to the indexer on the originals;
+  * misa_indexer_paged, reading the pages in place, == misa_indexer_cached on
+    the contiguous keys (decode and a short chunk, bf16 and fp8, pages of 64
+    to 256 keys, from an empty cache and from a previous step's cache).
 """
 import numpy as np
 import pytest
@@ -174,3 +177,67 @@ def test_paged_keys_gather(kdtype, page_keys):
     if sb is not None:
         assert bool((sb[1, lo:hi] == 1.0).all())
     assert torch.equal(kb[0], kg[0]) and torch.equal(kb[1, :lo], kg[1, :lo])
+
+
+def paged_copy(inp, page_keys, seed):
+    """The inputs' keys laid into shuffled pages of page_keys keys, with spare
+    pages and a partial last page: (k_pages, scale_pages, table) on the GPU."""
+    S, N = inp.cfg.n_seq, inp.cfg.n_keys
+    per_seq = -(-N // page_keys)
+    max_pages = per_seq + 2
+    n_pages = S * per_seq + 7
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(n_pages)[:S * per_seq].reshape(S, per_seq).astype(np.int32)
+    table = np.full((S, max_pages), -1, np.int32)
+    table[:, :per_seq] = ids
+    pages = np.zeros((n_pages, page_keys, 128), inp.k.dtype)
+    pscale = np.zeros((n_pages, page_keys), np.float32)
+    for b in range(S):
+        for p in range(per_seq):
+            rows = inp.k[b, p * page_keys:(p + 1) * page_keys]
+            pages[ids[b, p], :len(rows)] = rows
+            if inp.k_scale is not None:
+                pscale[ids[b, p], :len(rows)] = inp.k_scale[b, p * page_keys:(p + 1) * page_keys]
+    if inp.k_scale is not None:
+        kp, sp = torch.from_numpy(pages).cuda(), torch.from_numpy(pscale).cuda()
+    else:
+        kp, sp = torch.from_numpy(pages.view(np.int16)).cuda().view(torch.bfloat16), None
+    return kp, sp, torch.from_numpy(table).cuda()
+
+
+@pytest.mark.parametrize("kdtype,page_keys,m", [(gen.KDTYPE_BF16, 64, 1), (gen.KDTYPE_FP8, 128, 1),
+                                                (gen.KDTYPE_BF16, 256, 24), (gen.KDTYPE_FP8, 64, 24)])
+def test_paged_indexer_reads_the_pages_in_place(kdtype, page_keys, m):
+    say("paged indexer", kdtype, page_keys, m)
+    cfg = gen.small_config(name="paged_ix", n_seq=3, m=m, n=20011, hh=16, b=64, h=8, k=512, kdtype=kdtype,
+                           seed=71 + m)
+    inp = gen.generate(cfg)
+    kp, sp, tt = paged_copy(inp, page_keys, 72)
+    st = staged(inp)
+    sh, t = st["sh"], st["t"]
+    S, N, B = cfg.n_seq, cfg.n_keys, cfg.block
+    wi, wv = whole(st, cfg)
+    # from an empty cache
+    ca, cb = lcsb.PooledCache(S, N // B), lcsb.PooledCache(S, N // B)
+    pi, pv = lcsb.misa_indexer_paged(sh, t["q"], t["w"], kp, tt, cfg.h, cfg.topk, ca, scale_pages=sp)
+    ci, cv = lcsb.misa_indexer_cached(sh, t["q"], t["w"], t["k"], cfg.h, cfg.topk, cb, k_scale=t["k_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(pi, ci) and torch.equal(pv, cv), "paged != cached (empty cache)"
+    assert torch.equal(pi, wi) and torch.equal(pv, wv), "paged != one call"
+    assert torch.equal(ca.pooled, cb.pooled) and torch.equal(ca.split, cb.split)
+    # from a previous step's cache: blocks of the first N - 700 keys pooled before
+    prev = lcsb.make_shape(S, 0, N - 700, N - 700, cfg.n_heads, B)
+    pk = t["k"][:, :N - 700].contiguous()
+    pks = None if t["k_scale"] is None else t["k_scale"][:, :N - 700].contiguous()
+    cc = lcsb.PooledCache(S, N // B)
+    lcsb.misa_pool_keys_cached(prev, pk, cc, k_scale=pks)
+    pi2, pv2 = lcsb.misa_indexer_paged(sh, t["q"], t["w"], kp, tt, cfg.h, cfg.topk, cc, scale_pages=sp)
+    torch.cuda.synchronize()
+    assert torch.equal(pi2, wi) and torch.equal(pv2, wv), "paged != one call (previous cache)"
+    assert torch.equal(cc.pooled, ca.pooled)
+    # an empty step only brings the cache up to date
+    cd = lcsb.PooledCache(S, N // B)
+    none = lcsb.make_shape(S, 0, N, N, cfg.n_heads, B)
+    lcsb.misa_indexer_paged(none, t["q"][:, :0], t["w"][:, :0], kp, tt, cfg.h, cfg.topk, cd, scale_pages=sp)
+    torch.cuda.synchronize()
+    assert torch.equal(cd.pooled, ca.pooled)
