@@ -580,7 +580,8 @@ def decode_leg(B_, args):
                ms_paged_in_place=dper["paged"], paged_equals_contiguous=same, page_keys=page_keys,
                key_bytes=kbytes, cached_key_read=roof_hbm(kbytes, dper["cached"]),
                paged_key_read=roof_hbm(kbytes, dper["paged"]),
-               stages_paged=B_.stage_ms(paged_step, ("pool", "route", "score_logits", "logits_topk"), 10))
+               stages_paged=B_.stage_ms(paged_step, ("pool", "route", "score_sample", "sample_threshold",
+                                                     "score_candidates", "region_select", "rescore"), 10))
     say(f"decode {dc.name}: {dper['scratch']:.3f} ms from scratch, {dper['cached']:.3f} ms with the pooled-key "
         f"cache, {dper['paged']:.3f} ms on pages read in place (same result: {same})")
     return out

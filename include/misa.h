@@ -416,9 +416,11 @@ size_t misa_indexer_cached_workspace_bytes(const misa_shape* shape, misa_kdtype 
  * page block_table[b * max_pages + t / page_keys], row t % page_keys, of the
  * pools k_pages (key rows of the kdtype, [n_pages][page_keys][128]) and, for
  * fp8 keys, scale_pages (float [n_pages][page_keys]).  No copy of the keys is
- * made.  The routed scores go to whole logits rows in the workspace and
- * misa_topk selects from them; the result equals misa_indexer_cached's on
- * the keys misa_gather_keys_paged would gather, bit for bit.
+ * made (fp8 pages are widened on their way into LDS, never into the
+ * workspace): the selection runs as misa_indexer_cached's does, its
+ * sampled pass looking up each sampled key's page, its 64-key tiles one page
+ * each, and the result equals misa_indexer_cached's on the keys
+ * misa_gather_keys_paged would gather, bit for bit.
  * page_keys >= 64 and a multiple of 64 (a 64-key scoring tile then lies in
  * one page), n_pages >= 1, max_pages >= ceil(N / page_keys), else
  * MISA_ERR_INVALID_ARG; table entries are a precondition (in [0, n_pages);

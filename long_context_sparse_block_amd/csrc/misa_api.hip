@@ -77,6 +77,7 @@ struct SelectLayout {
   size_t logits, kwide, sample, thr, flag, rcount, gvals, gkeys, topk_ws, end;
   int64_t ld;
   int slab_tiles, tr, n_flat;
+  bool widen;   // fp8 keys widened into kwide for the direct-load staging
   misa::FusedPlan fused;
 };
 
@@ -91,7 +92,6 @@ SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off, bool w
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
   L.ld = (s.n_keys + 3) / 4 * 4;
   L.fused = misa::plan_fused(s, h, k);
-  if (paged) L.fused.ok = false;   // paged keys: scored into whole logits rows
   if (!L.fused.ok) {
     L.logits = off;   // full logits
     off += align_up((size_t)rows * (size_t)L.ld * sizeof(float));
@@ -102,13 +102,17 @@ SelectLayout select_layout(const misa_shape& s, int h, int k, size_t off, bool w
   }
   const int n_qtiles = (s.q_per_seq + 31) / 32;
   L.n_flat = s.n_seq * n_qtiles;
+  // a widened copy pays when the keys are read by several query tiles; with
+  // one query tile per sequence (decode) each key is read once, so fp8 keys
+  // are staged as they are, through registers
+  L.widen = wide_keys && n_qtiles > 1 && !paged;   // paged keys are read in place, never copied
   L.tr = std::min(32, (int)s.q_per_seq);
   const size_t tile_bytes = (size_t)L.tr * (size_t)L.ld * sizeof(float);
   auto place = [&](const misa::FusedPlan& p, int64_t slab_tiles) {
     size_t o = off;
     L.fused = p;
     L.kwide = o;   // bf16 copy of fp8 keys
-    if (wide_keys) o += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128
+    if (L.widen) o += align_up((size_t)s.n_seq * (size_t)s.n_keys * 128 * sizeof(uint16_t));   // d = 128
     L.thr = o;
     o += align_up((size_t)rows * sizeof(float));
     L.flag = o;
@@ -171,7 +175,7 @@ inline misa_status stage_end(int stage, hipStream_t st) {
 // Routed scoring + exact top-k (see misa_sparse_head_topk); qq != nullptr:
 // fp8 queries and fp8 keys (misa_sparse_head_topk_q8).
 // pages != nullptr: k / k_scale are page pools read through the block table
-// (the layout must be the unfused one: select_layout with paged = true).
+// (the layout from select_layout with paged = true).
 misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, const uint16_t* q, const float* w,
                        const void* k, int kdtype, const float* k_scale, const int32_t* heads, int h, int topk,
                        bool sorted, int32_t* idx, float* vals, hipStream_t st, const QuantQ* qq = nullptr,
@@ -199,7 +203,7 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   uint32_t* rcount = reinterpret_cast<uint32_t*>(base + L.rcount);
   float* gvals = reinterpret_cast<float*>(base + L.gvals);
   int32_t* gkeys = reinterpret_cast<int32_t*>(base + L.gkeys);
-  if (qq != nullptr) {
+  if (qq != nullptr) {   // (the fp8-query calls take contiguous keys)
     MISA_TRY(stage_begin(MISA_STAGE_SCORE_SAMPLE, st));
     MISA_TRY(from_hip(misa::launch_score_q8_sampled(s, qq->q8, qq->q_scale, w, k8, k_scale, heads, h, p, sample, st)));
     MISA_TRY(stage_end(MISA_STAGE_SCORE_SAMPLE, st));
@@ -223,22 +227,26 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
     }
     return stage_end(MISA_STAGE_RESCORE, st);
   }
-  // the scoring launches stage bf16 keys by direct loads into LDS
+  // the scoring launches stage bf16 keys by direct loads into LDS (fp8 keys
+  // widened once), or fp8 keys read once through registers
   const void* kb = k;
-  if (kdtype == MISA_K_FP8_E4M3) {
+  const bool direct = kdtype != MISA_K_FP8_E4M3 || L.widen;
+  if (kdtype == MISA_K_FP8_E4M3 && L.widen) {
     uint16_t* kwide = reinterpret_cast<uint16_t*>(base + L.kwide);
     MISA_TRY(from_hip(misa::launch_widen_fp8(s, k, kwide, st)));
     kb = kwide;
   }
   MISA_TRY(stage_begin(MISA_STAGE_SCORE_SAMPLE, st));
-  MISA_TRY(from_hip(misa::launch_score_sampled(s, q, w, kb, kdtype, k_scale, heads, h, p, sample, st)));
+  MISA_TRY(from_hip(
+      misa::launch_score_sampled(s, q, w, kb, kdtype, k_scale, heads, h, p, sample, st, direct, pages)));
   MISA_TRY(stage_end(MISA_STAGE_SCORE_SAMPLE, st));
   MISA_TRY(stage_begin(MISA_STAGE_SAMPLE_THRESHOLD, st));
   MISA_TRY(from_hip(misa::launch_topk_sample_thresh(s, p, sample, thr, flag, st)));
   MISA_TRY(stage_end(MISA_STAGE_SAMPLE_THRESHOLD, st));
   MISA_TRY(stage_begin(MISA_STAGE_SCORE_CANDIDATES, st));
   MISA_TRY(from_hip(
-      misa::launch_score_cands(s, q, w, kb, kdtype, k_scale, heads, h, p, thr, gvals, gkeys, rcount, st)));
+      misa::launch_score_cands(s, q, w, kb, kdtype, k_scale, heads, h, p, thr, gvals, gkeys, rcount, st, direct,
+                               pages)));
   MISA_TRY(stage_end(MISA_STAGE_SCORE_CANDIDATES, st));
   MISA_TRY(stage_begin(MISA_STAGE_REGION_SELECT, st));
   MISA_TRY(from_hip(misa::launch_topk_regions(s, p, topk, thr, gvals, gkeys, rcount, flag, idx, vals, sorted, st)));
@@ -248,7 +256,8 @@ misa_status run_select(const misa_shape& s, const SelectLayout& L, char* base, c
   MISA_TRY(stage_begin(MISA_STAGE_RESCORE, st));
   for (int64_t first = 0; first < L.n_flat; first += L.slab_tiles) {
     const misa::SlabBatch sb{first, (int)std::min<int64_t>(L.slab_tiles, L.n_flat - first), L.tr};
-    MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, kb, kdtype, k_scale, heads, h, flag, logits, L.ld, sb, st)));
+    MISA_TRY(from_hip(misa::launch_score_rescore(s, q, w, kb, kdtype, k_scale, heads, h, flag, logits, L.ld, sb, st,
+                                                 direct, pages)));
     MISA_TRY(from_hip(misa::launch_topk_flagged(s, topk, logits, L.ld, sb, flag, idx, vals, sorted, st)));
   }
   return stage_end(MISA_STAGE_RESCORE, st);

@@ -117,24 +117,28 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k);
 // candidates (the least-workspace plan)
 FusedPlan lean_plan(const FusedPlan& fast, const misa_shape& s);
 
-// The fused path's scoring launches take bf16 keys in `k` whatever kdtype is
-// (fp8 keys widened by launch_widen_fp8; kdtype then says that k_scale
-// applies) and stage them by direct global -> LDS loads.
+// The fused path's scoring launches: direct == true takes bf16 keys in `k`
+// whatever kdtype is (fp8 keys widened by launch_widen_fp8; kdtype then says
+// that k_scale applies) and stages them by direct global -> LDS loads;
+// direct == false takes the keys as they are and stages them through
+// registers (fp8 widened on the way into LDS: the same bf16 tiles).
 hipError_t launch_widen_fp8(const misa_shape& s, const void* k, uint16_t* out, hipStream_t st);
 hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                                 const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
-                                float* sample_logits, hipStream_t st);
+                                float* sample_logits, hipStream_t st, bool direct = true,
+                                const KeyPages* pages = nullptr);
 // candidate regions: groups of 4 consecutive scores (gvals, float4 each) and
 // their first key (gkeys), cap_region groups per (row, key range)
 hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                               const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
-                              const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st);
+                              const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st,
+                              bool direct = true, const KeyPages* pages = nullptr);
 // logits rows, into a slab batch, of the workgroups that hold a row with
 // row_flag != 0
 hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                                 int kdtype, const float* k_scale, const int32_t* heads, int h,
                                 const uint32_t* row_flag, float* slab, int64_t ld, const SlabBatch& sb,
-                                hipStream_t st);
+                                hipStream_t st, bool direct = true, const KeyPages* pages = nullptr);
 // thr[row] from the sample logits; row_flag[row] = 0
 hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, const float* sample_logits,
                                      float* thr, uint32_t* row_flag, hipStream_t st);

@@ -80,6 +80,26 @@ struct KStageSw {
   __device__ __forceinline__ void load(const void* kbase, const float* sbase, int key0, int N, int ks, int tid,
                                        const KeyPages* pages = nullptr, int b = 0) {
     const int64_t first = (int64_t)key0 * ks;   // position of the tile's first key
+    if (pages != nullptr && ks > 1) {
+      // sampled keys lie on different pages: each key row is looked up
+      // through the block table (rows past N read as zeros)
+#pragma unroll
+      for (int u = 0; u < kPerThread; ++u) {
+        const int e = tid + u * NT;
+        const int j = e / kVecPerKey, c = e % kVecPerKey;
+        const int64_t key = first + (int64_t)sw_tile_key(j) * ks;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (key < N)
+          v = *reinterpret_cast<const uint4*>(static_cast<const char*>(kbase) + paged_row(*pages, b, key) * kRowBytes +
+                                              c * 16);
+        r[u] = v;
+      }
+      if (KDT == MISA_K_FP8_E4M3) {
+        const int64_t key = first + (int64_t)sw_tile_key(tid % kSwKT) * ks;
+        sc = key < N ? sbase[paged_row(*pages, b, key)] : 0.f;
+      }
+      return;
+    }
     const int rem = (int)max((int64_t)0, min((int64_t)kSwKT * ks, (int64_t)N - first));   // keys in range
     const int64_t row0 = pages != nullptr ? paged_row(*pages, b, first) : first;
     const __amdgpu_buffer_rsrc_t kr =
@@ -304,14 +324,16 @@ __global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q
   // sequences x 131072 keys; with many query tiles the keys are re-read and
   // must stay cached)
   const bool stream_keys = n_qtiles == 1;
+  auto kbuf = [&](int buf) { return buf ? s_k1 : s_k0; };
+  auto scbuf = [&](int buf) { return buf ? s_sc1 : s_sc0; };
   auto stage_issue = [&](int key, int buf) {
     if (DMA) {
       if (stream_keys)
         dma_tile<KDT, NT, kStream>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
-                                   buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0, pg, b);
+                                   kbuf(buf), scbuf(buf), pg, b);
       else
         dma_tile<KDT, NT>(reinterpret_cast<const uint16_t*>(kb_ptr), sc_ptr, key, Nk, kstride, lane, wave,
-                          buf ? s_k1 : s_k0, buf ? s_sc1 : s_sc0, pg, b);
+                          kbuf(buf), scbuf(buf), pg, b);
     }
     else
       stg.load(kb_ptr, sc_ptr, key, Nk, kstride, tid, pg, b);
@@ -680,12 +702,6 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   // (k at most a quarter of the shortest prefix; below 16384 keys the
   // materialised logits are cheap anyway)
   p.ok = h <= 8 && k <= 8192 && n_min >= std::max<int64_t>(16384, 4 * (int64_t)k) && s.q_per_seq > 0;
-  // a few queries per sequence (decode): the sampled pass, the threshold and
-  // the region select each take a launch's latency for little work, while
-  // the whole logits are small (64 sequences x 131072 keys: 33.5 MB), so
-  // scoring into logits and the one-kernel top-k take less time
-  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
-  if (s.q_per_seq < 16 && rows * N <= ((int64_t)1 << 26)) p.ok = false;
   if (!p.ok) return p;
   p.kstride = (int)std::max<int64_t>(32, (N + 4095) / 4096);   // <= 4096 sampled keys per row
   p.n_sample = (N + p.kstride - 1) / p.kstride;
@@ -733,25 +749,36 @@ FusedPlan lean_plan(const FusedPlan& fast, const misa_shape& s) {
 
 hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                                 const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
-                                float* sample_logits, hipStream_t st) {
+                                float* sample_logits, hipStream_t st, bool direct, const KeyPages* pages) {
   int nks;
   int64_t KR;
   plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
   const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+  if (pages != nullptr)   // the sampled keys' rows are looked up one by one: staged through registers
+    return launch_h8<kLogits, false, true>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st, pages);
+  if (!direct) return launch_h8<kLogits, false>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
   return launch_h8<kLogits, true>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
 }
 
 hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                               const float* k_scale, const int32_t* heads, int h, const FusedPlan& p,
-                              const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st) {
+                              const float* thr, float* gvals, int32_t* gkeys, uint32_t* rcount, hipStream_t st,
+                              bool direct, const KeyPages* pages) {
   const ScoreOut o{nullptr, 0, thr, reinterpret_cast<f32x4*>(gvals), gkeys, rcount, p.cap_region, nullptr};
-  return launch_h8<kCands, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, p.n_splits, p.key_range, st);
+  const int nks = p.n_splits;
+  const int64_t KR = p.key_range;
+  if (pages != nullptr) {
+    if (direct) return launch_h8<kCands, true, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
+    return launch_h8<kCands, false, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
+  }
+  if (!direct) return launch_h8<kCands, false>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
+  return launch_h8<kCands, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
 }
 
 hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const float* w, const void* k,
                                 int kdtype, const float* k_scale, const int32_t* heads, int h,
                                 const uint32_t* row_flag, float* slab, int64_t ld, const SlabBatch& sb,
-                                hipStream_t st) {
+                                hipStream_t st, bool direct, const KeyPages* pages) {
   int nks;
   int64_t KR;
   const int n_qtiles = (s.q_per_seq + 31) / 32;
@@ -761,6 +788,11 @@ hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const fl
   o.slab_first = (int)sb.first;
   o.slab_tr = sb.tr;
   o.n_flat = s.n_seq * n_qtiles;
+  if (pages != nullptr) {
+    if (direct) return launch_h8<kLogits, true, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
+    return launch_h8<kLogits, false, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
+  }
+  if (!direct) return launch_h8<kLogits, false>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
   return launch_h8<kLogits, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
 }
 

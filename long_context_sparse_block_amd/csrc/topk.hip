@@ -728,6 +728,9 @@ __global__ void __launch_bounds__(NT, 2) k_topk(const float* __restrict__ logits
 // rank work, which reads no logits, runs afterwards on short candidate lists.
 // ---------------------------------------------------------------------------
 constexpr int kSplitMinCols = 16384;   // rows at least this long take the split path
+// k_topk_fused (one workgroup per row) when there are at least this many
+// rows; fewer rows (decode) fill the chip better split into chunks
+constexpr int64_t kFusedMinRows = 512;
 constexpr int kChunkMax = 65536;       // elements per filter workgroup, at most (256 KB of logits)
 constexpr int kChunkCap = 4096;        // candidates a filter workgroup (4 waves) can hold
 
@@ -769,7 +772,7 @@ static SplitWs split_ws(void* ws, int64_t rows, int k) {
 // the bytes it used).  A line's scores are neighbours and may be correlated
 // (a block of related keys), so each line counts at most 16 of its scores: a
 // cluster of large scores cannot take more than a bounded share of the
-// sample.  The threshold is the lower edge of the 20-bit order-key bucket
+// sample.  The threshold is the lower edge of the 16-bit order-key bucket
 // above which the capped count reaches k_s = target * 4096 / n + 2, so that
 // about `target` row elements are expected at or above it; rows too short
 // for the sample keep every element (-inf).  Computed by one wave: lane l
@@ -794,7 +797,7 @@ __device__ __forceinline__ float row_threshold(const float* __restrict__ lrow, i
   }
   // bits decided from the top: capped per-line counts, one wave sum per bit
   uint32_t T = 0;
-  for (int bit = 31; bit >= 12; --bit) {
+  for (int bit = 31; bit >= 16; --bit) {
     const uint32_t c = T | (1u << bit);
     uint32_t cl = 0;
 #pragma unroll
@@ -1101,8 +1104,10 @@ __global__ void __launch_bounds__(NT, 2) k_topk_fused(const float* __restrict__ 
 }
 
 size_t topk_workspace_bytes(const misa_shape& s, int n_cols, int k) {
-  if (n_cols < kSplitMinCols || k <= 4096) return 0;   // k <= 4096: k_topk_fused keeps its list in LDS
-  return split_ws_bytes((int64_t)s.n_seq * s.q_per_seq, k);
+  const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
+  // k <= 4096 over enough rows: k_topk_fused keeps its list in LDS
+  if (n_cols < kSplitMinCols || (k <= 4096 && rows >= kFusedMinRows)) return 0;
+  return split_ws_bytes(rows, k);
 }
 
 hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, const int32_t* cand,
@@ -1110,7 +1115,7 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
                        bool sorted) {
   dim3 grid((unsigned)s.q_per_seq, (unsigned)s.n_seq);
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
-  if (cand == nullptr && n_cols >= kSplitMinCols && k <= 4096) {
+  if (cand == nullptr && n_cols >= kSplitMinCols && k <= 4096 && rows >= kFusedMinRows) {
     const int target = min(3 * k / 2, (k + list_cap(k)) / 2);
     hipLaunchKernelGGL((k_topk_fused<8192, 512>), grid, dim3(512), 0, st, logits, ld, n_cols, k, target, s.q_pos0,
                        s.q_per_seq, idx, vals, (int)sorted);
@@ -1124,8 +1129,10 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
     hipLaunchKernelGGL(k_topk_thresh, dim3((unsigned)((rows + kThreshWaves - 1) / kThreshWaves)),
                        dim3(64 * kThreshWaves), 0, st, logits, ld, n_cols, target, s.q_pos0, s.q_per_seq, rows,
                        w.thr, w.count, w.flag);
-    // chunk length: about target / 2 candidates expected per chunk buffer half
+    // chunk length: about target / 2 candidates expected per chunk buffer
+    // half, and with few rows short enough for about 2048 workgroups
     int64_t chunk = (int64_t)(kChunkCap / 2) * n_cols / target;
+    chunk = std::min<int64_t>(chunk, n_cols / std::max<int64_t>(1, 2048 / rows));
     chunk = chunk >= kChunkMax ? kChunkMax : (chunk < 4096 ? 4096 : chunk / 4096 * 4096);
     const int n_chunks = (int)((n_cols + chunk - 1) / chunk);
     dim3 fgrid((unsigned)((int64_t)s.q_per_seq * n_chunks), (unsigned)s.n_seq);
@@ -1154,7 +1161,7 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
 // ---------------------------------------------------------------------------
 
 // One wave per row: the threshold from the row's sampled scores (key indices
-// u <= t / kstride of the sample logits), the lower edge of the 20-bit
+// u <= t / kstride of the sample logits), the lower edge of the 16-bit
 // order-key bucket of the k_s-th largest sample, k_s chosen so that about
 // `target` of the row's t + 1 scores are expected at or above it.  Every
 // sampled key is one key, so a cluster of large scores takes only its share
@@ -1184,7 +1191,7 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const 
       for (int e = 0; e < 4; ++e) key[4 * j + e] = (4 * f + e < ns) ? order_key(v[e]) : 0u;
     }
     uint32_t T = 0;
-    for (int bit = 31; bit >= 12; --bit) {
+    for (int bit = 31; bit >= 16; --bit) {
       const uint32_t c = T | (1u << bit);
       uint32_t cl = 0;
 #pragma unroll

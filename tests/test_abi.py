@@ -235,9 +235,13 @@ def test_paged_indexer_checks_its_arguments(lib):
     assert call(h=17) == -1                # more heads than the shape has
     assert call(h=9) == -2                 # the routed kernel that reads pages takes h <= 8
     assert call(ws_bytes=need - 1) == -3   # workspace too small
-    # no logits for rows the fused path would take: the paged path always scores whole rows
+    # the fast plan: the re-scoring slab holds every query tile, and fp8 pages
+    # are never widened into the workspace (unlike contiguous fp8 keys)
     big = lcsb.make_shape(1, 8192, 131072, 131072 - 8192, 64, 128)
-    assert lib.misa_indexer_paged_workspace_bytes(ctypes.byref(big), 1, 8, 2048) >= 8192 * 131072 * 4
+    paged = lib.misa_indexer_paged_workspace_bytes(ctypes.byref(big), 1, 8, 2048)
+    assert paged >= 8192 * 131072 * 4
+    cached = lib.misa_indexer_cached_workspace_bytes(ctypes.byref(big), 1, 8, 2048, 0)
+    assert cached - paged == 131072 * 256
 
 
 def test_workspace_queries_of_a_cache_update_without_queries(lib):

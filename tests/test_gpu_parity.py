@@ -594,6 +594,45 @@ def test_topk_long_rows_split_path(n, k, q0):
         assert set(idx2[0, i].cpu().numpy().tolist()) == set(idx[0, i].cpu().numpy().tolist())
 
 
+@pytest.mark.parametrize("kind", ["ties", "sample_too_high", "sample_too_low", "all_equal", "short_prefixes"])
+def test_topk_one_kernel_and_chunked_paths_agree(kind):
+    """Rows of at least 16384 keys: 512 rows or more take the one-kernel top-k,
+    fewer take the chunked threshold / filter / list kernels.  Both are exact,
+    so the same rows through each agree bit for bit (ids, values, order), and
+    sampled rows equal the oracle.  The kinds defeat the sampled threshold in
+    both directions, tie everything, or keep every element (prefixes shorter
+    than the sample)."""
+    say("one-kernel vs chunked top-k", kind)
+    M, N, k = 512, 20000, 2048
+    rng = np.random.default_rng(31)
+    vals = rng.standard_normal((1, M, N)).astype(np.float32)
+    line = np.arange(N) // 32
+    sampled = (line % 4) == 0          # around the lines a 20000-key row's sample reads
+    if kind == "ties":
+        vals = np.round(vals, 1)
+    elif kind == "sample_too_high":
+        vals[0, :, sampled & (np.arange(N) % 32 == 7)] = 100.0
+    elif kind == "sample_too_low":
+        vals = np.where(sampled, vals - 10.0, vals + 10.0).astype(np.float32)
+    elif kind == "all_equal":
+        vals[...] = 0.25
+    q_pos0 = 300 if kind == "short_prefixes" else N - M
+    dev = torch.device("cuda:0")
+    lg = torch.from_numpy(vals).to(dev)
+    one, one_v = lcsb.misa_topk(lcsb.make_shape(1, M, N, q_pos0, 1, 1), lg, k)
+    a, a_v = lcsb.misa_topk(lcsb.make_shape(1, 256, N, q_pos0, 1, 1), lg[:, :256].contiguous(), k)
+    b, b_v = lcsb.misa_topk(lcsb.make_shape(1, 256, N, q_pos0 + 256, 1, 1), lg[:, 256:].contiguous(), k)
+    torch.cuda.synchronize()
+    assert torch.equal(one[:, :256], a) and torch.equal(one[:, 256:], b)
+    assert torch.equal(one_v[:, :256], a_v) and torch.equal(one_v[:, 256:], b_v)
+    rows = [0, 1, 255, 256, 511] + list(rng.choice(M, 5, replace=False))
+    gi, gv = one.cpu().numpy(), one_v.cpu().numpy()
+    for i in rows:
+        oi, ov = oracle.topk_prefix(vals[0, i].astype(np.float64), q_pos0 + i, k)
+        assert np.array_equal(gi[0, i], oi), f"row {i}"
+        assert np.array_equal(gv[0, i].astype(np.float64), ov)
+
+
 @pytest.mark.parametrize("k", [300, 2048, 8192])
 def test_topk_unsorted_returns_the_same_set(k):
     rng = np.random.default_rng(6)
