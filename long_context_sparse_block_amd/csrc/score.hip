@@ -196,14 +196,20 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
 // every key; a stride samples the keys): key index u < ceil(N / ks) is the key
 // at position u ks, and query t sees indices u <= t / ks.  N is 32-bit here.
 // ---------------------------------------------------------------------------
+// Registers: the occupancy hint (at least 3 waves per SIMD: at most 168
+// registers; 2 for the register-staged paged variants, which need a few more)
+// keeps the MFMA accumulators in ordinary VGPRs.  Given room for more than 256
+// registers the compiler accumulates in AGPRs and copies every result out with
+// a v_accvgpr_read, 64 more VALU instructions per tile.
 template <int KDT, int MODE, bool DMA, bool PAGED = false>
-__global__ void __launch_bounds__(256) k_score_h8(const uint16_t* __restrict__ q,
-                                                  const float* __restrict__ w,
-                                                  const void* __restrict__ kptr,
-                                                  const float* __restrict__ kscale,
-                                                  const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
-                                                  int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
-                                                  int n_qtiles, int n_ksplits, int64_t KR, KeyPages pages) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PAGED && !DMA ? 2 : 3)))
+k_score_h8(const uint16_t* __restrict__ q,
+           const float* __restrict__ w,
+           const void* __restrict__ kptr,
+           const float* __restrict__ kscale,
+           const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
+           int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
+           int n_qtiles, int n_ksplits, int64_t KR, KeyPages pages) {
   constexpr int NT = 256, KT = kSwKT, QT = 32;
   // B fragments read one column block ahead where the registers allow it
   // (16 more VGPRs; the other variants would drop to 2 waves per SIMD)

@@ -30,14 +30,17 @@ struct GatherRaw {
   float sc;
 };
 
+// (waves_per_eu(2): at most 256 registers, so the MFMA accumulators stay in
+// VGPRs instead of AGPRs read back one v_accvgpr_read per value)
 template <int KDT>
-__global__ void __launch_bounds__(256) k_score_gather(const uint16_t* __restrict__ q,
-                                                      const float* __restrict__ w,
-                                                      const void* __restrict__ kptr,
-                                                      const float* __restrict__ kscale,
-                                                      const int32_t* __restrict__ cand, int n_cand,
-                                                      float* __restrict__ logits, int64_t ld, int64_t N,
-                                                      int M, int H, int chunks_per_query) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+k_score_gather(const uint16_t* __restrict__ q,
+               const float* __restrict__ w,
+               const void* __restrict__ kptr,
+               const float* __restrict__ kscale,
+               const int32_t* __restrict__ cand, int n_cand,
+               float* __restrict__ logits, int64_t ld, int64_t N,
+               int M, int H, int chunks_per_query) {
   __shared__ int32_t s_id[4][kGatherCands];   // each wave's candidate ids
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, p16 = lane & 15;
@@ -169,13 +172,14 @@ __device__ __forceinline__ int32_t lds_read_i32(const void* p) {
 }
 
 template <int KDT, int NG>
-__global__ void __launch_bounds__(256) k_score_gather_lds(const uint16_t* __restrict__ q,
-                                                          const float* __restrict__ w,
-                                                          const void* __restrict__ kptr,
-                                                          const float* __restrict__ kscale,
-                                                          const int32_t* __restrict__ cand, int n_cand,
-                                                          float* __restrict__ logits, int64_t ld, int64_t N,
-                                                          int M, int H, int chunks_per_query) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+k_score_gather_lds(const uint16_t* __restrict__ q,
+                   const float* __restrict__ w,
+                   const void* __restrict__ kptr,
+                   const float* __restrict__ kscale,
+                   const int32_t* __restrict__ cand, int n_cand,
+                   float* __restrict__ logits, int64_t ld, int64_t N,
+                   int M, int H, int chunks_per_query) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   constexpr bool kFp8 = KDT == MISA_K_FP8_E4M3;
   constexpr int RB = kFp8 ? kD : 2 * kD;     // bytes per key row

@@ -75,13 +75,17 @@ __device__ __forceinline__ void q8_stage(const uint8_t* kbase, const float* sbas
 //   non-temporally, sampled rows stay cacheable (they are read at once);
 //   kCands: groups of 4 consecutive scores with one at or above the row's
 //   threshold appended to the (row, key range) regions, no logits.
+// (the occupancy hints of this file keep the MFMA accumulators in VGPRs, as
+// for k_score_h8: with room for more than 256 registers they go to AGPRs and
+// every result costs a v_accvgpr_read)
 template <int MODE>
-__global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
-                                                  const float* __restrict__ w, const uint8_t* __restrict__ kptr,
-                                                  const float* __restrict__ kscale,
-                                                  const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
-                                                  int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
-                                                  int n_qtiles, int n_ksplits, int64_t KR) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+k_score_q8(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
+           const float* __restrict__ w, const uint8_t* __restrict__ kptr,
+           const float* __restrict__ kscale,
+           const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
+           int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
+           int n_qtiles, int n_ksplits, int64_t KR) {
   constexpr int KT = kQ8KT, QT = 32;
   __shared__ __attribute__((aligned(16))) unsigned char s_k0[kQ8Tile], s_k1[kQ8Tile];
   __shared__ float s_sc0[KT], s_sc1[KT];
@@ -253,12 +257,13 @@ __global__ void __launch_bounds__(256) k_score_q8(const uint8_t* __restrict__ q8
 // butterfly adds; blocks add in order (the head order of the bf16 dense
 // kernel).  Lane group 0 stores a tile's 4 consecutive logits per lane.
 template <int NG>
-__global__ void __launch_bounds__(256) k_score_dense_q8(const uint8_t* __restrict__ q8,
-                                                        const float* __restrict__ q_scale,
-                                                        const float* __restrict__ w, const uint8_t* __restrict__ kptr,
-                                                        const float* __restrict__ kscale, float* __restrict__ logits,
-                                                        int64_t ld, int64_t N64, int64_t q_pos0_64, int M, int H,
-                                                        int n_qtiles, int n_ksplits, int64_t KR) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+k_score_dense_q8(const uint8_t* __restrict__ q8,
+                 const float* __restrict__ q_scale,
+                 const float* __restrict__ w, const uint8_t* __restrict__ kptr,
+                 const float* __restrict__ kscale, float* __restrict__ logits,
+                 int64_t ld, int64_t N64, int64_t q_pos0_64, int M, int H,
+                 int n_qtiles, int n_ksplits, int64_t KR) {
   constexpr int KT = kQ8KT, QT = 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_k0[kQ8Tile], s_k1[kQ8Tile];
   __shared__ float s_sc0[KT], s_sc1[KT];
