@@ -363,16 +363,21 @@ k_score_h8(const uint16_t* __restrict__ q,
   const uint64_t gmask = 0xFFFFull << (16 * g);
 
   // one tile from LDS buffer BUF
+  // a tile's scores; kCands keeps the previous tile's in a tile that lies
+  // after every query of the wave (its appends then use an infinite
+  // threshold: nothing qualifies), so no registers are filled for it
+  f32x4 out[2] = {f32x4{ninf, ninf, ninf, ninf}, f32x4{ninf, ninf, ninf, ninf}};
   auto tile = [&](auto buf_tag, int key0) {
     constexpr int BUF = decltype(buf_tag)::value;
     const unsigned char* sk = BUF ? s_k1 : s_k0;
     const float* ssc = BUF ? s_sc1 : s_sc0;
     const int kg = key0 + 4 * p16;   // this lane's first key index
-    f32x4 out[2];
-    if (key0 > t_hi) {
-      // the whole tile lies after every query of the wave
-      out[0] = f32x4{ninf, ninf, ninf, ninf};
-      out[1] = out[0];
+    const bool dead = key0 > t_hi;   // the whole tile lies after every query of the wave
+    if (dead) {
+      if (MODE == kLogits) {
+        out[0] = f32x4{ninf, ninf, ninf, ninf};
+        out[1] = out[0];
+      }
     } else {
       // DIAG: some key of the tile may lie after some query of the wave.  In
       // kCands only those tiles pay for the causal mask (the logits variants
@@ -438,7 +443,8 @@ k_score_h8(const uint16_t* __restrict__ q,
       // every lane issues its stores, so the wait for the next tile's
       // prefetch, issued before them, is a fixed count
 #pragma unroll
-      for (int G = 0; G < 2; ++G) append_group(orsrc, out[G], thr[G], gmask, run[G], reg[G], out_spec.cap, kg);
+      for (int G = 0; G < 2; ++G)
+        append_group(orsrc, out[G], dead ? __builtin_inff() : thr[G], gmask, run[G], reg[G], out_spec.cap, kg);
     }
   };
 
