@@ -46,8 +46,8 @@ hipError_t launch_route(const misa_shape& s, const uint16_t* q, const float* w, 
                         hipStream_t st, int64_t ld_blk = -1, float* part_ws = nullptr);
 
 // Key-range split of a scoring grid: n_ksplits ranges of KR keys (a multiple
-// of the tile KT), enough workgroups to fill the chip.
-void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR);
+// of the tile KT), about `target` workgroups (several per CU) in the grid.
+void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int64_t* KR, int64_t target = 2048);
 
 // Paged key cache -> contiguous [n_seq][N][128] keys (and fp8 scales [n_seq][N]).
 hipError_t launch_gather_pages(const misa_shape& s, const void* pages, int kdtype, const float* page_scales,
