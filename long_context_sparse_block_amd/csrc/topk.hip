@@ -1166,26 +1166,34 @@ hipError_t launch_topk(const misa_shape& s, const float* logits, int64_t ld, con
 // `target` of the row's t + 1 scores are expected at or above it.  Every
 // sampled key is one key, so a cluster of large scores takes only its share
 // of the sample.  Also clears the row's flag.
+// WPR waves per row (1, or kThreshWaves for calls with few rows: decode):
+// each wave counts its share of the row's samples, the counts meet in LDS
+// once per bit (two slots, so one barrier a bit).  The threshold is the same
+// for every WPR.
+template <int WPR>
 __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const float* __restrict__ sample,
                                                                           int64_t ld_s, int n_sample, int kstride,
                                                                           int target, int64_t q_pos0, int M,
                                                                           int64_t rows, float* __restrict__ thr,
                                                                           uint32_t* __restrict__ flag) {
-  constexpr int L = 16;   // float4 loads per lane: 4096 sampled scores at most
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kThreshWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int64_t t = q_pos0 + row % M;
+  constexpr int L = 16 / WPR;   // float4 loads per lane: 4096 sampled scores at most per row
+  __shared__ uint32_t s_cnt[2][kThreshWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = ((int64_t)blockIdx.x * kThreshWaves + wave) / WPR;
+  const int part = wave % WPR;   // this wave's share of the row
+  if (WPR == 1 && row >= rows) return;   // (WPR > 1: every wave reaches the barriers)
+  const int64_t rowc = row < rows ? row : rows - 1;
+  const int64_t t = q_pos0 + rowc % M;
   const int ns = (int)min((int64_t)n_sample, t / kstride + 1);   // sampled keys the query sees
   const uint64_t ks = (uint64_t)target * (uint64_t)ns / (uint64_t)(t + 1) + 2;
   float tf = -__builtin_inff();
-  if (ks < (uint64_t)ns) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(sample + row * ld_s);   // ld_s % 4 == 0
+  if (ks < (uint64_t)ns) {   // uniform over the row's waves
+    const f32x4* src = reinterpret_cast<const f32x4*>(sample + rowc * ld_s);   // ld_s % 4 == 0
     const int n4 = (ns + 3) / 4;
     uint32_t key[4 * L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-      const int f = j * 64 + lane;
+      const int f = (j * WPR + part) * 64 + lane;
       const f32x4 v = src[min(f, n4 - 1)];
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[4 * j + e] = (4 * f + e < ns) ? order_key(v[e]) : 0u;
@@ -1196,12 +1204,20 @@ __global__ void __launch_bounds__(64 * kThreshWaves) k_topk_sample_thresh(const 
       uint32_t cl = 0;
 #pragma unroll
       for (int j = 0; j < 4 * L; ++j) cl += (key[j] >= c) ? 1u : 0u;
-      if (__reduce_add_sync(~0ull, cl) >= (uint32_t)ks) T = c;
+      uint32_t tot = __reduce_add_sync(~0ull, cl);
+      if (WPR > 1) {
+        if (lane == 0) s_cnt[bit & 1][wave] = tot;
+        __syncthreads();
+        tot = 0;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) tot += s_cnt[bit & 1][wave - part + w];
+      }
+      if (tot >= (uint32_t)ks) T = c;
     }
     tf = key_to_float(T);
     if (tf != tf) tf = -__builtin_inff();
   }
-  if (lane == 0) {
+  if (row < rows && part == 0 && lane == 0) {
     thr[row] = tf;
     flag[row] = 0;
   }
@@ -1371,9 +1387,15 @@ __global__ void __launch_bounds__(NT, 2) k_topk_flagged(const float* __restrict_
 hipError_t launch_topk_sample_thresh(const misa_shape& s, const FusedPlan& p, const float* sample_logits,
                                      float* thr, uint32_t* row_flag, hipStream_t st) {
   const int64_t rows = (int64_t)s.n_seq * s.q_per_seq;
-  hipLaunchKernelGGL(k_topk_sample_thresh, dim3((unsigned)((rows + kThreshWaves - 1) / kThreshWaves)),
-                     dim3(64 * kThreshWaves), 0, st, sample_logits, p.ld_sample, (int)p.n_sample, p.kstride,
-                     p.target, s.q_pos0, s.q_per_seq, rows, thr, row_flag);
+  if (rows < 1024) {   // few rows (decode): a workgroup per row, so the chip is not left idle
+    hipLaunchKernelGGL(k_topk_sample_thresh<kThreshWaves>, dim3((unsigned)rows), dim3(64 * kThreshWaves), 0, st,
+                       sample_logits, p.ld_sample, (int)p.n_sample, p.kstride, p.target, s.q_pos0, s.q_per_seq, rows,
+                       thr, row_flag);
+  } else {
+    hipLaunchKernelGGL(k_topk_sample_thresh<1>, dim3((unsigned)((rows + kThreshWaves - 1) / kThreshWaves)),
+                       dim3(64 * kThreshWaves), 0, st, sample_logits, p.ld_sample, (int)p.n_sample, p.kstride,
+                       p.target, s.q_pos0, s.q_per_seq, rows, thr, row_flag);
+  }
   return hipGetLastError();
 }
 
