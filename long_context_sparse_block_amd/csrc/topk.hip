@@ -1408,7 +1408,13 @@ hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, c
   hipLaunchKernelGGL((k_topk_regions<CAP_, 512, IDX_>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0,       \
                      s.q_per_seq, p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, \
                      vals, (int)sorted)
-  if (p.cap_list <= 4096)
+  if (p.cap_list <= 4096 && (int64_t)s.n_seq * s.q_per_seq < 1024)
+    // few rows (decode): twice the threads per row, so each row's chain of
+    // gather, counting sort and ranks is shorter while most CUs are idle
+    hipLaunchKernelGGL((k_topk_regions<4096, 1024, true>), grid, dim3(1024), 0, st, s.n_keys, k, s.q_pos0,
+                       s.q_per_seq, p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx,
+                       vals, (int)sorted);
+  else if (p.cap_list <= 4096)
     MISA_REGIONS_LAUNCH(4096, true);
   else if (p.cap_list <= 8192)
     MISA_REGIONS_LAUNCH(8192, false);
