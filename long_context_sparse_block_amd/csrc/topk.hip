@@ -1280,10 +1280,14 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
   const uint32_t total = s_start[n_splits];
   float gmax = -__builtin_inff();
   for (uint32_t e0 = 0; e0 < total; e0 += U * NT) {
+    // slots past the last group are skipped by the whole workgroup (a row
+    // holds ~2,000 groups: 4 or 5 of the 8 slots of 512 threads)
+    const int nu = (int)min((uint32_t)U, (total - e0 + NT - 1) / NT);
     f32x4 v[U];
     int32_t key[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (u >= nu) break;   // uniform
       const uint32_t e = e0 + u * NT + tid;
       v[u] = f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
       key[u] = 0;
@@ -1302,6 +1306,7 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
     uint32_t fl = 0;   // bit 4u + j: element j of group u is a candidate
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (u >= nu) break;   // uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j) fl |= (uint32_t)(v[u][j] >= tf) << (4 * u + j);
       const float m01 = __builtin_fmaxf(v[u][0], v[u][1]), m23 = __builtin_fmaxf(v[u][2], v[u][3]);
@@ -1319,13 +1324,15 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
     if (lane == 0) wbase = atomicAdd(&sh.count, wtot);
     pos += __builtin_amdgcn_readfirstlane(wbase);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (u >= nu) break;   // uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (fl & (1u << (4 * u + j))) {
           if (pos < (uint32_t)CAP) sh.buf[pos] = pack_raw(v[u][j], key[u] + j);
           ++pos;
         }
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) gmax = __builtin_fmaxf(gmax, __shfl_xor(gmax, o));
