@@ -201,8 +201,14 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
 // keeps the MFMA accumulators in ordinary VGPRs.  Given room for more than 256
 // registers the compiler accumulates in AGPRs and copies every result out with
 // a v_accvgpr_read, 64 more VALU instructions per tile.
-template <int KDT, int MODE, bool DMA, bool PAGED = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PAGED && !DMA ? 2 : 3)))
+// NW: waves per workgroup (8 NW queries a query tile).  One wave (NW = 1)
+// serves calls with at most 8 queries per sequence (decode): there the key
+// stream is the whole cost, and four-wave workgroups would leave three waves
+// without queries while each workgroup holds one tile in flight; one-wave
+// workgroups take a quarter of the registers and the same LDS, so more of
+// them, and more tiles in flight, fit on a CU.
+template <int KDT, int MODE, bool DMA, bool PAGED = false, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PAGED && !DMA ? 2 : 3)))
 k_score_h8(const uint16_t* __restrict__ q,
            const float* __restrict__ w,
            const void* __restrict__ kptr,
@@ -210,7 +216,7 @@ k_score_h8(const uint16_t* __restrict__ q,
            const int32_t* __restrict__ heads, int h, ScoreOut out_spec,
            int64_t N64, int kstride, int64_t q_pos0_64, int M, int H,
            int n_qtiles, int n_ksplits, int64_t KR, KeyPages pages) {
-  constexpr int NT = 256, KT = kSwKT, QT = 32;
+  constexpr int NT = 64 * NW, KT = kSwKT, QT = 8 * NW;
   // B fragments read one column block ahead where the registers allow it
   // (16 more VGPRs; the other variants would drop to 2 waves per SIMD)
   constexpr bool kPrefetchB = MODE == kLogits && KDT == MISA_K_FP8_E4M3;
@@ -626,20 +632,21 @@ void plan_split(int64_t N, int n_seq, int n_qtiles, int KT, int* n_ksplits, int6
 
 // DMA: k holds bf16 keys (for kdtype fp8: the widened copy; k_scale still
 // applies), staged by direct loads into LDS
-template <int MODE, bool DMA = false, bool PAGED = false>
+template <int MODE, bool DMA = false, bool PAGED = false, int NW = 4>
 static hipError_t launch_h8(const misa_shape& s, const uint16_t* q, const float* w, const void* k, int kdtype,
                             const float* k_scale, const int32_t* heads, int h, const ScoreOut& o, int kstride,
                             int nks, int64_t KR, hipStream_t st, const KeyPages* pages = nullptr) {
   const int M = s.q_per_seq;
-  const int n_qtiles = (M + 31) / 32;
+  const int n_qtiles = (M + 8 * NW - 1) / (8 * NW);
   dim3 grid((unsigned)((int64_t)n_qtiles * nks), (unsigned)s.n_seq);
   if (o.slab_tiles > 0) grid = dim3((unsigned)((int64_t)o.slab_tiles * nks), 1);
   const KeyPages pg = pages != nullptr ? *pages : KeyPages{nullptr, 0, 0, 1};
   if (kdtype == MISA_K_BF16)
-    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE, DMA, PAGED>), grid, dim3(256), 0, st, q, w, k, k_scale,
+    hipLaunchKernelGGL((k_score_h8<MISA_K_BF16, MODE, DMA, PAGED, NW>), grid, dim3(64 * NW), 0, st, q, w, k, k_scale,
                        heads, h, o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR, pg);
   else
-    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE, DMA, PAGED>), grid, dim3(256), 0, st, q, w, k, k_scale,
+    hipLaunchKernelGGL((k_score_h8<MISA_K_FP8_E4M3, MODE, DMA, PAGED, NW>), grid, dim3(64 * NW), 0, st, q, w, k,
+                       k_scale,
                        heads, h, o, s.n_keys, kstride, s.q_pos0, M, s.n_heads, n_qtiles, nks, KR, pg);
   return hipGetLastError();
 }
@@ -727,7 +734,11 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   p.target = std::min((int)(k * (1.0 + margin)), (k + p.cap_list) / 2);
   int nks;
   int64_t KR;
-  plan_split(N, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR);
+  // with at most 8 queries per sequence (decode) the candidate pass runs
+  // one-wave workgroups, four per CU: 1024 of them are one resident round.
+  // Same-box, 64 sequences x 131072 bf16 keys: 333 -> 323 us (2048 of them:
+  // 2 rounds), 335 us at 4096, 348 us at 8192; paged keys 325 -> 318 us
+  plan_split(N, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR, s.q_per_seq <= 8 ? 1024 : 2048);
   p.n_splits = nks;
   p.key_range = KR;
   if (nks > kMaxRegionSplits) {
@@ -783,6 +794,18 @@ hipError_t launch_score_cands(const misa_shape& s, const uint16_t* q, const floa
   const ScoreOut o{nullptr, 0, thr, reinterpret_cast<f32x4*>(gvals), gkeys, rcount, p.cap_region, nullptr};
   const int nks = p.n_splits;
   const int64_t KR = p.key_range;
+  // at most 8 queries per sequence (decode): one-wave workgroups (one query
+  // tile per sequence either way).  Same-box, 64 sequences x 131072 bf16
+  // keys, against four-wave workgroups: 338 -> 334 us, paged keys 368 -> 325 us
+  if (s.q_per_seq <= 8) {
+    if (pages != nullptr) {
+      if (direct)
+        return launch_h8<kCands, true, true, 1>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
+      return launch_h8<kCands, false, true, 1>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
+    }
+    if (!direct) return launch_h8<kCands, false, false, 1>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
+    return launch_h8<kCands, true, false, 1>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st);
+  }
   if (pages != nullptr) {
     if (direct) return launch_h8<kCands, true, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
     return launch_h8<kCands, false, true>(s, q, w, k, kdtype, k_scale, heads, h, o, 1, nks, KR, st, pages);
