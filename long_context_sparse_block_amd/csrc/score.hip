@@ -208,7 +208,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* kbase, const float* sba
 // workgroups take a quarter of the registers and the same LDS, so more of
 // them, and more tiles in flight, fit on a CU.
 template <int KDT, int MODE, bool DMA, bool PAGED = false, int NW = 4>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PAGED && !DMA ? 2 : 3)))
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1 ? 1 : (PAGED && !DMA ? 2 : 3))))
 k_score_h8(const uint16_t* __restrict__ q,
            const float* __restrict__ w,
            const void* __restrict__ kptr,
@@ -779,8 +779,18 @@ hipError_t launch_score_sampled(const misa_shape& s, const uint16_t* q, const fl
   // (head ids, then weights and q rows, the first tile) weighs more.
   // Same-box: 82 -> 76 us for the 8192 x 131072 chunk, 31 -> 23 us for 64
   // decode rows (2048 workgroups before)
-  plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR, 768);
   const ScoreOut o{sample_logits, p.ld_sample, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+  // at most 8 queries per sequence (decode), contiguous keys: one-wave
+  // workgroups, 512 of them (same-box, 64 sequences x 131072 keys: 22.7 ->
+  // 19.7 us; 2048 of them 23.2 us).  Paged keys keep four-wave workgroups:
+  // their per-key block-table lookups ran 42 -> 95 us in one-wave ones
+  if (s.q_per_seq <= 8 && pages == nullptr) {
+    plan_split(p.n_sample, s.n_seq, 1, 64, &nks, &KR, 512);
+    if (!direct)
+      return launch_h8<kLogits, false, false, 1>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
+    return launch_h8<kLogits, true, false, 1>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
+  }
+  plan_split(p.n_sample, s.n_seq, (s.q_per_seq + 31) / 32, 64, &nks, &KR, 768);
   if (pages != nullptr)   // the sampled keys' rows are looked up one by one: staged through registers
     return launch_h8<kLogits, false, true>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st, pages);
   if (!direct) return launch_h8<kLogits, false>(s, q, w, k, kdtype, k_scale, heads, h, o, p.kstride, nks, KR, st);
@@ -821,7 +831,10 @@ hipError_t launch_score_rescore(const misa_shape& s, const uint16_t* q, const fl
   int nks;
   int64_t KR;
   const int n_qtiles = (s.q_per_seq + 31) / 32;
-  plan_split(s.n_keys, s.n_seq, n_qtiles, 64, &nks, &KR);   // the candidate pass's key ranges
+  // any key split gives the same logits rows; with few queries per sequence
+  // (decode) a small grid, since the workgroups of unflagged rows only check
+  // their flags and leave (8.6 -> 8.2 us at 64 decode rows)
+  plan_split(s.n_keys, s.n_seq, n_qtiles, 64, &nks, &KR, s.q_per_seq <= 8 ? 256 : 2048);
   ScoreOut o{slab, ld, nullptr, nullptr, nullptr, nullptr, 0, row_flag};
   o.slab_tiles = sb.tiles;
   o.slab_first = (int)sb.first;
