@@ -353,6 +353,10 @@ FUSED_CASES = [
     # indexer's router splits each block sum into 4 parts (the last ragged) and a finishing pass
     dict(name="fused_split_router_h64", n_seq=2, m=5, n=40000, hh=64, b=64, h=8, k=2048,
          kdtype=gen.KDTYPE_FP8),
+    # the edge of the few-query passes: 8 queries per sequence still run one-wave workgroups (every
+    # lane row of the wave holds a query), 9 the four-wave ones
+    dict(name="fused_8q", n_seq=2, m=8, n=40000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_BF16),
+    dict(name="fused_9q_fp8", n_seq=2, m=9, n=40000, hh=32, b=64, h=8, k=2048, kdtype=gen.KDTYPE_FP8),
 ]
 
 
