@@ -724,9 +724,12 @@ FusedPlan plan_fused(const misa_shape& s, int h, int k) {
   p.kstride = (int)std::max<int64_t>(32, (N + 4095) / 4096);   // <= 4096 sampled keys per row
   p.n_sample = (N + p.kstride - 1) / p.kstride;
   p.ld_sample = (p.n_sample + 3) / 4 * 4;
-  // the region select's list capacity (its LDS variant: 4096 in the compact
-  // one that fits three workgroups per CU)
-  p.cap_list = k <= 2048 ? 4096 : (k <= 4096 ? 8192 : 16384);
+  // the region select's list capacity (its LDS variant: 4608 in the compact
+  // one that fits three workgroups per CU, 4096 in its few-row variant).  A
+  // row with more candidates is re-scored whole: at k = 2048 the list holds
+  // 1.5 times the target (4096 held 1.33 times, and 4 of the 8192 rows of a
+  // 32K-key chunk overflowed it, each costing the slow path about 0.15 ms)
+  p.cap_list = k <= 2048 ? 4608 : (k <= 4096 ? 8192 : 16384);
   // candidates aimed for: k plus a margin of 4 standard deviations of the
   // sampled threshold's error (about k / kstride sampled keys lie above it,
   // relative spread 1/sqrt of that), at most k/2

@@ -444,11 +444,13 @@ struct TopkSharedIdx {
 // max composite: each thread holds its entries' composites in registers, the
 // counting sort scatters them back into sh.buf (now bucket-sorted
 // composites), and each candidate's rank inside its bucket is found by
-// comparing with the bucket's other entries.
+// comparing with the bucket's other entries.  Returns false, writing nothing,
+// for a list of more than 8 NT entries with a crowded bucket (the bitonic
+// fallback holds 8 entries per thread): the caller flags the row.
 template <int CAP, int NT>
-__device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
+__device__ __forceinline__ bool rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
                                                int32_t* idx_out, float* val_out, uint32_t kmin, uint32_t kmax) {
-  static_assert(CAP <= 8 * NT, "the bitonic fallback holds 8 entries per thread");
+  static_assert(CAP % NT == 0, "whole entries per thread");
   constexpr int EPT = CAP / NT;   // entries per thread
   const int tid = threadIdx.x;
   constexpr int HB = kHistBinsIdx;   // finer buckets than rank_write: fewer in-bucket comparisons
@@ -474,6 +476,7 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
     uint32_t total;
     uint32_t start = block_exclusive_scan<NT>(ls, sh.wave, &total);
     const uint32_t n_big = __syncthreads_or(big > kMaxRankBucket);
+    if (n_big && cnt > 8u * NT) return false;   // uniform over the workgroup
     if (n_big) {
       if (cnt <= (uint32_t)NT) bitonic_write<NT, 1>(sh.buf, cnt, k, row, idx_out, val_out);
       else if (cnt <= 2u * NT) bitonic_write<NT, 2>(sh.buf, cnt, k, row, idx_out, val_out);
@@ -515,6 +518,7 @@ __device__ __forceinline__ void rank_write_idx(TopkSharedIdx<CAP, NT>& sh, uint3
     idx_out[row * k + p] = -1;
     if (val_out) val_out[row * k + p] = -__builtin_inff();
   }
+  return true;
 }
 
 template <int CAP, int NT>
@@ -947,15 +951,14 @@ __device__ __forceinline__ void finish_list(TopkShared<CAP, NT>& sh, uint32_t cn
 
 // finish_list for the compact LDS: sorted output ranks every candidate;
 // the set alone is an exact select to k and a compaction.
+// Returns false when the list could not be ranked (see rank_write_idx).
 template <int CAP, int NT>
-__device__ __forceinline__ void finish_list_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
+__device__ __forceinline__ bool finish_list_idx(TopkSharedIdx<CAP, NT>& sh, uint32_t cnt, int k, int64_t row,
                                                 int32_t* __restrict__ idx_out, float* __restrict__ val_out,
                                                 int sorted, uint32_t kmin, uint32_t kmax) {
-  if (sorted) {
-    rank_write_idx<CAP, NT>(sh, cnt, k, row, idx_out, val_out, kmin, kmax);
-    return;
-  }
+  if (sorted) return rank_write_idx<CAP, NT>(sh, cnt, k, row, idx_out, val_out, kmin, kmax);
   write_set<NT>(sh.buf, cnt, k, row, idx_out, val_out, sh.hist, sh.wave, sh.sel, sh.red, false, 0, 0);
+  return true;
 }
 
 // Exact top-k of a row's candidate list (every element at or above the row's
@@ -1237,7 +1240,12 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
                                                         uint32_t* __restrict__ flag, int32_t* __restrict__ idx_out,
                                                         float* __restrict__ val_out, int sorted) {
   __shared__ std::conditional_t<IDX, TopkSharedIdx<CAP, NT>, TopkShared<CAP, NT>> sh;
-  __shared__ uint32_t s_start[kMaxRegionSplits + 1];   // first flat group of each region
+  // first flat group of each region.  The compact variant keeps it in the
+  // rank histogram, which is not used before the gather has finished: the
+  // 4 KB go to the candidate list instead
+  __shared__ uint32_t s_start_own[IDX ? 1 : kMaxRegionSplits + 1];
+  static_assert(!IDX || kHistBinsIdx >= kMaxRegionSplits + 1, "the region starts fit in the histogram");
+  uint32_t* const s_start = IDX ? sh.hist : s_start_own;
   __shared__ uint32_t s_bad;
   const int tid = threadIdx.x, lane = tid & 63;
   const int i = blockIdx.x, b = blockIdx.y;
@@ -1345,9 +1353,11 @@ __global__ void __launch_bounds__(NT) k_topk_regions(int64_t n_keys, int k, int6
   }
   for (int wv = 0; wv < NT / 64; ++wv) gmax = __builtin_fmaxf(gmax, __uint_as_float((uint32_t)sh.red[wv]));
   __syncthreads();   // sh.red is reused by the select
-  if constexpr (IDX)
-    finish_list_idx<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, order_key(tf), order_key(gmax));
-  else
+  if constexpr (IDX) {
+    if (!finish_list_idx<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted, order_key(tf), order_key(gmax)) &&
+        tid == 0)
+      flag[row] = 1;
+  } else
     finish_list<CAP, NT>(sh, tot, k, row, idx_out, val_out, sorted);
 }
 
@@ -1415,14 +1425,14 @@ hipError_t launch_topk_regions(const misa_shape& s, const FusedPlan& p, int k, c
   hipLaunchKernelGGL((k_topk_regions<CAP_, 512, IDX_>), grid, dim3(512), 0, st, s.n_keys, k, s.q_pos0,       \
                      s.q_per_seq, p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx, \
                      vals, (int)sorted)
-  if (p.cap_list <= 4096 && (int64_t)s.n_seq * s.q_per_seq < 1024)
+  if (p.cap_list <= 4608 && (int64_t)s.n_seq * s.q_per_seq < 1024)
     // few rows (decode): twice the threads per row, so each row's chain of
     // gather, counting sort and ranks is shorter while most CUs are idle
     hipLaunchKernelGGL((k_topk_regions<4096, 1024, true>), grid, dim3(1024), 0, st, s.n_keys, k, s.q_pos0,
                        s.q_per_seq, p.n_splits, p.cap_region, p.cap_list, thr, gv, gkeys, rcount, row_flag, idx,
                        vals, (int)sorted);
-  else if (p.cap_list <= 4096)
-    MISA_REGIONS_LAUNCH(4096, true);
+  else if (p.cap_list <= 4608)
+    MISA_REGIONS_LAUNCH(4608, true);
   else if (p.cap_list <= 8192)
     MISA_REGIONS_LAUNCH(8192, false);
   else {
