@@ -431,6 +431,39 @@ def test_fused_indexer_rows_the_sample_misjudges():
     _check_sparse_head_topk(inp, st)
 
 
+def test_fused_select_tied_list_past_4096():
+    """4,400 keys of every query's prefix share one key vector far above the
+    others, so in every row they tie on one score: the sampled threshold (about
+    one sample in nine is a tied key) admits exactly them, a list of more than
+    4096 and at most 4608 entries in one rank bucket.  The compact list ranks a
+    crowded bucket only up to 4096 entries, so each row must be flagged and
+    selected from full logits; ties go to the lower token id."""
+    say("fused select: tied list past 4096")
+    cfg = gen.small_config(name="fused_tied", m=1024, n=40000, hh=16, b=64, h=8, k=2048, seed=47, plant=False)
+    inp = gen.generate(cfg)
+    q = oracle.bf16_bits_to_f64(inp.q).astype(np.float32)
+    kf = oracle.bf16_bits_to_f64(inp.k).astype(np.float32)
+    u = np.ones(128, np.float32) / np.sqrt(128.0)
+    q += 4.0 * u
+    tied = np.random.default_rng(48).choice(inp.q_pos0 - 500, size=4400, replace=False)
+    kf[:, tied, :] = 40.0 * u
+    inp.q[...] = gen.to_bf16_bits(q)
+    inp.k[...] = gen.to_bf16_bits(kf)
+    inp.w[...] = np.abs(inp.w)
+    st = run_stages(inp)
+    sh, t = st["sh"], st["t"]
+    idx, vals = lcsb.misa_sparse_head_topk(sh, t["q"], t["w"], t["k"], st["heads"], cfg.topk)
+    sidx, svals = lcsb.misa_topk(sh, st["logits"], cfg.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sidx) and torch.equal(vals, svals)
+    # every row's top-k: the 2048 lowest tied ids, all at one value
+    gi = idx.cpu().numpy()[0]
+    lowest = np.sort(tied)[:cfg.topk]
+    for i in sample_rows(cfg.q_per_seq, 16):
+        assert np.array_equal(gi[i], lowest), f"query {i}"
+    check_topk_exact(inp, st["logits"], cfg.topk, idx, vals)
+
+
 def _threshold_defeated(inp):
     """Every key at a multiple of the sampling stride (32) gets a huge score,
     so the sampled threshold admits far fewer than k candidates: every row is
